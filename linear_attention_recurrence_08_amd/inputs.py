@@ -1,0 +1,212 @@
+"""Seeded synthetic KDA workloads.
+
+This module only draws random inputs; it holds none of the recurrence's arithmetic.  It is the one
+piece shared by the CPU oracle's tests and the GPU path's tests and benchmark, so both sides see the
+exact same numbers: every tensor is drawn in float32 with numpy's PCG64, prepared (L2 norm of q and
+k, sigmoid for beta, the gate recipe for g = log alpha), then rounded once to the dtype the GPU
+receives.  The oracle upcasts those rounded values to float64.
+
+Shapes follow the K3 KDA layer described in "Kimi K3's hybrid block, from first principles"
+(section "From linear attention to the delta rule", paragraph "What the state costs"): 96 heads,
+a 128 x 128 state per head.  Layouts are token-major and packed:
+
+    q, k, g : [Ttot, H, dk]      v, o : [Ttot, H, dv]      beta : [Ttot, H]
+    h0, hT  : [N, H, dk, dv] float32 (N sequences)
+
+with Ttot = B * T for equal-length batches, or the sum of the sequence lengths for a packed
+variable-length batch described by cu_seqlens (int32 [N + 1]).
+
+Draw order, fixed for reproducibility: the sequence lengths (variable-length batches only); then,
+for each block of BLOCK_TOKENS packed tokens, q, k, v, the beta logits and the gate noise; then the
+initial states sequence by sequence.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+BLOCK_TOKENS = 8192  # token block of the draw order (bounds host memory for long sequences)
+
+GATE_RECIPES = ("sigmoid", "sigmoid_shift1", "sigmoid_shiftm1", "bimodal", "zero")
+
+
+@dataclasses.dataclass
+class KDAInputs:
+    """One synthetic batch, as host tensors in the dtype the GPU receives."""
+
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    beta: torch.Tensor
+    h0: Optional[torch.Tensor]
+    cu_seqlens: Optional[torch.Tensor]  # int32 [N+1] or None (equal lengths)
+    B: int
+    T: int  # per-sequence length when cu_seqlens is None, else the packed total
+    H: int
+    dk: int
+    dv: int
+    dtype: str  # "bf16" | "f32"
+    name: str = ""
+
+    @property
+    def num_seqs(self) -> int:
+        return self.B if self.cu_seqlens is None else int(self.cu_seqlens.numel() - 1)
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    def seq_bounds(self):
+        """(start, end) token indices of every sequence in the packed layout."""
+        if self.cu_seqlens is None:
+            return [(b * self.T, (b + 1) * self.T) for b in range(self.B)]
+        cu = self.cu_seqlens.tolist()
+        return [(cu[i], cu[i + 1]) for i in range(len(cu) - 1)]
+
+    def to(self, device) -> "KDAInputs":
+        f = lambda t: None if t is None else t.to(device)
+        return dataclasses.replace(
+            self, q=f(self.q), k=f(self.k), v=f(self.v), g=f(self.g), beta=f(self.beta),
+            h0=f(self.h0), cu_seqlens=f(self.cu_seqlens))
+
+
+def _torch_dtype(dtype: str):
+    if dtype == "bf16":
+        return torch.bfloat16
+    if dtype == "f32":
+        return torch.float32
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return (1.0 / (1.0 + np.exp(-x))).astype(np.float32)
+
+
+def _l2_normalise(x: np.ndarray) -> np.ndarray:
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32))
+    return (x / np.maximum(n, np.float32(1e-30))).astype(np.float32)
+
+
+def _gate(z: np.ndarray, recipe: str) -> np.ndarray:
+    """g = log(alpha) from standard-normal noise z, per the workload recipe; values in [-5, 0]."""
+    if recipe == "sigmoid":          # -5 * sigmoid(N(0,1))
+        return (-5.0 * _sigmoid(z)).astype(np.float32)
+    if recipe == "sigmoid_shift1":   # -5 * sigmoid(N(1,1)), as the varlen workload states it
+        return (-5.0 * _sigmoid(z + 1.0)).astype(np.float32)
+    if recipe == "sigmoid_shiftm1":  # -5 * sigmoid(N(-1,1)): slower decay, long carries
+        return (-5.0 * _sigmoid(z - 1.0)).astype(np.float32)
+    if recipe == "bimodal":          # half the key channels slow (-0.005), half fast (-4.5)
+        dk = z.shape[-1]
+        centre = np.where(np.arange(dk) < dk // 2, np.float32(-0.005), np.float32(-4.5))
+        return np.clip(centre + np.float32(0.01) * z, -5.0, 0.0).astype(np.float32)
+    if recipe == "zero":             # alpha = 1 everywhere
+        return np.zeros_like(z, dtype=np.float32)
+    raise ValueError(f"unknown gate recipe {recipe!r}")
+
+
+def make_inputs(seq_lens: Sequence[int], H: int, dk: int, dv: int, dtype: str, seed: int,
+                gate: str = "sigmoid", h0_sigma: Optional[float] = None,
+                packed: Optional[bool] = None, name: str = "") -> KDAInputs:
+    """Draw one batch.
+
+    seq_lens: the sequence lengths.  With packed=False (default when all lengths are equal) the
+    batch is B equal-length sequences without cu_seqlens; otherwise it is one packed batch with
+    cu_seqlens.  h0_sigma None means h0 = zeros (passed as None).
+    """
+    seq_lens = [int(s) for s in seq_lens]
+    if packed is None:
+        packed = len(set(seq_lens)) > 1
+    if not packed and len(set(seq_lens)) > 1:
+        raise ValueError("unequal lengths need packed=True")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    tdt = _torch_dtype(dtype)
+    ttot = int(sum(seq_lens))
+    q = torch.empty((ttot, H, dk), dtype=tdt)
+    k = torch.empty((ttot, H, dk), dtype=tdt)
+    v = torch.empty((ttot, H, dv), dtype=tdt)
+    g = torch.empty((ttot, H, dk), dtype=tdt)
+    beta = torch.empty((ttot, H), dtype=tdt)
+    for t0 in range(0, ttot, BLOCK_TOKENS):
+        n = min(BLOCK_TOKENS, ttot - t0)
+        qb = rng.standard_normal((n, H, dk), dtype=np.float32)
+        kb = rng.standard_normal((n, H, dk), dtype=np.float32)
+        vb = rng.standard_normal((n, H, dv), dtype=np.float32)
+        bb = rng.standard_normal((n, H), dtype=np.float32)
+        zb = rng.standard_normal((n, H, dk), dtype=np.float32)
+        q[t0:t0 + n] = torch.from_numpy(_l2_normalise(qb)).to(tdt)
+        k[t0:t0 + n] = torch.from_numpy(_l2_normalise(kb)).to(tdt)
+        v[t0:t0 + n] = torch.from_numpy(vb).to(tdt)
+        beta[t0:t0 + n] = torch.from_numpy(_sigmoid(bb)).to(tdt)
+        g[t0:t0 + n] = torch.from_numpy(_gate(zb, gate)).to(tdt)
+    N = len(seq_lens)
+    h0 = None
+    if h0_sigma is not None:
+        h0 = torch.empty((N, H, dk, dv), dtype=torch.float32)
+        for i in range(N):
+            h0[i] = torch.from_numpy(
+                rng.standard_normal((H, dk, dv), dtype=np.float32) * np.float32(h0_sigma))
+    if packed:
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(seq_lens)]), dtype=torch.int32)
+        return KDAInputs(q, k, v, g, beta, h0, cu, 1, ttot, H, dk, dv, dtype, name)
+    B = N
+    T = seq_lens[0] if N else 0
+    return KDAInputs(q, k, v, g, beta, h0, None, B, T, H, dk, dv, dtype, name)
+
+
+def varlen_lengths(seed: int, n: int = 16, lo: int = 1024, hi: int = 16384):
+    """Sequence lengths uniform on [lo, hi] (inclusive), drawn first from the workload's stream."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(lo, hi, size=n, endpoint=True).tolist(), rng
+
+
+# Named workloads.  Index = seed.
+WORKLOADS = {
+    # tiny fp32 forward: B=1, H=2, T=64, dk=dv=32, h0 = 0
+    "tiny_T64_H2_d32_f32": dict(kind="prefill", seq_lens=[64], H=2, dk=32, dv=32, dtype="f32",
+                                seed=0, gate="sigmoid", h0_sigma=None),
+    # one K3 KDA layer, prefill: B=1, T=4096, H=96, d=128, bf16, h0 = 0
+    "prefill_T4096_H96_d128_bf16": dict(kind="prefill", seq_lens=[4096], H=96, dk=128, dv=128,
+                                        dtype="bf16", seed=1, gate="sigmoid", h0_sigma=None),
+    # packed variable-length prefill: 16 sequences of U[1024, 16384] tokens, h0 ~ N(0, 0.02)
+    "varlen_16seq_H96_d128_bf16": dict(kind="varlen", n_seqs=16, H=96, dk=128, dv=128,
+                                       dtype="bf16", seed=2, gate="sigmoid_shift1",
+                                       h0_sigma=0.02),
+    # long-context prefill: B=1, T=131072, bimodal per-channel decay
+    "long_T131072_H96_d128_bf16": dict(kind="prefill", seq_lens=[131072], H=96, dk=128, dv=128,
+                                       dtype="bf16", seed=3, gate="bimodal", h0_sigma=None),
+    # batched decode: 256 sequences x 1 token, S ~ N(0, 0.05) read and written in place
+    "decode_N256_H96_d128_bf16": dict(kind="decode", N=256, H=96, dk=128, dv=128, dtype="bf16",
+                                      seed=4, gate="sigmoid", s_sigma=0.05),
+}
+
+
+def make_workload(name: str, gate: Optional[str] = None) -> KDAInputs:
+    """Build a named workload on the host.  gate overrides the gate recipe (parity variants)."""
+    w = dict(WORKLOADS[name])
+    gate = gate or w["gate"]
+    kind = w["kind"]
+    if kind == "prefill":
+        return make_inputs(w["seq_lens"], w["H"], w["dk"], w["dv"], w["dtype"], w["seed"],
+                           gate=gate, h0_sigma=w["h0_sigma"], packed=False, name=name)
+    if kind == "varlen":
+        # lengths are the first draw of the workload's stream; the rest continues from a seed
+        # derived from it so the token draws do not depend on how many lengths were drawn
+        lens, _ = varlen_lengths(w["seed"], w["n_seqs"])
+        return make_inputs(lens, w["H"], w["dk"], w["dv"], w["dtype"], w["seed"] * 1000 + 1,
+                           gate=gate, h0_sigma=w["h0_sigma"], packed=True, name=name)
+    if kind == "decode":
+        return make_decode_inputs(w["N"], w["H"], w["dk"], w["dv"], w["dtype"], w["seed"],
+                                  gate=gate, s_sigma=w["s_sigma"], name=name)
+    raise ValueError(kind)
+
+
+def make_decode_inputs(N: int, H: int, dk: int, dv: int, dtype: str, seed: int,
+                       gate: str = "sigmoid", s_sigma: float = 0.05, name: str = "") -> KDAInputs:
+    """One token for each of N sequences plus their float32 states S [N, H, dk, dv] (in h0)."""
+    inp = make_inputs([1] * N, H, dk, dv, dtype, seed, gate=gate, h0_sigma=s_sigma,
+                      packed=False, name=name)
+    return inp
