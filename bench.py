@@ -1,0 +1,257 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Prints ONE JSON line.  `value` is prefill throughput in tokens/s on the one-layer K3 KDA prefill
+(B=1, T=4096, H=96, dk=dv=128, bf16 inputs, float32 state, 16-token tiles), inputs resident in HBM
+before the timed region.  A `decode` object reports the batched single-token decode step
+(256 sequences, H=96, float32 states read and written in place) the same way.
+
+Roofline: algorithmic bytes per launch divided by the kernel's average duration, measured with
+HIP events recorded on the stream the kernels are launched on, against MI355X's 8 TB/s HBM.
+  prefill bytes / (token, head) = q, k, g (3 x 256) + v (256) + o (256) + beta (2) = 1282 B,
+                                  plus 64 KiB per (sequence, head) for each of h0 (when given)
+                                  and hT;
+  prefill flops / (token, head) = 6 dk dv + d (5C - 1) = 108,416 at d = 128, C = 16;
+  decode bytes / (sequence, head) = 2 x 65,536 (state in and out) + 4 x 256 (q, k, v, g)
+                                    + 256 (o) + 2 (beta) = 132,354 B.
+`cpu_baseline` times the float64 CPU oracle on the host cores on a bounded sample of the same
+workload (rank 0, N = 1).  `traffic` is the HBM traffic per launch from rocprofv3 FETCH_SIZE +
+WRITE_SIZE counters recorded in profiles/, used only while the kernel sources are unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2516.6   # MI355X dense bf16 matrix peak (256 CU x 4096 flop/clk x 2.4 GHz)
+CHUNK = 16
+
+PREFILL_WORKLOADS = ("prefill_T4096_H96_d128_bf16", "varlen_16seq_H96_d128_bf16",
+                     "long_T131072_H96_d128_bf16", "tiny_T64_H2_d32_f32")
+DECODE_WORKLOAD = "decode_N256_H96_d128_bf16"
+
+
+def _esize(dtype):
+    return 2 if dtype == "bf16" else 4
+
+
+def prefill_bytes(x) -> int:
+    es = _esize(x.dtype)
+    per_tok_head = (3 * x.dk + 2 * x.dv) * es + es
+    state = x.dk * x.dv * 4
+    n_states = x.num_seqs * x.H * (2 if x.h0 is not None else 1)
+    return x.total_tokens * x.H * per_tok_head + n_states * state
+
+
+def prefill_flops(x) -> int:
+    d = x.dk
+    return x.total_tokens * x.H * (6 * x.dk * x.dv + d * (5 * CHUNK - 1))
+
+
+def decode_bytes(d) -> int:
+    es = _esize(d.dtype)
+    per = 2 * d.dk * d.dv * 4 + (3 * d.dk + 2 * d.dv) * es + es
+    return d.B * d.H * per
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources and the public header: identifies the kernels measured."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_recurrence_08_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel_tag: str):
+    """HBM bytes per launch from the committed counter summary for this kernel, if its recorded
+    source digest matches the current sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_d = re.search(r"source_digest:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_d or not m_b or m_d.group(1) != kernel_source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def time_launches(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return start.elapsed_time(end) / steps, wall  # ms per launch (one kernel per step), seconds
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_T4096_H96_d128_bf16",
+                    choices=PREFILL_WORKLOADS)
+    ap.add_argument("--decode-steps", type=int, default=None)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(heads and sequences would shard across GPUs with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd, kda_decode_step
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- prefill ----------------
+    x = inputs.make_workload(args.workload)
+    xd = x.to(dev)
+    args_views = xd.call_views()
+    o = torch.empty_like(args_views[2])
+    hT = torch.empty((x.num_seqs, x.H, x.dk, x.dv), dtype=torch.float32, device=dev)
+    print(f"[bench] prefill {args.workload}: Ttot={x.total_tokens} H={x.H} warmup={args.warmup} "
+          f"steps={args.steps}", file=sys.stderr, flush=True)
+
+    def prefill():
+        kda_chunk_fwd(*args_views, h0=xd.h0, cu_seqlens=xd.cu_seqlens, o=o, hT=hT)
+
+    ms, wall = time_launches(prefill, args.steps, args.warmup, stream)
+    tokens = x.total_tokens
+    value = tokens / (ms * 1e-3)
+    nbytes = prefill_bytes(x)
+    flops = prefill_flops(x)
+    achieved_gbs = nbytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    traffic = recorded_traffic("kda_chunk_fwd_" + args.workload)
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+        "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "kernel": "kda_prefill_mfma" if (x.dtype == "bf16" and x.dk == 128 and x.dv == 128)
+        else "kda_prefill_general",
+        "algorithmic_bytes_per_launch": nbytes,
+        "algorithmic_flops_per_launch": flops,
+        "kernel_ms": round(ms, 5),
+        "mfma_bf16_tflops": round(tflops, 2),
+        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFS, 4),
+        # fraction of the attainable roofline: the faster of the HBM and matrix-core bounds
+        "attainable_frac": round(max(nbytes / (HBM_PEAK_GBS * 1e9),
+                                     flops / (MFMA_BF16_PEAK_TFS * 1e12)) / (ms * 1e-3), 4),
+        "source_digest": kernel_source_digest(),
+    }
+
+    result = {
+        "metric": "KDA prefill tokens/s & decode tokens/s (H=96,d=128), % of MFMA/HBM roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": x.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": x.B, "T": x.T, "H": x.H, "dk": x.dk,
+                   "dv": x.dv, "chunk": CHUNK, "num_seqs": x.num_seqs,
+                   "total_tokens": tokens, "state": "f32"},
+        "roofline": roofline,
+        "wall_s_timed": round(wall, 4),
+    }
+
+    # ---------------- decode ----------------
+    if not args.no_decode:
+        d = inputs.make_workload(DECODE_WORKLOAD)
+        qd, kd, vd, gd, bd = (t.to(dev) for t in (d.q, d.k, d.v, d.g, d.beta))
+        S = d.h0.to(dev)
+        od = torch.empty_like(vd)
+        del d
+        ksteps = args.decode_steps or args.steps
+        print(f"[bench] decode {DECODE_WORKLOAD}: N=256 H=96 steps={ksteps}", file=sys.stderr,
+              flush=True)
+
+        def decode():
+            kda_decode_step(qd, kd, vd, gd, bd, S, o=od)
+
+        dms, _ = time_launches(decode, ksteps, args.warmup, stream)
+        dbytes = 256 * 96 * (2 * 128 * 128 * 4 + 5 * 128 * 2 + 2)
+        dgbs = dbytes / (dms * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": DECODE_WORKLOAD, "value": round(256 / (dms * 1e-3), 1),
+            "unit": "tokens/s", "ms_per_step": round(dms, 5),
+            "roofline": {"bound": "hbm", "achieved": round(dgbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(dgbs / HBM_PEAK_GBS, 4),
+                         "traffic": recorded_traffic("kda_decode_" + DECODE_WORKLOAD),
+                         "kernel": "kda_decode_d128", "algorithmic_bytes_per_launch": dbytes},
+        }
+        del qd, kd, vd, gd, bd, S, od
+        torch.cuda.empty_cache()
+
+    # ---------------- CPU baseline: the float64 oracle on the host cores ----------------
+    if not args.no_cpu_baseline and x.num_seqs >= 1:
+        import oracle
+        oracle.build(force=False)
+        to64 = lambda t: t.detach().cpu().double().numpy()
+        # bounded sample: the first sequence, heads [0, nh) (all 96 heads of the 4096-token
+        # prefill is ~30 s of single-core work)
+        nh = min(x.H, 96)
+        a, e = x.seq_bounds()[0]
+        e = min(e, a + 4096)
+        sl = slice(a, e)
+        h0 = None if x.h0 is None else to64(x.h0[0:1, :nh])
+        cores = oracle.default_threads()
+        print(f"[bench] cpu baseline: oracle on tokens [{a},{e}) x {nh} heads, {cores} threads",
+              file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        o_ref, _ = oracle.recurrence(to64(x.q[sl, :nh]), to64(x.k[sl, :nh]), to64(x.v[sl, :nh]),
+                                     to64(x.g[sl, :nh]), to64(x.beta[sl, :nh]), h0,
+                                     [0, e - a], nthreads=cores)
+        cpu_s = time.perf_counter() - t0
+        toks = e - a
+        cpu_value = toks * nh / x.H / cpu_s  # tokens/s of full-width (all-head) layers
+        result["cpu_baseline"] = {
+            "value": round(cpu_value, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{args.workload}: sequence 0 tokens [{a},{e}), heads 0..{nh - 1} of "
+                      f"{x.H}; float64 token loop; {cpu_s:.2f} s wall",
+        }
+        if x.h0 is None and a == 0 and e == x.seq_bounds()[0][1]:
+            o_gpu = to64(o.reshape(x.total_tokens, x.H, x.dv)[sl, :nh])
+            result["parity_sample"] = {
+                "max_norm_err_o": float(np.abs(o_gpu - o_ref).max() / np.abs(o_ref).max()),
+                "heads": nh, "tokens": toks}
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

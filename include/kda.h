@@ -1,0 +1,127 @@
+/*
+ * kda.h -- C ABI of the KDA (Kimi Delta Attention) token mixer for AMD MI355X (gfx950).
+ *
+ * The operation.  KDA is a gated delta rule with one retention factor per key channel.  For each
+ * sequence and head the state S is a dk x dv matrix ("Kimi K3's hybrid block, from first
+ * principles", section "From linear attention to the delta rule": the state is dk x dv and the
+ * same size at every token; K3 uses dk = dv = 128 and 96 heads, paragraph "What the state
+ * costs").  Token by token, with alpha_t = exp(g_t) in (0,1]^dk:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,     o_t = S_t^T q_t
+ *
+ * i.e. fade every key channel by its own factor, then remove what the memory returns for k_t and
+ * write v_t (a gradient step of size beta_t on 1/2 |S^T k_t - v_t|^2), then read the updated
+ * state with q_t ("Kimi K3, explained", section "Kimi Delta Attention: making the radical option
+ * work": fade, remove, write; q reads the updated S(t); "What's new in Kimi K3", section "KDA in
+ * one page": the forget gate sits in front of the erase).  No query scaling is applied.
+ *
+ * Number formats.  q, k, v, g, beta and o are all bfloat16 (KDA_BF16) or all float32 (KDA_F32);
+ * states (h0, hT, S) are always float32; arithmetic is float32 (bf16 matrix-core products with
+ * float32 accumulation on the bf16 path).
+ *
+ * Layouts.  Row-major, contiguous, token-major ("packed"):
+ *     q, k, g : [Ttot, H, dk]     v, o : [Ttot, H, dv]     beta : [Ttot, H]
+ *     h0, hT, S : [N, H, dk, dv]  (float32; S row r = key channel r)
+ * Ttot = B * T for B equal-length sequences (cu_seqlens == NULL; sequence b owns tokens
+ * b*T .. b*T+T-1) or the packed total for a variable-length batch (cu_seqlens != NULL, B == 1).
+ *
+ * Preconditions (documented, not checked unless the environment variable KDA_VALIDATE=1 is set
+ * when the call is made): g in [-5, 0] -- the pages' bounded log-decay ("Kimi K3", section
+ * "Forgetting different features at different rates": retention never falls below e^-5, which
+ * keeps the tile rescaling factors of the chunked algorithm finite); cu_seqlens non-decreasing
+ * with cu[0] = 0 and cu[N] = Ttot.  q and k are expected L2-normalised upstream but the result is
+ * defined for any values.  NaN/Inf inputs propagate; they are not checked.
+ *
+ * Ownership and streams.  The caller owns every buffer (device memory, e.g. allocated by PyTorch)
+ * and passes a HIP stream (hipStream_t as void*, NULL = the null stream).  The library allocates
+ * nothing, keeps no state between calls and is thread-safe.  Calls are asynchronous: the return
+ * status reports argument errors and launch failures; execution faults surface at the caller's
+ * next synchronisation of the stream.
+ *
+ * Supported sizes.  dk and dv: multiples of 16 from 16 to 128 (any combination).  The fast
+ * matrix-core path is used for dtype KDA_BF16 with dk = dv = 128; every other supported
+ * combination runs the general float32 tile path.  H >= 1; B, T, N >= 0 (empty input is a no-op
+ * that still copies h0 to hT).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype of q, k, v, g, beta and o */
+typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
+
+/* status codes (0 = success) */
+enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = -1,        /* a required pointer is NULL */
+    KDA_ERR_SHAPE = -2,       /* negative or inconsistent sizes */
+    KDA_ERR_DTYPE = -3,       /* dtype not KDA_BF16 / KDA_F32 */
+    KDA_ERR_UNSUPPORTED = -4, /* dk or dv not a multiple of 16 in [16, 128] */
+    KDA_ERR_SEQLENS = -5,     /* cu_seqlens with B != 1, or (KDA_VALIDATE) bad contents */
+    KDA_ERR_RANGE = -6,       /* (KDA_VALIDATE) g outside [-5, 0] */
+    KDA_ERR_HIP = -7          /* a HIP runtime call or kernel launch failed */
+};
+
+/*
+ * kda_chunk_fwd -- prefill: run the recurrence over whole sequences and return every output and
+ * the final state.  Computed chunkwise, in parallel inside 16-token tiles and recurrently across
+ * tiles ("Kimi K3's hybrid block, from first principles", section "From linear attention to the
+ * delta rule": KDA runs in parallel inside a chunk and recurrently across chunks; the cumulative
+ * log-decay over a 16-token tile stays within (-80, 0)).  The chunked result equals the token
+ * loop up to floating-point rounding ("Kimi K3", section "Forgetting different features at
+ * different rates").  Tiles restart at every sequence start; a sequence's last tile may be
+ * partial.
+ *
+ *   q, k, g   [Ttot, H, dk]  dtype    device      inputs (g = log alpha, natural log)
+ *   v         [Ttot, H, dv]  dtype    device
+ *   beta      [Ttot, H]      dtype    device      write strength per token and head
+ *   h0        [N, H, dk, dv] float32  device      initial states; NULL = zeros
+ *   cu_seqlens [N+1]         int32    device      NULL = B equal sequences of length T
+ *   num_seqs  N (used only with cu_seqlens; else N = B)
+ *   o         [Ttot, H, dv]  dtype    device      output (written)
+ *   hT        [N, H, dk, dv] float32  device      final states (written); NULL = not written.
+ *                                                 hT may alias h0 (in-place state update).
+ *   B, T      with cu_seqlens: B must be 1 and T = Ttot; else Ttot = B * T
+ *   H, dk, dv heads and head dimensions
+ *   dtype     kda_dtype
+ *   stream    hipStream_t as void*
+ * Returns KDA_OK or a negative status; nothing is written on an argument error.
+ */
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  const float* h0, const int32_t* cu_seqlens, int num_seqs,
+                  void* o, float* hT,
+                  int B, int T, int H, int dk, int dv, int dtype, void* stream);
+
+/*
+ * kda_decode_step -- one token for each of N sequences, updating their states in place and
+ * returning the outputs: S <- (I - beta k k^T) Diag(exp g) S + beta k v^T, o = S^T q ("Kimi K3,
+ * explained", section "Kimi Delta Attention: making the radical option work": one KDA token
+ * step; k and v update S(t-1), q reads the updated S(t); "Kimi K3's hybrid block, from first
+ * principles", paragraph "What the state costs": the same work at every token).
+ *
+ *   q, k, g   [N, H, dk]      dtype    device
+ *   v         [N, H, dv]      dtype    device
+ *   beta      [N, H]          dtype    device
+ *   S         [N, H, dk, dv]  float32  device      read, then overwritten with the new state
+ *   o         [N, H, dv]      dtype    device      output (written)
+ * Returns KDA_OK or a negative status.
+ */
+int kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                    float* S, void* o, int N, int H, int dk, int dv, int dtype, void* stream);
+
+/* Text for a status code (static storage; never NULL). */
+const char* kda_status_string(int status);
+
+/* ABI version of this library (major * 10000 + minor * 100 + patch). */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,157 @@
+// C ABI of the KDA library: argument validation, optional content checks, and dispatch to the
+// HIP launchers.  Declared in include/kda.h, which states the operation, layouts, ownership and
+// error behaviour.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "kda_internal.h"
+
+namespace {
+
+bool supported_dim(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool validate_enabled() {
+    const char* e = std::getenv("KDA_VALIDATE");
+    return e && std::strcmp(e, "1") == 0;
+}
+
+float host_bf16(uint16_t b) {
+    uint32_t u = static_cast<uint32_t>(b) << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+// Copy a device buffer to the host on the caller's stream and wait (validation mode only).
+int fetch(void* dst, const void* src, size_t bytes, hipStream_t s) {
+    if (bytes == 0) return KDA_OK;
+    if (hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, s) != hipSuccess) return KDA_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+int check_gate_range(const void* g, int64_t count, int dtype, hipStream_t s) {
+    if (count == 0) return KDA_OK;
+    if (dtype == KDA_BF16) {
+        std::vector<uint16_t> h(static_cast<size_t>(count));
+        int st = fetch(h.data(), g, h.size() * 2, s);
+        if (st) return st;
+        for (uint16_t b : h) {
+            const float x = host_bf16(b);
+            if (!(x >= -5.0f && x <= 0.0f)) return KDA_ERR_RANGE;
+        }
+    } else {
+        std::vector<float> h(static_cast<size_t>(count));
+        int st = fetch(h.data(), g, h.size() * 4, s);
+        if (st) return st;
+        for (float x : h)
+            if (!(x >= -5.0f && x <= 0.0f)) return KDA_ERR_RANGE;
+    }
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return 100; }  // 0.1.0
+
+const char* kda_status_string(int status) {
+    switch (status) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL: return "a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "negative or inconsistent sizes";
+        case KDA_ERR_DTYPE: return "dtype must be KDA_BF16 or KDA_F32";
+        case KDA_ERR_UNSUPPORTED: return "dk and dv must be multiples of 16 in [16, 128]";
+        case KDA_ERR_SEQLENS: return "bad cu_seqlens (needs B == 1; non-decreasing from 0 to T)";
+        case KDA_ERR_RANGE: return "g (log alpha) outside [-5, 0]";
+        case KDA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  const float* h0, const int32_t* cu_seqlens, int num_seqs, void* o, float* hT,
+                  int B, int T, int H, int dk, int dv, int dtype, void* stream) {
+    if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
+    if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
+    if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    int64_t N, Ttot;
+    if (cu_seqlens) {
+        if (B != 1) return KDA_ERR_SEQLENS;
+        N = num_seqs;
+        Ttot = T;
+    } else {
+        N = B;
+        Ttot = static_cast<int64_t>(B) * T;
+    }
+    if (Ttot > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
+    if (N == 0 || (Ttot == 0 && !hT)) return KDA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (validate_enabled()) {
+        if (cu_seqlens) {
+            std::vector<int32_t> cu(static_cast<size_t>(N + 1));
+            int st = fetch(cu.data(), cu_seqlens, cu.size() * 4, s);
+            if (st) return st;
+            if (cu[0] != 0 || cu[N] != Ttot) return KDA_ERR_SEQLENS;
+            for (int64_t i = 0; i < N; ++i)
+                if (cu[i + 1] < cu[i]) return KDA_ERR_SEQLENS;
+        }
+        int st = check_gate_range(g, Ttot * H * dk, dtype, s);
+        if (st) return st;
+    }
+
+    kda::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.h0 = h0; a.cu = cu_seqlens; a.o = o; a.hT = hT;
+    a.N = N; a.T = cu_seqlens ? 0 : T; a.H = H; a.dk = dk; a.dv = dv; a.dtype = dtype;
+
+    hipError_t e;
+    if (dtype == KDA_BF16 && dk == 128 && dv == 128 && !std::getenv("KDA_FORCE_GENERAL"))
+        e = kda::launch_prefill_mfma(a, s);
+    else
+        e = kda::launch_prefill_general(a, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                    float* S, void* o, int N, int H, int dk, int dv, int dtype, void* stream) {
+    if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
+    if (N < 0 || H <= 0) return KDA_ERR_SHAPE;
+    if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !S || !o) return KDA_ERR_NULL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (validate_enabled()) {
+        int st = check_gate_range(g, static_cast<int64_t>(N) * H * dk, dtype, s);
+        if (st) return st;
+    }
+    hipError_t e;
+    // the 128 x 128 kernel uses 16-byte state accesses and 4-element input/output accesses
+    const uintptr_t va = dtype == KDA_BF16 ? 8 : 16;
+    if (dk == 128 && dv == 128 && aligned(S, 16) && aligned(v, va) && aligned(o, va)) {
+        kda::DecodeArgs a;
+        a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S = S; a.o = o;
+        a.N = N; a.H = H; a.dk = dk; a.dv = dv; a.dtype = dtype;
+        e = kda::launch_decode_d128(a, s);
+    } else {
+        // other head sizes: the general tile path over N one-token sequences, state in place
+        kda::PrefillArgs a;
+        a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+        a.h0 = S; a.cu = nullptr; a.o = o; a.hT = S;
+        a.N = N; a.T = 1; a.H = H; a.dk = dk; a.dv = dv; a.dtype = dtype;
+        e = kda::launch_prefill_general(a, s);
+    }
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

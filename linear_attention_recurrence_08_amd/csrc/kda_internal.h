@@ -1,0 +1,71 @@
+// Internal declarations shared by the KDA HIP sources (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Arguments of one prefill call after validation.  Token t of sequence n lives at packed index
+// bos(n) + t, where bos(n) = cu[n] when cu != nullptr and n * T otherwise.
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    const float* h0;      // [N, H, dk, dv] or nullptr (zeros)
+    const int32_t* cu;    // [N+1] or nullptr
+    void* o;              // [Ttot, H, dv]
+    float* hT;            // [N, H, dk, dv] or nullptr
+    int64_t N;            // sequences
+    int64_t T;            // per-sequence length when cu == nullptr
+    int64_t H, dk, dv;
+    int dtype;            // 0 = bf16, 1 = f32
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    float* S;             // [N, H, dk, dv], updated in place
+    void* o;              // [N, H, dv]
+    int64_t N, H, dk, dv;
+    int dtype;
+};
+
+// Each launcher returns hipSuccess or the launch error.
+hipError_t launch_prefill_general(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);   // bf16, dk = dv = 128
+hipError_t launch_decode_d128(const DecodeArgs& a, hipStream_t s);     // dk = dv = 128
+
+// ---------------------------------------------------------------------------------------------
+// Number-format helpers (device)
+// ---------------------------------------------------------------------------------------------
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// round to nearest even; NaN stays NaN
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> struct io;
+template <> struct io<float> {
+    __device__ static __forceinline__ float load(const float* p) { return *p; }
+    __device__ static __forceinline__ void store(float* p, float x) { *p = x; }
+};
+template <> struct io<bf16_t> {
+    __device__ static __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+    __device__ static __forceinline__ void store(bf16_t* p, float x) { *p = f32_to_bf16(x); }
+};
+
+}  // namespace kda

@@ -1,0 +1,178 @@
+// KDA chunkwise prefill, general path: float32 arithmetic on the vector ALUs, any dk, dv that are
+// multiples of 16 up to 128, bf16 or float32 inputs.  It serves the float32 dtype, head sizes
+// other than 128, and the in-place decode of those sizes (one-token sequences).
+//
+// The chunked algorithm ("Kimi K3's hybrid block, from first principles", section "From linear
+// attention to the delta rule": parallel inside a chunk, recurrent across chunks, cumulative
+// log-decay over 16-token tiles).  For a tile of C = 16 tokens entering with state S (dk x dv)
+// and Gam_i = sum_{j<=i} g_j (inclusive, per key channel, restarted at every tile):
+//     A_ij = sum_c k_ic k_jc e^{Gam_ic - Gam_jc}  (j < i)     P_ij = sum_c q_ic k_jc e^{...} (j <= i)
+//     (I + Diag(beta) A) U = Diag(beta) (V - (K.e^Gam) S)        solved by forward substitution
+//     O = (Q.e^Gam) S + P U
+//     S <- Diag(e^{Gam_C}) S + (K.e^{Gam_C - Gam})^T U
+// which is the token loop S_t = (I - b k k^T) Diag(e^g) S + b k v^T, o_t = S_t^T q_t unrolled
+// over the tile.  Because g >= -5, |Gam| <= 80 inside a tile and e^{+-Gam} stay finite in float32
+// ("Kimi K3", section "Forgetting different features at different rates").
+//
+// Work decomposition: one workgroup of 256 threads per (sequence, head, 16-column slice of dv);
+// columns of S evolve independently, so slices need no communication.  The slice's state lives
+// in LDS for the whole sequence.  Padded rows of a partial last tile carry k = q = v = g = beta = 0,
+// which leaves the state untouched and keeps Gam_C at the last real token.
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int C = 16;        // tile tokens
+constexpr int DKMAX = 128;
+constexpr int LD = DKMAX + 1; // padded row stride of the [16][dk] tiles (bank spread)
+constexpr int BV = 16;       // dv columns per workgroup
+
+template <typename Tin>
+__global__ __launch_bounds__(256) void kda_prefill_general_kernel(PrefillArgs a) {
+    __shared__ float sS[DKMAX * BV];     // state slice [dk][16]
+    __shared__ float sKp[C * LD];        // k e^{Gam}   (first raw k)
+    __shared__ float sKn[C * LD];        // k e^{-Gam}
+    __shared__ float sQp[C * LD];        // q e^{Gam}   (first raw q)
+    __shared__ float sKd[C * LD];        // k e^{Gam_C - Gam}
+    __shared__ float sG[C * LD];         // g, then Gam
+    __shared__ float sEC[DKMAX];         // e^{Gam_C}
+    __shared__ float sV[C * BV], sU[C * BV], sQS[C * BV], sA[C * C], sP[C * C], sB[C];
+
+    const int tid = threadIdx.x;
+    const int64_t H = a.H, dk = a.dk, dv = a.dv;
+    const int64_t nslices = dv / BV;
+    const int64_t wg = blockIdx.x;
+    const int64_t cb = wg % nslices;
+    const int64_t h = (wg / nslices) % H;
+    const int64_t n = wg / (nslices * H);
+
+    int64_t bos, eos;
+    if (a.cu) { bos = a.cu[n]; eos = a.cu[n + 1]; }
+    else { bos = n * a.T; eos = bos + a.T; }
+
+    const Tin* q = static_cast<const Tin*>(a.q);
+    const Tin* k = static_cast<const Tin*>(a.k);
+    const Tin* v = static_cast<const Tin*>(a.v);
+    const Tin* g = static_cast<const Tin*>(a.g);
+    const Tin* beta = static_cast<const Tin*>(a.beta);
+    Tin* o = static_cast<Tin*>(a.o);
+
+    // initial state slice
+    const int64_t sbase = (n * H + h) * dk * dv + cb * BV;
+    for (int idx = tid; idx < dk * BV; idx += 256) {
+        const int r = idx / BV, c = idx % BV;
+        sS[idx] = a.h0 ? a.h0[sbase + r * dv + c] : 0.0f;
+    }
+
+    for (int64_t t0 = bos; t0 < eos; t0 += C) {
+        const int L = (int)min<int64_t>(C, eos - t0);
+        // 1. load the tile (zero padding past the sequence end)
+        for (int idx = tid; idx < C * dk; idx += 256) {
+            const int i = idx / dk, c = idx % dk;
+            float kk = 0.f, qq = 0.f, gg = 0.f;
+            if (i < L) {
+                const int64_t off = ((t0 + i) * H + h) * dk + c;
+                kk = io<Tin>::load(k + off);
+                qq = io<Tin>::load(q + off);
+                gg = io<Tin>::load(g + off);
+            }
+            sKp[i * LD + c] = kk;
+            sQp[i * LD + c] = qq;
+            sG[i * LD + c] = gg;
+        }
+        {
+            const int i = tid / BV, c = tid % BV;
+            sV[tid] = (i < L) ? io<Tin>::load(v + ((t0 + i) * H + h) * dv + cb * BV + c) : 0.f;
+            if (tid < C) sB[tid] = (tid < L) ? io<Tin>::load(beta + (t0 + tid) * H + h) : 0.f;
+        }
+        __syncthreads();
+        // 2. inclusive cumulative log-decay per key channel
+        for (int c = tid; c < dk; c += 256) {
+            float run = 0.f;
+            for (int i = 0; i < C; ++i) { run += sG[i * LD + c]; sG[i * LD + c] = run; }
+        }
+        __syncthreads();
+        // 3. decay-rescaled operands
+        for (int idx = tid; idx < C * dk; idx += 256) {
+            const int i = idx / dk, c = idx % dk;
+            const float gam = sG[i * LD + c], gC = sG[(C - 1) * LD + c];
+            const float kk = sKp[i * LD + c], qq = sQp[i * LD + c];
+            sKp[i * LD + c] = kk * expf(gam);
+            sKn[i * LD + c] = kk * expf(-gam);
+            sQp[i * LD + c] = qq * expf(gam);
+            sKd[i * LD + c] = kk * expf(gC - gam);
+            if (i == C - 1) sEC[c] = expf(gC);
+        }
+        __syncthreads();
+        // 4. A, P (thread = (i, j)); right-hand side and Q-readout of the entering state
+        //    (thread = (i, col))
+        {
+            const int i = tid / C, j = tid % C;
+            float accA = 0.f, accP = 0.f, accW = 0.f, accQ = 0.f;
+            for (int c = 0; c < dk; ++c) {
+                const float kn = sKn[j * LD + c];
+                const float kp = sKp[i * LD + c], qp = sQp[i * LD + c];
+                const float s = sS[c * BV + j];
+                accA += kp * kn;
+                accP += qp * kn;
+                accW += kp * s;
+                accQ += qp * s;
+            }
+            sA[i * C + j] = (j < i) ? accA : 0.f;
+            sP[i * C + j] = (j <= i) ? accP : 0.f;
+            sU[i * BV + j] = sB[i] * (sV[i * BV + j] - accW);
+            sQS[i * BV + j] = accQ;
+        }
+        __syncthreads();
+        // 5. forward substitution: u_i = rhs_i - beta_i sum_{j<i} A_ij u_j  (one thread per column)
+        if (tid < BV) {
+            const int col = tid;
+            for (int i = 1; i < C; ++i) {
+                float acc = sU[i * BV + col];
+                const float bi = sB[i];
+                for (int j = 0; j < i; ++j) acc -= bi * sA[i * C + j] * sU[j * BV + col];
+                sU[i * BV + col] = acc;
+            }
+        }
+        __syncthreads();
+        // 6. outputs O = (Q e^Gam) S + P U
+        {
+            const int i = tid / BV, col = tid % BV;
+            float acc = sQS[i * BV + col];
+            for (int j = 0; j <= i; ++j) acc += sP[i * C + j] * sU[j * BV + col];
+            if (i < L) io<Tin>::store(o + ((t0 + i) * H + h) * dv + cb * BV + col, acc);
+        }
+        // 7. carry: S <- Diag(e^{Gam_C}) S + (K e^{Gam_C - Gam})^T U
+        for (int idx = tid; idx < dk * BV; idx += 256) {
+            const int r = idx / BV, col = idx % BV;
+            float acc = sEC[r] * sS[idx];
+            for (int j = 0; j < C; ++j) acc += sKd[j * LD + r] * sU[j * BV + col];
+            sS[idx] = acc;
+        }
+        __syncthreads();
+    }
+
+    if (a.hT) {
+        for (int idx = tid; idx < dk * BV; idx += 256) {
+            const int r = idx / BV, c = idx % BV;
+            a.hT[sbase + r * dv + c] = sS[idx];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_general(const PrefillArgs& a, hipStream_t s) {
+    const int64_t grid = a.N * a.H * (a.dv / BV);
+    if (grid <= 0) return hipSuccess;
+    if (a.dtype == 0)
+        hipLaunchKernelGGL(kda_prefill_general_kernel<bf16_t>, dim3((unsigned)grid), dim3(256), 0,
+                           s, a);
+    else
+        hipLaunchKernelGGL(kda_prefill_general_kernel<float>, dim3((unsigned)grid), dim3(256), 0,
+                           s, a);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -16,19 +16,26 @@ a 128 x 128 state per head.  Layouts are token-major and packed:
 with Ttot = B * T for equal-length batches, or the sum of the sequence lengths for a packed
 variable-length batch described by cu_seqlens (int32 [N + 1]).
 
-Draw order, fixed for reproducibility: the sequence lengths (variable-length batches only); then,
-for each block of BLOCK_TOKENS packed tokens, q, k, v, the beta logits and the gate noise; then the
-initial states sequence by sequence.
+Draw order, fixed for reproducibility: every block of BLOCK_TOKENS packed tokens has its own PCG64
+stream, seeded by SeedSequence([seed, block]), from which q, k, v, the beta logits and the gate
+noise are drawn in that order; sequence i's initial state comes from SeedSequence([seed, 10**6 + i])
+and variable-length batches draw their lengths from SeedSequence([seed, 2 * 10**6]).  Independent
+streams let the blocks be drawn in parallel threads with a result that does not depend on the
+thread count.
 """
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Optional, Sequence
 
 import numpy as np
 import torch
 
-BLOCK_TOKENS = 8192  # token block of the draw order (bounds host memory for long sequences)
+BLOCK_TOKENS = 2048  # token block of the draw order (one random stream per block)
+H0_STREAM = 10 ** 6
+LEN_STREAM = 2 * 10 ** 6
 
 GATE_RECIPES = ("sigmoid", "sigmoid_shift1", "sigmoid_shiftm1", "bimodal", "zero")
 
@@ -67,6 +74,16 @@ class KDAInputs:
         cu = self.cu_seqlens.tolist()
         return [(cu[i], cu[i + 1]) for i in range(len(cu) - 1)]
 
+    def call_views(self):
+        """(q, k, v, g, beta) shaped for the binding: [B, T, H, d] for equal-length batches,
+        packed [Ttot, H, d] when cu_seqlens describes the sequences."""
+        if self.cu_seqlens is not None:
+            return self.q, self.k, self.v, self.g, self.beta
+        B, T = self.B, self.T
+        return (self.q.view(B, T, *self.q.shape[1:]), self.k.view(B, T, *self.k.shape[1:]),
+                self.v.view(B, T, *self.v.shape[1:]), self.g.view(B, T, *self.g.shape[1:]),
+                self.beta.view(B, T, *self.beta.shape[1:]))
+
     def to(self, device) -> "KDAInputs":
         f = lambda t: None if t is None else t.to(device)
         return dataclasses.replace(
@@ -80,6 +97,18 @@ def _torch_dtype(dtype: str):
     if dtype == "f32":
         return torch.float32
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _stream(seed: int, index: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(index)])))
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(8, n))
 
 
 def _sigmoid(x: np.ndarray) -> np.ndarray:
@@ -122,7 +151,6 @@ def make_inputs(seq_lens: Sequence[int], H: int, dk: int, dv: int, dtype: str, s
         packed = len(set(seq_lens)) > 1
     if not packed and len(set(seq_lens)) > 1:
         raise ValueError("unequal lengths need packed=True")
-    rng = np.random.Generator(np.random.PCG64(seed))
     tdt = _torch_dtype(dtype)
     ttot = int(sum(seq_lens))
     q = torch.empty((ttot, H, dk), dtype=tdt)
@@ -130,8 +158,11 @@ def make_inputs(seq_lens: Sequence[int], H: int, dk: int, dv: int, dtype: str, s
     v = torch.empty((ttot, H, dv), dtype=tdt)
     g = torch.empty((ttot, H, dk), dtype=tdt)
     beta = torch.empty((ttot, H), dtype=tdt)
-    for t0 in range(0, ttot, BLOCK_TOKENS):
+
+    def draw_block(b):
+        t0 = b * BLOCK_TOKENS
         n = min(BLOCK_TOKENS, ttot - t0)
+        rng = _stream(seed, b)
         qb = rng.standard_normal((n, H, dk), dtype=np.float32)
         kb = rng.standard_normal((n, H, dk), dtype=np.float32)
         vb = rng.standard_normal((n, H, dv), dtype=np.float32)
@@ -142,13 +173,22 @@ def make_inputs(seq_lens: Sequence[int], H: int, dk: int, dv: int, dtype: str, s
         v[t0:t0 + n] = torch.from_numpy(vb).to(tdt)
         beta[t0:t0 + n] = torch.from_numpy(_sigmoid(bb)).to(tdt)
         g[t0:t0 + n] = torch.from_numpy(_gate(zb, gate)).to(tdt)
+
     N = len(seq_lens)
     h0 = None
     if h0_sigma is not None:
         h0 = torch.empty((N, H, dk, dv), dtype=torch.float32)
-        for i in range(N):
-            h0[i] = torch.from_numpy(
-                rng.standard_normal((H, dk, dv), dtype=np.float32) * np.float32(h0_sigma))
+
+    def draw_h0(i):
+        rng = _stream(seed, H0_STREAM + i)
+        h0[i] = torch.from_numpy(
+            rng.standard_normal((H, dk, dv), dtype=np.float32) * np.float32(h0_sigma))
+
+    nblocks = (ttot + BLOCK_TOKENS - 1) // BLOCK_TOKENS
+    with ThreadPoolExecutor(max_workers=_workers()) as ex:
+        list(ex.map(draw_block, range(nblocks)))
+        if h0 is not None:
+            list(ex.map(draw_h0, range(N)))
     if packed:
         cu = torch.tensor(np.concatenate([[0], np.cumsum(seq_lens)]), dtype=torch.int32)
         return KDAInputs(q, k, v, g, beta, h0, cu, 1, ttot, H, dk, dv, dtype, name)
@@ -158,9 +198,9 @@ def make_inputs(seq_lens: Sequence[int], H: int, dk: int, dv: int, dtype: str, s
 
 
 def varlen_lengths(seed: int, n: int = 16, lo: int = 1024, hi: int = 16384):
-    """Sequence lengths uniform on [lo, hi] (inclusive), drawn first from the workload's stream."""
-    rng = np.random.Generator(np.random.PCG64(seed))
-    return rng.integers(lo, hi, size=n, endpoint=True).tolist(), rng
+    """Sequence lengths uniform on [lo, hi] (inclusive) from the workload's length stream."""
+    rng = _stream(seed, LEN_STREAM)
+    return rng.integers(lo, hi, size=n, endpoint=True).tolist()
 
 
 # Named workloads.  Index = seed.
@@ -193,10 +233,8 @@ def make_workload(name: str, gate: Optional[str] = None) -> KDAInputs:
         return make_inputs(w["seq_lens"], w["H"], w["dk"], w["dv"], w["dtype"], w["seed"],
                            gate=gate, h0_sigma=w["h0_sigma"], packed=False, name=name)
     if kind == "varlen":
-        # lengths are the first draw of the workload's stream; the rest continues from a seed
-        # derived from it so the token draws do not depend on how many lengths were drawn
-        lens, _ = varlen_lengths(w["seed"], w["n_seqs"])
-        return make_inputs(lens, w["H"], w["dk"], w["dv"], w["dtype"], w["seed"] * 1000 + 1,
+        lens = varlen_lengths(w["seed"], w["n_seqs"])
+        return make_inputs(lens, w["H"], w["dk"], w["dv"], w["dtype"], w["seed"],
                            gate=gate, h0_sigma=w["h0_sigma"], packed=True, name=name)
     if kind == "decode":
         return make_decode_inputs(w["N"], w["H"], w["dk"], w["dv"], w["dtype"], w["seed"],

@@ -1,0 +1,169 @@
+"""Python binding of libkda.so (ctypes).  Argument marshalling only: every step of the KDA path runs
+in the library's HIP kernels.  PyTorch supplies device memory and the current stream.
+
+    kda_chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, output_final_state=True)
+        -> (o, hT)
+    kda_decode_step(q, k, v, g, beta, S) -> o         (S is updated in place)
+    kda_status_string(code) -> str
+
+Layouts (see include/kda.h): q, k, g [B, T, H, dk] or packed [Ttot, H, dk]; v [.., H, dv];
+beta [B, T, H] or [Ttot, H]; h0 / hT / S float32 [N, H, dk, dv]; cu_seqlens int32 [N+1] on the
+device (packed inputs only).  q, k, v, g, beta and o share one dtype: bfloat16 or float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_BF16, KDA_F32 = 0, 1
+KDA_OK = 0
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {kda_status_string(code)} (status {code})")
+        self.code = code
+
+
+def load_library():
+    """Open libkda.so; raises if the HIP library has not been built (there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int
+        lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
+                                      i32, i32, i32, i32, i32, i32, vp]
+        lib.kda_chunk_fwd.restype = i32
+        lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        lib.kda_decode_step.restype = i32
+        lib.kda_status_string.argtypes = [i32]
+        lib.kda_status_string.restype = ctypes.c_char_p
+        lib.kda_version.argtypes = []
+        lib.kda_version.restype = i32
+        _lib = lib
+    return _lib
+
+
+def kda_status_string(code: int) -> str:
+    return load_library().kda_status_string(int(code)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: torch.Tensor, name: str, device, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, h0: Optional[torch.Tensor] = None,
+                  cu_seqlens: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                  o: Optional[torch.Tensor] = None, hT: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA prefill.  Returns (o, hT); hT is None when output_final_state is False.
+    o / hT may be passed preallocated (hT may be h0 itself for an in-place state update)."""
+    dev = q.device
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        _check(t, name, dev, dt)
+    if q.dim() == 4:
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens needs packed [Ttot, H, d] inputs")
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        lead = (B, T)
+    elif q.dim() == 3:
+        T, H, dk = q.shape
+        dv = v.shape[-1]
+        B = 1
+        lead = (T,)
+    else:
+        raise ValueError("q must be [B, T, H, dk] or [Ttot, H, dk]")
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (*lead, H, dv) \
+            or beta.shape != (*lead, H):
+        raise ValueError("inconsistent q/k/v/g/beta shapes")
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", dev, torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if h0 is not None:
+        _check(h0, "h0", dev, torch.float32)
+        if h0.shape != (N, H, dk, dv):
+            raise ValueError(f"h0 must be [{N}, {H}, {dk}, {dv}]")
+    if o is None:
+        o = torch.empty((*lead, H, dv), dtype=dt, device=dev)
+    else:
+        _check(o, "o", dev, dt)
+    if output_final_state:
+        if hT is None:
+            hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        else:
+            _check(hT, "hT", dev, torch.float32)
+    else:
+        hT = None
+    st = load_library().kda_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), N,
+        _ptr(o), _ptr(hT), B, T, H, dk, dv, _dtype_code(q), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd")
+    return o, hT
+
+
+def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, S: torch.Tensor,
+                    o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token per sequence: q, k, g [N, H, dk], v [N, H, dv], beta [N, H]; S float32
+    [N, H, dk, dv] is updated in place.  Returns o [N, H, dv]."""
+    dev = q.device
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        _check(t, name, dev, dt)
+    _check(S, "S", dev, torch.float32)
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, dk]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (N, H, dv) or beta.shape != (N, H) \
+            or S.shape != (N, H, dk, dv):
+        raise ValueError("inconsistent decode shapes")
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    else:
+        _check(o, "o", dev, dt)
+    st = load_library().kda_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o), N, H, dk, dv,
+        _dtype_code(q), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_decode_step")
+    return o

@@ -1,0 +1,107 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the header declares, and
+rejects bad arguments with the documented status codes before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "kda.h")
+LIB = os.path.join(ROOT, "linear_attention_recurrence_08_amd", "libkda.so")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(kda_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from linear_attention_recurrence_08_amd import build
+        build.build()
+    from linear_attention_recurrence_08_amd import kda
+    return kda.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == ["kda_chunk_fwd", "kda_decode_step", "kda_status_string",
+                                     "kda_version"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    from linear_attention_recurrence_08_amd.kda import kda_status_string
+    assert kda_status_string(0) == "ok"
+    for code in range(-7, 0):
+        s = kda_status_string(code)
+        assert s and s != "unknown status"
+    assert kda_status_string(-99) == "unknown status"
+    assert lib.kda_version() >= 100
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, num_seqs=0, o=FAKE,
+             hT=FAKE, B=1, T=16, H=2, dk=128, dv=128, dtype=0)
+    a.update(kw)
+    return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"],
+                             a["num_seqs"], a["o"], a["hT"], a["B"], a["T"], a["H"], a["dk"],
+                             a["dv"], a["dtype"], None)
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, S=FAKE, o=FAKE, N=4, H=2, dk=128,
+             dv=128, dtype=0)
+    a.update(kw)
+    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S"], a["o"],
+                               a["N"], a["H"], a["dk"], a["dv"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -3), (dict(dtype=-1), -3),
+    (dict(B=-1), -2), (dict(T=-5), -2), (dict(H=0), -2), (dict(num_seqs=-1), -2),
+    (dict(dk=130), -4), (dict(dk=8), -4), (dict(dv=120), -4), (dict(dk=144), -4), (dict(dv=0), -4),
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(g=None), -1),
+    (dict(beta=None), -1), (dict(o=None), -1),
+    (dict(cu=FAKE, B=2, num_seqs=3), -5),
+])
+def test_prefill_argument_errors(lib, kw, code):
+    assert _prefill(lib, **kw) == code
+
+
+def test_prefill_empty_is_noop(lib):
+    # no sequences, or no tokens and no final state requested: nothing to launch
+    assert _prefill(lib, B=0) == 0
+    assert _prefill(lib, T=0, hT=None) == 0
+    assert _prefill(lib, cu=FAKE, B=1, T=0, num_seqs=0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), -3), (dict(N=-1), -2), (dict(H=0), -2), (dict(dk=100), -4),
+    (dict(dv=256), -4), (dict(q=None), -1), (dict(S=None), -1), (dict(o=None), -1),
+    (dict(beta=None), -1),
+])
+def test_decode_argument_errors(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_decode_empty_is_noop(lib):
+    assert _decode(lib, N=0, q=None) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    from linear_attention_recurrence_08_amd import kda_chunk_fwd
+    x = torch.zeros(16, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kda_chunk_fwd(x, x, x, x, torch.zeros(16, 2, dtype=torch.bfloat16))

@@ -1,0 +1,255 @@
+"""GPU parity: the HIP path through the C ABI against the float64 CPU oracle, element by element on
+the same seeded inputs.
+
+Error metric: max|x - x_ref| / max|x_ref| over the compared tensor (o, and separately the final
+state).  Bars: 2e-2 for bf16 inputs with float32 state and accumulation, 1e-4 for the float32
+path.  Full-size workloads run every head on the GPU in the launch configuration the benchmark
+times; the oracle checks a sample of heads (or of (sequence, head) pairs for decode), each in full.
+"""
+import os
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import to64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+def err(x, ref):
+    return float(np.abs(x - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def gpu_prefill(x, dev, **kw):
+    from linear_attention_recurrence_08_amd import kda_chunk_fwd
+    xd = x.to(dev)
+    o, hT = kda_chunk_fwd(*xd.call_views(), h0=xd.h0, cu_seqlens=xd.cu_seqlens, **kw)
+    torch.cuda.synchronize()
+    return o.reshape(x.total_tokens, x.H, x.dv), hT
+
+
+def oracle_prefill(oracle, x, heads=None):
+    hs = slice(None) if heads is None else list(heads)
+    cu = x.cu_seqlens.tolist() if x.cu_seqlens is not None else \
+        [b * x.T for b in range(x.B + 1)]
+    h0 = None if x.h0 is None else to64(x.h0[:, hs])
+    return oracle.recurrence(to64(x.q[:, hs]), to64(x.k[:, hs]), to64(x.v[:, hs]),
+                             to64(x.g[:, hs]), to64(x.beta[:, hs]), h0, cu)
+
+
+def check_prefill(oracle_mod, x, dev, heads=None, tol=None, label=""):
+    tol = tol or TOL[x.dtype]
+    _say(f"{label}: GPU prefill Ttot={x.total_tokens} N={x.num_seqs} H={x.H} "
+         f"dk={x.dk} dv={x.dv} {x.dtype}")
+    o, hT = gpu_prefill(x, dev)
+    _say(f"{label}: oracle on heads {'all' if heads is None else list(heads)}")
+    o_ref, h_ref = oracle_prefill(oracle_mod, x, heads)
+    hs = slice(None) if heads is None else list(heads)
+    eo, eh = err(to64(o[:, hs]), o_ref), err(to64(hT[:, hs]), h_ref)
+    _say(f"{label}: error o={eo:.3e} hT={eh:.3e} (bar {tol})")
+    assert np.isfinite(to64(o)).all() and np.isfinite(to64(hT)).all()
+    assert eo <= tol and eh <= tol, (eo, eh)
+    return o, hT
+
+
+# ------------------------------------------------------------------------------------------------
+# small cases: several tiles, ragged tails, empty sequences, both paths, both dtypes
+# ------------------------------------------------------------------------------------------------
+SMALL = [
+    # (seq_lens, H, dk, dv, dtype, h0_sigma, gate, packed)
+    ([48], 2, 128, 128, "bf16", None, "sigmoid", False),
+    ([64, 64, 64], 3, 128, 128, "bf16", 0.05, "sigmoid", False),
+    ([37, 0, 16, 5, 81, 1], 3, 128, 128, "bf16", 0.1, "sigmoid", True),
+    ([200], 2, 128, 128, "bf16", None, "bimodal", False),
+    ([90], 2, 128, 128, "bf16", 0.1, "zero", False),
+    ([77], 2, 128, 128, "f32", 0.05, "sigmoid", False),
+    ([50], 2, 64, 32, "f32", None, "sigmoid", False),
+    ([33, 19], 2, 16, 128, "bf16", 0.1, "sigmoid_shiftm1", True),
+    ([64], 2, 32, 32, "f32", None, "sigmoid", False),
+    ([29], 1, 112, 48, "f32", 0.1, "sigmoid", False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-H{c[1]}-{c[2]}x{c[3]}-{c[4]}-{c[6]}")
+def test_small_prefill(oracle_mod, case):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs
+    lens, H, dk, dv, dt, h0s, gate, packed = case
+    x = inputs.make_inputs(lens, H, dk, dv, dt, seed=sum(lens) + dk, gate=gate, h0_sigma=h0s,
+                           packed=packed)
+    check_prefill(oracle_mod, x, dev, label="small")
+
+
+def test_tiny_f32_workload(oracle_mod):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs
+    check_prefill(oracle_mod, inputs.make_workload("tiny_T64_H2_d32_f32"), dev, label="tiny")
+
+
+def test_general_path_matches_fast_path_bf16(oracle_mod, monkeypatch):
+    """Both prefill paths on the same bf16 d=128 input agree with the oracle."""
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs
+    x = inputs.make_inputs([100, 45], 2, 128, 128, "bf16", seed=3, h0_sigma=0.05, packed=True)
+    check_prefill(oracle_mod, x, dev, label="fast")
+    monkeypatch.setenv("KDA_FORCE_GENERAL", "1")
+    check_prefill(oracle_mod, x, dev, label="general")
+
+
+# ------------------------------------------------------------------------------------------------
+# full-size workloads
+# ------------------------------------------------------------------------------------------------
+def test_prefill_T4096_H96(oracle_mod):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs
+    x = inputs.make_workload("prefill_T4096_H96_d128_bf16")
+    check_prefill(oracle_mod, x, dev, heads=None, label="prefill_T4096_H96")
+
+
+@pytest.mark.parametrize("gate", ["sigmoid_shift1", "sigmoid_shiftm1"])
+def test_varlen_16seq_H96(oracle_mod, gate):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs
+    x = inputs.make_workload("varlen_16seq_H96_d128_bf16", gate=gate)
+    check_prefill(oracle_mod, x, dev, heads=[0, 41, 95], label=f"varlen[{gate}]")
+
+
+def test_long_T131072_H96(oracle_mod):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs
+    x = inputs.make_workload("long_T131072_H96_d128_bf16")
+    check_prefill(oracle_mod, x, dev, heads=[0, 95], label="long_T131072")
+
+
+def test_decode_N256_H96(oracle_mod):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_decode_step
+    d = inputs.make_workload("decode_N256_H96_d128_bf16")
+    _say("decode_N256_H96: GPU step")
+    S = d.h0.to(dev)
+    o = kda_decode_step(d.q.to(dev), d.k.to(dev), d.v.to(dev), d.g.to(dev), d.beta.to(dev), S)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(99)
+    units = sorted(set(map(tuple, rng.integers(0, [256, 96], size=(96, 2)).tolist())))
+    ns = [u[0] for u in units]
+    hs = [u[1] for u in units]
+    sel = lambda t: to64(t[ns, hs])[:, None]  # [units, 1, ...]
+    o_ref, S_ref = oracle_mod.decode_step(sel(d.q), sel(d.k), sel(d.v), sel(d.g),
+                                          to64(d.beta[ns, hs])[:, None], sel(d.h0))
+    eo = err(to64(o[ns, hs]), o_ref[:, 0])
+    es = err(to64(S[ns, hs]), S_ref[:, 0])
+    _say(f"decode_N256_H96: {len(units)} sampled units, error o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dims,dt", [((128, 128), "f32"), ((128, 128), "bf16"),
+                                     ((64, 32), "f32"), ((16, 128), "bf16")])
+def test_decode_small(oracle_mod, dims, dt):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_decode_step
+    dk, dv = dims
+    d = inputs.make_decode_inputs(7, 3, dk, dv, dt, seed=dk + dv, s_sigma=0.5)
+    S = d.h0.to(dev).clone()
+    o = kda_decode_step(d.q.to(dev), d.k.to(dev), d.v.to(dev), d.g.to(dev), d.beta.to(dev), S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_mod.decode_step(to64(d.q), to64(d.k), to64(d.v), to64(d.g),
+                                          to64(d.beta), to64(d.h0))
+    assert err(to64(o), o_ref) <= TOL[dt] and err(to64(S), S_ref) <= TOL[dt]
+
+
+def test_decode_chain_matches_oracle_sequence(oracle_mod):
+    """T decode steps in a row follow the token loop (the decode state carried on the GPU)."""
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_decode_step
+    x = inputs.make_inputs([40] * 4, 2, 128, 128, "f32", seed=12, h0_sigma=0.1)
+    qd, kd, vd, gd, bd = (t.view(4, 40, *t.shape[1:]).to(dev) for t in
+                          (x.q, x.k, x.v, x.g, x.beta))
+    S = x.h0.to(dev).clone()
+    outs = []
+    for t in range(40):
+        outs.append(kda_decode_step(qd[:, t].contiguous(), kd[:, t].contiguous(),
+                                    vd[:, t].contiguous(), gd[:, t].contiguous(),
+                                    bd[:, t].contiguous(), S))
+    torch.cuda.synchronize()
+    o_gpu = torch.stack(outs, 1).reshape(160, 2, 128)
+    o_ref, h_ref = oracle_prefill(oracle_mod, x)
+    assert err(to64(o_gpu), o_ref) <= TOL["f32"] and err(to64(S), h_ref) <= TOL["f32"]
+
+
+# ------------------------------------------------------------------------------------------------
+# state handling: resume, in place, empty, determinism, validation
+# ------------------------------------------------------------------------------------------------
+def test_resume_from_final_state(oracle_mod):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd
+    x = inputs.make_inputs([300], 2, 128, 128, "bf16", seed=21, h0_sigma=0.05)
+    xd = x.to(dev)
+    a = 117  # not a tile multiple
+    o1, h1 = kda_chunk_fwd(xd.q[:a], xd.k[:a], xd.v[:a], xd.g[:a], xd.beta[:a], h0=xd.h0)
+    o2, h2 = kda_chunk_fwd(xd.q[a:], xd.k[a:], xd.v[a:], xd.g[a:], xd.beta[a:], h0=h1)
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle_prefill(oracle_mod, x)
+    assert err(to64(torch.cat([o1, o2])), o_ref) <= TOL["bf16"]
+    assert err(to64(h2), h_ref) <= TOL["bf16"]
+
+
+def test_in_place_final_state_and_determinism():
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd
+    x = inputs.make_inputs([130, 70], 3, 128, 128, "bf16", seed=22, h0_sigma=0.05, packed=True)
+    xd = x.to(dev)
+    args = xd.call_views()
+    o_a, h_a = kda_chunk_fwd(*args, h0=xd.h0, cu_seqlens=xd.cu_seqlens)
+    o_b, h_b = kda_chunk_fwd(*args, h0=xd.h0, cu_seqlens=xd.cu_seqlens)
+    S = xd.h0.clone()
+    o_c, h_c = kda_chunk_fwd(*args, h0=S, cu_seqlens=xd.cu_seqlens, hT=S)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(h_a, h_b)
+    assert torch.equal(o_a, o_c) and torch.equal(h_a, S)
+
+
+def test_empty_sequences_copy_h0():
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd
+    x = inputs.make_inputs([0, 0, 0], 2, 128, 128, "bf16", seed=23, h0_sigma=1.0, packed=True)
+    xd = x.to(dev)
+    o, hT = kda_chunk_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, h0=xd.h0, cu_seqlens=xd.cu_seqlens)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(hT, xd.h0)
+    # equal-length batch with T = 0 and no h0: zero states
+    e = torch.empty(2, 0, 2, 128, dtype=torch.bfloat16, device=dev)
+    o, hT = kda_chunk_fwd(e, e, e, e, torch.empty(2, 0, 2, dtype=torch.bfloat16, device=dev))
+    torch.cuda.synchronize()
+    assert hT.shape == (2, 2, 128, 128) and float(hT.abs().max()) == 0.0
+
+
+def test_validation_mode_reports_bad_contents(monkeypatch):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import KDAError, inputs, kda_chunk_fwd
+    x = inputs.make_inputs([20, 12], 1, 128, 128, "bf16", seed=24, packed=True).to(dev)
+    monkeypatch.setenv("KDA_VALIDATE", "1")
+    kda_chunk_fwd(x.q, x.k, x.v, x.g, x.beta, cu_seqlens=x.cu_seqlens)  # valid: no error
+    bad_g = x.g.clone()
+    bad_g[3, 0, 7] = -5.5
+    with pytest.raises(KDAError) as ei:
+        kda_chunk_fwd(x.q, x.k, x.v, bad_g, x.beta, cu_seqlens=x.cu_seqlens)
+    assert ei.value.code == -6
+    bad_cu = torch.tensor([0, 25, 20], dtype=torch.int32, device=dev)
+    with pytest.raises(KDAError) as ei:
+        kda_chunk_fwd(x.q, x.k, x.v, x.g, x.beta, cu_seqlens=bad_cu)
+    assert ei.value.code == -5
+    torch.cuda.synchronize()
