@@ -25,6 +25,8 @@ def hipcc_flags():
         # no packed-fp32 instructions in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wno-unused-command-line-argument",
+        # keep matrix-core accumulators in VGPRs (no AGPR round trips for the vector ALUs)
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", INCLUDE, "-I", CSRC,
     ]
 
