@@ -78,7 +78,7 @@ def kernel_source_digest() -> str:
 def recorded_traffic(kernel_tag: str):
     """HBM bytes per launch from the committed counter summary for this kernel, if its recorded
     source digest matches the current sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_hbm_traffic.md")  # noqa: E501
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -87,6 +87,122 @@ def recorded_traffic(kernel_tag: str):
     if not m_d or not m_b or m_d.group(1) != kernel_source_digest():
         return None
     return float(m_b.group(1))
+
+
+CALIB_BYTES = 1 << 30   # calibration copy: reads and writes exactly this many bytes
+
+
+def traffic_pass(dev):
+    """A plain copy of known size (y = x * 1 over 1 GiB of float32), then 3 launches of the
+    prefill and the decode kernels on their benchmark workloads."""
+    import torch
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd, kda_decode_step
+    x = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    del x, y
+    w = inputs.make_workload("prefill_T4096_H96_d128_bf16").to(dev)
+    for _ in range(3):
+        kda_chunk_fwd(*w.call_views(), h0=w.h0, cu_seqlens=w.cu_seqlens)
+    torch.cuda.synchronize()
+    del w
+    d = inputs.make_workload(DECODE_WORKLOAD)
+    qd, kd, vd, gd, bd, S = (t.to(dev) for t in (d.q, d.k, d.v, d.g, d.beta, d.h0))
+    for _ in range(3):
+        kda_decode_step(qd, kd, vd, gd, bd, S)
+    torch.cuda.synchronize()
+    print("traffic pass done", file=sys.stderr)
+
+
+SUMMARY_KERNELS = {
+    # kernel name fragment -> (summary tag, workload, algorithmic bytes per launch)
+    "kda_prefill_mfma_kernel": ("kda_chunk_fwd_prefill_T4096_H96_d128_bf16",
+                                "prefill_T4096_H96_d128_bf16", None),
+    "kda_decode_d128_kernel": ("kda_decode_decode_N256_H96_d128_bf16",
+                               "decode_N256_H96_d128_bf16", None),
+}
+
+
+def _algorithmic_bytes(workload):
+    from linear_attention_recurrence_08_amd import inputs
+    w = inputs.WORKLOADS[workload]
+    if w["kind"] == "decode":
+        return w["N"] * w["H"] * (2 * w["dk"] * w["dv"] * 4 + (3 * w["dk"] + 2 * w["dv"]) * 2 + 2)
+    T = sum(w["seq_lens"])
+    return T * w["H"] * ((3 * w["dk"] + 2 * w["dv"]) * 2 + 2) + len(w["seq_lens"]) * w["H"] * \
+        w["dk"] * w["dv"] * 4
+
+
+def summarize(dirs, command):
+    """profiles/<kernel>_<workload>_kernel_trace.md from a --kernel-trace --stats run and
+    profiles/<kernel>_<workload>_hbm_traffic.md from FETCH_SIZE + WRITE_SIZE counter runs (each
+    scaled by what the same counter reads for the 1 GiB calibration copy)."""
+    import csv
+    import glob
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    digest = kernel_source_digest()
+    counters = {}     # (kernel tag or "copy", counter) -> list of per-dispatch values (KiB)
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                for frag, (tag, wl, _) in SUMMARY_KERNELS.items():
+                    if frag in r["Name"]:
+                        path = os.path.join(out_dir, f"{tag}_kernel_trace.md")
+                        with open(path, "w") as fo:
+                            fo.write(f"# {frag} on {wl}: rocprofv3 kernel trace\n\n")
+                            fo.write(f"command: `{command}`\n\n")
+                            fo.write("| calls | average ns | min ns | max ns | total ns |\n")
+                            fo.write("|---|---|---|---|---|\n")
+                            fo.write(f"| {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                                     f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | "
+                                     f"{float(r['TotalDurationNs']):.0f} |\n\n")
+                            fo.write(f"source_digest: {digest}\n")
+                        print("wrote", path)
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                name = r["Kernel_Name"]
+                key = None
+                if "elementwise" in name or "vectorized" in name:
+                    key = "copy"
+                for frag, (tag, _, _) in SUMMARY_KERNELS.items():
+                    if frag in name:
+                        key = tag
+                if key is None:
+                    continue
+                counters.setdefault((key, r["Counter_Name"]), []).append(
+                    float(r["Counter_Value"]))
+    if counters:
+        cal = {}
+        for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+            vals = counters.get(("copy", cn))
+            if vals:
+                cal[cn] = max(vals) * 1024.0 / CALIB_BYTES   # counter bytes per true byte
+        for frag, (tag, wl, _) in SUMMARY_KERNELS.items():
+            f_vals = counters.get((tag, "FETCH_SIZE"))
+            w_vals = counters.get((tag, "WRITE_SIZE"))
+            if not f_vals or not w_vals or "FETCH_SIZE" not in cal or "WRITE_SIZE" not in cal:
+                continue
+            fetch = sum(f_vals) / len(f_vals) * 1024.0 / cal["FETCH_SIZE"]
+            write = sum(w_vals) / len(w_vals) * 1024.0 / cal["WRITE_SIZE"]
+            algo = _algorithmic_bytes(wl)
+            path = os.path.join(out_dir, f"{tag}_hbm_traffic.md")
+            with open(path, "w") as fo:
+                fo.write(f"# {frag} on {wl}: HBM traffic per launch (rocprofv3 counters)\n\n")
+                fo.write(f"command: `{command}`\n\n")
+                fo.write("Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each taken in its "
+                         "own run and scaled by what the same counter reads for a copy of exactly "
+                         f"{CALIB_BYTES} bytes read and {CALIB_BYTES} bytes written "
+                         f"(factor FETCH {cal['FETCH_SIZE']:.4f}, WRITE "
+                         f"{cal['WRITE_SIZE']:.4f} counter bytes per byte).\n\n")
+                fo.write("| dispatches | fetch bytes | write bytes | total bytes | algorithmic "
+                         "bytes | total / algorithmic |\n|---|---|---|---|---|---|\n")
+                fo.write(f"| {len(f_vals)} | {fetch:.4g} | {write:.4g} | {fetch + write:.4g} | "
+                         f"{algo} | {(fetch + write) / algo:.3f} |\n\n")
+                fo.write(f"source_digest: {digest}\n")
+                fo.write(f"hbm_bytes_per_launch: {fetch + write:.6g}\n")
+            print("wrote", path)
 
 
 def time_launches(fn, steps, warmup, stream):
@@ -116,7 +232,17 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-pass", action="store_true",
+                    help="run a 1 GiB calibration copy and 3 launches of each kernel (for "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE); prints no JSON")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="write profiles/*.md from rocprofv3 output directories: a kernel-trace "
+                         "--stats run and/or FETCH_SIZE and WRITE_SIZE counter runs")
+    ap.add_argument("--command", default="", help="command line recorded in the summaries")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(heads and sequences would shard across GPUs with no exchange)",
@@ -131,6 +257,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    if args.traffic_pass:
+        traffic_pass(dev)
+        return
 
     # ---------------- prefill ----------------
     x = inputs.make_workload(args.workload)
