@@ -16,20 +16,21 @@
 // only regroups per-channel factors).  T is the unit-lower-triangular inverse, evaluated exactly
 // as the finite product (I - N)(I + N^2)(I + N^4)(I + N^8) with N = Diag(beta) A (N^16 = 0).
 //
-// Mapping to gfx950.  One workgroup of 8 waves owns one (sequence, head, 64-column slice of dv);
+// Mapping to gfx950.  One workgroup of 12 waves owns one (sequence, head, 64-column slice of dv);
 // the two slices of a head are dispatched to the same XCD so their shared q/k/g reads meet in
 // that XCD's L2.  The work of a tile is split into three stages that run as a software pipeline,
 // one tile apart, separated by a single workgroup barrier per tile:
-//   stage A (waves 0-3, tile i+2): wave s loads key channels [32s, 32s+32) of q, k, g and value
+//   stage A (waves 4-7, tile i+3): wave s loads key channels [32s, 32s+32) of q, k, g and value
 //      columns [16s, 16s+16) of the slice, runs the cumulative log-decay as a product with a
 //      triangular 0/1 matrix, and forms the decayed operands Kp, Qp, Kd (the exponentials are
 //      the only transcendental work);
-//   stage B (waves 4-7, tile i+1): every wave forms A, A^T, P^T over all 128 channels, evaluates
-//      T, and forms W and Qpp for key channels [32b, 32b+32), Ut and PUt for columns
-//      [16b, 16b+16), and the channel-major Kd blocks the carry consumes;
+//   stage B (waves 8-11): B1 (tile i+2) forms A, A^T, P^T over all 128 channels and evaluates T;
+//      B2 (tile i+1) forms W and Qpp for key channels [32b, 32b+32), Ut and PUt for columns
+//      [16b, 16b+16), and the channel-major Kd blocks the carry consumes; the two chains belong
+//      to different tiles, so they interleave;
 //   stage S (waves 0-3, tile i): wave s carries its 128 x 16 strip of S, which lives in registers
 //      as eight 16x16 float32 accumulator blocks for the whole sequence, and writes o.
-// Loads run two tiles ahead of their use.  All products use v_mfma_f32_16x16x{16,32}_bf16;
+// Three waves share each SIMD, one per stage.  Loads run two tiles ahead of their use.  All products use v_mfma_f32_16x16x{16,32}_bf16;
 // changes between token-major and channel-major fragments are products with 0/1 selector
 // matrices on the matrix cores (exact for bf16 data), which keeps the vector ALUs for the
 // exponentials and the conversions.
@@ -54,8 +55,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int C = 16;      // tile tokens
 constexpr int D = 128;     // dk = dv
 constexpr int BV = 64;     // dv columns per workgroup
-constexpr int NT = 512;    // threads per workgroup (8 waves)
+constexpr int NT = 768;    // threads per workgroup (12 waves: 4 per stage)
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float L2E_HI = 1.4453125f;          // bf16(log2 e)
+constexpr float L2E_LO = -0.00262451171875f;  // bf16(log2 e - L2E_HI)
 
 __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -119,22 +122,29 @@ struct Raw {
     bool ok;      // token inside the sequence
 };
 
+// Stage-to-stage buffers, grouped by hand-off so that one dynamic base address reaches every
+// member of a group.
+struct FromA {                 // stage A -> stages B1 and B2 (indexed by tile % 3)
+    bf16x8 kp[4][64];          // token-major Kp per 32-channel k-step (operand fragments)
+    bf16x8 kd[4][64];          // token-major Kd
+    bf16x8 qp[4][64];          // token-major Qp
+    f32x4 qpf[8][64];          // Qp in float32 as acc(Qp^T) per 16-channel block (C input)
+    uint2 vraw[4][64];         // token-major V per 16-column strip (A operand of the transpose)
+    float beta[C];
+};
+struct FromB {                 // stage B1 -> B2 and stage B2 -> S (indexed by tile % 2)
+    uint2 kdc[8][64];          // channel-major Kd per block (A operand of Kd^T U)
+    bf16x8 w[4][64];           // A operands of W per 32-channel k-step
+    bf16x8 qpp[4][64];         // A operands of Qpp per 32-channel k-step
+    f32x4 ut[4][64];           // Ut per strip (accumulator fragments)
+    f32x4 put[4][64];          // P Ut per strip
+    uint2 tbt[64];             // acc((T Diag(beta))^T) as bf16 (B1 -> B2)
+    uint2 y3[64];              // acc((P T Diag(beta))^T) as bf16 (B1 -> B2)
+};
 struct Shared {
-    // stage A -> stage B (double-buffered by tile parity)
-    bf16x8 kp[2][4][64];       // token-major Kp per 32-channel k-step (operand fragments)
-    bf16x8 kd[2][4][64];       // token-major Kd
-    bf16x8 qp[2][4][64];       // token-major Qp
-    f32x4 qpf[2][8][64];       // Qp in float32 as acc(Qp^T) per 16-channel block (C input)
-    uint2 vraw[2][4][64];      // token-major V per 16-column strip (A operand of the transpose)
-    float beta[2][C];
-    // stage A -> stage S (triple-buffered)
-    float ec[3][D];            // e^{Gam_C}
-    // stage B -> stage S (double-buffered)
-    uint2 kdc[2][8][64];       // channel-major Kd per block (A operand of Kd^T U)
-    bf16x8 w[2][4][64];        // A operands of W per 32-channel k-step
-    bf16x8 qpp[2][4][64];      // A operands of Qpp per 32-channel k-step
-    f32x4 ut[2][4][64];        // Ut per strip (accumulator fragments)
-    f32x4 put[2][4][64];       // P Ut per strip
+    FromA a[3];
+    FromB b[2];
+    float ec[4][D];            // e^{Gam_C} (stage A -> stage S, tile % 4)
 };
 
 __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
@@ -143,7 +153,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
     const int lane = tid & 63, ln = lane & 15, lg = lane >> 4;
-    const bool stageA = wave < 4;      // waves 0-3: stages A and S; waves 4-7: stage B
+    const int role = wave >> 2;        // 0: stage S, 1: stage A, 2: stage B
     const int s = wave & 3;            // channel group / strip index of this wave
     const int64_t H = a.H;
 
@@ -170,10 +180,16 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             sel[hh][j] = (__bf16)((lg == (ln >> 2) && j == 4 * hh + (ln & 3)) ? 1.f : 0.f);
     bf16x4 eye;      // identity (B operand, K = 16)
     for (int j = 0; j < 4; ++j) eye[j] = (__bf16)((4 * lg + j == ln) ? 1.f : 0.f);
-    bf16x4 scanB;    // M^T with M[i][j] = -1 for j > i: row i of M g gives -sum_{j>i} g_j
-    for (int j = 0; j < 4; ++j) scanB[j] = (__bf16)((4 * lg + j > ln) ? -1.f : 0.f);
-    bf16x4 onesB;    // all ones: every row of the product gives Gam_C = sum_j g_j
-    for (int j = 0; j < 4; ++j) onesB[j] = (__bf16)1.f;
+    // M^T scaled by log2(e) as a two-term bf16 split (hi + lo = log2(e) to 5e-6 relative), with
+    // M[i][j] = -1 for j > i: row i of M g gives -log2(e) sum_{j>i} g_j, the exponent in base 2
+    bf16x4 scanHi, scanLo;
+    for (int j = 0; j < 4; ++j) {
+        const bool up = 4 * lg + j > ln;
+        scanHi[j] = (__bf16)(up ? -L2E_HI : 0.f);
+        scanLo[j] = (__bf16)(up ? -L2E_LO : 0.f);
+    }
+    bf16x4 onesA;    // all ones (A operand): column c of the product is Gam_C of channel c
+    for (int j = 0; j < 4; ++j) onesA[j] = (__bf16)1.f;
 
     // ---- stage S state: rows 16 mb + 4 lg + r, column col of this workgroup's slice ----
     const int64_t col = (int64_t)slice * BV + 16 * s + ln;
@@ -181,7 +197,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     f32x4 S[8];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) S[mb] = zero4();
-    if (stageA && a.h0) {
+    if (role == 0 && a.h0) {
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
@@ -189,7 +205,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
                 S[mb][r] = a.h0[sbase + (int64_t)(16 * mb + 4 * lg + r) * D + col];
     }
     if (ntiles == 0) {
-        if (stageA && a.hT) {
+        if (role == 0 && a.hT) {
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
@@ -224,63 +240,70 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         run_tok += C;
     };
 
-    // stage A for tile `tile` (its buffers: parity tile & 1, triple index tile % 3)
+    // Buffer indices of a tile: FromA by tile % 3, FromB by tile % 2, ec by tile % 4.
+    auto fa = [&](int64_t tile) -> FromA& { return sh.a[(uint32_t)tile % 3u]; };
+    auto fb = [&](int64_t tile) -> FromB& { return sh.b[(uint32_t)tile & 1u]; };
+    auto ecb = [&](int64_t tile) -> float* { return sh.ec[(uint32_t)tile & 3u]; };
+
+    // stage A for tile `tile`
     auto stage_a = [&](int64_t tile, const Raw& R) {
-        const int b2 = (int)(tile & 1), b3 = (int)(tile % 3);
+        FromA& A = fa(tile);
+        float* ec = ecb(tile);
         const uint2 z = make_uint2(0u, 0u);
         const uint2 g0 = R.ok ? R.g0 : z, g1 = R.ok ? R.g1 : z;
         const float bt = R.ok ? bf16_to_f32(R.b) : 0.f;
         const bf16x8 ga = cat8(as_bf4(g0), as_bf4(g1));
         const f32x4 kf[2] = {unpack4(R.k0), unpack4(R.k1)};
         const f32x4 qf[2] = {unpack4(R.q0), unpack4(R.q1)};
-        f32x4 Gp[2], Gc[2];
+        f32x4 X[2];    // log2(e) * Gp, token-major
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const bf16x4 gc = bf4(mma32(ga, sel[hh], zero4()));   // channel-major g (exact)
-            Gp[hh] = mma16(gc, scanB, zero4());                   // -sums over later tokens
-            Gc[hh] = mma16(gc, onesB, zero4());                   // Gam_C in every row
+            X[hh] = mma16(gc, scanLo, mma16(gc, scanHi, zero4()));
+            // Gam_C of channel 32s + 16hh + ln, in every register and lane group; all four lane
+            // groups store the same value
+            const f32x4 gsum = mma16(onesA, gc, zero4());
+            ec[32 * s + 16 * hh + ln] = __builtin_amdgcn_exp2f(gsum[0] * LOG2E);
         }
         bf16x4 Kpb[2], Qpb[2], Kdb[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            f32x4 kp, kd, qp, ec;
+            f32x4 kp, kd, qp;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float x = Gp[hh][r] * LOG2E;
-                const float e = __builtin_amdgcn_exp2f(x), dd = __builtin_amdgcn_exp2f(-x);
+                const float e = __builtin_amdgcn_exp2f(X[hh][r]);
+                const float dd = __builtin_amdgcn_exp2f(-X[hh][r]);
                 kp[r] = kf[hh][r] * e;
                 qp[r] = qf[hh][r] * e;
                 kd[r] = kf[hh][r] * dd;
-                ec[r] = __builtin_amdgcn_exp2f(Gc[hh][r] * LOG2E);
             }
             Kpb[hh] = bf4(kp);
             Qpb[hh] = bf4(qp);
             Kdb[hh] = bf4(kd);
-            sh.qpf[b2][2 * s + hh][lane] = qp;
-            // the 16 lanes of a lane group hold the same channels: identical values, no branch
-            *reinterpret_cast<f32x4*>(&sh.ec[b3][32 * s + 16 * hh + 4 * lg]) = ec;
+            A.qpf[2 * s + hh][lane] = qp;
         }
-        sh.beta[b2][ln] = bt;   // every writer of an entry holds the same value
-        sh.kp[b2][s][lane] = cat8(Kpb[0], Kpb[1]);
-        sh.qp[b2][s][lane] = cat8(Qpb[0], Qpb[1]);
-        sh.kd[b2][s][lane] = cat8(Kdb[0], Kdb[1]);
-        sh.vraw[b2][s][lane] = R.v;
+        A.beta[ln] = bt;   // every writer of an entry holds the same value
+        A.kp[s][lane] = cat8(Kpb[0], Kpb[1]);
+        A.qp[s][lane] = cat8(Qpb[0], Qpb[1]);
+        A.kd[s][lane] = cat8(Kdb[0], Kdb[1]);
+        A.vraw[s][lane] = R.v;
     };
 
-    // stage B for tile `tile`, wave 4 + s: channels [32s, 32s+32), columns [16s, 16s+16)
-    auto stage_b = [&](int64_t tile) {
-        const int b2 = (int)(tile & 1);
+    // stage B1 for tile `tile`: A, A^T, P^T over all 128 channels and the inverse T; every
+    // stage-B wave evaluates it (identical results) so that no wave waits for another
+    auto stage_b1 = [&](int64_t tile) {
+        const FromA& A = fa(tile);
+        FromB& B = fb(tile);
         f32x4 Am = zero4(), At = zero4(), Pt = zero4();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 kp8 = sh.kp[b2][ks][lane], kd8 = sh.kd[b2][ks][lane];
-            const bf16x8 qp8 = sh.qp[b2][ks][lane];
+            const bf16x8 kp8 = A.kp[ks][lane], kd8 = A.kd[ks][lane], qp8 = A.qp[ks][lane];
             Am = mma32(kp8, kd8, Am);    // A  = Kp Kd^T
             At = mma32(kd8, kp8, At);    // A^T
             Pt = mma32(kd8, qp8, Pt);    // P^T = Kd Qp^T
         }
-        const float bcol = sh.beta[b2][ln];
-        const f32x4 brow = *reinterpret_cast<const f32x4*>(&sh.beta[b2][4 * lg]);
+        const float bcol = A.beta[ln];
+        const f32x4 brow = *reinterpret_cast<const f32x4*>(&A.beta[4 * lg]);
         f32x4 N, Nt, id;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -291,58 +314,71 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             id[r] = (i == ln) ? 1.f : 0.f;
         }
         // T = (I - N)(I + N^2)(I + N^4)(I + N^8); only the transposes that are consumed as A
-        // operands are formed
-        const f32x4 N2 = mul16(Nt, N), N2t = mul16(N, Nt);
-        const f32x4 N4 = mul16(N2t, N2), N4t = mul16(N2, N2t);
-        const f32x4 N8 = mul16(N4t, N4);
-        const f32x4 F1t = id - Nt, F2 = id + N2, F4 = id + N4, F8 = id + N8;
+        // operands are formed; the identity of each factor enters as the product's C input
+        const bf16x4 Nb = bf4(N), Ntb = bf4(Nt);
+        const f32x4 N2 = mma16(Ntb, Nb, zero4()), N2t = mma16(Nb, Ntb, zero4());
+        const bf16x4 N2b = bf4(N2), N2tb = bf4(N2t);
+        const f32x4 N4 = mma16(N2tb, N2b, zero4()), N4t = mma16(N2b, N2tb, zero4());
+        const f32x4 F8 = mma16(bf4(N4t), bf4(N4), id);             // I + N^8
+        const f32x4 F1t = id - Nt, F2 = id + N2, F4 = id + N4;
         const f32x4 Gt = mul16(F2, F1t);               // ((I-N)(I+N^2))^T
         const f32x4 Ht = mul16(F4, Gt);                // (... (I+N^4))^T
-        const f32x4 Tm = mul16(Ht, F8);                // T
-        const f32x4 Tt = mul16(F8, Ht);                // T^T
+        const bf16x4 Htb = bf4(Ht), F8b = bf4(F8);
+        const f32x4 Tm = mma16(Htb, F8b, zero4());     // T
+        const f32x4 Tt = mma16(F8b, Htb, zero4());     // T^T
         f32x4 TbT, Tb;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             TbT[r] = brow[r] * Tt[r];   // (T Diag(beta))^T
             Tb[r] = bcol * Tm[r];       // T Diag(beta)
         }
-        const f32x4 Y3 = mma16(bf4(Tb), bf4(Pt), zero4());   // (P Tb)^T
-        const bf16x4 TbTb = bf4(TbT), Y3b = bf4(Y3), nY3b = bf4(-Y3);
-        // channel-major Kp and Kd of this wave's two 16-channel blocks
-        const bf16x8 kps = sh.kp[b2][s][lane], kds = sh.kd[b2][s][lane];
+        B.tbt[lane] = as_u2(bf4(TbT));
+        B.y3[lane] = as_u2(bf4(mma16(bf4(Tb), bf4(Pt), zero4())));   // (P Tb)^T
+    };
+
+    // stage B2 for tile `tile`, wave 8 + s: W and Qpp for channels [32s, 32s+32), Ut and PUt for
+    // columns [16s, 16s+16), and the channel-major Kd blocks of those channels
+    auto stage_b2 = [&](int64_t tile) {
+        const FromA& A = fa(tile);
+        FromB& B = fb(tile);
+        const uint2 tbu = B.tbt[lane], y3u = B.y3[lane];
+        const bf16x4 TbTb = as_bf4(tbu), Y3b = as_bf4(y3u);
+        const bf16x4 nY3b = as_bf4(make_uint2(y3u.x ^ 0x80008000u, y3u.y ^ 0x80008000u));
+        const bf16x8 kps = A.kp[s][lane], kds = A.kd[s][lane];
         bf16x4 Wf[2], Qf[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const bf16x4 kpc = bf4(mma32(kps, sel[hh], zero4()));
-            sh.kdc[b2][2 * s + hh][lane] = as_u2(bf4(mma32(kds, sel[hh], zero4())));
-            Wf[hh] = bf4(mma16(kpc, TbTb, zero4()));                         // W^T
-            Qf[hh] = bf4(mma16(kpc, nY3b, sh.qpf[b2][2 * s + hh][lane]));    // Qpp^T
+            const bf16x4 kpc = bf4(mma32(kps, sel[hh], zero4()));    // channel-major Kp
+            B.kdc[2 * s + hh][lane] = as_u2(bf4(mma32(kds, sel[hh], zero4())));
+            Wf[hh] = bf4(mma16(kpc, TbTb, zero4()));                   // W^T
+            Qf[hh] = bf4(mma16(kpc, nY3b, A.qpf[2 * s + hh][lane]));   // Qpp^T
         }
-        sh.w[b2][s][lane] = cat8(Wf[0], Wf[1]);
-        sh.qpp[b2][s][lane] = cat8(Qf[0], Qf[1]);
-        const bf16x4 vcs = bf4(mma16(as_bf4(sh.vraw[b2][s][lane]), eye, zero4()));  // column-major V
-        sh.ut[b2][s][lane] = mma16(TbTb, vcs, zero4());     // Tb V
-        sh.put[b2][s][lane] = mma16(Y3b, vcs, zero4());     // P Tb V
+        B.w[s][lane] = cat8(Wf[0], Wf[1]);
+        B.qpp[s][lane] = cat8(Qf[0], Qf[1]);
+        const bf16x4 vcs = bf4(mma16(as_bf4(A.vraw[s][lane]), eye, zero4()));  // column-major V
+        B.ut[s][lane] = mma16(TbTb, vcs, zero4());     // Tb V
+        B.put[s][lane] = mma16(Y3b, vcs, zero4());     // P Tb V
     };
 
     // stage S for tile `tile`: strip s; returns the token-major o fragment (stored by the caller)
     auto stage_s = [&](int64_t tile) -> bf16x4 {
-        const int b2 = (int)(tile & 1), b3 = (int)(tile % 3);
+        const FromB& B = fb(tile);
+        const float* ec = ecb(tile);
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
-            S[mb] *= *reinterpret_cast<const f32x4*>(&sh.ec[b3][16 * mb + 4 * lg]);   // St
+            S[mb] *= *reinterpret_cast<const f32x4*>(&ec[16 * mb + 4 * lg]);   // St
         f32x4 XW = zero4(), XQ = zero4();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const bf16x8 sb = cat8(bf4(S[2 * ks]), bf4(S[2 * ks + 1]));
-            XW = mma32(sh.w[b2][ks][lane], sb, XW);
-            XQ = mma32(sh.qpp[b2][ks][lane], sb, XQ);
+            XW = mma32(B.w[ks][lane], sb, XW);
+            XQ = mma32(B.qpp[ks][lane], sb, XQ);
         }
-        const f32x4 U = sh.ut[b2][s][lane] - XW;
-        const f32x4 O = XQ + sh.put[b2][s][lane];
+        const f32x4 U = B.ut[s][lane] - XW;
+        const f32x4 O = XQ + B.put[s][lane];
         const bf16x4 Ub = bf4(U);
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb) S[mb] = mma16(as_bf4(sh.kdc[b2][mb][lane]), Ub, S[mb]);
+        for (int mb = 0; mb < 8; ++mb) S[mb] = mma16(as_bf4(B.kdc[mb][lane]), Ub, S[mb]);
         return bf4(mma16(bf4(O), eye, zero4()));    // token-major o
     };
     auto store_o = [&](int64_t tile, bf16x4 Ot, bool masked) {
@@ -351,51 +387,63 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         if (!masked || t0 + ln < eos) *reinterpret_cast<uint2*>(dst) = as_u2(Ot);
     };
 
-    // Iteration i runs A(i+2), B(i+1) and S(i).  Each role has its own loop with the same
-    // number of barriers, so that its body is straight-line code; the loops are unrolled by two
-    // so that the in-flight loads of R0 / R1 never need a register copy.  An odd tile count runs
-    // one extra tile past the end: its inputs are all zero (k = 0: no write; g = 0: no decay),
-    // so it leaves the state unchanged and stores nothing.
+    // Iteration i runs A(i+3), B1(i+2), B2(i+1) and S(i) with one barrier per iteration (the
+    // same count in every role).  The stage-A loop is unrolled by two so that the in-flight loads
+    // of R0 / R1 never need a register copy.  An odd tile count runs one extra tile past the
+    // end, and stages A and B run up to three tiles past it: those tiles' inputs are all zero
+    // (k = 0: no write; g = 0: no decay), so they leave the state unchanged and store nothing.
     const int64_t nsteps = ntiles + (ntiles & 1);
-    if (stageA) {
-        Raw R0, R1, Rt;
-        load_tile(Rt);
-        load_tile(R1);
-        stage_a(0, Rt);
+    if (role == 1) {
+        Raw R0, R1;
+        load_tile(R0);     // tile 0
+        load_tile(R1);     // tile 1
+        stage_a(0, R0);
+        load_tile(R0);     // tile 2
         lds_barrier();
         stage_a(1, R1);
-        load_tile(R0);
-        load_tile(R1);
+        load_tile(R1);     // tile 3
         lds_barrier();
-        auto iteration = [&](int64_t i, Raw& R, bool masked) {
-            const bf16x4 Ot = stage_s(i);
-            stage_a(i + 2, R);
-            load_tile(R);      // tile i + 4
-            store_o(i, Ot, masked);
+        stage_a(2, R0);
+        load_tile(R0);     // tile 4
+        lds_barrier();
+        for (int64_t i = 0; i < nsteps; i += 2) {
+            stage_a(i + 3, R1);
+            load_tile(R1);     // tile i + 5
             lds_barrier();
-        };
-        // tiles whose 16 tokens all lie inside the sequence store without a mask
-        const int64_t nfull = ((eos - bos) / C) & ~(int64_t)1;
-        int64_t i = 0;
-        for (; i < nfull; i += 2) {
-            iteration(i, R0, false);
-            iteration(i + 1, R1, false);
+            stage_a(i + 4, R0);
+            load_tile(R0);     // tile i + 6
+            lds_barrier();
         }
-        for (; i < nsteps; i += 2) {
-            iteration(i, R0, true);
-            iteration(i + 1, R1, true);
+    } else if (role == 2) {
+        lds_barrier();
+        stage_b1(0);
+        lds_barrier();
+        stage_b1(1);
+        stage_b2(0);
+        lds_barrier();
+        for (int64_t i = 0; i < nsteps; ++i) {
+            stage_b1(i + 2);
+            stage_b2(i + 1);
+            lds_barrier();
         }
     } else {
         lds_barrier();
-        stage_b(0);
         lds_barrier();
-        for (int64_t i = 0; i < nsteps; ++i) {
-            stage_b(i + 1);
+        lds_barrier();
+        // tiles whose 16 tokens all lie inside the sequence store without a mask
+        const int64_t nfull = (eos - bos) / C;
+        int64_t i = 0;
+        for (; i < nfull; ++i) {
+            store_o(i, stage_s(i), false);
+            lds_barrier();
+        }
+        for (; i < nsteps; ++i) {
+            store_o(i, stage_s(i), true);
             lds_barrier();
         }
     }
 
-    if (stageA && a.hT) {
+    if (role == 0 && a.hT) {
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
