@@ -6,7 +6,9 @@
 // from first principles", paragraph "What the state costs": a fixed 128 x 128 state per head.)
 //
 // The step is bound by HBM: each (sequence, head) reads and writes its 64 KiB state once and
-// does ~7 flops per state element.  One workgroup of 256 threads owns one (sequence, head):
+// does ~7 flops per state element.  A workgroup of 256 threads owns two (sequence, head) pairs
+// (one when N * H is odd) and requests both states before reducing the first, so one head's
+// loads overlap the other's reduction and stores.  Per head:
 // thread (rg, cg) holds rows rg, rg+8, ..., rg+120 (16 rows) x columns 4cg..4cg+3 of S in
 // registers as 16 float4, so the state is loaded once with full 16-byte accesses, reduced over
 // the key axis (two column partial sums S'^T k and S'^T q, plus k.q) with one cross-lane step
@@ -52,90 +54,108 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float x[4]) {
 constexpr int D = 128;
 constexpr int NRED = 9;  // per column group: S'^T k (4), S'^T q (4), k.q
 
-template <typename Tin>
+// HPW heads per workgroup: every head's 64 KiB state is requested before the first one is
+// reduced, so the second head's loads are in flight while the first head is reduced and stored.
+template <typename Tin, int HPW>
 __global__ __launch_bounds__(256) void kda_decode_d128_kernel(DecodeArgs a) {
-    __shared__ float sk[D], sq[D], sa[D];
-    __shared__ float red[4][32][NRED + 1];
+    __shared__ float sk[HPW][D], sq[HPW][D], sa[HPW][D];
+    __shared__ float red[HPW][4][32][NRED + 1];
 
     const int tid = threadIdx.x;
     const int cg = tid & 31;          // columns 4cg .. 4cg+3
     const int rg = tid >> 5;          // rows rg + 8 i
-    const int64_t unit = blockIdx.x;  // n * H + h
-    float* S = a.S + unit * (int64_t)(D * D);
-
-    // issue the whole state slice first (64 KiB per workgroup in flight)
-    f4 s[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-        s[i] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(S + (rg + 8 * i) * D + 4 * cg));
-
-    const Tin* q = static_cast<const Tin*>(a.q) + unit * D;
-    const Tin* k = static_cast<const Tin*>(a.k) + unit * D;
-    const Tin* g = static_cast<const Tin*>(a.g) + unit * D;
-    if (tid < D) {
-        sk[tid] = io<Tin>::load(k + tid);
-        sq[tid] = io<Tin>::load(q + tid);
-        sa[tid] = __expf(io<Tin>::load(g + tid));
-    }
-    float vv[4];
-    load4<Tin>(static_cast<const Tin*>(a.v) + unit * D + 4 * cg, vv);
-    const float b = io<Tin>::load(static_cast<const Tin*>(a.beta) + unit);
-    __syncthreads();
-
-    // fade and partial reductions over this thread's 16 rows
-    float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int r = rg + 8 * i;
-        const float al = sa[r], kr = sk[r], qr = sq[r];
-        s[i] *= al;
-        pk[0] += s[i].x * kr; pk[1] += s[i].y * kr; pk[2] += s[i].z * kr; pk[3] += s[i].w * kr;
-        pq[0] += s[i].x * qr; pq[1] += s[i].y * qr; pq[2] += s[i].z * qr; pq[3] += s[i].w * qr;
-        kq += kr * qr;
-    }
-    // lanes l and l^32 of a wave hold row groups 2w and 2w+1 of the same columns
-    float part[NRED] = {pk[0], pk[1], pk[2], pk[3], pq[0], pq[1], pq[2], pq[3], kq};
-#pragma unroll
-    for (int j = 0; j < NRED; ++j) part[j] += __shfl_xor(part[j], 32, 64);
     const int w = tid >> 6, lane = tid & 63;
-    if (lane < 32) {
+    const int64_t unit0 = (int64_t)blockIdx.x * HPW;   // (n * H + h) of the first head
+
+    f4 s[HPW][16];
+    float vv[HPW][4], b[HPW];
 #pragma unroll
-        for (int j = 0; j < NRED; ++j) red[w][lane][j] = part[j];
+    for (int hp = 0; hp < HPW; ++hp) {
+        const int64_t unit = unit0 + hp;
+        const float* S = a.S + unit * (int64_t)(D * D);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            s[hp][i] = __builtin_nontemporal_load(
+                reinterpret_cast<const f4*>(S + (rg + 8 * i) * D + 4 * cg));
+    }
+#pragma unroll
+    for (int hp = 0; hp < HPW; ++hp) {
+        const int64_t unit = unit0 + hp;
+        const Tin* q = static_cast<const Tin*>(a.q) + unit * D;
+        const Tin* k = static_cast<const Tin*>(a.k) + unit * D;
+        const Tin* g = static_cast<const Tin*>(a.g) + unit * D;
+        if (tid < D) {
+            sk[hp][tid] = io<Tin>::load(k + tid);
+            sq[hp][tid] = io<Tin>::load(q + tid);
+            sa[hp][tid] = __expf(io<Tin>::load(g + tid));
+        }
+        load4<Tin>(static_cast<const Tin*>(a.v) + unit * D + 4 * cg, vv[hp]);
+        b[hp] = io<Tin>::load(static_cast<const Tin*>(a.beta) + unit);
     }
     __syncthreads();
-    float tot[NRED];
-#pragma unroll
-    for (int j = 0; j < NRED; ++j)
-        tot[j] = red[0][cg][j] + red[1][cg][j] + red[2][cg][j] + red[3][cg][j];
-
-    float u[4], out[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        u[j] = b * (vv[j] - tot[j]);
-        out[j] = tot[4 + j] + tot[8] * u[j];
-    }
-    if (rg == 0) store4<Tin>(static_cast<Tin*>(a.o) + unit * D + 4 * cg, out);
 
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float kr = sk[rg + 8 * i];
-        f4 y = s[i];
-        y.x += kr * u[0]; y.y += kr * u[1]; y.z += kr * u[2]; y.w += kr * u[3];
-        __builtin_nontemporal_store(y, reinterpret_cast<f4*>(S + (rg + 8 * i) * D + 4 * cg));
+    for (int hp = 0; hp < HPW; ++hp) {
+        const int64_t unit = unit0 + hp;
+        // fade and partial reductions over this thread's 16 rows
+        float part[NRED] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = rg + 8 * i;
+            const float al = sa[hp][r], kr = sk[hp][r], qr = sq[hp][r];
+            s[hp][i] *= al;
+            part[0] += s[hp][i].x * kr; part[1] += s[hp][i].y * kr;
+            part[2] += s[hp][i].z * kr; part[3] += s[hp][i].w * kr;
+            part[4] += s[hp][i].x * qr; part[5] += s[hp][i].y * qr;
+            part[6] += s[hp][i].z * qr; part[7] += s[hp][i].w * qr;
+            part[8] += kr * qr;
+        }
+        // lanes l and l^32 of a wave hold row groups 2w and 2w+1 of the same columns
+#pragma unroll
+        for (int j = 0; j < NRED; ++j) part[j] += __shfl_xor(part[j], 32, 64);
+        if (lane < 32) {
+#pragma unroll
+            for (int j = 0; j < NRED; ++j) red[hp][w][lane][j] = part[j];
+        }
+        __syncthreads();
+        float tot[NRED];
+#pragma unroll
+        for (int j = 0; j < NRED; ++j)
+            tot[j] = red[hp][0][cg][j] + red[hp][1][cg][j] + red[hp][2][cg][j] + red[hp][3][cg][j];
+
+        float u[4], out[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u[j] = b[hp] * (vv[hp][j] - tot[j]);
+            out[j] = tot[4 + j] + tot[8] * u[j];
+        }
+        if (rg == 0) store4<Tin>(static_cast<Tin*>(a.o) + unit * D + 4 * cg, out);
+
+        float* S = a.S + unit * (int64_t)(D * D);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float kr = sk[hp][rg + 8 * i];
+            f4 y = s[hp][i];
+            y.x += kr * u[0]; y.y += kr * u[1]; y.z += kr * u[2]; y.w += kr * u[3];
+            __builtin_nontemporal_store(y, reinterpret_cast<f4*>(S + (rg + 8 * i) * D + 4 * cg));
+        }
     }
 }
 
 }  // namespace
 
 hipError_t launch_decode_d128(const DecodeArgs& a, hipStream_t s) {
-    const int64_t grid = a.N * a.H;
-    if (grid <= 0) return hipSuccess;
-    if (a.dtype == 0)
-        hipLaunchKernelGGL(kda_decode_d128_kernel<bf16_t>, dim3((unsigned)grid), dim3(256), 0, s,
-                           a);
-    else
-        hipLaunchKernelGGL(kda_decode_d128_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s,
-                           a);
+    const int64_t units = a.N * a.H;
+    if (units <= 0) return hipSuccess;
+    const bool pair = (units % 2) == 0;
+    const dim3 grid((unsigned)(pair ? units / 2 : units));
+    if (a.dtype == 0) {
+        if (pair) hipLaunchKernelGGL((kda_decode_d128_kernel<bf16_t, 2>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((kda_decode_d128_kernel<bf16_t, 1>), grid, dim3(256), 0, s, a);
+    } else {
+        if (pair) hipLaunchKernelGGL((kda_decode_d128_kernel<float, 2>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((kda_decode_d128_kernel<float, 1>), grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 
