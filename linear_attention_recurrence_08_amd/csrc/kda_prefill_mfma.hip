@@ -18,22 +18,23 @@
 //
 // Mapping to gfx950.  One workgroup of 12 waves owns one (sequence, head, 64-column slice of dv);
 // the two slices of a head are dispatched to the same XCD so their shared q/k/g reads meet in
-// that XCD's L2.  The work of a tile is split into three stages that run as a software pipeline,
-// one tile apart, separated by a single workgroup barrier per tile:
-//   stage A (waves 4-7, tile i+3): wave s loads key channels [32s, 32s+32) of q, k, g and value
-//      columns [16s, 16s+16) of the slice, runs the cumulative log-decay as a product with a
-//      triangular 0/1 matrix, and forms the decayed operands Kp, Qp, Kd (the exponentials are
-//      the only transcendental work);
-//   stage B (waves 8-11): B1 (tile i+2) forms A, A^T, P^T over all 128 channels and evaluates T;
-//      B2 (tile i+1) forms W and Qpp for key channels [32b, 32b+32), Ut and PUt for columns
-//      [16b, 16b+16), and the channel-major Kd blocks the carry consumes; the two chains belong
-//      to different tiles, so they interleave;
-//   stage S (waves 0-3, tile i): wave s carries its 128 x 16 strip of S, which lives in registers
-//      as eight 16x16 float32 accumulator blocks for the whole sequence, and writes o.
-// Three waves share each SIMD, one per stage.  Loads run two tiles ahead of their use.  All products use v_mfma_f32_16x16x{16,32}_bf16;
-// changes between token-major and channel-major fragments are products with 0/1 selector
-// matrices on the matrix cores (exact for bf16 data), which keeps the vector ALUs for the
-// exponentials and the conversions.
+// that XCD's L2.  Each wave keeps one role for the whole sequence, and the work of a tile runs
+// as a software pipeline with a single workgroup barrier per period; period q holds
+//   stage A (waves 4-7) for tile q: wave s loads key channels [32s, 32s+32) of q, k, g and value
+//      columns [16s, 16s+16) of the slice through buffer resources, runs the cumulative
+//      log-decay as a product with a triangular 0/1 matrix, and forms the decayed operands Kp,
+//      Qp, Kd (the exponentials are the only transcendental work);
+//   stage B1 (waves 8-11) for tiles q-1 and q-2: A, A^T, P^T over all 128 channels and T, split
+//      into two halves that run in consecutive periods; waves 8-9 take even tiles and waves
+//      10-11 odd ones, so each SIMD carries half an inverse per period;
+//   stage B2 (waves 0-3) for tile q-3: W and Qpp for key channels [32s, 32s+32), Ut and PUt
+//      for columns [16s, 16s+16), and the channel-major Kd blocks the carry consumes;
+//   stage S (waves 0-3) for tile q-4: wave s carries its 128 x 16 strip of S, which lives in
+//      registers as eight 16x16 float32 accumulator blocks for the whole sequence, and writes o.
+// Three waves share each SIMD.  Loads run two tiles ahead of their use.  All products use
+// v_mfma_f32_16x16x{16,32}_bf16.  Token-major -> channel-major changes of layout are LDS transpose
+// reads where the data already sits in LDS, and products with 0/1 selector matrices on the
+// matrix cores otherwise (both exact for bf16 data).
 //
 // Fragment conventions for a 16x16 block, lane l = ln + 16 lg (ln = l % 16, lg = l / 16):
 //   accumulator  acc(X): register r holds X[4 lg + r][ln]
@@ -86,6 +87,22 @@ __device__ __forceinline__ f32x4 unpack4(uint2 u) {  // bf16 x4 -> float32 x4 (e
     return (f32x4){__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                    __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
 }
+// LDS transpose read (ds_read_b64_tr_b16): in each group of 16 lanes, lane i receives, as
+// element e, element i % 4 of the four 16-bit values that lane 4e + i / 4 of the group addresses.
+// With lane 16q + 4r + a addressing the four values (row 4q + r, columns 4a .. 4a+3) of a
+// row-major 16 x 16 block, lane 16q + i receives column i of rows 4q .. 4q+3: the accumulator
+// layout of the block (the transpose of its row-major operand fragment).
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_tr16(const void* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+}
+// Raw buffer resource word 3 for gfx9 (32-bit data format, no swizzle, no thread-id offset);
+// loads past the record count return zero.
+constexpr int kBufferFlags = 0x00020000;
+__device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
 // Workgroup barrier that orders LDS only: global loads issued before it stay in flight (a full
 // __syncthreads() would also wait for the prefetched tiles).
 __device__ __forceinline__ void lds_barrier() {
@@ -93,8 +110,6 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
-// Z = X Y given acc(X^T) and acc(Y) in float32 (rounded to bf16 for the matrix core)
-__device__ __forceinline__ f32x4 mul16(f32x4 xT, f32x4 y) { return mma16(bf4(xT), bf4(y), zero4()); }
 
 // (workgroup index) -> (pair index p = n * H + head, slice) with both slices of a pair on one XCD
 // (workgroups are dealt to the 8 XCDs round-robin by index).
@@ -112,19 +127,18 @@ __device__ __forceinline__ void map_workgroup(int64_t b, int64_t pairs, int64_t&
 }
 
 // Raw inputs of one tile for one stage-A lane: token ln, key channels 32s + 16hh + 4lg + r,
-// value columns 16s + 4lg + r of the slice, beta of token ln.  Lanes whose token lies past the
-// sequence end load a clamped (valid) token; only their g and beta are zeroed, at the point of
-// use: with beta = 0 a padded token's rows of T Diag(beta), Ut and U vanish, so its q, k and v
-// never reach a stored output or the state.
+// value columns 16s + 4lg + r of the slice, beta of token ln.  They are read through buffer
+// resources whose record count ends at the sequence's last token, so a token past the end (and
+// every token of a tile past the end) reads as zero: with beta = 0 and k = v = 0 it neither
+// writes the state nor reaches a stored output, and with g = 0 it does not decay the state.
 struct Raw {
     uint2 q0, q1, k0, k1, g0, g1, v;
-    bf16_t b;     // raw bf16 bits of beta
-    bool ok;      // token inside the sequence
+    uint32_t b;   // raw bf16 bits of beta in the low half
 };
 
 // Stage-to-stage buffers, grouped by hand-off so that one dynamic base address reaches every
 // member of a group.
-struct FromA {                 // stage A -> stages B1 and B2 (indexed by tile % 3)
+struct FromA {                 // stage A -> stages B1 and B2 (indexed by tile % 4)
     bf16x8 kp[4][64];          // token-major Kp per 32-channel k-step (operand fragments)
     bf16x8 kd[4][64];          // token-major Kd
     bf16x8 qp[4][64];          // token-major Qp
@@ -132,19 +146,22 @@ struct FromA {                 // stage A -> stages B1 and B2 (indexed by tile %
     uint2 vraw[4][64];         // token-major V per 16-column strip (A operand of the transpose)
     float beta[C];
 };
-struct FromB {                 // stage B1 -> B2 and stage B2 -> S (indexed by tile % 2)
+struct FromB1 {                // stage B1 -> stage B2 (indexed by tile % 2)
+    uint2 tbt[64];             // acc((T Diag(beta))^T) as bf16
+    uint2 y3[64];              // acc((P T Diag(beta))^T) as bf16
+};
+struct FromB {                 // stage B2 -> stage S (indexed by tile % 2)
     uint2 kdc[8][64];          // channel-major Kd per block (A operand of Kd^T U)
     bf16x8 w[4][64];           // A operands of W per 32-channel k-step
     bf16x8 qpp[4][64];         // A operands of Qpp per 32-channel k-step
     f32x4 ut[4][64];           // Ut per strip (accumulator fragments)
     f32x4 put[4][64];          // P Ut per strip
-    uint2 tbt[64];             // acc((T Diag(beta))^T) as bf16 (B1 -> B2)
-    uint2 y3[64];              // acc((P T Diag(beta))^T) as bf16 (B1 -> B2)
 };
 struct Shared {
-    FromA a[3];
+    FromA a[4];
     FromB b[2];
-    float ec[4][D];            // e^{Gam_C} (stage A -> stage S, tile % 4)
+    FromB1 b1[2];
+    float ec[8][D];            // e^{Gam_C} (stage A -> stage S, tile % 8)
 };
 
 __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
@@ -188,6 +205,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         scanHi[j] = (__bf16)(up ? -L2E_HI : 0.f);
         scanLo[j] = (__bf16)(up ? -L2E_LO : 0.f);
     }
+    const bf16x8 scanHL = cat8(scanHi, scanLo);   // both terms in one K = 32 product
     bf16x4 onesA;    // all ones (A operand): column c of the product is Gam_C of channel c
     for (int j = 0; j < 4; ++j) onesA[j] = (__bf16)1.f;
 
@@ -215,51 +233,67 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         return;
     }
 
-    // ---- stage A: loads.  Offsets advance by one tile per call (tiles are loaded in order);
-    //      a token past the sequence end reads the sequence's last token instead ----
+    // ---- stage A: loads.  Tile j of the sequence starts at token bos + 16 j; its buffer
+    //      resources start at that token's head row (scalar base) and end after the last token
+    //      of the sequence that the tile holds; lanes add a fixed byte offset ----
     const int64_t chan0 = 32 * s + 4 * lg;
     const int64_t vcol0 = (int64_t)slice * BV + 16 * s + 4 * lg;
-    const int64_t tstride = (int64_t)C * H * D;
-    const int64_t last_off = ((eos - 1) * H + h) * D;
-    int64_t run_off = ((bos + ln) * H + h) * D;     // element offset of this lane's next token
-    int64_t run_tok = ln;                           // its index within the sequence
     const int64_t len = eos - bos;
+    const int64_t row_bytes = H * D * 2;                       // one token, all heads
+    const uint32_t vo_qkg = (uint32_t)(ln * row_bytes + chan0 * 2);
+    const uint32_t vo_v = (uint32_t)(ln * row_bytes + vcol0 * 2);
+    const uint32_t vo_b = (uint32_t)(ln * H * 2);
+    int ld_tile = 0;                                           // next tile to load (uniform)
+    const int len32 = (int)len;                                // token counts fit int32 (ABI)
+    const int rb32 = (int)row_bytes, hb32 = (int)(H * 2);
     auto load_tile = [&](Raw& R) {
-        const bool ok = run_tok < len;
-        const int64_t off = ok ? run_off : last_off;
-        R.q0 = *reinterpret_cast<const uint2*>(q + off + chan0);
-        R.q1 = *reinterpret_cast<const uint2*>(q + off + chan0 + 16);
-        R.k0 = *reinterpret_cast<const uint2*>(k + off + chan0);
-        R.k1 = *reinterpret_cast<const uint2*>(k + off + chan0 + 16);
-        R.g0 = *reinterpret_cast<const uint2*>(g + off + chan0);
-        R.g1 = *reinterpret_cast<const uint2*>(g + off + chan0 + 16);
-        R.v = *reinterpret_cast<const uint2*>(v + off + vcol0);
-        R.b = beta[off / D];
-        R.ok = ok;
-        run_off += tstride;
-        run_tok += C;
+        const int64_t t0 = bos + (int64_t)ld_tile * C;
+        // tokens of the sequence held by this tile, 0..16; the record counts end after the last
+        // of them (row_bytes >= 256 and H >= 1 make both counts 0 for an empty tile)
+        const int nv = min(max(len32 - ld_tile * C, 0), C);
+        const int nrec = max((nv - 1) * rb32 + D * 2, 0);
+        const int nrec_b = max((nv - 1) * hb32 + 2, 0);
+        const int64_t e0 = (t0 * H + h) * D;                   // element offset of the head row
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(q + e0), (short)0, nrec, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(k + e0), (short)0, nrec, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(g + e0), (short)0, nrec, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(v + e0), (short)0, nrec, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(beta + (t0 * H + h)), (short)0, nrec_b, kBufferFlags);
+        R.q0 = ld8(rq, vo_qkg);
+        R.q1 = ld8(rq, vo_qkg + 32);
+        R.k0 = ld8(rk, vo_qkg);
+        R.k1 = ld8(rk, vo_qkg + 32);
+        R.g0 = ld8(rg, vo_qkg);
+        R.g1 = ld8(rg, vo_qkg + 32);
+        R.v = ld8(rv, vo_v);
+        R.b = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, vo_b, 0, 0);
+        ++ld_tile;
     };
 
-    // Buffer indices of a tile: FromA by tile % 3, FromB by tile % 2, ec by tile % 4.
-    auto fa = [&](int64_t tile) -> FromA& { return sh.a[(uint32_t)tile % 3u]; };
+    // Buffer indices of a tile: FromA by tile % 4, FromB and FromB1 by tile % 2, ec by tile % 8.
+    auto fa = [&](int64_t tile) -> FromA& { return sh.a[(uint32_t)tile & 3u]; };
     auto fb = [&](int64_t tile) -> FromB& { return sh.b[(uint32_t)tile & 1u]; };
-    auto ecb = [&](int64_t tile) -> float* { return sh.ec[(uint32_t)tile & 3u]; };
+    auto fb1 = [&](int64_t tile) -> FromB1& { return sh.b1[(uint32_t)tile & 1u]; };
+    auto ecb = [&](int64_t tile) -> float* { return sh.ec[(uint32_t)tile & 7u]; };
 
     // stage A for tile `tile`
     auto stage_a = [&](int64_t tile, const Raw& R) {
         FromA& A = fa(tile);
         float* ec = ecb(tile);
-        const uint2 z = make_uint2(0u, 0u);
-        const uint2 g0 = R.ok ? R.g0 : z, g1 = R.ok ? R.g1 : z;
-        const float bt = R.ok ? bf16_to_f32(R.b) : 0.f;
-        const bf16x8 ga = cat8(as_bf4(g0), as_bf4(g1));
+        const float bt = __uint_as_float(R.b << 16);
+        const bf16x8 ga = cat8(as_bf4(R.g0), as_bf4(R.g1));
         const f32x4 kf[2] = {unpack4(R.k0), unpack4(R.k1)};
         const f32x4 qf[2] = {unpack4(R.q0), unpack4(R.q1)};
         f32x4 X[2];    // log2(e) * Gp, token-major
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const bf16x4 gc = bf4(mma32(ga, sel[hh], zero4()));   // channel-major g (exact)
-            X[hh] = mma16(gc, scanLo, mma16(gc, scanHi, zero4()));
+            X[hh] = mma32(cat8(gc, gc), scanHL, zero4());
             // Gam_C of channel 32s + 16hh + ln, in every register and lane group; all four lane
             // groups store the same value
             const f32x4 gsum = mma16(onesA, gc, zero4());
@@ -289,11 +323,13 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         A.vraw[s][lane] = R.v;
     };
 
-    // stage B1 for tile `tile`: A, A^T, P^T over all 128 channels and the inverse T; every
-    // stage-B wave evaluates it (identical results) so that no wave waits for another
-    auto stage_b1 = [&](int64_t tile) {
+    // stage B1 for tile `tile`: A, A^T, P^T over all 128 channels and the inverse T, in two
+    // halves that run in consecutive periods (the registers in B1Carry cross the barrier).  Waves
+    // 8 and 9 take the even tiles and waves 10 and 11 the odd ones, so every SIMD runs one half
+    // per period; the two waves of a pair compute identical results.
+    struct B1Carry { f32x4 N4, N4t, Gt, Pt, brow; float bcol; };
+    auto stage_b1a = [&](int64_t tile) -> B1Carry {
         const FromA& A = fa(tile);
-        FromB& B = fb(tile);
         f32x4 Am = zero4(), At = zero4(), Pt = zero4();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -302,38 +338,46 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             At = mma32(kd8, kp8, At);    // A^T
             Pt = mma32(kd8, qp8, Pt);    // P^T = Kd Qp^T
         }
-        const float bcol = A.beta[ln];
-        const f32x4 brow = *reinterpret_cast<const f32x4*>(&A.beta[4 * lg]);
-        f32x4 N, Nt, id;
+        B1Carry c;
+        c.bcol = A.beta[ln];
+        c.brow = *reinterpret_cast<const f32x4*>(&A.beta[4 * lg]);
+        f32x4 N, Nt, F1t;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 4 * lg + r;
-            N[r] = (ln < i) ? brow[r] * Am[r] : 0.f;    // N[i][ln]
-            Nt[r] = (i < ln) ? bcol * At[r] : 0.f;      // N^T[i][ln]
-            Pt[r] = (i <= ln) ? Pt[r] : 0.f;            // P^T[i][ln]
-            id[r] = (i == ln) ? 1.f : 0.f;
+            N[r] = (ln < i) ? c.brow[r] * Am[r] : 0.f;    // N[i][ln]
+            Nt[r] = (i < ln) ? c.bcol * At[r] : 0.f;      // N^T[i][ln]
+            c.Pt[r] = (i <= ln) ? Pt[r] : 0.f;            // P^T[i][ln]
+            F1t[r] = ((i == ln) ? 1.f : 0.f) - Nt[r];     // (I - N)^T
         }
         // T = (I - N)(I + N^2)(I + N^4)(I + N^8); only the transposes that are consumed as A
         // operands are formed; the identity of each factor enters as the product's C input
         const bf16x4 Nb = bf4(N), Ntb = bf4(Nt);
         const f32x4 N2 = mma16(Ntb, Nb, zero4()), N2t = mma16(Nb, Ntb, zero4());
         const bf16x4 N2b = bf4(N2), N2tb = bf4(N2t);
-        const f32x4 N4 = mma16(N2tb, N2b, zero4()), N4t = mma16(N2b, N2tb, zero4());
-        const f32x4 F8 = mma16(bf4(N4t), bf4(N4), id);             // I + N^8
-        const f32x4 F1t = id - Nt, F2 = id + N2, F4 = id + N4;
-        const f32x4 Gt = mul16(F2, F1t);               // ((I-N)(I+N^2))^T
-        const f32x4 Ht = mul16(F4, Gt);                // (... (I+N^4))^T
+        c.N4 = mma16(N2tb, N2b, zero4());
+        c.N4t = mma16(N2b, N2tb, zero4());
+        c.Gt = mma16(N2b, bf4(F1t), F1t);             // ((I - N)(I + N^2))^T
+        return c;
+    };
+    auto stage_b1b = [&](int64_t tile, const B1Carry& c) {
+        FromB1& B = fb1(tile);
+        f32x4 id;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) id[r] = (4 * lg + r == ln) ? 1.f : 0.f;
+        const f32x4 F8 = mma16(bf4(c.N4t), bf4(c.N4), id);          // I + N^8
+        const f32x4 Ht = mma16(bf4(c.N4), bf4(c.Gt), c.Gt);   // ((I-N)(I+N^2)(I+N^4))^T
         const bf16x4 Htb = bf4(Ht), F8b = bf4(F8);
         const f32x4 Tm = mma16(Htb, F8b, zero4());     // T
         const f32x4 Tt = mma16(F8b, Htb, zero4());     // T^T
         f32x4 TbT, Tb;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            TbT[r] = brow[r] * Tt[r];   // (T Diag(beta))^T
-            Tb[r] = bcol * Tm[r];       // T Diag(beta)
+            TbT[r] = c.brow[r] * Tt[r];   // (T Diag(beta))^T
+            Tb[r] = c.bcol * Tm[r];       // T Diag(beta)
         }
         B.tbt[lane] = as_u2(bf4(TbT));
-        B.y3[lane] = as_u2(bf4(mma16(bf4(Tb), bf4(Pt), zero4())));   // (P Tb)^T
+        B.y3[lane] = as_u2(bf4(mma16(bf4(Tb), bf4(c.Pt), zero4())));   // (P Tb)^T
     };
 
     // stage B2 for tile `tile`, wave 8 + s: W and Qpp for channels [32s, 32s+32), Ut and PUt for
@@ -341,21 +385,25 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     auto stage_b2 = [&](int64_t tile) {
         const FromA& A = fa(tile);
         FromB& B = fb(tile);
-        const uint2 tbu = B.tbt[lane], y3u = B.y3[lane];
+        const uint2 tbu = fb1(tile).tbt[lane], y3u = fb1(tile).y3[lane];
         const bf16x4 TbTb = as_bf4(tbu), Y3b = as_bf4(y3u);
         const bf16x4 nY3b = as_bf4(make_uint2(y3u.x ^ 0x80008000u, y3u.y ^ 0x80008000u));
-        const bf16x8 kps = A.kp[s][lane], kds = A.kd[s][lane];
+        // channel-major blocks by transpose reads of the token-major fragments: this lane
+        // addresses token 4lg + ln / 4, channels 4 (ln % 4) .. +3 of each 16-channel half,
+        // which stage-A lane (token) + 16 (ln % 4) stored
+        const int src = 4 * lg + (ln >> 2) + 16 * (ln & 3);
         bf16x4 Wf[2], Qf[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const bf16x4 kpc = bf4(mma32(kps, sel[hh], zero4()));    // channel-major Kp
-            B.kdc[2 * s + hh][lane] = as_u2(bf4(mma32(kds, sel[hh], zero4())));
+            const bf16x4 kpc = lds_tr16(reinterpret_cast<const char*>(&A.kp[s][src]) + 8 * hh);
+            B.kdc[2 * s + hh][lane] =
+                as_u2(lds_tr16(reinterpret_cast<const char*>(&A.kd[s][src]) + 8 * hh));
             Wf[hh] = bf4(mma16(kpc, TbTb, zero4()));                   // W^T
             Qf[hh] = bf4(mma16(kpc, nY3b, A.qpf[2 * s + hh][lane]));   // Qpp^T
         }
         B.w[s][lane] = cat8(Wf[0], Wf[1]);
         B.qpp[s][lane] = cat8(Qf[0], Qf[1]);
-        const bf16x4 vcs = bf4(mma16(as_bf4(A.vraw[s][lane]), eye, zero4()));  // column-major V
+        const bf16x4 vcs = lds_tr16(&A.vraw[s][src]);  // column-major V
         B.ut[s][lane] = mma16(TbTb, vcs, zero4());     // Tb V
         B.put[s][lane] = mma16(Y3b, vcs, zero4());     // P Tb V
     };
@@ -387,11 +435,12 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         if (!masked || t0 + ln < eos) *reinterpret_cast<uint2*>(dst) = as_u2(Ot);
     };
 
-    // Iteration i runs A(i+3), B1(i+2), B2(i+1) and S(i) with one barrier per iteration (the
-    // same count in every role).  The stage-A loop is unrolled by two so that the in-flight loads
-    // of R0 / R1 never need a register copy.  An odd tile count runs one extra tile past the
-    // end, and stages A and B run up to three tiles past it: those tiles' inputs are all zero
-    // (k = 0: no write; g = 0: no decay), so they leave the state unchanged and store nothing.
+    // Period q (one barrier after each) runs A(q), the first half of B1(q-1), the second half of
+    // B1(q-2), B2(q-3) and S(q-4); every role passes nsteps + 4 barriers.  The stage-A loop is
+    // unrolled by two so that the in-flight loads of R0 / R1 never need a register copy.  An odd
+    // tile count runs one extra tile past the end, and stages A and B run up to two tiles past
+    // it: those tiles read as zero (k = 0: no write; g = 0: no decay), so they leave the state
+    // unchanged and store nothing.
     const int64_t nsteps = ntiles + (ntiles & 1);
     if (role == 1) {
         Raw R0, R1;
@@ -403,41 +452,45 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         stage_a(1, R1);
         load_tile(R1);     // tile 3
         lds_barrier();
-        stage_a(2, R0);
-        load_tile(R0);     // tile 4
-        lds_barrier();
         for (int64_t i = 0; i < nsteps; i += 2) {
+            stage_a(i + 2, R0);
+            load_tile(R0);     // tile i + 4
+            lds_barrier();
             stage_a(i + 3, R1);
             load_tile(R1);     // tile i + 5
             lds_barrier();
-            stage_a(i + 4, R0);
-            load_tile(R0);     // tile i + 6
-            lds_barrier();
         }
+        lds_barrier();
+        lds_barrier();
     } else if (role == 2) {
+        const int par = s >> 1;            // tiles of this parity
         lds_barrier();
-        stage_b1(0);
-        lds_barrier();
-        stage_b1(1);
-        stage_b2(0);
-        lds_barrier();
-        for (int64_t i = 0; i < nsteps; ++i) {
-            stage_b1(i + 2);
-            stage_b2(i + 1);
+        if (par) lds_barrier();
+        for (int64_t j = par; j < nsteps; j += 2) {
+            const B1Carry c = stage_b1a(j);
+            lds_barrier();
+            stage_b1b(j, c);
             lds_barrier();
         }
+        lds_barrier();
+        lds_barrier();
+        if (!par) lds_barrier();
     } else {
         lds_barrier();
         lds_barrier();
+        lds_barrier();
+        stage_b2(0);
         lds_barrier();
         // tiles whose 16 tokens all lie inside the sequence store without a mask
         const int64_t nfull = (eos - bos) / C;
         int64_t i = 0;
         for (; i < nfull; ++i) {
+            stage_b2(i + 1);
             store_o(i, stage_s(i), false);
             lds_barrier();
         }
         for (; i < nsteps; ++i) {
+            stage_b2(i + 1);
             store_o(i, stage_s(i), true);
             lds_barrier();
         }
