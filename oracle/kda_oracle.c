@@ -34,6 +34,13 @@
  * gate_is_alpha = 1 (test use) passes alpha itself instead of log(alpha), so that dyadic test
  * inputs avoid the rounding of exp(log(alpha)).
  *
+ * Snapshots (kda_oracle_recurrence_snap).  A cached prefix of a KDA layer can be resumed only from
+ * a state saved at exactly that boundary, so states are saved every `stride` tokens ("Kimi K3's
+ * hybrid block, from first principles", section "Gated MLA without positions", paragraph "The
+ * cache, in bytes"; "What's new in Kimi K3", section "What it costs to serve").  After token
+ * j * stride of sequence n (counted from the sequence start, j = 1 .. len_n / stride) the state
+ * S is copied to snaps[snap_cu[n] + j - 1, h], a [dk, dv] block of snaps [*, H, dk, dv].
+ *
  * Layouts (row-major, packed tokens): q,k,g [Ttot,H,dk]; v,o [Ttot,H,dv]; beta [Ttot,H];
  * h0,hT [N,H,dk,dv]; cu_seqlens int64 [N+1] (sequence n owns tokens cu[n] .. cu[n+1]-1).
  */
@@ -49,6 +56,9 @@ typedef struct {
     int64_t N, H, dk, dv;
     int gate_is_alpha;
     double *o, *hT;
+    int64_t stride;         /* snapshot stride in tokens (0: no snapshots) */
+    const int64_t *snap_cu; /* first snapshot index of each sequence */
+    double *snaps;
     int64_t next;           /* next (sequence, head) unit to take */
     pthread_mutex_t lock;
     int status;
@@ -87,6 +97,12 @@ static int run_unit(job_t *J, int64_t unit, double *S, double *pred, double *u, 
         for (int64_t c = 0; c < dv; ++c) ot[c] = 0.0;
         for (int64_t r = 0; r < dk; ++r)
             for (int64_t c = 0; c < dv; ++c) ot[c] += S[r * dv + c] * qt[r];
+        /* the state that resumes the prefix ending after this token */
+        const int64_t done = t - J->cu[n] + 1;
+        if (J->stride > 0 && done % J->stride == 0) {
+            double *snap = J->snaps + ((J->snap_cu[n] + done / J->stride - 1) * H + h) * dk * dv;
+            for (int64_t i = 0; i < dk * dv; ++i) snap[i] = S[i];
+        }
     }
     if (J->hT) {
         double *hT = J->hT + (n * H + h) * dk * dv;
@@ -119,13 +135,16 @@ static void *worker(void *arg)
     return NULL;
 }
 
-/* Returns 0 on success, -1 on allocation failure, -2 on bad arguments. */
-int kda_oracle_recurrence(const double *q, const double *k, const double *v, const double *g,
-                          const double *beta, const double *h0, const int64_t *cu_seqlens,
-                          int64_t num_seqs, int64_t H, int64_t dk, int64_t dv,
-                          int gate_is_alpha, double *o, double *hT, int nthreads)
+/* Returns 0 on success, -1 on allocation failure, -2 on bad arguments.  stride = 0 saves no
+ * snapshots (snap_cu and snaps may then be NULL). */
+int kda_oracle_recurrence_snap(const double *q, const double *k, const double *v, const double *g,
+                               const double *beta, const double *h0, const int64_t *cu_seqlens,
+                               int64_t num_seqs, int64_t H, int64_t dk, int64_t dv,
+                               int gate_is_alpha, double *o, double *hT, int64_t stride,
+                               const int64_t *snap_cu, double *snaps, int nthreads)
 {
     if (!cu_seqlens || num_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0) return -2;
+    if (stride < 0 || (stride > 0 && (!snap_cu || !snaps))) return -2;
     for (int64_t n = 0; n < num_seqs; ++n)
         if (cu_seqlens[n + 1] < cu_seqlens[n]) return -2;
     if (cu_seqlens[num_seqs] > cu_seqlens[0] && (!q || !k || !v || !g || !beta || !o)) return -2;
@@ -135,6 +154,7 @@ int kda_oracle_recurrence(const double *q, const double *k, const double *v, con
     J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.h0 = h0;
     J.cu = cu_seqlens; J.N = num_seqs; J.H = H; J.dk = dk; J.dv = dv;
     J.gate_is_alpha = gate_is_alpha; J.o = o; J.hT = hT;
+    J.stride = stride; J.snap_cu = snap_cu; J.snaps = snaps;
     pthread_mutex_init(&J.lock, NULL);
 
     int64_t units = num_seqs * H;
@@ -151,4 +171,13 @@ int kda_oracle_recurrence(const double *q, const double *k, const double *v, con
     free(th);
     pthread_mutex_destroy(&J.lock);
     return J.status;
+}
+
+int kda_oracle_recurrence(const double *q, const double *k, const double *v, const double *g,
+                          const double *beta, const double *h0, const int64_t *cu_seqlens,
+                          int64_t num_seqs, int64_t H, int64_t dk, int64_t dv,
+                          int gate_is_alpha, double *o, double *hT, int nthreads)
+{
+    return kda_oracle_recurrence_snap(q, k, v, g, beta, h0, cu_seqlens, num_seqs, H, dk, dv,
+                                      gate_is_alpha, o, hT, 0, NULL, NULL, nthreads);
 }

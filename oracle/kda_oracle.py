@@ -57,6 +57,12 @@ def load_library(path: str):
                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_int, dp, dp, ctypes.c_int]
     lib.kda_oracle_recurrence.restype = ctypes.c_int
+    lib.kda_oracle_recurrence_snap.argtypes = [dp, dp, dp, dp, dp, dp,
+                                               ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+                                               ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                               ctypes.c_int, dp, dp, ctypes.c_int64,
+                                               ctypes.POINTER(ctypes.c_int64), dp, ctypes.c_int]
+    lib.kda_oracle_recurrence_snap.restype = ctypes.c_int
     return lib
 
 
@@ -83,13 +89,17 @@ def default_threads() -> int:
 
 
 def recurrence(q, k, v, g, beta, h0=None, cu_seqlens: Optional[Sequence[int]] = None,
-               gate_is_alpha: bool = False, nthreads: Optional[int] = None, lib=None):
+               gate_is_alpha: bool = False, nthreads: Optional[int] = None, lib=None,
+               snapshot_stride: Optional[int] = None):
     """The token-by-token recurrence in float64.
 
     q, k, g: [Ttot, H, dk]; v: [Ttot, H, dv]; beta: [Ttot, H]; h0: [N, H, dk, dv] or None
     (zeros).  cu_seqlens: [N+1] sequence boundaries in the packed token axis; None means one
     sequence over all Ttot tokens.  lib: a library from load_library (default: the built one).
-    Returns (o [Ttot, H, dv], hT [N, H, dk, dv]).
+    Returns (o [Ttot, H, dv], hT [N, H, dk, dv]), and with snapshot_stride = s also
+    (snaps [sum_n len_n // s, H, dk, dv], snap_cu [N+1]): the state after token j*s of sequence n
+    (j = 1 .. len_n // s) is snaps[snap_cu[n] + j - 1], the state that resumes that prefix
+    ("Kimi K3's hybrid block, from first principles", paragraph "The cache, in bytes").
     """
     q = np.ascontiguousarray(q, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
@@ -111,12 +121,23 @@ def recurrence(q, k, v, g, beta, h0=None, cu_seqlens: Optional[Sequence[int]] = 
             raise ValueError("h0 shape")
     o = np.zeros((Ttot, H, dv), dtype=np.float64)
     hT = np.zeros((N, H, dk, dv), dtype=np.float64)
-    st = (lib or _load()).kda_oracle_recurrence(
+    stride = int(snapshot_stride or 0)
+    if stride < 0:
+        raise ValueError("snapshot_stride must be positive")
+    snap_cu = np.zeros(N + 1, dtype=np.int64)
+    if stride:
+        snap_cu[1:] = np.cumsum(np.diff(cu) // stride)
+    snaps = np.zeros((int(snap_cu[-1]), H, dk, dv), dtype=np.float64)
+    st = (lib or _load()).kda_oracle_recurrence_snap(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
         cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), N, H, dk, dv,
-        1 if gate_is_alpha else 0, _ptr(o), _ptr(hT), nthreads or default_threads())
+        1 if gate_is_alpha else 0, _ptr(o), _ptr(hT), stride,
+        snap_cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ptr(snaps),
+        nthreads or default_threads())
     if st != 0:
         raise RuntimeError(f"oracle failed with status {st}")
+    if stride:
+        return o, hT, snaps, snap_cu
     return o, hT
 
 

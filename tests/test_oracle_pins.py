@@ -175,8 +175,32 @@ def pin_brute_force(rec, brute):
     np.testing.assert_allclose(hT, np.array(hb, dtype=float), rtol=1e-11, atol=1e-11)
 
 
+def pin_snapshots(rec):
+    """Every saved state is the state that resumes its prefix: snapshot j of sequence n equals, bit
+    for bit, the final state of a run over the first 16 j tokens of that sequence alone ("Kimi
+    K3's hybrid block, from first principles", paragraph "The cache, in bytes": a cached prefix is
+    reusable only if the state was saved at exactly that boundary).  Saving snapshots leaves o and
+    hT unchanged."""
+    rng = np.random.default_rng(16)
+    lens = [37, 0, 32, 15, 48]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, g, beta, _ = _rand_case(rng, int(cu[-1]), 2, 5, 4)
+    S0 = rng.standard_normal((len(lens), 2, 5, 4))
+    o, hT, snaps, scu = rec(q, k, v, g, beta, S0, cu, snapshot_stride=16)
+    assert list(scu) == [0, 2, 2, 4, 4, 7]
+    o_plain, hT_plain = rec(q, k, v, g, beta, S0, cu)
+    assert np.array_equal(o, o_plain) and np.array_equal(hT, hT_plain)
+    for n, L in enumerate(lens):
+        for j in range(1, L // 16 + 1):
+            a, e = cu[n], cu[n] + 16 * j
+            _, hp = rec(q[a:e], k[a:e], v[a:e], g[a:e], beta[a:e], S0[n:n + 1])
+            assert np.array_equal(snaps[scu[n] + j - 1], hp[0]), (n, j)
+        if L and L % 16 == 0:
+            assert np.array_equal(snaps[scu[n + 1] - 1], hT[n])
+
+
 ALL_PINS = [pin_unit_key_beta_one, pin_unit_key_partial_beta, pin_gradient_step, pin_pure_decay,
-            pin_half_life, pin_whiteboard]
+            pin_half_life, pin_whiteboard, pin_snapshots]
 
 
 # --------------------------------------------------------------------------------------------
@@ -361,6 +385,11 @@ MUTANTS = {
     "write_along_query": _swap("S[r * dv + c] += kt[r] * u[c];", "S[r * dv + c] += qt[r] * u[c];"),
     "h0_ignored": _swap("S[i] = h0 ? h0[i] : 0.0;", "S[i] = 0.0;"),
     "read_before_write": _read_before_write,
+    # snapshot bookkeeping (in-bounds for the pin's lengths)
+    "snapshot_one_token_early": _swap("const int64_t done = t - J->cu[n] + 1;",
+                                      "const int64_t done = t - J->cu[n] + 2;"),
+    "snapshot_wrong_sequence": _swap("(J->snap_cu[n] + done / J->stride - 1)",
+                                     "(J->snap_cu[0] + done / J->stride - 1)"),
 }
 
 
