@@ -64,7 +64,9 @@ enum {
     KDA_ERR_UNSUPPORTED = -4, /* dk or dv not a multiple of 16 in [16, 128] */
     KDA_ERR_SEQLENS = -5,     /* cu_seqlens with B != 1, or (KDA_VALIDATE) bad contents */
     KDA_ERR_RANGE = -6,       /* (KDA_VALIDATE) g outside [-5, 0] */
-    KDA_ERR_HIP = -7          /* a HIP runtime call or kernel launch failed */
+    KDA_ERR_HIP = -7,         /* a HIP runtime call or kernel launch failed */
+    KDA_ERR_STRIDE = -8       /* snapshot stride not a positive multiple of 16, or (KDA_VALIDATE)
+                                 snap_offsets inconsistent with the sequence lengths */
 };
 
 /*
@@ -96,6 +98,37 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
                   const float* h0, const int32_t* cu_seqlens, int num_seqs,
                   void* o, float* hT,
                   int B, int T, int H, int dk, int dv, int dtype, void* stream);
+
+/*
+ * kda_chunk_fwd_snapshots -- kda_chunk_fwd that also saves the state at every multiple of
+ * snap_stride tokens of each sequence, for prefix caching.  A KDA layer keeps one state that
+ * summarises the whole prefix, so a cached prefix can be resumed only from a state saved at
+ * exactly its boundary ("Kimi K3's hybrid block, from first principles", section "Gated MLA
+ * without positions", paragraph "The cache, in bytes"); a float32 snapshot costs 64 KiB per head,
+ * so strides below 64 tokens hold more bytes than the per-token cache they replace ("What's new in
+ * Kimi K3", section "What it costs to serve").  Passing a snapshot as h0 of a later call resumes
+ * the sequence after that prefix.
+ *
+ * Arguments as kda_chunk_fwd, plus
+ *   snaps        [Nsnap, H, dk, dv] float32 device   written: snapshot j (j = 1 .. len_n / snap_stride,
+ *                                                    rounded down) of sequence n is the state after
+ *                                                    its first j * snap_stride tokens, at index
+ *                                                    snap_offsets[n] + j - 1
+ *   snap_offsets [N+1] int32 device   snap_offsets[0] = 0 and snap_offsets[n+1] - snap_offsets[n] =
+ *                                     len_n / snap_stride (rounded down); required with
+ *                                     cu_seqlens; NULL without it (then index n * (T / snap_stride)
+ *                                     + j - 1)
+ *   snap_stride  a positive multiple of 16 (the tile size), else KDA_ERR_STRIDE
+ * snaps = NULL is KDA_ERR_NULL when some sequence has snap_stride tokens or more (known from T
+ * without cu_seqlens; checked from the offsets with KDA_VALIDATE=1), and otherwise writes nothing,
+ * so an empty snapshot buffer may be passed as NULL.  With KDA_VALIDATE=1 the offsets are checked
+ * against cu_seqlens (KDA_ERR_STRIDE).  Returns KDA_OK or a negative status.
+ */
+int kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* h0, const int32_t* cu_seqlens,
+                            int num_seqs, void* o, float* hT, float* snaps,
+                            const int32_t* snap_offsets, int snap_stride,
+                            int B, int T, int H, int dk, int dv, int dtype, void* stream);
 
 /*
  * kda_decode_step -- one token for each of N sequences, updating their states in place and

@@ -58,6 +58,74 @@ int check_gate_range(const void* g, int64_t count, int dtype, hipStream_t s) {
     return KDA_OK;
 }
 
+// Prefill with optional snapshots (snap_stride 0: none).
+int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                   const float* h0, const int32_t* cu_seqlens, int num_seqs, void* o, float* hT,
+                   float* snaps, const int32_t* snap_offsets, int snap_stride, int B, int T,
+                   int H, int dk, int dv, int dtype, void* stream) {
+    if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
+    if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
+    if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    if (snap_stride < 0 || snap_stride % 16 != 0) return KDA_ERR_STRIDE;
+    const bool want_snaps = snap_stride > 0;
+    int64_t N, Ttot;
+    if (cu_seqlens) {
+        if (B != 1) return KDA_ERR_SEQLENS;
+        N = num_seqs;
+        Ttot = T;
+        if (want_snaps && !snap_offsets) return KDA_ERR_NULL;
+    } else {
+        N = B;
+        Ttot = static_cast<int64_t>(B) * T;
+    }
+    if (Ttot > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
+    // with equal lengths, snapshots exist iff T >= stride; with cu_seqlens the offsets say so
+    if (want_snaps && !snaps && !cu_seqlens && N > 0 && T >= snap_stride) return KDA_ERR_NULL;
+    if (N == 0 || (Ttot == 0 && !hT)) return KDA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (validate_enabled()) {
+        std::vector<int32_t> cu;
+        if (cu_seqlens) {
+            cu.resize(static_cast<size_t>(N + 1));
+            int st = fetch(cu.data(), cu_seqlens, cu.size() * 4, s);
+            if (st) return st;
+            if (cu[0] != 0 || cu[N] != Ttot) return KDA_ERR_SEQLENS;
+            for (int64_t i = 0; i < N; ++i)
+                if (cu[i + 1] < cu[i]) return KDA_ERR_SEQLENS;
+        }
+        if (want_snaps && cu_seqlens) {
+            std::vector<int32_t> so(static_cast<size_t>(N + 1));
+            int st = fetch(so.data(), snap_offsets, so.size() * 4, s);
+            if (st) return st;
+            if (so[0] != 0) return KDA_ERR_STRIDE;
+            for (int64_t i = 0; i < N; ++i)
+                if (so[i + 1] - so[i] != (cu[i + 1] - cu[i]) / snap_stride) return KDA_ERR_STRIDE;
+            if (so[N] > 0 && !snaps) return KDA_ERR_NULL;
+        }
+        int st = check_gate_range(g, Ttot * H * dk, dtype, s);
+        if (st) return st;
+    }
+
+    kda::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.h0 = h0; a.cu = cu_seqlens; a.o = o; a.hT = hT;
+    a.N = N; a.T = cu_seqlens ? 0 : T; a.H = H; a.dk = dk; a.dv = dv; a.dtype = dtype;
+    if (want_snaps && snaps) {
+        a.snaps = snaps;
+        a.snap_cu = cu_seqlens ? snap_offsets : nullptr;
+        a.snap_tiles = snap_stride / 16;
+        a.snap_per_seq = cu_seqlens ? 0 : T / snap_stride;
+    }
+
+    hipError_t e;
+    if (dtype == KDA_BF16 && dk == 128 && dv == 128 && !std::getenv("KDA_FORCE_GENERAL"))
+        e = kda::launch_prefill_mfma(a, s);
+    else
+        e = kda::launch_prefill_general(a, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -74,6 +142,8 @@ const char* kda_status_string(int status) {
         case KDA_ERR_SEQLENS: return "bad cu_seqlens (needs B == 1; non-decreasing from 0 to T)";
         case KDA_ERR_RANGE: return "g (log alpha) outside [-5, 0]";
         case KDA_ERR_HIP: return "HIP runtime error";
+        case KDA_ERR_STRIDE:
+            return "snapshot stride must be a positive multiple of 16, with matching snap_offsets";
         default: return "unknown status";
     }
 }
@@ -81,46 +151,18 @@ const char* kda_status_string(int status) {
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                   const float* h0, const int32_t* cu_seqlens, int num_seqs, void* o, float* hT,
                   int B, int T, int H, int dk, int dv, int dtype, void* stream) {
-    if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
-    if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
-    if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
-    int64_t N, Ttot;
-    if (cu_seqlens) {
-        if (B != 1) return KDA_ERR_SEQLENS;
-        N = num_seqs;
-        Ttot = T;
-    } else {
-        N = B;
-        Ttot = static_cast<int64_t>(B) * T;
-    }
-    if (Ttot > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
-    if (N == 0 || (Ttot == 0 && !hT)) return KDA_OK;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    return chunk_fwd_impl(q, k, v, g, beta, h0, cu_seqlens, num_seqs, o, hT, nullptr, nullptr, 0,
+                          B, T, H, dk, dv, dtype, stream);
+}
 
-    if (validate_enabled()) {
-        if (cu_seqlens) {
-            std::vector<int32_t> cu(static_cast<size_t>(N + 1));
-            int st = fetch(cu.data(), cu_seqlens, cu.size() * 4, s);
-            if (st) return st;
-            if (cu[0] != 0 || cu[N] != Ttot) return KDA_ERR_SEQLENS;
-            for (int64_t i = 0; i < N; ++i)
-                if (cu[i + 1] < cu[i]) return KDA_ERR_SEQLENS;
-        }
-        int st = check_gate_range(g, Ttot * H * dk, dtype, s);
-        if (st) return st;
-    }
-
-    kda::PrefillArgs a;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
-    a.h0 = h0; a.cu = cu_seqlens; a.o = o; a.hT = hT;
-    a.N = N; a.T = cu_seqlens ? 0 : T; a.H = H; a.dk = dk; a.dv = dv; a.dtype = dtype;
-
-    hipError_t e;
-    if (dtype == KDA_BF16 && dk == 128 && dv == 128 && !std::getenv("KDA_FORCE_GENERAL"))
-        e = kda::launch_prefill_mfma(a, s);
-    else
-        e = kda::launch_prefill_general(a, s);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+int kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* h0, const int32_t* cu_seqlens,
+                            int num_seqs, void* o, float* hT, float* snaps,
+                            const int32_t* snap_offsets, int snap_stride,
+                            int B, int T, int H, int dk, int dv, int dtype, void* stream) {
+    if (snap_stride <= 0) return KDA_ERR_STRIDE;
+    return chunk_fwd_impl(q, k, v, g, beta, h0, cu_seqlens, num_seqs, o, hT, snaps, snap_offsets,
+                          snap_stride, B, T, H, dk, dv, dtype, stream);
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta,

@@ -18,6 +18,10 @@ struct PrefillArgs {
     const int32_t* cu;    // [N+1] or nullptr
     void* o;              // [Ttot, H, dv]
     float* hT;            // [N, H, dk, dv] or nullptr
+    float* snaps = nullptr;              // [Nsnap, H, dk, dv] or nullptr (no snapshots)
+    const int32_t* snap_cu = nullptr;    // first snapshot index per sequence, or nullptr
+    int64_t snap_tiles = 0;              // snapshot stride in 16-token tiles (0: none)
+    int64_t snap_per_seq = 0;            // snapshots per sequence when snap_cu == nullptr
     int64_t N;            // sequences
     int64_t T;            // per-sequence length when cu == nullptr
     int64_t H, dk, dv;

@@ -151,6 +151,19 @@ __global__ __launch_bounds__(256) void kda_prefill_general_kernel(PrefillArgs a)
             sS[idx] = acc;
         }
         __syncthreads();
+        // snapshot: the state after a full tile that ends a multiple of the stride
+        if (a.snaps && L == C) {
+            const int64_t done = (t0 - bos) / C + 1;         // tiles of this sequence done
+            if (done % a.snap_tiles == 0) {
+                const int64_t idx = (a.snap_cu ? (int64_t)a.snap_cu[n] : n * a.snap_per_seq) +
+                                    done / a.snap_tiles - 1;
+                const int64_t base = (idx * H + h) * dk * dv + cb * BV;
+                for (int id = tid; id < dk * BV; id += 256) {
+                    const int r = id / BV, c = id % BV;
+                    a.snaps[base + r * dv + c] = sS[id];
+                }
+            }
+        }
     }
 
     if (a.hT) {

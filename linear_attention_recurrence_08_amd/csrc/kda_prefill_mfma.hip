@@ -481,12 +481,26 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         lds_barrier();
         stage_b2(0);
         lds_barrier();
+        // snapshots: after tile i the registers hold the state after (i + 1) * 16 tokens; every
+        // snap_tiles-th full tile saves it (the next index in the snapshot array)
+        int64_t snap_at = a.snaps ? a.snap_tiles : -1;
+        int64_t snap_idx = a.snaps ? (a.snap_cu ? (int64_t)a.snap_cu[n] : n * a.snap_per_seq) : 0;
         // tiles whose 16 tokens all lie inside the sequence store without a mask
         const int64_t nfull = (eos - bos) / C;
         int64_t i = 0;
         for (; i < nfull; ++i) {
             stage_b2(i + 1);
             store_o(i, stage_s(i), false);
+            if (i + 1 == snap_at) {
+                float* dst = a.snaps + (snap_idx * H + h) * (int64_t)(D * D);
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        dst[(int64_t)(16 * mb + 4 * lg + r) * D + col] = S[mb][r];
+                ++snap_idx;
+                snap_at += a.snap_tiles;
+            }
             lds_barrier();
         }
         for (; i < nsteps; ++i) {

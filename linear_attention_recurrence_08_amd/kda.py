@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_BF16, KDA_F32 = 0, 1
 KDA_OK = 0
+KDA_ERR_STRIDE = -8
 _lib = None
 
 
@@ -44,6 +45,9 @@ def load_library():
         lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
                                       i32, i32, i32, i32, i32, i32, vp]
         lib.kda_chunk_fwd.restype = i32
+        lib.kda_chunk_fwd_snapshots.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
+                                                i32, i32, i32, i32, i32, i32, i32, vp]
+        lib.kda_chunk_fwd_snapshots.restype = i32
         lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         lib.kda_decode_step.restype = i32
         lib.kda_status_string.argtypes = [i32]
@@ -85,13 +89,8 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-                  beta: torch.Tensor, h0: Optional[torch.Tensor] = None,
-                  cu_seqlens: Optional[torch.Tensor] = None, output_final_state: bool = True,
-                  o: Optional[torch.Tensor] = None, hT: Optional[torch.Tensor] = None
-                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunkwise KDA prefill.  Returns (o, hT); hT is None when output_final_state is False.
-    o / hT may be passed preallocated (hT may be h0 itself for an in-place state update)."""
+def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, output_final_state, o, hT):
+    """Shape/device checks shared by the prefill entry points; allocates o and hT if needed."""
     dev = q.device
     dt = q.dtype
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
@@ -132,12 +131,75 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
             _check(hT, "hT", dev, torch.float32)
     else:
         hT = None
+    return dev, B, T, H, dk, dv, N, o, hT
+
+
+def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, h0: Optional[torch.Tensor] = None,
+                  cu_seqlens: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                  o: Optional[torch.Tensor] = None, hT: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA prefill.  Returns (o, hT); hT is None when output_final_state is False.
+    o / hT may be passed preallocated (hT may be h0 itself for an in-place state update)."""
+    dev, B, T, H, dk, dv, N, o, hT = _prefill_args(q, k, v, g, beta, h0, cu_seqlens,
+                                                   output_final_state, o, hT)
     st = load_library().kda_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), N,
         _ptr(o), _ptr(hT), B, T, H, dk, dv, _dtype_code(q), _stream(dev))
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd")
     return o, hT
+
+
+def kda_chunk_fwd_snapshots(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                            beta: torch.Tensor, snap_stride: int,
+                            h0: Optional[torch.Tensor] = None,
+                            cu_seqlens: Optional[torch.Tensor] = None,
+                            snap_offsets: Optional[torch.Tensor] = None,
+                            output_final_state: bool = True, o: Optional[torch.Tensor] = None,
+                            hT: Optional[torch.Tensor] = None,
+                            snaps: Optional[torch.Tensor] = None):
+    """Prefill that also saves the state every snap_stride tokens of each sequence (prefix
+    caching).  Returns (o, hT, snaps, snap_offsets): snapshot j (1-based) of sequence n, the state
+    after its first j * snap_stride tokens, is snaps[snap_offsets[n] + j - 1] (snap_offsets is
+    None for equal-length batches, where the index is n * (T // snap_stride) + j - 1).
+
+    With cu_seqlens and no snap_offsets, the offsets are derived from the sequence lengths on the
+    device; sizing snaps then reads their total back to the host (one synchronisation), which a
+    caller avoids by passing both snap_offsets and snaps."""
+    dev, B, T, H, dk, dv, N, o, hT = _prefill_args(q, k, v, g, beta, h0, cu_seqlens,
+                                                   output_final_state, o, hT)
+    stride = int(snap_stride)
+    if stride <= 0 or stride % 16:
+        raise KDAError(KDA_ERR_STRIDE, "kda_chunk_fwd_snapshots")
+    if cu_seqlens is not None:
+        if snap_offsets is None:
+            counts = torch.div(cu_seqlens[1:] - cu_seqlens[:-1], stride, rounding_mode="floor")
+            snap_offsets = torch.zeros(N + 1, dtype=torch.int32, device=dev)
+            snap_offsets[1:] = torch.cumsum(counts, 0)
+        _check(snap_offsets, "snap_offsets", dev, torch.int32)
+        if snap_offsets.numel() != N + 1:
+            raise ValueError(f"snap_offsets must have {N + 1} entries")
+        if snaps is None:
+            snaps = torch.empty((int(snap_offsets[-1].item()), H, dk, dv), dtype=torch.float32,
+                                device=dev)
+    else:
+        if snap_offsets is not None:
+            raise ValueError("snap_offsets is only used with cu_seqlens")
+        if snaps is None:
+            snaps = torch.empty((N * (T // stride), H, dk, dv), dtype=torch.float32, device=dev)
+        elif snaps.shape[0] < N * (T // stride):
+            raise ValueError(f"snaps needs {N * (T // stride)} entries")
+    _check(snaps, "snaps", dev, torch.float32)
+    if snaps.shape[1:] != (H, dk, dv):
+        raise ValueError(f"snaps must be [*, {H}, {dk}, {dv}]")
+    st = load_library().kda_chunk_fwd_snapshots(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), N,
+        _ptr(o), _ptr(hT), _ptr(snaps) if snaps.numel() else None, _ptr(snap_offsets), stride,
+        B, T, H, dk, dv, _dtype_code(q), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd_snapshots")
+    return o, hT, snaps, snap_offsets
 
 
 def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

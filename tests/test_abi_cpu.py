@@ -28,8 +28,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["kda_chunk_fwd", "kda_decode_step", "kda_status_string",
-                                     "kda_version"]
+    assert _declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_snapshots",
+                                     "kda_decode_step", "kda_status_string", "kda_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     from linear_attention_recurrence_08_amd.kda import kda_status_string
     assert kda_status_string(0) == "ok"
-    for code in range(-7, 0):
+    for code in range(-8, 0):
         s = kda_status_string(code)
         assert s and s != "unknown status"
     assert kda_status_string(-99) == "unknown status"
@@ -57,6 +57,16 @@ def _prefill(lib, **kw):
     return lib.kda_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"],
                              a["num_seqs"], a["o"], a["hT"], a["B"], a["T"], a["H"], a["dk"],
                              a["dv"], a["dtype"], None)
+
+
+def _prefill_snap(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, num_seqs=0, o=FAKE,
+             hT=FAKE, snaps=FAKE, offs=None, stride=64, B=1, T=128, H=2, dk=128, dv=128, dtype=0)
+    a.update(kw)
+    return lib.kda_chunk_fwd_snapshots(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"],
+                                       a["cu"], a["num_seqs"], a["o"], a["hT"], a["snaps"],
+                                       a["offs"], a["stride"], a["B"], a["T"], a["H"], a["dk"],
+                                       a["dv"], a["dtype"], None)
 
 
 def _decode(lib, **kw):
@@ -84,6 +94,23 @@ def test_prefill_empty_is_noop(lib):
     assert _prefill(lib, B=0) == 0
     assert _prefill(lib, T=0, hT=None) == 0
     assert _prefill(lib, cu=FAKE, B=1, T=0, num_seqs=0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(stride=0), -8), (dict(stride=-16), -8), (dict(stride=24), -8), (dict(stride=8), -8),
+    (dict(cu=FAKE, num_seqs=2, offs=None), -1),     # varlen snapshots need their offsets
+    (dict(snaps=None), -1),                         # T >= stride: snapshots are due
+    (dict(dk=96, dtype=2), -3), (dict(H=0), -2), (dict(dv=8), -4), (dict(q=None), -1),
+])
+def test_snapshot_argument_errors(lib, kw, code):
+    assert _prefill_snap(lib, **kw) == code
+
+
+def test_snapshot_empty_is_noop(lib):
+    assert _prefill_snap(lib, B=0) == 0
+    # no sequence reaches the stride: an empty snapshot buffer may be NULL (nothing launched here
+    # because there are no tokens and no final state)
+    assert _prefill_snap(lib, T=0, hT=None, snaps=None) == 0
 
 
 @pytest.mark.parametrize("kw,code", [

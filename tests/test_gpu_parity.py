@@ -253,3 +253,92 @@ def test_validation_mode_reports_bad_contents(monkeypatch):
         kda_chunk_fwd(x.q, x.k, x.v, x.g, x.beta, cu_seqlens=bad_cu)
     assert ei.value.code == -5
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------------------------------------
+# state snapshots every `stride` tokens (prefix caching)
+# ------------------------------------------------------------------------------------------------
+def gpu_prefill_snapshots(x, dev, stride):
+    from linear_attention_recurrence_08_amd import kda_chunk_fwd_snapshots
+    xd = x.to(dev)
+    o, hT, snaps, offs = kda_chunk_fwd_snapshots(*xd.call_views(), stride, h0=xd.h0,
+                                                 cu_seqlens=xd.cu_seqlens)
+    torch.cuda.synchronize()
+    return o.reshape(x.total_tokens, x.H, x.dv), hT, snaps, offs
+
+
+SNAP_CASES = [
+    # (seq_lens, H, dk, dv, dtype, stride, packed)
+    ([37, 0, 64, 15, 130, 128], 3, 128, 128, "bf16", 16, True),
+    ([37, 0, 64, 15, 130, 128], 3, 128, 128, "bf16", 64, True),
+    ([96, 96], 2, 128, 128, "bf16", 48, False),
+    ([70, 33, 160], 2, 128, 128, "f32", 32, True),
+    ([100, 64], 2, 64, 32, "f32", 16, True),
+    ([128], 2, 32, 96, "bf16", 64, False),
+]
+
+
+@pytest.mark.parametrize("case", SNAP_CASES, ids=lambda c: f"{c[0]}-{c[2]}x{c[3]}-{c[4]}-s{c[5]}")
+def test_snapshots_small(oracle_mod, case):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs
+    lens, H, dk, dv, dt, stride, packed = case
+    x = inputs.make_inputs(lens, H, dk, dv, dt, seed=31 + stride, h0_sigma=0.05, packed=packed)
+    _say(f"snapshots {lens} H={H} {dk}x{dv} {dt} stride={stride}")
+    o, hT, snaps, offs = gpu_prefill_snapshots(x, dev, stride)
+    o_plain, hT_plain = gpu_prefill(x, dev)
+    # saving snapshots does not change the outputs or the final state
+    assert torch.equal(o, o_plain) and torch.equal(hT, hT_plain)
+    cu = x.cu_seqlens.tolist() if x.cu_seqlens is not None else [b * x.T for b in range(x.B + 1)]
+    h0 = None if x.h0 is None else to64(x.h0)
+    o_ref, h_ref, s_ref, scu = oracle_mod.recurrence(to64(x.q), to64(x.k), to64(x.v), to64(x.g),
+                                                     to64(x.beta), h0, cu, snapshot_stride=stride)
+    if offs is not None:
+        assert offs.cpu().tolist() == scu.tolist()
+    assert snaps.shape == s_ref.shape, (tuple(snaps.shape), s_ref.shape)
+    tol = TOL[dt]
+    if s_ref.shape[0]:
+        es = err(to64(snaps), s_ref)
+        _say(f"snapshots: {s_ref.shape[0]} saved, error {es:.3e} (bar {tol})")
+        assert es <= tol
+    # a sequence whose length is a stride multiple saves its final state as its last snapshot
+    for n in range(len(cu) - 1):
+        L = cu[n + 1] - cu[n]
+        if L and L % stride == 0:
+            assert torch.equal(snaps[int(scu[n + 1]) - 1], hT[n])
+
+
+def test_snapshot_resumes_prefix(oracle_mod):
+    """A snapshot passed as h0 resumes the sequence after its prefix."""
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd, kda_chunk_fwd_snapshots
+    x = inputs.make_inputs([400], 2, 128, 128, "bf16", seed=41, h0_sigma=0.05)
+    xd = x.to(dev)
+    o, hT, snaps, _ = kda_chunk_fwd_snapshots(*xd.call_views(), 128, h0=xd.h0)
+    a = 256                                   # snapshot 2: the state after 256 tokens
+    o2, h2 = kda_chunk_fwd(xd.q[a:], xd.k[a:], xd.v[a:], xd.g[a:], xd.beta[a:],
+                           h0=snaps[1:2].contiguous())
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle_prefill(oracle_mod, x)
+    assert err(to64(o2), o_ref[a:]) <= TOL["bf16"]
+    assert err(to64(h2), h_ref) <= TOL["bf16"]
+    assert err(to64(o[0, a:]), to64(o2)) <= 1e-2
+
+
+def test_snapshots_T4096_H96(oracle_mod):
+    """The 4096-token, 96-head prefill with a snapshot every 512 tokens, sampled heads checked."""
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs
+    x = inputs.make_workload("prefill_T4096_H96_d128_bf16")
+    o, hT, snaps, _ = gpu_prefill_snapshots(x, dev, 512)
+    assert snaps.shape == (8, 96, 128, 128)
+    heads = [0, 47, 95]
+    cu = [0, x.total_tokens]
+    o_ref, h_ref, s_ref, _ = oracle_mod.recurrence(
+        to64(x.q[:, heads]), to64(x.k[:, heads]), to64(x.v[:, heads]), to64(x.g[:, heads]),
+        to64(x.beta[:, heads]), None, cu, snapshot_stride=512)
+    es = err(to64(snaps[:, heads]), s_ref)
+    _say(f"T4096 snapshots: error {es:.3e}")
+    assert es <= TOL["bf16"]
+    assert err(to64(o[:, heads]), o_ref) <= TOL["bf16"]
+    assert torch.equal(snaps[-1], hT[0])
