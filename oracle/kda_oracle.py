@@ -13,6 +13,7 @@ chunked(...)      an independent chunkwise form (numpy float64): parallel inside
                   recurrent across tiles.
 brute_force(...)  the unrolled sum of explicit dk x dk transition products (tiny inputs only).
 exact(...)        the recurrence in exact rational arithmetic (fractions.Fraction; tiny inputs).
+output_gate(...)  the output stage after the mixer: per-head RMSNorm times a sigmoid gate.
 
 The recurrence these compute (decay first, then erase-and-write, then read the updated state):
     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t,
@@ -321,3 +322,23 @@ def exact(q, k, v, alpha, beta, h0=None, cu_seqlens=None):
                 o[t][h] = [sum((S[r][c] * qt[r] for r in range(dk)), F(0)) for c in range(dv)]
             hT[n][h] = S
     return o, hT
+
+
+# ---------------------------------------------------------------------------------------------
+# Output stage.  "Kimi K3's hybrid block, from first principles", section "From linear attention
+# to the delta rule": the layer's output is RMS-normalised per head and multiplied by a full-rank
+# sigmoid gate of the token before the output projection.  Per (token, head) row of dv outputs:
+#     y = o / sqrt(mean_c o_c^2 + eps) * w * sigmoid(gate)
+# with w the norm's gain per value channel (ones when not given).
+# ---------------------------------------------------------------------------------------------
+def output_gate(o, gate, weight=None, eps: float = 1e-6):
+    """o, gate: [..., dv]; weight: [dv] or None; returns y [..., dv] in float64."""
+    o = np.asarray(o, dtype=np.float64)
+    gate = np.asarray(gate, dtype=np.float64)
+    if gate.shape != o.shape:
+        raise ValueError("o and gate shapes differ")
+    mean_sq = np.mean(o * o, axis=-1, keepdims=True)
+    normed = o / np.sqrt(mean_sq + eps)
+    if weight is not None:
+        normed = normed * np.asarray(weight, dtype=np.float64)
+    return normed / (1.0 + np.exp(-gate))
