@@ -63,10 +63,11 @@ enum {
     KDA_ERR_DTYPE = -3,       /* dtype not KDA_BF16 / KDA_F32 */
     KDA_ERR_UNSUPPORTED = -4, /* dk or dv not a multiple of 16 in [16, 128] */
     KDA_ERR_SEQLENS = -5,     /* cu_seqlens with B != 1, or (KDA_VALIDATE) bad contents */
-    KDA_ERR_RANGE = -6,       /* (KDA_VALIDATE) g outside [-5, 0] */
+    KDA_ERR_RANGE = -6,       /* (KDA_VALIDATE) g outside [-5, 0]; or eps < 0 */
     KDA_ERR_HIP = -7,         /* a HIP runtime call or kernel launch failed */
-    KDA_ERR_STRIDE = -8       /* snapshot stride not a positive multiple of 16, or (KDA_VALIDATE)
+    KDA_ERR_STRIDE = -8,      /* snapshot stride not a positive multiple of 16, or (KDA_VALIDATE)
                                  snap_offsets inconsistent with the sequence lengths */
+    KDA_ERR_ALIGN = -9        /* a buffer of the output stage is not 16-byte aligned */
 };
 
 /*
@@ -146,6 +147,40 @@ int kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const v
  */
 int kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
                     float* S, void* o, int N, int H, int dk, int dv, int dtype, void* stream);
+
+/*
+ * kda_output_gate -- the output stage after the mixer: every (token, head) row of dv outputs is
+ * RMS-normalised and multiplied by a sigmoid gate of the token ("Kimi K3's hybrid block, from first
+ * principles", section "From linear attention to the delta rule": the layer's output is
+ * RMSNorm'd per head and multiplied by a full-rank sigmoid gate before the output projection):
+ *
+ *     y[t,h,:] = o[t,h,:] / sqrt(mean_c o[t,h,c]^2 + eps) * weight * sigmoid(gate[t,h,:])
+ *
+ *   o, gate, y [Ttot, H, dv]  dtype    device   16-byte aligned; y may alias o or gate
+ *   weight     [dv]           float32  device   the norm's gain per value channel; NULL = ones
+ *   eps        >= 0 (KDA_ERR_RANGE otherwise); an all-zero row with eps = 0 gives NaN
+ *   Ttot, H, dv               tokens, heads, head size (dv a multiple of 16 in [16, 128])
+ * Returns KDA_OK or a negative status.
+ */
+int kda_output_gate(const void* o, const void* gate, const float* weight, float eps, void* y,
+                    int Ttot, int H, int dv, int dtype, void* stream);
+
+/*
+ * kda_decode_step_gated -- kda_decode_step followed by the output stage of kda_output_gate on its
+ * outputs.  Writes both o and y.  For dk = dv = 128 (16-byte aligned S, 8-byte aligned v/o/gate/y
+ * for bf16, 16-byte for float32) the stage runs inside the decode kernel, on the outputs while
+ * they are still in registers; other sizes run the decode and then kda_output_gate.
+ *
+ *   arguments as kda_decode_step, plus gate [N, H, dv] (dtype), weight [dv] (float32 or NULL),
+ *   eps >= 0 and y [N, H, dv] (dtype, written; may alias o or gate, which are then overwritten).
+ * When the fused kernel does not apply, o, gate and y must be 16-byte aligned (KDA_ERR_ALIGN,
+ * returned before anything runs).
+ * Returns KDA_OK or a negative status.
+ */
+int kda_decode_step_gated(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, float* S, const void* gate, const float* weight,
+                          float eps, void* o, void* y, int N, int H, int dk, int dv, int dtype,
+                          void* stream);
 
 /* Text for a status code (static storage; never NULL). */
 const char* kda_status_string(int status);

@@ -140,10 +140,11 @@ const char* kda_status_string(int status) {
         case KDA_ERR_DTYPE: return "dtype must be KDA_BF16 or KDA_F32";
         case KDA_ERR_UNSUPPORTED: return "dk and dv must be multiples of 16 in [16, 128]";
         case KDA_ERR_SEQLENS: return "bad cu_seqlens (needs B == 1; non-decreasing from 0 to T)";
-        case KDA_ERR_RANGE: return "g (log alpha) outside [-5, 0]";
+        case KDA_ERR_RANGE: return "g (log alpha) outside [-5, 0], or eps < 0";
         case KDA_ERR_HIP: return "HIP runtime error";
         case KDA_ERR_STRIDE:
             return "snapshot stride must be a positive multiple of 16, with matching snap_offsets";
+        case KDA_ERR_ALIGN: return "output-stage buffers must be 16-byte aligned";
         default: return "unknown status";
     }
 }
@@ -165,8 +166,27 @@ int kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const v
                           snap_stride, B, T, H, dk, dv, dtype, stream);
 }
 
-int kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                    float* S, void* o, int N, int H, int dk, int dv, int dtype, void* stream) {
+int kda_output_gate(const void* o, const void* gate, const float* weight, float eps, void* y,
+                    int Ttot, int H, int dv, int dtype, void* stream) {
+    if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
+    if (Ttot < 0 || H <= 0) return KDA_ERR_SHAPE;
+    if (!supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return KDA_ERR_RANGE;
+    if (Ttot == 0) return KDA_OK;
+    if (!o || !gate || !y) return KDA_ERR_NULL;
+    if (!aligned(o, 16) || !aligned(gate, 16) || !aligned(y, 16)) return KDA_ERR_ALIGN;
+    kda::GateArgs a;
+    a.o = o; a.gate = gate; a.weight = weight; a.eps = eps; a.y = y;
+    a.rows = static_cast<int64_t>(Ttot) * H; a.dv = dv; a.dtype = dtype;
+    const hipError_t e = kda::launch_output_gate(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+namespace {
+// Decode with an optional fused output stage (gate == nullptr: none).
+int decode_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                float* S, const void* gate, const float* weight, float eps, void* o, void* y,
+                int N, int H, int dk, int dv, int dtype, void* stream) {
     if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
     if (N < 0 || H <= 0) return KDA_ERR_SHAPE;
     if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
@@ -180,11 +200,13 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g, 
     hipError_t e;
     // the 128 x 128 kernel uses 16-byte state accesses and 4-element input/output accesses
     const uintptr_t va = dtype == KDA_BF16 ? 8 : 16;
-    if (dk == 128 && dv == 128 && aligned(S, 16) && aligned(v, va) && aligned(o, va)) {
+    if (dk == 128 && dv == 128 && aligned(S, 16) && aligned(v, va) && aligned(o, va) &&
+        (!gate || (aligned(gate, va) && aligned(y, va)))) {
         kda::DecodeArgs a;
         a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S = S; a.o = o;
         a.N = N; a.H = H; a.dk = dk; a.dv = dv; a.dtype = dtype;
-        e = kda::launch_decode_d128(a, s);
+        a.gate = gate; a.weight = weight; a.eps = eps; a.y = y;
+        return kda::launch_decode_d128(a, s) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     } else {
         // other head sizes: the general tile path over N one-token sequences, state in place
         kda::PrefillArgs a;
@@ -193,7 +215,35 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g, 
         a.N = N; a.T = 1; a.H = H; a.dk = dk; a.dv = dv; a.dtype = dtype;
         e = kda::launch_prefill_general(a, s);
     }
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    if (gate) return kda_output_gate(o, gate, weight, eps, y, N, H, dv, dtype, stream);
+    return KDA_OK;
+}
+}  // namespace
+
+int kda_decode_step(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                    float* S, void* o, int N, int H, int dk, int dv, int dtype, void* stream) {
+    return decode_impl(q, k, v, g, beta, S, nullptr, nullptr, 0.f, o, nullptr, N, H, dk, dv,
+                       dtype, stream);
+}
+
+int kda_decode_step_gated(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, float* S, const void* gate, const float* weight,
+                          float eps, void* o, void* y, int N, int H, int dk, int dv, int dtype,
+                          void* stream) {
+    if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
+    if (N < 0 || H <= 0) return KDA_ERR_SHAPE;
+    if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return KDA_ERR_RANGE;
+    if (N == 0) return KDA_OK;
+    if (!gate || !y) return KDA_ERR_NULL;
+    // decided before anything runs: the fused kernel (same test as in decode_impl), else the
+    // decode followed by the output-stage kernel, which needs 16-byte aligned rows
+    const uintptr_t va = dtype == KDA_BF16 ? 8 : 16;
+    const bool fused = dk == 128 && dv == 128 && aligned(S, 16) && aligned(v, va) &&
+                       aligned(o, va) && aligned(gate, va) && aligned(y, va);
+    if (!fused && (!aligned(o, 16) || !aligned(gate, 16) || !aligned(y, 16))) return KDA_ERR_ALIGN;
+    return decode_impl(q, k, v, g, beta, S, gate, weight, eps, o, y, N, H, dk, dv, dtype, stream);
 }
 
 }  // extern "C"

@@ -56,7 +56,12 @@ constexpr int NRED = 9;  // per column group: S'^T k (4), S'^T q (4), k.q
 
 // HPW heads per workgroup: every head's 64 KiB state is requested before the first one is
 // reduced, so the second head's loads are in flight while the first head is reduced and stored.
-template <typename Tin, int HPW>
+// GATED adds the output stage y = o / sqrt(mean(o^2) + eps) * w * sigmoid(gate) over the head's
+// 128 outputs ("Kimi K3's hybrid block, from first principles", section "From linear attention to
+// the delta rule": the output is RMS-normalised per head and multiplied by a sigmoid gate of the
+// token): every 32-lane half-wave holds the whole row (4 columns per lane), so the sum of squares
+// is five xor shuffles.
+template <typename Tin, int HPW, bool GATED>
 __global__ __launch_bounds__(256) void kda_decode_d128_kernel(DecodeArgs a) {
     __shared__ float sk[HPW][D], sq[HPW][D], sa[HPW][D];
     __shared__ float red[HPW][4][32][NRED + 1];
@@ -130,6 +135,21 @@ __global__ __launch_bounds__(256) void kda_decode_d128_kernel(DecodeArgs a) {
             out[j] = tot[4 + j] + tot[8] * u[j];
         }
         if (rg == 0) store4<Tin>(static_cast<Tin*>(a.o) + unit * D + 4 * cg, out);
+        if (GATED) {
+            float gz[4];
+            load4<Tin>(static_cast<const Tin*>(a.gate) + unit * D + 4 * cg, gz);
+            float ss = out[0] * out[0] + out[1] * out[1] + out[2] * out[2] + out[3] * out[3];
+#pragma unroll
+            for (int m = 16; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 32);
+            const float r = rsqrtf(ss * (1.f / D) + a.eps);
+            float yv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float w = a.weight ? a.weight[4 * cg + j] : 1.f;
+                yv[j] = out[j] * r * w / (1.f + __expf(-gz[j]));
+            }
+            if (rg == 0) store4<Tin>(static_cast<Tin*>(a.y) + unit * D + 4 * cg, yv);
+        }
 
         float* S = a.S + unit * (int64_t)(D * D);
 #pragma unroll
@@ -144,18 +164,27 @@ __global__ __launch_bounds__(256) void kda_decode_d128_kernel(DecodeArgs a) {
 
 }  // namespace
 
+namespace {
+template <bool GATED>
+void launch_d128(const DecodeArgs& a, hipStream_t s, int64_t units) {
+    const bool pair = (units % 2) == 0;
+    const dim3 grid((unsigned)(pair ? units / 2 : units));
+    const dim3 block(256);
+    if (a.dtype == 0) {
+        if (pair) hipLaunchKernelGGL((kda_decode_d128_kernel<bf16_t, 2, GATED>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((kda_decode_d128_kernel<bf16_t, 1, GATED>), grid, block, 0, s, a);
+    } else {
+        if (pair) hipLaunchKernelGGL((kda_decode_d128_kernel<float, 2, GATED>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((kda_decode_d128_kernel<float, 1, GATED>), grid, block, 0, s, a);
+    }
+}
+}  // namespace
+
 hipError_t launch_decode_d128(const DecodeArgs& a, hipStream_t s) {
     const int64_t units = a.N * a.H;
     if (units <= 0) return hipSuccess;
-    const bool pair = (units % 2) == 0;
-    const dim3 grid((unsigned)(pair ? units / 2 : units));
-    if (a.dtype == 0) {
-        if (pair) hipLaunchKernelGGL((kda_decode_d128_kernel<bf16_t, 2>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((kda_decode_d128_kernel<bf16_t, 1>), grid, dim3(256), 0, s, a);
-    } else {
-        if (pair) hipLaunchKernelGGL((kda_decode_d128_kernel<float, 2>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((kda_decode_d128_kernel<float, 1>), grid, dim3(256), 0, s, a);
-    }
+    if (a.gate) launch_d128<true>(a, s, units);
+    else launch_d128<false>(a, s, units);
     return hipGetLastError();
 }
 

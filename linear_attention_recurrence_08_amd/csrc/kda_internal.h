@@ -38,12 +38,30 @@ struct DecodeArgs {
     void* o;              // [N, H, dv]
     int64_t N, H, dk, dv;
     int dtype;
+    // fused output stage (nullptr gate: none): y = RMSNorm(o) * weight * sigmoid(gate)
+    const void* gate = nullptr;          // [N, H, dv]
+    const float* weight = nullptr;       // [dv] or nullptr (ones)
+    float eps = 0.f;
+    void* y = nullptr;                   // [N, H, dv]
+};
+
+// Output stage over rows of dv values: y = o / sqrt(mean(o^2) + eps) * weight * sigmoid(gate).
+struct GateArgs {
+    const void* o;
+    const void* gate;
+    const float* weight;  // [dv] or nullptr (ones)
+    float eps;
+    void* y;
+    int64_t rows;         // Ttot * H
+    int64_t dv;
+    int dtype;
 };
 
 // Each launcher returns hipSuccess or the launch error.
 hipError_t launch_prefill_general(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);   // bf16, dk = dv = 128
 hipError_t launch_decode_d128(const DecodeArgs& a, hipStream_t s);     // dk = dv = 128
+hipError_t launch_output_gate(const GateArgs& a, hipStream_t s);      // 16-byte aligned rows
 
 // ---------------------------------------------------------------------------------------------
 // Number-format helpers (device)

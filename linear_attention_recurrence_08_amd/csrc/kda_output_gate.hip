@@ -1,0 +1,103 @@
+// KDA output stage: per-head RMSNorm of the mixer output times a full-rank sigmoid gate.
+//
+// "Kimi K3's hybrid block, from first principles", section "From linear attention to the delta
+// rule": the layer's output is RMS-normalised per head and multiplied by a sigmoid gate of the
+// token (a full-rank projection, given here as the tensor `gate`) before the output projection.
+// Per (token, head) row of dv values:
+//     y = o / sqrt(mean(o^2) + eps) * w * sigmoid(gate),     w: a gain per value channel (or 1)
+//
+// The stage is HBM-bound (three dv-wide rows per (token, head), a few flops per element).  A group
+// of 16 lanes owns one row: lane j holds elements 8j .. 8j+7 (one 16-byte access for bf16, two
+// for float32), the sum of squares is reduced across the group with four xor shuffles, and the
+// row is written back once.  Lanes past dv / 8 hold nothing (dv is a multiple of 16, <= 128).
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+template <typename Tin>
+struct Row8;
+template <>
+struct Row8<bf16_t> {
+    static __device__ __forceinline__ void load(const bf16_t* p, float x[8]) {
+        const u4 u = __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void store(bf16_t* p, const float x[8]) {
+        u4 u;
+        u.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+        u.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+        u.z = (uint32_t)f32_to_bf16(x[4]) | ((uint32_t)f32_to_bf16(x[5]) << 16);
+        u.w = (uint32_t)f32_to_bf16(x[6]) | ((uint32_t)f32_to_bf16(x[7]) << 16);
+        __builtin_nontemporal_store(u, reinterpret_cast<u4*>(p));
+    }
+};
+template <>
+struct Row8<float> {
+    static __device__ __forceinline__ void load(const float* p, float x[8]) {
+        const f4 a = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+        const f4 b = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p) + 1);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+    static __device__ __forceinline__ void store(float* p, const float x[8]) {
+        __builtin_nontemporal_store((f4){x[0], x[1], x[2], x[3]}, reinterpret_cast<f4*>(p));
+        __builtin_nontemporal_store((f4){x[4], x[5], x[6], x[7]}, reinterpret_cast<f4*>(p) + 1);
+    }
+};
+
+constexpr int ROWS_PER_BLOCK = 16;   // 256 threads, 16 lanes per row
+
+template <typename Tin>
+__global__ __launch_bounds__(256) void kda_output_gate_kernel(GateArgs a) {
+    const int tid = threadIdx.x;
+    const int j = tid & 15;                                    // lane within the row group
+    const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (tid >> 4);
+    const bool active = row < a.rows && 8 * j < a.dv;
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const int64_t off = row * a.dv + 8 * j;
+    if (active) {
+        Row8<Tin>::load(static_cast<const Tin*>(a.o) + off, x);
+        Row8<Tin>::load(static_cast<const Tin*>(a.gate) + off, z);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 16);
+    const float r = rsqrtf(ss / (float)a.dv + a.eps);
+    if (active) {
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float w = a.weight ? a.weight[8 * j + i] : 1.f;
+            y[i] = x[i] * r * w / (1.f + __expf(-z[i]));
+        }
+        Row8<Tin>::store(static_cast<Tin*>(a.y) + off, y);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_output_gate(const GateArgs& a, hipStream_t s) {
+    if (a.rows <= 0) return hipSuccess;
+    const int64_t grid = (a.rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+    if (a.dtype == 0)
+        hipLaunchKernelGGL(kda_output_gate_kernel<bf16_t>, dim3((unsigned)grid), dim3(256), 0, s,
+                           a);
+    else
+        hipLaunchKernelGGL(kda_output_gate_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s,
+                           a);
+    return hipGetLastError();
+}
+
+}  // namespace kda

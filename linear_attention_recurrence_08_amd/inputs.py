@@ -248,3 +248,16 @@ def make_decode_inputs(N: int, H: int, dk: int, dv: int, dtype: str, seed: int,
     inp = make_inputs([1] * N, H, dk, dv, dtype, seed, gate=gate, h0_sigma=s_sigma,
                       packed=False, name=name)
     return inp
+
+
+def make_output_gate_inputs(Ttot: int, H: int, dv: int, dtype: str, seed: int):
+    """Inputs of the output stage: rows o [Ttot, H, dv] ~ N(0, 0.3^2) (the scale of a mixer output;
+    the stage is scale-free), gate logits [Ttot, H, dv] ~ N(0, 1) (a full-rank projection of the
+    token) and the norm's gain [dv] = 1 + 0.1 N(0, 1) in float32.  Streams SeedSequence([seed,
+    3 * 10**6 + i]) for i = 0 (o), 1 (gate), 2 (gain).  Returns CPU tensors (o, gate, weight)."""
+    shape = (int(Ttot), int(H), int(dv))
+    o = (_stream(seed, 3 * 10**6).standard_normal(shape, dtype=np.float32) * np.float32(0.3))
+    z = _stream(seed, 3 * 10**6 + 1).standard_normal(shape, dtype=np.float32)
+    w = (1.0 + 0.1 * _stream(seed, 3 * 10**6 + 2).standard_normal(dv)).astype(np.float32)
+    td = _torch_dtype(dtype)
+    return (torch.from_numpy(o).to(td), torch.from_numpy(z).to(td), torch.from_numpy(w))

@@ -50,6 +50,12 @@ def load_library():
         lib.kda_chunk_fwd_snapshots.restype = i32
         lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         lib.kda_decode_step.restype = i32
+        f32 = ctypes.c_float
+        lib.kda_output_gate.argtypes = [vp, vp, vp, f32, vp, i32, i32, i32, i32, vp]
+        lib.kda_output_gate.restype = i32
+        lib.kda_decode_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, i32,
+                                              i32, i32, i32, i32, vp]
+        lib.kda_decode_step_gated.restype = i32
         lib.kda_status_string.argtypes = [i32]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_version.argtypes = []
@@ -202,11 +208,7 @@ def kda_chunk_fwd_snapshots(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g
     return o, hT, snaps, snap_offsets
 
 
-def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-                    beta: torch.Tensor, S: torch.Tensor,
-                    o: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """One token per sequence: q, k, g [N, H, dk], v [N, H, dv], beta [N, H]; S float32
-    [N, H, dk, dv] is updated in place.  Returns o [N, H, dv]."""
+def _decode_args(q, k, v, g, beta, S, o):
     dev = q.device
     dt = q.dtype
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
@@ -223,9 +225,77 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
         o = torch.empty((N, H, dv), dtype=dt, device=dev)
     else:
         _check(o, "o", dev, dt)
+    return dev, N, H, dk, dv, o
+
+
+def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, S: torch.Tensor,
+                    o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token per sequence: q, k, g [N, H, dk], v [N, H, dv], beta [N, H]; S float32
+    [N, H, dk, dv] is updated in place.  Returns o [N, H, dv]."""
+    dev, N, H, dk, dv, o = _decode_args(q, k, v, g, beta, S, o)
     st = load_library().kda_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o), N, H, dk, dv,
         _dtype_code(q), _stream(dev))
     if st != KDA_OK:
         raise KDAError(st, "kda_decode_step")
     return o
+
+
+def _gate_weight(weight, dv, dev):
+    if weight is None:
+        return None
+    _check(weight, "weight", dev, torch.float32)
+    if weight.shape != (dv,):
+        raise ValueError(f"weight must be [{dv}]")
+    return weight
+
+
+def kda_decode_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                          beta: torch.Tensor, S: torch.Tensor, gate: torch.Tensor,
+                          weight: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                          o: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None
+                          ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """kda_decode_step followed by the output stage y = RMSNorm(o) * weight * sigmoid(gate) (fused
+    into the decode kernel for 128 x 128 heads).  gate [N, H, dv]; weight [dv] float32 or None.
+    Returns (o, y)."""
+    dev, N, H, dk, dv, o = _decode_args(q, k, v, g, beta, S, o)
+    _check(gate, "gate", dev, q.dtype)
+    if gate.shape != (N, H, dv):
+        raise ValueError("gate must be [N, H, dv]")
+    weight = _gate_weight(weight, dv, dev)
+    if y is None:
+        y = torch.empty_like(o)
+    else:
+        _check(y, "y", dev, q.dtype)
+    st = load_library().kda_decode_step_gated(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(gate), _ptr(weight),
+        float(eps), _ptr(o), _ptr(y), N, H, dk, dv, _dtype_code(q), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_decode_step_gated")
+    return o, y
+
+
+def kda_output_gate(o: torch.Tensor, gate: torch.Tensor, weight: Optional[torch.Tensor] = None,
+                    eps: float = 1e-6, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The output stage on [..., H, dv] rows: y = o / sqrt(mean(o^2) + eps) * weight *
+    sigmoid(gate).  Returns y (may be passed preallocated; may be o itself)."""
+    dev = o.device
+    _check(o, "o", dev)
+    _check(gate, "gate", dev, o.dtype)
+    if gate.shape != o.shape or o.dim() < 2:
+        raise ValueError("o and gate must have the same [..., H, dv] shape")
+    H, dv = o.shape[-2], o.shape[-1]
+    rows = o.numel() // (H * dv) if o.numel() else 0
+    weight = _gate_weight(weight, dv, dev)
+    if y is None:
+        y = torch.empty_like(o)
+    else:
+        _check(y, "y", dev, o.dtype)
+        if y.shape != o.shape:
+            raise ValueError("y must have o's shape")
+    st = load_library().kda_output_gate(_ptr(o), _ptr(gate), _ptr(weight), float(eps), _ptr(y),
+                                        rows, H, dv, _dtype_code(o), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_output_gate")
+    return y

@@ -342,3 +342,67 @@ def test_snapshots_T4096_H96(oracle_mod):
     assert es <= TOL["bf16"]
     assert err(to64(o[:, heads]), o_ref) <= TOL["bf16"]
     assert torch.equal(snaps[-1], hT[0])
+
+
+# ------------------------------------------------------------------------------------------------
+# output stage: per-head RMSNorm times a sigmoid gate (standalone and fused into decode)
+# ------------------------------------------------------------------------------------------------
+GATE_TOL = {"bf16": 1e-2, "f32": 1e-5}   # one bf16 rounding of y; float32 transcendentals
+
+
+@pytest.mark.parametrize("Ttot,H,dv,dt,with_w", [
+    (37, 3, 128, "bf16", True), (64, 2, 128, "f32", False), (19, 5, 64, "bf16", False),
+    (33, 2, 16, "f32", True), (1, 1, 48, "bf16", True), (100, 4, 96, "f32", True)])
+def test_output_gate_small(oracle_mod, Ttot, H, dv, dt, with_w):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_output_gate
+    o, z, w = inputs.make_output_gate_inputs(Ttot, H, dv, dt, seed=51 + dv)
+    w = w if with_w else None
+    y = kda_output_gate(o.to(dev), z.to(dev), None if w is None else w.to(dev), eps=1e-6)
+    od = o.to(dev)
+    y2 = kda_output_gate(od, z.to(dev), None if w is None else w.to(dev), eps=1e-6, y=od)
+    torch.cuda.synchronize()
+    ref = oracle_mod.output_gate(to64(o), to64(z), None if w is None else to64(w), 1e-6)
+    e = err(to64(y), ref)
+    _say(f"output gate [{Ttot},{H},{dv}] {dt}: error {e:.3e}")
+    assert e <= GATE_TOL[dt]
+    assert torch.equal(y2, y)     # in place gives the same rows
+
+
+def test_output_gate_T4096_H96(oracle_mod):
+    """The output stage on the 4096-token, 96-head layer output shape; every row checked."""
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_output_gate
+    o, z, w = inputs.make_output_gate_inputs(4096, 96, 128, "bf16", seed=61)
+    y = kda_output_gate(o.to(dev), z.to(dev), w.to(dev), eps=1e-6)
+    torch.cuda.synchronize()
+    ref = oracle_mod.output_gate(to64(o), to64(z), to64(w), 1e-6)
+    e = err(to64(y), ref)
+    _say(f"output gate [4096,96,128] bf16: error {e:.3e}")
+    assert e <= GATE_TOL["bf16"]
+
+
+@pytest.mark.parametrize("N,H,dk,dv,dt", [(256, 96, 128, 128, "bf16"), (7, 3, 128, 128, "f32"),
+                                          (5, 2, 64, 32, "f32"), (9, 3, 32, 128, "bf16")])
+def test_decode_gated(oracle_mod, N, H, dk, dv, dt):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_decode_step, kda_decode_step_gated
+    d = inputs.make_decode_inputs(N, H, dk, dv, dt, seed=71 + N)
+    _, z, w = inputs.make_output_gate_inputs(N, H, dv, dt, seed=72 + N)
+    args = [t.to(dev) for t in (d.q, d.k, d.v, d.g, d.beta)]
+    S1, S2 = d.h0.to(dev), d.h0.to(dev)
+    o, y = kda_decode_step_gated(*args, S1, z.to(dev), w.to(dev), eps=1e-6)
+    o_plain = kda_decode_step(*args, S2)
+    torch.cuda.synchronize()
+    # the fused stage leaves the decode itself unchanged
+    assert torch.equal(o, o_plain) and torch.equal(S1, S2)
+    rng = np.random.default_rng(5)
+    units = sorted(set(map(tuple, rng.integers(0, [N, H], size=(min(96, N * H), 2)).tolist())))
+    ns, hs = [u[0] for u in units], [u[1] for u in units]
+    sel = lambda t: to64(t[ns, hs])[:, None]
+    o_ref, _ = oracle_mod.decode_step(sel(d.q), sel(d.k), sel(d.v), sel(d.g),
+                                      to64(d.beta[ns, hs])[:, None], sel(d.h0))
+    y_ref = oracle_mod.output_gate(o_ref[:, 0], to64(z[ns, hs]), to64(w), 1e-6)
+    eo, ey = err(to64(o[ns, hs]), o_ref[:, 0]), err(to64(y[ns, hs]), y_ref)
+    _say(f"decode gated N={N} H={H} {dk}x{dv} {dt}: error o={eo:.3e} y={ey:.3e}")
+    assert eo <= TOL[dt] and ey <= TOL[dt]
