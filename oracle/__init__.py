@@ -4,7 +4,7 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg may import 
 shares no code with the HIP path and does not import the product package.
 """
 from .kda_oracle import (brute_force, build, chunked, decode_step, default_threads, exact,
-                         output_gate, recurrence)
+                         frontend, output_gate, recurrence)
 
 __all__ = ["brute_force", "build", "chunked", "decode_step", "default_threads", "exact",
-           "output_gate", "recurrence"]
+           "frontend", "output_gate", "recurrence"]

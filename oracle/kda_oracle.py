@@ -14,6 +14,8 @@ chunked(...)      an independent chunkwise form (numpy float64): parallel inside
 brute_force(...)  the unrolled sum of explicit dk x dk transition products (tiny inputs only).
 exact(...)        the recurrence in exact rational arithmetic (fractions.Fraction; tiny inputs).
 output_gate(...)  the output stage after the mixer: per-head RMSNorm times a sigmoid gate.
+frontend(...)     the input stage before the mixer: short convolution, Swish, L2 norm, the sigmoid
+                  write strength and the bounded log-decay.
 
 The recurrence these compute (decay first, then erase-and-write, then read the updated state):
     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t,
@@ -342,3 +344,58 @@ def output_gate(o, gate, weight=None, eps: float = 1e-6):
     if weight is not None:
         normed = normed * np.asarray(weight, dtype=np.float64)
     return normed / (1.0 + np.exp(-gate))
+
+
+# ---------------------------------------------------------------------------------------------
+# Input stage.  "Kimi K3's hybrid block, from first principles", section "From linear attention to
+# the delta rule": queries and keys pass through a short convolution of width 4, Swish and L2
+# normalisation; values through the convolution and Swish; beta_t is a sigmoid of a projection of
+# the token; the decay logit z_t is a low-rank projection plus a per-channel bias, and the
+# log-decay is bounded below by g_min = -5 with one learned scale A_h per head (every factor then
+# lies between e^-5 and 1).  Readings where the pages are silent or garbled:
+#   * the convolution is causal and depthwise along tokens, y[t,c] = sum_{i<4} w[c,i] x[t-3+i,c]
+#     (w[c,3] weighs the current token), without bias, restarting at every sequence start from a
+#     saved state of the last three inputs (zeros when none is given);
+#   * L2 normalisation divides by sqrt(sum_c x_c^2 + eps) per (token, head), eps = 1e-6;
+#   * the bounded log-decay is g = g_min * sigmoid(A_h (z + bias_c)), which lies in (g_min, 0).
+# Layouts: x_q, x_k, x_z [Ttot, H, dk]; x_v [Ttot, H, dv]; x_b [Ttot, H]; conv weights w_q, w_k
+# [H*dk, 4] and w_v [H*dv, 4]; z_bias [H*dk]; A [H].  The convolution state holds, per sequence,
+# the last three inputs of q, k and v: [N, 3, H*dk + H*dk + H*dv], oldest first.
+# ---------------------------------------------------------------------------------------------
+def _swish(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def frontend(x_q, x_k, x_v, x_z, x_b, w_q, w_k, w_v, z_bias, A, g_min: float = -5.0,
+             cu_seqlens=None, conv_in=None, eps: float = 1e-6):
+    """Returns (q, k, v, g, beta, conv_out) in float64; conv_out [N, 3, H*(2dk+dv)]."""
+    f = lambda a: np.asarray(a, dtype=np.float64)
+    x_q, x_k, x_v, x_z, x_b = f(x_q), f(x_k), f(x_v), f(x_z), f(x_b)
+    w_q, w_k, w_v, z_bias, A = f(w_q), f(w_k), f(w_v), f(z_bias), f(A)
+    Ttot, H, dk = x_q.shape
+    dv = x_v.shape[2]
+    cu = np.asarray([0, Ttot] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
+    N = cu.size - 1
+    C = H * (2 * dk + dv)
+    state = np.zeros((N, 3, C)) if conv_in is None else f(conv_in).reshape(N, 3, C)
+    rows = np.concatenate([x_q.reshape(Ttot, H * dk), x_k.reshape(Ttot, H * dk),
+                           x_v.reshape(Ttot, H * dv)], axis=1)          # [Ttot, C]
+    w = np.concatenate([w_q, w_k, w_v], axis=0)                          # [C, 4]
+    conv = np.zeros((Ttot, C))
+    conv_out = np.zeros((N, 3, C))
+    for n in range(N):
+        a, e = int(cu[n]), int(cu[n + 1])
+        seq = np.concatenate([state[n], rows[a:e]], axis=0)             # [3 + len, C]
+        for t in range(e - a):
+            conv[a + t] = np.sum(w.T * seq[t:t + 4], axis=0)            # taps t-3 .. t
+        conv_out[n] = seq[-3:]
+    act = _swish(conv)
+    q = act[:, :H * dk].reshape(Ttot, H, dk)
+    k = act[:, H * dk:2 * H * dk].reshape(Ttot, H, dk)
+    v = act[:, 2 * H * dk:].reshape(Ttot, H, dv)
+    q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + eps)
+    k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + eps)
+    zz = A[None, :, None] * (x_z + z_bias.reshape(H, dk)[None])
+    g = g_min / (1.0 + np.exp(-zz))
+    beta = 1.0 / (1.0 + np.exp(-x_b))
+    return q, k, v, g, beta, conv_out
