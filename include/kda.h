@@ -182,6 +182,46 @@ int kda_decode_step_gated(const void* q, const void* k, const void* v, const voi
                           float eps, void* o, void* y, int N, int H, int dk, int dv, int dtype,
                           void* stream);
 
+/*
+ * kda_frontend -- the input stage before the mixer: turns the projected pre-activations of every
+ * token into q, k, v, g and beta for kda_chunk_fwd / kda_decode_step ("Kimi K3's hybrid block,
+ * from first principles", section "From linear attention to the delta rule": queries and keys
+ * pass through a short convolution of width 4, Swish and L2 normalisation; values through the
+ * convolution and Swish; beta is a sigmoid of a projection of the token; the log-decay is bounded
+ * below by g_min with one learned scale A_h per head).  Per token t, head h, channel c:
+ *
+ *     conv(x)[t,c] = sum_{i<4} w[c,i] x[t-3+i,c]     causal and depthwise; at a sequence start the
+ *                                                   three earlier inputs come from conv_in (zeros
+ *                                                   when conv_in is NULL)
+ *     q = l2(swish(conv(x_q)))   k = l2(swish(conv(x_k)))   v = swish(conv(x_v))
+ *     g = g_min * sigmoid(A[h] * (x_z + z_bias[c]))           beta = sigmoid(x_b)
+ *     swish(y) = y * sigmoid(y);   l2(y) = y / sqrt(sum_c y_c^2 + eps) over the head's dk values
+ *
+ * The printed formula of the bounded gate is lost on the pages; this is the reading that matches
+ * their statement (every retention factor between e^g_min and 1, one scale per head).
+ *
+ *   x_q, x_k, x_z [Ttot, H, dk], x_v [Ttot, H, dv], x_b [Ttot, H]   dtype    device  inputs
+ *   w_q, w_k [H*dk, 4], w_v [H*dv, 4]      float32  device   taps; w[c,3] weighs the current token
+ *   z_bias [H*dk], A [H]                   float32  device
+ *   g_min (< 0), eps (>= 0)                                   else KDA_ERR_RANGE
+ *   cu_seqlens, num_seqs, B, T             as kda_chunk_fwd (sequence boundaries)
+ *   conv_in  [N, 3, H*(2dk+dv)]  dtype  device  the last three inputs of q | k | v before each
+ *                                               sequence, oldest first; NULL = zeros
+ *   conv_out [N, 3, H*(2dk+dv)]  dtype  device  written: the last three inputs of each sequence
+ *                                               (rows of conv_in when shorter); NULL = not
+ *                                               written; may alias conv_in (decode: one token per
+ *                                               sequence with the state updated in place)
+ *   q, k, g [Ttot, H, dk], v [Ttot, H, dv], beta [Ttot, H]   dtype  device  outputs
+ * Every [*, H, d] buffer and the state rows must be 16-byte aligned (KDA_ERR_ALIGN).
+ * Returns KDA_OK or a negative status.
+ */
+int kda_frontend(const void* x_q, const void* x_k, const void* x_v, const void* x_z,
+                 const void* x_b, const float* w_q, const float* w_k, const float* w_v,
+                 const float* z_bias, const float* A, float g_min, float eps,
+                 const int32_t* cu_seqlens, int num_seqs, const void* conv_in, void* conv_out,
+                 void* q, void* k, void* v, void* g, void* beta,
+                 int B, int T, int H, int dk, int dv, int dtype, void* stream);
+
 /* Text for a status code (static storage; never NULL). */
 const char* kda_status_string(int status);
 

@@ -246,4 +246,51 @@ int kda_decode_step_gated(const void* q, const void* k, const void* v, const voi
     return decode_impl(q, k, v, g, beta, S, gate, weight, eps, o, y, N, H, dk, dv, dtype, stream);
 }
 
+int kda_frontend(const void* x_q, const void* x_k, const void* x_v, const void* x_z,
+                 const void* x_b, const float* w_q, const float* w_k, const float* w_v,
+                 const float* z_bias, const float* A, float g_min, float eps,
+                 const int32_t* cu_seqlens, int num_seqs, const void* conv_in, void* conv_out,
+                 void* q, void* k, void* v, void* g, void* beta,
+                 int B, int T, int H, int dk, int dv, int dtype, void* stream) {
+    if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
+    if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
+    if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!(g_min < 0.f) || !std::isfinite(g_min) || !(eps >= 0.f) || !std::isfinite(eps))
+        return KDA_ERR_RANGE;
+    int64_t N, Ttot;
+    if (cu_seqlens) {
+        if (B != 1) return KDA_ERR_SEQLENS;
+        N = num_seqs;
+        Ttot = T;
+    } else {
+        N = B;
+        Ttot = static_cast<int64_t>(B) * T;
+    }
+    if (N == 0 || (Ttot == 0 && !conv_out)) return KDA_OK;
+    if (Ttot > 0 && (!x_q || !x_k || !x_v || !x_z || !x_b || !w_q || !w_k || !w_v || !z_bias ||
+                     !A || !q || !k || !v || !g || !beta))
+        return KDA_ERR_NULL;
+    for (const void* p : {x_q, x_k, x_v, x_z, conv_in, static_cast<const void*>(conv_out),
+                          static_cast<const void*>(q), static_cast<const void*>(k),
+                          static_cast<const void*>(v), static_cast<const void*>(g)})
+        if (p && !aligned(p, 16)) return KDA_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (validate_enabled() && cu_seqlens) {
+        std::vector<int32_t> cu(static_cast<size_t>(N + 1));
+        int st = fetch(cu.data(), cu_seqlens, cu.size() * 4, s);
+        if (st) return st;
+        if (cu[0] != 0 || cu[N] != Ttot) return KDA_ERR_SEQLENS;
+        for (int64_t i = 0; i < N; ++i)
+            if (cu[i + 1] < cu[i]) return KDA_ERR_SEQLENS;
+    }
+    kda::FrontArgs a;
+    a.xq = x_q; a.xk = x_k; a.xv = x_v; a.xz = x_z; a.xb = x_b;
+    a.wq = w_q; a.wk = w_k; a.wv = w_v; a.zbias = z_bias; a.A = A; a.g_min = g_min; a.eps = eps;
+    a.cu = cu_seqlens; a.conv_in = conv_in; a.conv_out = conv_out;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.N = N; a.T = cu_seqlens ? 0 : T; a.Ttot = Ttot; a.H = H; a.dk = dk; a.dv = dv;
+    a.dtype = dtype;
+    return kda::launch_frontend(a, s) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -57,11 +57,37 @@ struct GateArgs {
     int dtype;
 };
 
+// Input stage (short convolution, Swish, L2 norm, sigmoid beta, bounded log-decay).
+struct FrontArgs {
+    const void* xq;       // [Ttot, H, dk] pre-activations (dtype)
+    const void* xk;       // [Ttot, H, dk]
+    const void* xv;       // [Ttot, H, dv]
+    const void* xz;       // [Ttot, H, dk] decay logits before the bias
+    const void* xb;       // [Ttot, H] write-strength logits
+    const float* wq;      // [H * dk, 4] convolution taps (tap 3 = current token)
+    const float* wk;      // [H * dk, 4]
+    const float* wv;      // [H * dv, 4]
+    const float* zbias;   // [H * dk]
+    const float* A;       // [H]
+    float g_min, eps;
+    const int32_t* cu;    // [N + 1] or nullptr (N sequences of length T)
+    const void* conv_in;  // [N, 3, H * (2 dk + dv)] (dtype) or nullptr (zeros)
+    void* conv_out;       // [N, 3, H * (2 dk + dv)] or nullptr; may alias conv_in
+    void* q;              // [Ttot, H, dk] outputs (dtype)
+    void* k;
+    void* v;              // [Ttot, H, dv]
+    void* g;              // [Ttot, H, dk]
+    void* beta;           // [Ttot, H]
+    int64_t N, T, Ttot, H, dk, dv;
+    int dtype;
+};
+
 // Each launcher returns hipSuccess or the launch error.
 hipError_t launch_prefill_general(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);   // bf16, dk = dv = 128
 hipError_t launch_decode_d128(const DecodeArgs& a, hipStream_t s);     // dk = dv = 128
 hipError_t launch_output_gate(const GateArgs& a, hipStream_t s);      // 16-byte aligned rows
+hipError_t launch_frontend(const FrontArgs& a, hipStream_t s);        // 16-byte aligned rows
 
 // ---------------------------------------------------------------------------------------------
 // Number-format helpers (device)
@@ -88,6 +114,44 @@ template <> struct io<float> {
 template <> struct io<bf16_t> {
     __device__ static __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
     __device__ static __forceinline__ void store(bf16_t* p, float x) { *p = f32_to_bf16(x); }
+};
+
+// Eight consecutive elements as float32, one 16-byte access for bf16 and two for float32
+// (non-temporal: the streaming stages touch each element once).  Addresses must be 16-byte
+// aligned.
+typedef float f32v4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
+template <typename T> struct Row8;
+template <> struct Row8<bf16_t> {
+    static __device__ __forceinline__ void load(const bf16_t* p, float x[8]) {
+        const u32v4 u = __builtin_nontemporal_load(reinterpret_cast<const u32v4*>(p));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(u[i] << 16);
+            x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void store(bf16_t* p, const float x[8]) {
+        u32v4 u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            u[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
+        __builtin_nontemporal_store(u, reinterpret_cast<u32v4*>(p));
+    }
+};
+template <> struct Row8<float> {
+    static __device__ __forceinline__ void load(const float* p, float x[8]) {
+        const f32v4 a = __builtin_nontemporal_load(reinterpret_cast<const f32v4*>(p));
+        const f32v4 b = __builtin_nontemporal_load(reinterpret_cast<const f32v4*>(p) + 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+    }
+    static __device__ __forceinline__ void store(float* p, const float x[8]) {
+        __builtin_nontemporal_store((f32v4){x[0], x[1], x[2], x[3]},
+                                    reinterpret_cast<f32v4*>(p));
+        __builtin_nontemporal_store((f32v4){x[4], x[5], x[6], x[7]},
+                                    reinterpret_cast<f32v4*>(p) + 1);
+    }
 };
 
 }  // namespace kda

@@ -15,45 +15,6 @@
 namespace kda {
 namespace {
 
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-
-template <typename Tin>
-struct Row8;
-template <>
-struct Row8<bf16_t> {
-    static __device__ __forceinline__ void load(const bf16_t* p, float x[8]) {
-        const u4 u = __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[2 * i] = __uint_as_float(w[i] << 16);
-            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    }
-    static __device__ __forceinline__ void store(bf16_t* p, const float x[8]) {
-        u4 u;
-        u.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
-        u.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
-        u.z = (uint32_t)f32_to_bf16(x[4]) | ((uint32_t)f32_to_bf16(x[5]) << 16);
-        u.w = (uint32_t)f32_to_bf16(x[6]) | ((uint32_t)f32_to_bf16(x[7]) << 16);
-        __builtin_nontemporal_store(u, reinterpret_cast<u4*>(p));
-    }
-};
-template <>
-struct Row8<float> {
-    static __device__ __forceinline__ void load(const float* p, float x[8]) {
-        const f4 a = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
-        const f4 b = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p) + 1);
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    }
-    static __device__ __forceinline__ void store(float* p, const float x[8]) {
-        __builtin_nontemporal_store((f4){x[0], x[1], x[2], x[3]}, reinterpret_cast<f4*>(p));
-        __builtin_nontemporal_store((f4){x[4], x[5], x[6], x[7]}, reinterpret_cast<f4*>(p) + 1);
-    }
-};
-
 constexpr int ROWS_PER_BLOCK = 16;   // 256 threads, 16 lanes per row
 
 template <typename Tin>

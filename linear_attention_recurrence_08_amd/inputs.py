@@ -261,3 +261,49 @@ def make_output_gate_inputs(Ttot: int, H: int, dv: int, dtype: str, seed: int):
     w = (1.0 + 0.1 * _stream(seed, 3 * 10**6 + 2).standard_normal(dv)).astype(np.float32)
     td = _torch_dtype(dtype)
     return (torch.from_numpy(o).to(td), torch.from_numpy(z).to(td), torch.from_numpy(w))
+
+
+@dataclasses.dataclass
+class FrontInputs:
+    """Inputs of the input stage (pre-activations, taps, bias, per-head scale) on the CPU."""
+    x_q: torch.Tensor
+    x_k: torch.Tensor
+    x_v: torch.Tensor
+    x_z: torch.Tensor
+    x_b: torch.Tensor
+    w_q: torch.Tensor
+    w_k: torch.Tensor
+    w_v: torch.Tensor
+    z_bias: torch.Tensor
+    A: torch.Tensor
+    cu_seqlens: Optional[torch.Tensor]
+    conv_in: Optional[torch.Tensor]
+
+    def to(self, dev) -> "FrontInputs":
+        f = lambda t: None if t is None else t.to(dev)
+        return FrontInputs(*(f(getattr(self, fl.name)) for fl in dataclasses.fields(self)))
+
+
+def make_frontend_inputs(seq_lens: Sequence[int], H: int, dk: int, dv: int, dtype: str,
+                         seed: int, with_state: bool = False) -> FrontInputs:
+    """Pre-activations x_q, x_k, x_v, x_z ~ N(0, 1) and x_b ~ N(0, 1) (projection outputs), packed
+    [Ttot, H, d] with cu_seqlens; taps ~ U(-1/2, 1/2) (the usual width-4 convolution scale); the
+    decay bias ~ N(0, 1/4); A_h ~ U(1/2, 2); with_state adds a saved convolution state ~ N(0, 1)
+    [N, 3, H (2 dk + dv)].  Streams SeedSequence([seed, 4 * 10**6 + i])."""
+    lens = [int(x) for x in seq_lens]
+    Ttot, N = sum(lens), len(lens)
+    td = _torch_dtype(dtype)
+    r = lambda i, *shape: _stream(seed, 4 * 10**6 + i).standard_normal(shape, dtype=np.float32)
+    u = lambda i, lo, hi, *shape: _stream(seed, 4 * 10**6 + i).uniform(lo, hi, shape).astype(
+        np.float32)
+    t = lambda a, dt=td: torch.from_numpy(np.ascontiguousarray(a)).to(dt)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    C = H * (2 * dk + dv)
+    return FrontInputs(
+        x_q=t(r(0, Ttot, H, dk)), x_k=t(r(1, Ttot, H, dk)), x_v=t(r(2, Ttot, H, dv)),
+        x_z=t(r(3, Ttot, H, dk)), x_b=t(r(4, Ttot, H)),
+        w_q=t(u(5, -0.5, 0.5, H * dk, 4), torch.float32),
+        w_k=t(u(6, -0.5, 0.5, H * dk, 4), torch.float32),
+        w_v=t(u(7, -0.5, 0.5, H * dv, 4), torch.float32),
+        z_bias=t(0.5 * r(8, H * dk), torch.float32), A=t(u(9, 0.5, 2.0, H), torch.float32),
+        cu_seqlens=cu, conv_in=t(r(10, N, 3, C)) if with_state else None)

@@ -56,6 +56,9 @@ def load_library():
         lib.kda_decode_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, i32,
                                               i32, i32, i32, i32, vp]
         lib.kda_decode_step_gated.restype = i32
+        lib.kda_frontend.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, f32, vp, i32,
+                                     vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+        lib.kda_frontend.restype = i32
         lib.kda_status_string.argtypes = [i32]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_version.argtypes = []
@@ -299,3 +302,70 @@ def kda_output_gate(o: torch.Tensor, gate: torch.Tensor, weight: Optional[torch.
     if st != KDA_OK:
         raise KDAError(st, "kda_output_gate")
     return y
+
+
+def kda_frontend(x_q: torch.Tensor, x_k: torch.Tensor, x_v: torch.Tensor, x_z: torch.Tensor,
+                 x_b: torch.Tensor, w_q: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor,
+                 z_bias: torch.Tensor, A: torch.Tensor, g_min: float = -5.0, eps: float = 1e-6,
+                 cu_seqlens: Optional[torch.Tensor] = None, conv_in: Optional[torch.Tensor] = None,
+                 output_conv_state: bool = False, conv_out: Optional[torch.Tensor] = None):
+    """The input stage: pre-activations x_q, x_k, x_z [.., H, dk], x_v [.., H, dv], x_b [.., H]
+    ([B, T, ...] or packed [Ttot, ...] with cu_seqlens) -> (q, k, v, g, beta, conv_state) in the
+    layouts kda_chunk_fwd takes.  Taps w_q, w_k [H*dk, 4], w_v [H*dv, 4], z_bias [H*dk] and A [H]
+    are float32.  conv_in / the returned state [N, 3, H*(2dk+dv)] hold the last three inputs of
+    every sequence (pass conv_out=conv_in to update it in place); conv_state is None unless
+    output_conv_state or conv_out is given."""
+    dev = x_q.device
+    dt = x_q.dtype
+    for name, t in (("x_q", x_q), ("x_k", x_k), ("x_v", x_v), ("x_z", x_z), ("x_b", x_b)):
+        _check(t, name, dev, dt)
+    if x_q.dim() == 4:
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens needs packed [Ttot, H, d] inputs")
+        B, T, H, dk = x_q.shape
+        lead = (B, T)
+    elif x_q.dim() == 3:
+        T, H, dk = x_q.shape
+        B = 1
+        lead = (T,)
+    else:
+        raise ValueError("x_q must be [B, T, H, dk] or [Ttot, H, dk]")
+    dv = x_v.shape[-1]
+    if x_k.shape != x_q.shape or x_z.shape != x_q.shape or x_v.shape != (*lead, H, dv) \
+            or x_b.shape != (*lead, H):
+        raise ValueError("inconsistent pre-activation shapes")
+    for name, t, shape in (("w_q", w_q, (H * dk, 4)), ("w_k", w_k, (H * dk, 4)),
+                           ("w_v", w_v, (H * dv, 4)), ("z_bias", z_bias, (H * dk,)),
+                           ("A", A, (H,))):
+        _check(t, name, dev, torch.float32)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {list(shape)}")
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", dev, torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    C = H * (2 * dk + dv)
+    if conv_in is not None:
+        _check(conv_in, "conv_in", dev, dt)
+        if tuple(conv_in.shape) != (N, 3, C):
+            raise ValueError(f"conv_in must be [{N}, 3, {C}]")
+    if conv_out is None and output_conv_state:
+        conv_out = torch.empty((N, 3, C), dtype=dt, device=dev)
+    if conv_out is not None:
+        _check(conv_out, "conv_out", dev, dt)
+        if tuple(conv_out.shape) != (N, 3, C):
+            raise ValueError(f"conv_out must be [{N}, 3, {C}]")
+    q = torch.empty_like(x_q)
+    k = torch.empty_like(x_k)
+    v = torch.empty_like(x_v)
+    g = torch.empty_like(x_z)
+    beta = torch.empty_like(x_b)
+    st = load_library().kda_frontend(
+        _ptr(x_q), _ptr(x_k), _ptr(x_v), _ptr(x_z), _ptr(x_b), _ptr(w_q), _ptr(w_k), _ptr(w_v),
+        _ptr(z_bias), _ptr(A), float(g_min), float(eps), _ptr(cu_seqlens), N, _ptr(conv_in),
+        _ptr(conv_out), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), B, T, H, dk, dv,
+        _dtype_code(x_q), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_frontend")
+    return q, k, v, g, beta, conv_out

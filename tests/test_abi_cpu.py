@@ -29,7 +29,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_snapshots",
-                                     "kda_decode_step", "kda_decode_step_gated",
+                                     "kda_decode_step", "kda_decode_step_gated", "kda_frontend",
                                      "kda_output_gate", "kda_status_string", "kda_version"]
 
 
@@ -176,3 +176,30 @@ def _decode_gated(lib, **kw):
 ])
 def test_decode_gated_argument_errors(lib, kw, code):
     assert _decode_gated(lib, **kw) == code
+
+
+def _front(lib, **kw):
+    a = dict(xq=FAKE, xk=FAKE, xv=FAKE, xz=FAKE, xb=FAKE, wq=FAKE, wk=FAKE, wv=FAKE, zb=FAKE,
+             A=FAKE, gmin=-5.0, eps=1e-6, cu=None, num_seqs=0, cin=None, cout=None, q=FAKE,
+             k=FAKE, v=FAKE, g=FAKE, beta=FAKE, B=2, T=16, H=2, dk=128, dv=128, dtype=0)
+    a.update(kw)
+    return lib.kda_frontend(*(a[n] for n in ("xq", "xk", "xv", "xz", "xb", "wq", "wk", "wv", "zb",
+                                             "A", "gmin", "eps", "cu", "num_seqs", "cin", "cout",
+                                             "q", "k", "v", "g", "beta", "B", "T", "H", "dk",
+                                             "dv", "dtype")), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -3), (dict(B=-1), -2), (dict(H=0), -2), (dict(dk=8), -4), (dict(dv=136), -4),
+    (dict(gmin=0.0), -6), (dict(gmin=1.0), -6), (dict(eps=-1.0), -6),
+    (dict(cu=FAKE, B=2, num_seqs=1), -5),
+    (dict(xq=None), -1), (dict(wv=None), -1), (dict(A=None), -1), (dict(beta=None), -1),
+    (dict(q=UNALIGNED), -9), (dict(xv=UNALIGNED), -9), (dict(cin=UNALIGNED), -9),
+])
+def test_frontend_argument_errors(lib, kw, code):
+    assert _front(lib, **kw) == code
+
+
+def test_frontend_empty_is_noop(lib):
+    assert _front(lib, B=0) == 0
+    assert _front(lib, T=0) == 0

@@ -406,3 +406,89 @@ def test_decode_gated(oracle_mod, N, H, dk, dv, dt):
     eo, ey = err(to64(o[ns, hs]), o_ref[:, 0]), err(to64(y[ns, hs]), y_ref)
     _say(f"decode gated N={N} H={H} {dk}x{dv} {dt}: error o={eo:.3e} y={ey:.3e}")
     assert eo <= TOL[dt] and ey <= TOL[dt]
+
+
+# ------------------------------------------------------------------------------------------------
+# input stage: short convolution, Swish, L2 norm, sigmoid beta, bounded log-decay
+# ------------------------------------------------------------------------------------------------
+def _front_oracle(oracle_mod, f):
+    cin = None if f.conv_in is None else to64(f.conv_in)
+    return oracle_mod.frontend(to64(f.x_q), to64(f.x_k), to64(f.x_v), to64(f.x_z), to64(f.x_b),
+                               to64(f.w_q), to64(f.w_k), to64(f.w_v), to64(f.z_bias), to64(f.A),
+                               -5.0, f.cu_seqlens.tolist(), cin, 1e-6)
+
+
+def _front_gpu(f, dev, **kw):
+    from linear_attention_recurrence_08_amd import kda_frontend
+    d = f.to(dev)
+    out = kda_frontend(d.x_q, d.x_k, d.x_v, d.x_z, d.x_b, d.w_q, d.w_k, d.w_v, d.z_bias, d.A,
+                       -5.0, 1e-6, cu_seqlens=d.cu_seqlens, conv_in=d.conv_in,
+                       output_conv_state=True, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_front(out, ref, dt, label):
+    names = ("q", "k", "v", "g", "beta")
+    errs = [err(to64(out[i]), ref[i]) for i in range(5)]
+    _say(f"{label}: " + " ".join(f"{n}={e:.2e}" for n, e in zip(names, errs)))
+    tol = GATE_TOL[dt]
+    assert all(e <= tol for e in errs), errs
+    # the saved state is a copy of inputs: exact
+    assert np.array_equal(to64(out[5]), ref[5])
+
+
+@pytest.mark.parametrize("lens,H,dk,dv,dt,state", [
+    ([37, 0, 5, 2, 81, 16], 3, 128, 128, "bf16", True),
+    ([37, 0, 5, 2, 81, 16], 3, 128, 128, "bf16", False),
+    ([40, 40], 2, 64, 32, "f32", True),
+    ([17, 1, 30], 2, 16, 48, "f32", False),
+    ([3, 50], 4, 128, 64, "f32", True),
+])
+def test_frontend_small(oracle_mod, lens, H, dk, dv, dt, state):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs
+    f = inputs.make_frontend_inputs(lens, H, dk, dv, dt, seed=81 + dk + len(lens),
+                                    with_state=state)
+    out = _front_gpu(f, dev)
+    _check_front(out, _front_oracle(oracle_mod, f), dt, f"frontend {lens} {dk}x{dv} {dt}")
+
+
+def test_frontend_decode_in_place(oracle_mod):
+    """Decode mode: one token per sequence, convolution state updated in place."""
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_frontend
+    f = inputs.make_frontend_inputs([1] * 64, 96, 128, 128, "bf16", seed=91, with_state=True)
+    ref = _front_oracle(oracle_mod, f)
+    d = f.to(dev)
+    st = d.conv_in.clone()
+    out = kda_frontend(d.x_q, d.x_k, d.x_v, d.x_z, d.x_b, d.w_q, d.w_k, d.w_v, d.z_bias, d.A,
+                       cu_seqlens=d.cu_seqlens, conv_in=st, conv_out=st)
+    torch.cuda.synchronize()
+    _check_front(out, ref, "bf16", "frontend decode N=64 H=96")
+
+
+def test_frontend_resume_is_bitwise():
+    """Two calls with the state carried between them equal one call, bit for bit."""
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_frontend
+    f = inputs.make_frontend_inputs([300], 4, 128, 128, "bf16", seed=92).to(dev)
+    ws = (f.w_q, f.w_k, f.w_v, f.z_bias, f.A)
+    full = kda_frontend(f.x_q, f.x_k, f.x_v, f.x_z, f.x_b, *ws, output_conv_state=True)
+    a = 131
+    p1 = kda_frontend(f.x_q[:a], f.x_k[:a], f.x_v[:a], f.x_z[:a], f.x_b[:a], *ws,
+                      output_conv_state=True)
+    p2 = kda_frontend(f.x_q[a:], f.x_k[a:], f.x_v[a:], f.x_z[a:], f.x_b[a:], *ws,
+                      conv_in=p1[5], output_conv_state=True)
+    torch.cuda.synchronize()
+    for i in range(5):
+        assert torch.equal(torch.cat([p1[i], p2[i]]), full[i])
+    assert torch.equal(p2[5], full[5])
+
+
+def test_frontend_T4096_H96(oracle_mod):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs
+    f = inputs.make_frontend_inputs([4096], 96, 128, 128, "bf16", seed=93)
+    out = _front_gpu(f, dev)
+    _check_front(out, _front_oracle(oracle_mod, f), "bf16", "frontend T=4096 H=96")
