@@ -5,7 +5,14 @@
 Prints ONE JSON line.  `value` is prefill throughput in tokens/s on the one-layer K3 KDA prefill
 (B=1, T=4096, H=96, dk=dv=128, bf16 inputs, float32 state, 16-token tiles), inputs resident in HBM
 before the timed region.  A `decode` object reports the batched single-token decode step
-(256 sequences, H=96, float32 states read and written in place) the same way.
+(256 sequences, H=96, float32 states read and written in place) the same way, and a `snapshots`
+object the prefill that also saves the state every 64 tokens (kda_chunk_fwd_snapshots; 64 KiB per
+head and snapshot, the stride at which saved states cost as much as the per-token cache they
+replace).  An `output_gate` object times the output stage (per-head RMSNorm times a sigmoid
+gate; 3 x 256 B per (token, head) in bf16) on the same [4096, 96, 128] shape, and
+`decode.gated` the decode step with that stage fused.  A `frontend` object times the input stage
+(short convolution, Swish, L2 norm, sigmoid beta, bounded log-decay: reads 3 dk + dv values and
+beta's logit, writes as many per (token, head)) on the same token and head count.
 
 Roofline: algorithmic bytes per launch divided by the kernel's average duration, measured with
 HIP events recorded on the stream the kernels are launched on, against MI355X's 8 TB/s HBM.
@@ -96,7 +103,9 @@ def traffic_pass(dev):
     """A plain copy of known size (y = x * 1 over 1 GiB of float32), then 3 launches of the
     prefill and the decode kernels on their benchmark workloads."""
     import torch
-    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd, kda_decode_step
+    from linear_attention_recurrence_08_amd import (inputs, kda_chunk_fwd, kda_chunk_fwd_snapshots,
+                                                    kda_decode_step, kda_decode_step_gated,
+                                                    kda_frontend, kda_output_gate)
     x = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
     y = torch.empty_like(x)
     torch.mul(x, 1.0, out=y)
@@ -111,21 +120,48 @@ def traffic_pass(dev):
     qd, kd, vd, gd, bd, S = (t.to(dev) for t in (d.q, d.k, d.v, d.g, d.beta, d.h0))
     for _ in range(3):
         kda_decode_step(qd, kd, vd, gd, bd, S)
+    _, dz, dw = (t.to(dev) for t in inputs.make_output_gate_inputs(256, 96, 128, "bf16", 62))
+    for _ in range(3):
+        kda_decode_step_gated(qd, kd, vd, gd, bd, S, dz, dw, 1e-6)
+    torch.cuda.synchronize()
+    del qd, kd, vd, gd, bd, S, dz, dw
+    og, gz, gw = (t.to(dev) for t in inputs.make_output_gate_inputs(4096, 96, 128, "bf16", 61))
+    for _ in range(3):
+        kda_output_gate(og, gz, gw, 1e-6)
+    torch.cuda.synchronize()
+    del og, gz, gw
+    fr = inputs.make_frontend_inputs([4096], 96, 128, 128, "bf16", seed=93).to(dev)
+    for _ in range(3):
+        kda_frontend(fr.x_q, fr.x_k, fr.x_v, fr.x_z, fr.x_b, fr.w_q, fr.w_k, fr.w_v, fr.z_bias,
+                     fr.A, cu_seqlens=fr.cu_seqlens, output_conv_state=True)
     torch.cuda.synchronize()
     print("traffic pass done", file=sys.stderr)
 
 
 SUMMARY_KERNELS = {
-    # kernel name fragment -> (summary tag, workload, algorithmic bytes per launch)
+    # kernel name fragment (as rocprofv3 records it) -> (summary tag, workload)
     "kda_prefill_mfma_kernel": ("kda_chunk_fwd_prefill_T4096_H96_d128_bf16",
-                                "prefill_T4096_H96_d128_bf16", None),
-    "kda_decode_d128_kernel": ("kda_decode_decode_N256_H96_d128_bf16",
-                               "decode_N256_H96_d128_bf16", None),
+                                "prefill_T4096_H96_d128_bf16"),
+    "kda_decode_d128_kernel<unsigned short, 2, false>": ("kda_decode_decode_N256_H96_d128_bf16",
+                                                         "decode_N256_H96_d128_bf16"),
+    "kda_decode_d128_kernel<unsigned short, 2, true>": (
+        "kda_decode_step_gated_decode_N256_H96_d128_bf16", "decode_gated_N256_H96_d128_bf16"),
+    "kda_output_gate_kernel<unsigned short>": ("kda_output_gate_T4096_H96_d128_bf16",
+                                               "output_gate_T4096_H96_d128_bf16"),
+    "kda_frontend_kernel<unsigned short>": ("kda_frontend_T4096_H96_d128_bf16",
+                                            "frontend_T4096_H96_d128_bf16"),
 }
 
 
 def _algorithmic_bytes(workload):
     from linear_attention_recurrence_08_amd import inputs
+    tok_head = 4096 * 96
+    if workload == "decode_gated_N256_H96_d128_bf16":
+        return 256 * 96 * (2 * 128 * 128 * 4 + (3 * 128 + 2 * 128) * 2 + 2 + 2 * 128 * 2) + 512
+    if workload == "output_gate_T4096_H96_d128_bf16":
+        return 3 * tok_head * 128 * 2 + 128 * 4
+    if workload == "frontend_T4096_H96_d128_bf16":
+        return 2 * tok_head * ((3 * 128 + 128) * 2 + 2)
     w = inputs.WORKLOADS[workload]
     if w["kind"] == "decode":
         return w["N"] * w["H"] * (2 * w["dk"] * w["dv"] * 4 + (3 * w["dk"] + 2 * w["dv"]) * 2 + 2)
@@ -147,7 +183,7 @@ def summarize(dirs, command):
     for d in dirs:
         for f in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
-                for frag, (tag, wl, _) in SUMMARY_KERNELS.items():
+                for frag, (tag, wl) in SUMMARY_KERNELS.items():
                     if frag in r["Name"]:
                         path = os.path.join(out_dir, f"{tag}_kernel_trace.md")
                         with open(path, "w") as fo:
@@ -166,7 +202,7 @@ def summarize(dirs, command):
                 key = None
                 if "elementwise" in name or "vectorized" in name:
                     key = "copy"
-                for frag, (tag, _, _) in SUMMARY_KERNELS.items():
+                for frag, (tag, _) in SUMMARY_KERNELS.items():
                     if frag in name:
                         key = tag
                 if key is None:
@@ -179,7 +215,7 @@ def summarize(dirs, command):
             vals = counters.get(("copy", cn))
             if vals:
                 cal[cn] = max(vals) * 1024.0 / CALIB_BYTES   # counter bytes per true byte
-        for frag, (tag, wl, _) in SUMMARY_KERNELS.items():
+        for frag, (tag, wl) in SUMMARY_KERNELS.items():
             f_vals = counters.get((tag, "FETCH_SIZE"))
             w_vals = counters.get((tag, "WRITE_SIZE"))
             if not f_vals or not w_vals or "FETCH_SIZE" not in cal or "WRITE_SIZE" not in cal:
@@ -231,6 +267,10 @@ def main():
                     choices=PREFILL_WORKLOADS)
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--snapshot-stride", type=int, default=64)
+    ap.add_argument("--no-snapshots", action="store_true")
+    ap.add_argument("--no-output-gate", action="store_true")
+    ap.add_argument("--no-frontend", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="run a 1 GiB calibration copy and 3 launches of each kernel (for "
@@ -252,7 +292,9 @@ def main():
     import numpy as np
     import torch
 
-    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd, kda_decode_step
+    from linear_attention_recurrence_08_amd import (inputs, kda_chunk_fwd, kda_chunk_fwd_snapshots,
+                                                    kda_decode_step, kda_decode_step_gated,
+                                                    kda_frontend, kda_output_gate)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -318,6 +360,85 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
 
+    # ---------------- prefill with state snapshots ----------------
+    if not args.no_snapshots:
+        stride = args.snapshot_stride
+        _, _, snaps, offs = kda_chunk_fwd_snapshots(*args_views, stride, h0=xd.h0,
+                                                    cu_seqlens=xd.cu_seqlens, o=o, hT=hT)
+        print(f"[bench] prefill with snapshots every {stride} tokens: {snaps.shape[0]} saved",
+              file=sys.stderr, flush=True)
+
+        def prefill_snap():
+            kda_chunk_fwd_snapshots(*args_views, stride, h0=xd.h0, cu_seqlens=xd.cu_seqlens,
+                                    snap_offsets=offs, o=o, hT=hT, snaps=snaps)
+
+        sms, _ = time_launches(prefill_snap, args.steps, args.warmup, stream)
+        sbytes = nbytes + snaps.numel() * 4
+        result["snapshots"] = {
+            "stride": stride, "saved": int(snaps.shape[0]), "ms_per_step": round(sms, 5),
+            "value": round(tokens / (sms * 1e-3), 1), "unit": "tokens/s",
+            "overhead_vs_prefill": round(sms / ms - 1.0, 4),
+            "roofline": {"bound": "hbm", "achieved": round(sbytes / (sms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": sbytes},
+        }
+        del snaps, offs
+        torch.cuda.empty_cache()
+
+    # ---------------- output stage on the layer's output shape ----------------
+    if not args.no_output_gate:
+        og, gz, gw = (t.to(dev) for t in inputs.make_output_gate_inputs(
+            x.total_tokens, x.H, x.dv, x.dtype, seed=61))
+        gy = torch.empty_like(og)
+
+        def out_gate():
+            kda_output_gate(og, gz, gw, 1e-6, y=gy)
+
+        gms, _ = time_launches(out_gate, args.steps, args.warmup, stream)
+        gbytes = 3 * og.numel() * og.element_size() + gw.numel() * 4
+        ggbs = gbytes / (gms * 1e-3) / 1e9
+        result["output_gate"] = {
+            "shape": list(og.shape), "ms_per_step": round(gms, 5),
+            "value": round(x.total_tokens / (gms * 1e-3), 1), "unit": "tokens/s",
+            "roofline": {"bound": "hbm", "achieved": round(ggbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(ggbs / HBM_PEAK_GBS, 4),
+                         "traffic": recorded_traffic("kda_output_gate_T4096_H96_d128_bf16")
+                         if (x.total_tokens, x.H, x.dv, x.dtype) == (4096, 96, 128, "bf16")
+                         else None,
+                         "kernel": "kda_output_gate", "algorithmic_bytes_per_launch": gbytes},
+        }
+        del og, gz, gw, gy
+        torch.cuda.empty_cache()
+
+    # ---------------- input stage on the same token and head count ----------------
+    if not args.no_frontend:
+        fr = inputs.make_frontend_inputs([e - s for s, e in x.seq_bounds()], x.H, x.dk, x.dv,
+                                         x.dtype, seed=93).to(dev)
+        fst = torch.empty((x.num_seqs, 3, x.H * (2 * x.dk + x.dv)), dtype=fr.x_q.dtype,
+                          device=dev)
+
+        def front():
+            kda_frontend(fr.x_q, fr.x_k, fr.x_v, fr.x_z, fr.x_b, fr.w_q, fr.w_k, fr.w_v,
+                         fr.z_bias, fr.A, cu_seqlens=fr.cu_seqlens, conv_out=fst)
+
+        fms, _ = time_launches(front, args.steps, args.warmup, stream)
+        es = fr.x_q.element_size()
+        fbytes = 2 * x.total_tokens * x.H * ((3 * x.dk + x.dv) * es + es)
+        fgbs = fbytes / (fms * 1e-3) / 1e9
+        result["frontend"] = {
+            "ms_per_step": round(fms, 5), "value": round(x.total_tokens / (fms * 1e-3), 1),
+            "unit": "tokens/s",
+            "roofline": {"bound": "hbm", "achieved": round(fgbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(fgbs / HBM_PEAK_GBS, 4),
+                         "traffic": recorded_traffic("kda_frontend_T4096_H96_d128_bf16")
+                         if (x.total_tokens, x.H, x.dv, x.dtype) == (4096, 96, 128, "bf16")
+                         else None,
+                         "kernel": "kda_frontend", "algorithmic_bytes_per_launch": fbytes},
+        }
+        del fr, fst
+        torch.cuda.empty_cache()
+
     # ---------------- decode ----------------
     if not args.no_decode:
         d = inputs.make_workload(DECODE_WORKLOAD)
@@ -343,6 +464,29 @@ def main():
                          "traffic": recorded_traffic("kda_decode_" + DECODE_WORKLOAD),
                          "kernel": "kda_decode_d128", "algorithmic_bytes_per_launch": dbytes},
         }
+        if not args.no_output_gate:
+            _, dz, dw = (t.to(dev) for t in inputs.make_output_gate_inputs(256, 96, 128, "bf16",
+                                                                            seed=62))
+            dy = torch.empty_like(od)
+
+            def decode_gated():
+                kda_decode_step_gated(qd, kd, vd, gd, bd, S, dz, dw, 1e-6, o=od, y=dy)
+
+            gdms, _ = time_launches(decode_gated, ksteps, args.warmup, stream)
+            gdbytes = dbytes + 256 * 96 * 128 * 2 * 2 + 128 * 4   # + gate in, y out, gain
+            result["decode"]["gated"] = {
+                "ms_per_step": round(gdms, 5), "value": round(256 / (gdms * 1e-3), 1),
+                "unit": "tokens/s", "overhead_vs_decode": round(gdms / dms - 1.0, 4),
+                "roofline": {"bound": "hbm",
+                             "achieved": round(gdbytes / (gdms * 1e-3) / 1e9, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(gdbytes / (gdms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "traffic": recorded_traffic(
+                                 "kda_decode_step_gated_decode_N256_H96_d128_bf16"),
+                             "kernel": "kda_decode_d128 (gated)",
+                             "algorithmic_bytes_per_launch": gdbytes},
+            }
+            del dz, dw, dy
         del qd, kd, vd, gd, bd, S, od
         torch.cuda.empty_cache()
 

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void kda_decode_d128_kernel(DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float w = a.weight ? a.weight[4 * cg + j] : 1.f;
-                yv[j] = out[j] * r * w / (1.f + __expf(-gz[j]));
+                yv[j] = out[j] * r * w * __builtin_amdgcn_rcpf(1.f + __expf(-gz[j]));
             }
             if (rg == 0) store4<Tin>(static_cast<Tin*>(a.y) + unit * D + 4 * cg, yv);
         }

@@ -12,10 +12,12 @@
 // with swish(y) = y sigmoid(y) and l2(y) = y / sqrt(sum_c y_c^2 + eps) over the head's dk values.
 //
 // The stage is HBM-bound (reads 3 dk + dv values and writes as many per (token, head)).  A group
-// of 16 lanes owns a run of 16 consecutive packed tokens of one head; lane j holds channels
-// 8j .. 8j+7 of q, k, v and z, keeps the previous three inputs of q, k and v in registers (a
-// sliding window, so every input is read once) and restarts the window at each sequence start
-// inside the run.  The L2 norms are 16-lane xor reductions.  A second kernel writes the saved
+// of 16 lanes owns a run of 16 consecutive packed tokens of one head and one tensor (q, k, v, or
+// z with beta); lane j holds channels 8j .. 8j+7, keeps the previous three inputs in registers (a
+// sliding window, so every input is read once), requests all of its run's rows before computing
+// the first (16 bytes per token per lane in flight), and restarts the window at each sequence
+// start inside the run.  The L2 norms are
+// 16-lane xor reductions.  A second kernel writes the saved
 // convolution state (the last three inputs of every sequence) after the first has read it, so the
 // state may be updated in place.
 #include "kda_internal.h"
@@ -23,10 +25,12 @@
 namespace kda {
 namespace {
 
-constexpr int RUN = 16;          // tokens per lane group
+// tokens per lane group: all of a run's rows are requested before the first is used
+template <typename Tin> constexpr int run_of() { return sizeof(Tin) == 2 ? 16 : 8; }
 constexpr int GROUPS = 16;       // lane groups per 256-thread block
 
-__device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
+// logistic sigmoid with the hardware reciprocal (v_rcp_f32, 1 ulp)
+__device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 // index of the sequence holding packed token t: the last n with cu[n] <= t (skips empty ones)
 __device__ __forceinline__ int64_t seq_of(const FrontArgs& a, int64_t t) {
@@ -45,142 +49,122 @@ __device__ __forceinline__ int64_t seq_end(const FrontArgs& a, int64_t n) {
     return a.cu ? (int64_t)a.cu[n + 1] : (n + 1) * a.T;
 }
 
-template <typename Tin>
-struct Window {                  // inputs at tokens t-3, t-2, t-1 for this lane's 8 channels
-    float w[3][8];
-};
-
+// One 16-lane group: a run of RUN (16 for bf16, 8 for float32) packed tokens of head h for one tensor (blockIdx.y: 0 = q,
+// 1 = k, 2 = v with the convolution; 3 = z -> g and beta).  Lane j holds channels 8j .. 8j+7 and,
+// for the convolved tensors, their four taps and the previous three inputs.
 template <typename Tin>
 __global__ __launch_bounds__(256) void kda_frontend_kernel(FrontArgs a) {
+    constexpr int RUN = run_of<Tin>();
     const int tid = threadIdx.x;
     const int j = tid & 15;
+    const int kind = blockIdx.y;                       // uniform per block
     const int64_t unit = (int64_t)blockIdx.x * GROUPS + (tid >> 4);
     const int64_t nruns = (a.Ttot + RUN - 1) / RUN;
     if (unit >= nruns * a.H) return;     // whole 16-lane groups leave together
     const int64_t h = unit % a.H, run = unit / a.H;
     const int64_t t0 = run * RUN, t1 = min(t0 + RUN, a.Ttot);
-    const int64_t H = a.H, dk = a.dk, dv = a.dv;
-    const bool onk = 8 * j < dk, onv = 8 * j < dv;
-    const int64_t Cq = H * dk, C = H * (2 * dk + dv);
-    const int64_t cq = h * dk + 8 * j, cv = h * dv + 8 * j;     // this lane's first channel
+    const int64_t H = a.H, dk = a.dk, dv = a.dv, Cq = H * dk, C = H * (2 * dk + dv);
+    const int64_t d = kind == 2 ? dv : dk;
+    const bool on = 8 * j < d;
+    const Tin* x = static_cast<const Tin*>(kind == 0 ? a.xq : kind == 1 ? a.xk :
+                                           kind == 2 ? a.xv : a.xz);
+    Tin* out = static_cast<Tin*>(kind == 0 ? a.q : kind == 1 ? a.k : kind == 2 ? a.v : a.g);
+    const int64_t c0 = h * d + 8 * j;                  // first channel within the tensor
+    const int64_t scol = (kind == 0 ? 0 : kind == 1 ? Cq : 2 * Cq) + c0;   // state column
 
-    // taps of this lane's channels
-    float wq[8][4], wk[8][4], wv[8][4], zb[8];
+    if (kind == 3) {
+        // g = g_min sigmoid(A_h (z + bias)) and beta = sigmoid(x_b): elementwise
+        float zb[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < 8; ++c) zb[c] = on ? a.zbias[c0 + c] : 0.f;
+        const float Ah = a.A[h];
+        Raw8<Tin> rows[RUN];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wq[c][i] = onk ? a.wq[(cq + c) * 4 + i] : 0.f;
-            wk[c][i] = onk ? a.wk[(cq + c) * 4 + i] : 0.f;
-            wv[c][i] = onv ? a.wv[(cv + c) * 4 + i] : 0.f;
+        for (int i = 0; i < RUN; ++i) {
+            if (on && t0 + i < t1) rows[i].load(x + ((t0 + i) * H) * d + c0);
+            else rows[i].zero();
         }
-        zb[c] = onk ? a.zbias[cq + c] : 0.f;
+#pragma unroll
+        for (int i = 0; i < RUN; ++i) {
+            const int64_t t = t0 + i;
+            if (t >= t1) break;
+            float z[8], g8[8];
+            rows[i].unpack(z);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) g8[c] = a.g_min * sigm(Ah * (z[c] + zb[c]));
+            if (on) Row8<Tin>::store(out + (t * H) * d + c0, g8);
+            if (j == 0) {
+                const float bl = io<Tin>::load(static_cast<const Tin*>(a.xb) + t * H + h);
+                io<Tin>::store(static_cast<Tin*>(a.beta) + t * H + h, sigm(bl));
+            }
+        }
+        return;
     }
-    const float Ah = a.A[h];
-    const Tin* xq = static_cast<const Tin*>(a.xq);
-    const Tin* xk = static_cast<const Tin*>(a.xk);
-    const Tin* xv = static_cast<const Tin*>(a.xv);
-    const Tin* xz = static_cast<const Tin*>(a.xz);
-    const Tin* cin = static_cast<const Tin*>(a.conv_in);
 
-    Window<Tin> Wq, Wk, Wv;
+    const float* wsrc = kind == 0 ? a.wq : kind == 1 ? a.wk : a.wv;
+    float w[8][4];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[c][i] = on ? wsrc[(c0 + c) * 4 + i] : 0.f;
+    const Tin* cin = static_cast<const Tin*>(a.conv_in);
+    const bool norm = kind < 2;
+
+    float win[3][8];                    // inputs at t-3, t-2, t-1
     int64_t n = seq_of(a, t0);
     int64_t bos = seq_start(a, n), eos = seq_end(a, n);
-    // value at position p (from -3) of sequence n's input for this lane's channels
-    auto fill = [&](int slot, int64_t p) {
-        float tq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, tk[8], tv[8];
+    // the window for token t of sequence n: positions t-bos-3 .. t-bos-1, negative positions from
+    // the saved state (or zeros)
+    auto restart = [&](int64_t t) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) { tk[c] = 0.f; tv[c] = 0.f; }
-        if (p >= 0) {
-            const int64_t t = bos + p;
-            if (onk) {
-                Row8<Tin>::load(xq + (t * H + h) * dk + 8 * j, tq);
-                Row8<Tin>::load(xk + (t * H + h) * dk + 8 * j, tk);
+        for (int s = 0; s < 3; ++s) {
+            const int64_t p = t - bos - 3 + s;
+            float v8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (on) {
+                if (p >= 0) Row8<Tin>::load(x + ((bos + p) * H) * d + c0, v8);
+                else if (cin) Row8<Tin>::load(cin + (n * 3 + (3 + p)) * C + scol, v8);
             }
-            if (onv) Row8<Tin>::load(xv + (t * H + h) * dv + 8 * j, tv);
-        } else if (cin) {
-            const Tin* row = cin + (n * 3 + (3 + p)) * C;
-            if (onk) {
-                Row8<Tin>::load(row + cq, tq);
-                Row8<Tin>::load(row + Cq + cq, tk);
-            }
-            if (onv) Row8<Tin>::load(row + 2 * Cq + cv, tv);
-        }
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            Wq.w[slot][c] = tq[c];
-            Wk.w[slot][c] = tk[c];
-            Wv.w[slot][c] = tv[c];
+            for (int c = 0; c < 8; ++c) win[s][c] = v8[c];
         }
     };
-    auto restart = [&](int64_t t) {      // window for token t of sequence n
-        const int64_t p = t - bos;
-        fill(0, p - 3);
-        fill(1, p - 2);
-        fill(2, p - 1);
-    };
+    Raw8<Tin> rows[RUN];
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) {
+        if (on && t0 + i < t1) rows[i].load(x + ((t0 + i) * H) * d + c0);
+        else rows[i].zero();
+    }
     restart(t0);
-
-    Tin* oq = static_cast<Tin*>(a.q);
-    Tin* ok = static_cast<Tin*>(a.k);
-    Tin* ov = static_cast<Tin*>(a.v);
-    Tin* og = static_cast<Tin*>(a.g);
-    for (int64_t t = t0; t < t1; ++t) {
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) {
+        const int64_t t = t0 + i;
+        if (t >= t1) break;
         if (t >= eos) {                  // the run crosses into a later sequence
             do { ++n; } while (seq_end(a, n) <= t);
             bos = seq_start(a, n);
             eos = seq_end(a, n);
             restart(t);
         }
-        float xq8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, xk8[8], xv8[8], xz8[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) { xk8[c] = 0.f; xv8[c] = 0.f; xz8[c] = 0.f; }
-        const int64_t rk = (t * H + h) * dk + 8 * j, rv = (t * H + h) * dv + 8 * j;
-        if (onk) {
-            Row8<Tin>::load(xq + rk, xq8);
-            Row8<Tin>::load(xk + rk, xk8);
-            Row8<Tin>::load(xz + rk, xz8);
-        }
-        if (onv) Row8<Tin>::load(xv + rv, xv8);
-        float q8[8], k8[8], v8[8], g8[8], sq = 0.f, sk = 0.f;
+        float xc[8], y[8], ss = 0.f;
+        rows[i].unpack(xc);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            float yq = wq[c][3] * xq8[c], yk = wk[c][3] * xk8[c], yv = wv[c][3] * xv8[c];
+            const float u = w[c][0] * win[0][c] + w[c][1] * win[1][c] + w[c][2] * win[2][c] +
+                            w[c][3] * xc[c];
+            y[c] = u * sigm(u);
+            ss += y[c] * y[c];
+            win[0][c] = win[1][c];
+            win[1][c] = win[2][c];
+            win[2][c] = xc[c];
+        }
+        if (norm) {
 #pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                yq += wq[c][i] * Wq.w[i][c];
-                yk += wk[c][i] * Wk.w[i][c];
-                yv += wv[c][i] * Wv.w[i][c];
-            }
-            q8[c] = yq * sigm(yq);
-            k8[c] = yk * sigm(yk);
-            v8[c] = yv * sigm(yv);
-            g8[c] = a.g_min * sigm(Ah * (xz8[c] + zb[c]));
-            sq += q8[c] * q8[c];
-            sk += k8[c] * k8[c];
-            // slide the window
-            Wq.w[0][c] = Wq.w[1][c]; Wq.w[1][c] = Wq.w[2][c]; Wq.w[2][c] = xq8[c];
-            Wk.w[0][c] = Wk.w[1][c]; Wk.w[1][c] = Wk.w[2][c]; Wk.w[2][c] = xk8[c];
-            Wv.w[0][c] = Wv.w[1][c]; Wv.w[1][c] = Wv.w[2][c]; Wv.w[2][c] = xv8[c];
-        }
+            for (int m = 8; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 16);
+            const float r = rsqrtf(ss + a.eps);
 #pragma unroll
-        for (int m = 8; m >= 1; m >>= 1) {
-            sq += __shfl_xor(sq, m, 16);
-            sk += __shfl_xor(sk, m, 16);
+            for (int c = 0; c < 8; ++c) y[c] *= r;
         }
-        const float rq = rsqrtf(sq + a.eps), rkn = rsqrtf(sk + a.eps);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) { q8[c] *= rq; k8[c] *= rkn; }
-        if (onk) {
-            Row8<Tin>::store(oq + rk, q8);
-            Row8<Tin>::store(ok + rk, k8);
-            Row8<Tin>::store(og + rk, g8);
-        }
-        if (onv) Row8<Tin>::store(ov + rv, v8);
-        if (j == 0) {
-            const float b = io<Tin>::load(static_cast<const Tin*>(a.xb) + t * H + h);
-            io<Tin>::store(static_cast<Tin*>(a.beta) + t * H + h, sigm(b));
-        }
+        if (on) Row8<Tin>::store(out + (t * H) * d + c0, y);
     }
 }
 
@@ -217,8 +201,9 @@ __global__ __launch_bounds__(256) void kda_frontend_state_kernel(FrontArgs a) {
 
 hipError_t launch_frontend(const FrontArgs& a, hipStream_t s) {
     if (a.Ttot > 0) {
-        const int64_t units = (a.Ttot + RUN - 1) / RUN * a.H;
-        const dim3 grid((unsigned)((units + GROUPS - 1) / GROUPS));
+        const int run = a.dtype == 0 ? run_of<bf16_t>() : run_of<float>();
+        const int64_t units = (a.Ttot + run - 1) / run * a.H;
+        const dim3 grid((unsigned)((units + GROUPS - 1) / GROUPS), 4);
         if (a.dtype == 0) hipLaunchKernelGGL(kda_frontend_kernel<bf16_t>, grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL(kda_frontend_kernel<float>, grid, dim3(256), 0, s, a);
         const hipError_t e = hipGetLastError();

@@ -139,6 +139,34 @@ template <> struct Row8<bf16_t> {
         __builtin_nontemporal_store(u, reinterpret_cast<u32v4*>(p));
     }
 };
+// The same eight elements kept in their stored form (fewer registers while loads are in flight).
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+    u32v4 u;
+    __device__ __forceinline__ void load(const bf16_t* p) {
+        u = __builtin_nontemporal_load(reinterpret_cast<const u32v4*>(p));
+    }
+    __device__ __forceinline__ void zero() { u = (u32v4){0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ void unpack(float x[8]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(u[i] << 16);
+            x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    }
+};
+template <> struct Raw8<float> {
+    f32v4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = __builtin_nontemporal_load(reinterpret_cast<const f32v4*>(p));
+        b = __builtin_nontemporal_load(reinterpret_cast<const f32v4*>(p) + 1);
+    }
+    __device__ __forceinline__ void zero() { a = (f32v4){0.f, 0.f, 0.f, 0.f}; b = a; }
+    __device__ __forceinline__ void unpack(float x[8]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+    }
+};
 template <> struct Row8<float> {
     static __device__ __forceinline__ void load(const float* p, float x[8]) {
         const f32v4 a = __builtin_nontemporal_load(reinterpret_cast<const f32v4*>(p));

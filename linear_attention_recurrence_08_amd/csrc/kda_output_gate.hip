@@ -10,40 +10,56 @@
 // of 16 lanes owns one row: lane j holds elements 8j .. 8j+7 (one 16-byte access for bf16, two
 // for float32), the sum of squares is reduced across the group with four xor shuffles, and the
 // row is written back once.  Lanes past dv / 8 hold nothing (dv is a multiple of 16, <= 128).
+// Each group takes eight rows and issues all their loads before the arithmetic, so every lane
+// keeps 256 bytes (bf16) in flight.
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
 
-constexpr int ROWS_PER_BLOCK = 16;   // 256 threads, 16 lanes per row
+constexpr int GROUPS = 16;       // 16-lane row groups per 256-thread block
+constexpr int RPG = 8;           // rows per group: all their loads are issued before any math
 
 template <typename Tin>
 __global__ __launch_bounds__(256) void kda_output_gate_kernel(GateArgs a) {
     const int tid = threadIdx.x;
     const int j = tid & 15;                                    // lane within the row group
-    const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (tid >> 4);
-    const bool active = row < a.rows && 8 * j < a.dv;
-    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const int64_t off = row * a.dv + 8 * j;
-    if (active) {
-        Row8<Tin>::load(static_cast<const Tin*>(a.o) + off, x);
-        Row8<Tin>::load(static_cast<const Tin*>(a.gate) + off, z);
-    }
-    float ss = 0.f;
+    const int64_t row0 = ((int64_t)blockIdx.x * GROUPS + (tid >> 4)) * RPG;
+    const bool lane_on = 8 * j < a.dv;
+    float w[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+    for (int i = 0; i < 8; ++i) w[i] = (a.weight && lane_on) ? a.weight[8 * j + i] : 1.f;
+    Raw8<Tin> xr[RPG], zr[RPG];
 #pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 16);
-    const float r = rsqrtf(ss / (float)a.dv + a.eps);
-    if (active) {
-        float y[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float w = a.weight ? a.weight[8 * j + i] : 1.f;
-            y[i] = x[i] * r * w / (1.f + __expf(-z[i]));
+    for (int r = 0; r < RPG; ++r) {
+        const int64_t row = row0 + r;
+        if (row < a.rows && lane_on) {
+            xr[r].load(static_cast<const Tin*>(a.o) + row * a.dv + 8 * j);
+            zr[r].load(static_cast<const Tin*>(a.gate) + row * a.dv + 8 * j);
+        } else {
+            xr[r].zero();
+            zr[r].zero();
         }
-        Row8<Tin>::store(static_cast<Tin*>(a.y) + off, y);
+    }
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+        float x[8], z[8];
+        xr[r].unpack(x);
+        zr[r].unpack(z);
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+#pragma unroll
+        for (int m = 8; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 16);
+        const float rn = rsqrtf(ss / (float)a.dv + a.eps);
+        const int64_t row = row0 + r;
+        if (row < a.rows && lane_on) {
+            float y[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                y[i] = x[i] * rn * w[i] * __builtin_amdgcn_rcpf(1.f + __expf(-z[i]));
+            Row8<Tin>::store(static_cast<Tin*>(a.y) + row * a.dv + 8 * j, y);
+        }
     }
 }
 
@@ -51,7 +67,7 @@ __global__ __launch_bounds__(256) void kda_output_gate_kernel(GateArgs a) {
 
 hipError_t launch_output_gate(const GateArgs& a, hipStream_t s) {
     if (a.rows <= 0) return hipSuccess;
-    const int64_t grid = (a.rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+    const int64_t grid = (a.rows + GROUPS * RPG - 1) / (GROUPS * RPG);
     if (a.dtype == 0)
         hipLaunchKernelGGL(kda_output_gate_kernel<bf16_t>, dim3((unsigned)grid), dim3(256), 0, s,
                            a);
