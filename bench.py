@@ -271,6 +271,7 @@ def main():
     ap.add_argument("--no-snapshots", action="store_true")
     ap.add_argument("--no-output-gate", action="store_true")
     ap.add_argument("--no-frontend", action="store_true")
+    ap.add_argument("--no-chunk64", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="run a 1 GiB calibration copy and 3 launches of each kernel (for "
@@ -359,6 +360,37 @@ def main():
         "roofline": roofline,
         "wall_s_timed": round(wall, 4),
     }
+
+    # ---------------- 64-token chunks (float32 vector path) beside 16-token tiles ----------------
+    if not args.no_chunk64:
+        from linear_attention_recurrence_08_amd import kda_chunk_fwd_chunk64
+
+        o_c, hT_c = torch.empty_like(o), torch.empty_like(hT)   # leave the prefill's o intact
+
+        def prefill_c64():
+            kda_chunk_fwd_chunk64(*args_views, h0=xd.h0, cu_seqlens=xd.cu_seqlens, o=o_c, hT=hT_c)
+
+        def prefill_c16_general():
+            os.environ["KDA_FORCE_GENERAL"] = "1"
+            try:
+                kda_chunk_fwd(*args_views, h0=xd.h0, cu_seqlens=xd.cu_seqlens, o=o_c, hT=hT_c)
+            finally:
+                del os.environ["KDA_FORCE_GENERAL"]
+
+        csteps = max(3, args.steps // 10)
+        c64ms, _ = time_launches(prefill_c64, csteps, 1, stream)
+        c16ms, _ = time_launches(prefill_c16_general, csteps, 1, stream)
+        result["chunk64"] = {
+            "kernel": "kda_prefill_c64 (float32 vector ALUs)", "steps": csteps,
+            "ms_per_step": round(c64ms, 4), "value": round(tokens / (c64ms * 1e-3), 1),
+            "unit": "tokens/s",
+            "chunk16_general_ms_per_step": round(c16ms, 4),
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / (c64ms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(nbytes / (c64ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": nbytes},
+        }
+        del o_c, hT_c
 
     # ---------------- prefill with state snapshots ----------------
     if not args.no_snapshots:

@@ -101,6 +101,22 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
                   int B, int T, int H, int dk, int dv, int dtype, void* stream);
 
 /*
+ * kda_chunk_fwd_chunk64 -- kda_chunk_fwd computed with 64-token chunks made of four 16-token
+ * sub-tiles: the state is carried once per chunk, and the chunk's 64x64 triangular system is
+ * solved by blocks, the diagonal sub-tiles by forward substitution and the coupling between
+ * sub-tiles as separate off-diagonal products ("What's new in Kimi K3", section "KDA in one page":
+ * the per-token cost is quoted at chunk size 64; "Kimi K3's hybrid block, from first principles",
+ * section "From linear attention to the delta rule": the cumulative log-decay over 16 tokens
+ * stays within (-80, 0), so every exponent is kept within one sub-tile or made non-positive).
+ * Float32 arithmetic on the vector ALUs for every supported dtype and head size; same arguments,
+ * layouts, results (up to rounding) and errors as kda_chunk_fwd.
+ */
+int kda_chunk_fwd_chunk64(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, const float* h0, const int32_t* cu_seqlens,
+                          int num_seqs, void* o, float* hT,
+                          int B, int T, int H, int dk, int dv, int dtype, void* stream);
+
+/*
  * kda_chunk_fwd_snapshots -- kda_chunk_fwd that also saves the state at every multiple of
  * snap_stride tokens of each sequence, for prefix caching.  A KDA layer keeps one state that
  * summarises the whole prefix, so a cached prefix can be resumed only from a state saved at

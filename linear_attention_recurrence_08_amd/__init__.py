@@ -4,10 +4,12 @@ behind the C ABI in include/kda.h.
 
 The binding (kda.py) loads libkda.so built in-tree by build.py; it has no CPU fallback.
 """
-from .kda import (KDA_BF16, KDA_F32, KDAError, kda_chunk_fwd, kda_chunk_fwd_snapshots,
+from .kda import (KDA_BF16, KDA_F32, KDAError, kda_chunk_fwd, kda_chunk_fwd_chunk64,
+                  kda_chunk_fwd_snapshots,
                   kda_decode_step, kda_decode_step_gated, kda_frontend, kda_output_gate,
                   kda_status_string, load_library)
 
-__all__ = ["KDA_BF16", "KDA_F32", "KDAError", "kda_chunk_fwd", "kda_chunk_fwd_snapshots",
+__all__ = ["KDA_BF16", "KDA_F32", "KDAError", "kda_chunk_fwd", "kda_chunk_fwd_chunk64",
+           "kda_chunk_fwd_snapshots",
            "kda_decode_step", "kda_decode_step_gated", "kda_frontend", "kda_output_gate",
            "kda_status_string", "load_library"]

@@ -58,11 +58,12 @@ int check_gate_range(const void* g, int64_t count, int dtype, hipStream_t s) {
     return KDA_OK;
 }
 
-// Prefill with optional snapshots (snap_stride 0: none).
+// Prefill with optional snapshots (snap_stride 0: none); chunk64 selects the 64-token-chunk
+// kernel (no snapshots).
 int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
                    const float* h0, const int32_t* cu_seqlens, int num_seqs, void* o, float* hT,
                    float* snaps, const int32_t* snap_offsets, int snap_stride, int B, int T,
-                   int H, int dk, int dv, int dtype, void* stream) {
+                   int H, int dk, int dv, int dtype, void* stream, bool chunk64 = false) {
     if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
     if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
     if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
@@ -119,7 +120,9 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, c
     }
 
     hipError_t e;
-    if (dtype == KDA_BF16 && dk == 128 && dv == 128 && !std::getenv("KDA_FORCE_GENERAL"))
+    if (chunk64)
+        e = kda::launch_prefill_c64(a, s);
+    else if (dtype == KDA_BF16 && dk == 128 && dv == 128 && !std::getenv("KDA_FORCE_GENERAL"))
         e = kda::launch_prefill_mfma(a, s);
     else
         e = kda::launch_prefill_general(a, s);
@@ -154,6 +157,14 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
                   int B, int T, int H, int dk, int dv, int dtype, void* stream) {
     return chunk_fwd_impl(q, k, v, g, beta, h0, cu_seqlens, num_seqs, o, hT, nullptr, nullptr, 0,
                           B, T, H, dk, dv, dtype, stream);
+}
+
+int kda_chunk_fwd_chunk64(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, const float* h0, const int32_t* cu_seqlens,
+                          int num_seqs, void* o, float* hT,
+                          int B, int T, int H, int dk, int dv, int dtype, void* stream) {
+    return chunk_fwd_impl(q, k, v, g, beta, h0, cu_seqlens, num_seqs, o, hT, nullptr, nullptr, 0,
+                          B, T, H, dk, dv, dtype, stream, true);
 }
 
 int kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const void* g,

@@ -85,6 +85,7 @@ struct FrontArgs {
 // Each launcher returns hipSuccess or the launch error.
 hipError_t launch_prefill_general(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);   // bf16, dk = dv = 128
+hipError_t launch_prefill_c64(const PrefillArgs& a, hipStream_t s);    // 64-token chunks
 hipError_t launch_decode_d128(const DecodeArgs& a, hipStream_t s);     // dk = dv = 128
 hipError_t launch_output_gate(const GateArgs& a, hipStream_t s);      // 16-byte aligned rows
 hipError_t launch_frontend(const FrontArgs& a, hipStream_t s);        // 16-byte aligned rows

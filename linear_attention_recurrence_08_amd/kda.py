@@ -45,6 +45,9 @@ def load_library():
         lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
                                       i32, i32, i32, i32, i32, i32, vp]
         lib.kda_chunk_fwd.restype = i32
+        lib.kda_chunk_fwd_chunk64.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
+                                              i32, i32, i32, i32, i32, i32, vp]
+        lib.kda_chunk_fwd_chunk64.restype = i32
         lib.kda_chunk_fwd_snapshots.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                                 i32, i32, i32, i32, i32, i32, i32, vp]
         lib.kda_chunk_fwd_snapshots.restype = i32
@@ -157,6 +160,24 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         _ptr(o), _ptr(hT), B, T, H, dk, dv, _dtype_code(q), _stream(dev))
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd")
+    return o, hT
+
+
+def kda_chunk_fwd_chunk64(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                          beta: torch.Tensor, h0: Optional[torch.Tensor] = None,
+                          cu_seqlens: Optional[torch.Tensor] = None,
+                          output_final_state: bool = True, o: Optional[torch.Tensor] = None,
+                          hT: Optional[torch.Tensor] = None
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_chunk_fwd computed with 64-token chunks of four 16-token sub-tiles (one state carry per
+    chunk; float32 vector arithmetic).  Same arguments and results as kda_chunk_fwd."""
+    dev, B, T, H, dk, dv, N, o, hT = _prefill_args(q, k, v, g, beta, h0, cu_seqlens,
+                                                   output_final_state, o, hT)
+    st = load_library().kda_chunk_fwd_chunk64(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), N,
+        _ptr(o), _ptr(hT), B, T, H, dk, dv, _dtype_code(q), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd_chunk64")
     return o, hT
 
 

@@ -28,7 +28,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_snapshots",
+    assert _declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_chunk64",
+                                     "kda_chunk_fwd_snapshots",
                                      "kda_decode_step", "kda_decode_step_gated", "kda_frontend",
                                      "kda_output_gate", "kda_status_string", "kda_version"]
 

@@ -492,3 +492,60 @@ def test_frontend_T4096_H96(oracle_mod):
     f = inputs.make_frontend_inputs([4096], 96, 128, 128, "bf16", seed=93)
     out = _front_gpu(f, dev)
     _check_front(out, _front_oracle(oracle_mod, f), "bf16", "frontend T=4096 H=96")
+
+
+# ------------------------------------------------------------------------------------------------
+# 64-token chunks of four 16-token sub-tiles (one carry per chunk)
+# ------------------------------------------------------------------------------------------------
+C64_CASES = SMALL + [
+    ([300], 2, 128, 128, "bf16", 0.05, "sigmoid", False),          # several chunks, ragged tail
+    ([130, 64, 65, 1, 0, 255], 3, 128, 128, "bf16", 0.1, "sigmoid_shiftm1", True),
+    ([256], 2, 64, 64, "f32", 0.1, "sigmoid_shift1", False),       # exact chunk multiple
+    ([200], 2, 128, 128, "f32", 0.05, "bimodal", False),           # decays near e^-5 per token
+]
+
+
+@pytest.mark.parametrize("case", C64_CASES,
+                         ids=lambda c: f"{c[0]}-H{c[1]}-{c[2]}x{c[3]}-{c[4]}-{c[6]}")
+def test_chunk64_small(oracle_mod, case):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd_chunk64
+    lens, H, dk, dv, dt, h0s, gate, packed = case
+    x = inputs.make_inputs(lens, H, dk, dv, dt, seed=sum(lens) + dk + 7, gate=gate,
+                           h0_sigma=h0s, packed=packed)
+    xd = x.to(dev)
+    o, hT = kda_chunk_fwd_chunk64(*xd.call_views(), h0=xd.h0, cu_seqlens=xd.cu_seqlens)
+    torch.cuda.synchronize()
+    o = o.reshape(x.total_tokens, x.H, x.dv)
+    o_ref, h_ref = oracle_prefill(oracle_mod, x)
+    eo, eh = err(to64(o), o_ref), err(to64(hT), h_ref)
+    _say(f"chunk64 {lens} {dk}x{dv} {dt} {gate}: error o={eo:.3e} hT={eh:.3e}")
+    assert np.isfinite(to64(o)).all() and np.isfinite(to64(hT)).all()
+    assert eo <= TOL[dt] and eh <= TOL[dt]
+
+
+def test_chunk64_matches_chunk16_f32():
+    """Both chunkings compute the same recurrence: float32 results agree closely."""
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd, kda_chunk_fwd_chunk64
+    x = inputs.make_inputs([333, 64], 2, 128, 128, "f32", seed=101, h0_sigma=0.05, packed=True)
+    xd = x.to(dev)
+    o16, h16 = kda_chunk_fwd(*xd.call_views(), h0=xd.h0, cu_seqlens=xd.cu_seqlens)
+    o64, h64 = kda_chunk_fwd_chunk64(*xd.call_views(), h0=xd.h0, cu_seqlens=xd.cu_seqlens)
+    torch.cuda.synchronize()
+    assert err(to64(o64), to64(o16)) <= 1e-4 and err(to64(h64), to64(h16)) <= 1e-4
+
+
+def test_chunk64_T4096_H96(oracle_mod):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd_chunk64
+    x = inputs.make_workload("prefill_T4096_H96_d128_bf16")
+    xd = x.to(dev)
+    o, hT = kda_chunk_fwd_chunk64(*xd.call_views(), h0=xd.h0, cu_seqlens=xd.cu_seqlens)
+    torch.cuda.synchronize()
+    o = o.reshape(x.total_tokens, x.H, x.dv)
+    heads = [0, 47, 95]
+    o_ref, h_ref = oracle_prefill(oracle_mod, x, heads)
+    eo, eh = err(to64(o[:, heads]), o_ref), err(to64(hT[:, heads]), h_ref)
+    _say(f"chunk64 T4096 H96: error o={eo:.3e} hT={eh:.3e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
