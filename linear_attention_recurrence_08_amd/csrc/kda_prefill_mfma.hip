@@ -27,8 +27,8 @@
 //   stage B1 (waves 8-11) for tiles q-1 and q-2: A, A^T, P^T over all 128 channels and T, split
 //      into two halves that run in consecutive periods; waves 8-9 take even tiles and waves
 //      10-11 odd ones, so each SIMD carries half an inverse per period;
-//   stage B2 (waves 0-3) for tile q-3: W and Qpp for key channels [32s, 32s+32), Ut and PUt
-//      for columns [16s, 16s+16), and the channel-major Kd blocks the carry consumes;
+//   stage B2 (waves 8-11, beside B1) for tile q-3: W and Qpp for key channels [32s, 32s+32), Ut
+//      and PUt for columns [16s, 16s+16), and the channel-major Kd blocks the carry consumes;
 //   stage S (waves 0-3) for tile q-4: wave s carries its 128 x 16 strip of S, which lives in
 //      registers as eight 16x16 float32 accumulator blocks for the whole sequence, and writes o.
 // Three waves share each SIMD.  Loads run two tiles ahead of their use.  All products use
@@ -105,10 +105,14 @@ __device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 // Workgroup barrier that orders LDS only: global loads issued before it stay in flight (a full
 // __syncthreads() would also wait for the prefetched tiles).
+// The scheduling fences keep the compiler from hoisting the next tile's arithmetic above the
+// barrier, where it would consume registers whose loads were issued only one tile ago.
 __device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // (workgroup index) -> (pair index p = n * H + head, slice) with both slices of a pair on one XCD
@@ -463,23 +467,33 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         lds_barrier();
         lds_barrier();
     } else if (role == 2) {
+        // every stage-B wave runs B2 of period q (tile q - 3) for its channel group, and its pair
+        // alternates the two halves of B1 for the tiles of its parity
         const int par = s >> 1;            // tiles of this parity
-        lds_barrier();
-        if (par) lds_barrier();
+        auto b2_at = [&](int64_t q) {
+            if (q >= 3 && q - 3 < nsteps) stage_b2(q - 3);
+        };
+        int64_t q = 0;                     // period
+        for (; q < 1 + par; ++q) {
+            b2_at(q);
+            lds_barrier();
+        }
         for (int64_t j = par; j < nsteps; j += 2) {
+            b2_at(q++);
             const B1Carry c = stage_b1a(j);
             lds_barrier();
+            b2_at(q++);
             stage_b1b(j, c);
             lds_barrier();
         }
-        lds_barrier();
-        lds_barrier();
-        if (!par) lds_barrier();
+        for (; q < nsteps + 4; ++q) {
+            b2_at(q);
+            lds_barrier();
+        }
     } else {
         lds_barrier();
         lds_barrier();
         lds_barrier();
-        stage_b2(0);
         lds_barrier();
         // snapshots: after tile i the registers hold the state after (i + 1) * 16 tokens; every
         // snap_tiles-th full tile saves it (the next index in the snapshot array)
@@ -489,7 +503,6 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         const int64_t nfull = (eos - bos) / C;
         int64_t i = 0;
         for (; i < nfull; ++i) {
-            stage_b2(i + 1);
             store_o(i, stage_s(i), false);
             if (i + 1 == snap_at) {
                 float* dst = a.snaps + (snap_idx * H + h) * (int64_t)(D * D);
@@ -504,7 +517,6 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             lds_barrier();
         }
         for (; i < nsteps; ++i) {
-            stage_b2(i + 1);
             store_o(i, stage_s(i), true);
             lds_barrier();
         }
