@@ -73,12 +73,16 @@ def decode_bytes(d) -> int:
 
 
 def kernel_source_digest() -> str:
-    """sha256 over the HIP sources and the public header: identifies the kernels measured."""
+    """sha256 over the HIP sources and the build script (which holds the code-generation options):
+    identifies the kernels measured."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "linear_attention_recurrence_08_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+    pkg = os.path.join(ROOT, "linear_attention_recurrence_08_amd")
+    csrc = os.path.join(pkg, "csrc")
+    files = [os.path.join(csrc, n) for n in sorted(os.listdir(csrc))]
+    files.append(os.path.join(pkg, "build.py"))
+    for path in files:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 

@@ -1,11 +1,17 @@
 """Build step for the KDA HIP library: compiles every source under csrc/ for gfx950 into
-libkda.so next to this file (in-tree, so it travels with the repository)."""
+libkda.so next to this file (in-tree, so it travels with the repository).
+
+Each source is compiled to an object of its own (in parallel, in a temporary folder) so that a
+kernel can take code-generation options of its own; the objects are then linked into one shared
+library."""
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -14,6 +20,14 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkda.so")
 ARCH = "gfx950"
 
+# Per-source code-generation options.  The chunked prefill is bound by instruction issue across
+# its twelve role waves; the scheduler that favours instruction-level parallelism interleaves the
+# independent MFMA chains and LDS reads of a stage better than the default (measured: 3.5% less
+# time per tile at 160 VGPRs, still three waves per SIMD, no spills).
+PER_SOURCE = {
+    "kda_prefill_mfma.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
 
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
@@ -21,7 +35,7 @@ def sources():
 
 def hipcc_flags():
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # no packed-fp32 instructions in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wno-unused-command-line-argument",
@@ -31,16 +45,30 @@ def hipcc_flags():
     ]
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc] + hipcc_flags() + sources() + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libkda.so")
+        raise RuntimeError("hipcc failed: " + " ".join(cmd))
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = LIB + ".tmp"
+    with tempfile.TemporaryDirectory(prefix="kda_build_") as objdir:
+        jobs = []
+        for src in sources():
+            name = os.path.basename(src)
+            obj = os.path.join(objdir, name + ".o")
+            jobs.append(([hipcc] + hipcc_flags() + PER_SOURCE.get(name, []) +
+                         ["-c", src, "-o", obj], obj))
+        workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+        with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+            list(pool.map(lambda j: _run(j[0], verbose), jobs))
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + [o for _, o in jobs] +
+             ["-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 
