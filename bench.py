@@ -152,8 +152,13 @@ SUMMARY_KERNELS = {
         "kda_decode_step_gated_decode_N256_H96_d128_bf16", "decode_gated_N256_H96_d128_bf16"),
     "kda_output_gate_kernel<unsigned short>": ("kda_output_gate_T4096_H96_d128_bf16",
                                                "output_gate_T4096_H96_d128_bf16"),
-    "kda_frontend_kernel<unsigned short>": ("kda_frontend_T4096_H96_d128_bf16",
-                                            "frontend_T4096_H96_d128_bf16"),
+    # the input stage runs as three kernels per call (q and k, v, the gates): one summary
+    "kda_frontend_conv_kernel<unsigned short, true, true>": ("kda_frontend_T4096_H96_d128_bf16",
+                                                             "frontend_T4096_H96_d128_bf16"),
+    "kda_frontend_conv_kernel<unsigned short, false, true>": ("kda_frontend_T4096_H96_d128_bf16",
+                                                              "frontend_T4096_H96_d128_bf16"),
+    "kda_frontend_gate_kernel<unsigned short, true>": ("kda_frontend_T4096_H96_d128_bf16",
+                                                       "frontend_T4096_H96_d128_bf16"),
 }
 
 
@@ -177,72 +182,95 @@ def _algorithmic_bytes(workload):
 def summarize(dirs, command):
     """profiles/<kernel>_<workload>_kernel_trace.md from a --kernel-trace --stats run and
     profiles/<kernel>_<workload>_hbm_traffic.md from FETCH_SIZE + WRITE_SIZE counter runs (each
-    scaled by what the same counter reads for the 1 GiB calibration copy)."""
+    scaled by what the same counter reads for the 1 GiB calibration copy).  Where one entry point
+    launches several kernels, the summary lists each and adds them up per call."""
     import csv
     import glob
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
     digest = kernel_source_digest()
-    counters = {}     # (kernel tag or "copy", counter) -> list of per-dispatch values (KiB)
+    tags = {}
+    for frag, (tag, wl) in SUMMARY_KERNELS.items():
+        tags.setdefault(tag, (wl, []))[1].append(frag)
+    trace = {}        # tag -> list of (fragment, stats row)
+    counters = {}     # (fragment or "copy", counter) -> list of per-dispatch values (KiB)
     for d in dirs:
         for f in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
-                for frag, (tag, wl) in SUMMARY_KERNELS.items():
+                for frag, (tag, _) in SUMMARY_KERNELS.items():
                     if frag in r["Name"]:
-                        path = os.path.join(out_dir, f"{tag}_kernel_trace.md")
-                        with open(path, "w") as fo:
-                            fo.write(f"# {frag} on {wl}: rocprofv3 kernel trace\n\n")
-                            fo.write(f"command: `{command}`\n\n")
-                            fo.write("| calls | average ns | min ns | max ns | total ns |\n")
-                            fo.write("|---|---|---|---|---|\n")
-                            fo.write(f"| {r['Calls']} | {float(r['AverageNs']):.0f} | "
-                                     f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | "
-                                     f"{float(r['TotalDurationNs']):.0f} |\n\n")
-                            fo.write(f"source_digest: {digest}\n")
-                        print("wrote", path)
+                        trace.setdefault(tag, []).append((frag, r))
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 name = r["Kernel_Name"]
                 key = None
                 if "elementwise" in name or "vectorized" in name:
                     key = "copy"
-                for frag, (tag, _) in SUMMARY_KERNELS.items():
+                for frag in SUMMARY_KERNELS:
                     if frag in name:
-                        key = tag
+                        key = frag
                 if key is None:
                     continue
                 counters.setdefault((key, r["Counter_Name"]), []).append(
                     float(r["Counter_Value"]))
+    for tag, rows in trace.items():
+        wl, _ = tags[tag]
+        path = os.path.join(out_dir, f"{tag}_kernel_trace.md")
+        with open(path, "w") as fo:
+            names = ", ".join(frag for frag, _ in rows)
+            fo.write(f"# {names} on {wl}: rocprofv3 kernel trace\n\n")
+            fo.write(f"command: `{command}`\n\n")
+            fo.write("| kernel | calls | average ns | min ns | max ns | total ns |\n")
+            fo.write("|---|---|---|---|---|---|\n")
+            for frag, r in rows:
+                fo.write(f"| {frag} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                         f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | "
+                         f"{float(r['TotalDurationNs']):.0f} |\n")
+            if len(rows) > 1:
+                fo.write(f"| sum per call | | "
+                         f"{sum(float(r['AverageNs']) for _, r in rows):.0f} | | | |\n")
+            fo.write(f"\nsource_digest: {digest}\n")
+        print("wrote", path)
     if counters:
         cal = {}
         for cn in ("FETCH_SIZE", "WRITE_SIZE"):
             vals = counters.get(("copy", cn))
             if vals:
                 cal[cn] = max(vals) * 1024.0 / CALIB_BYTES   # counter bytes per true byte
-        for frag, (tag, wl) in SUMMARY_KERNELS.items():
-            f_vals = counters.get((tag, "FETCH_SIZE"))
-            w_vals = counters.get((tag, "WRITE_SIZE"))
-            if not f_vals or not w_vals or "FETCH_SIZE" not in cal or "WRITE_SIZE" not in cal:
+        for tag, (wl, frags) in tags.items():
+            if "FETCH_SIZE" not in cal or "WRITE_SIZE" not in cal:
                 continue
-            fetch = sum(f_vals) / len(f_vals) * 1024.0 / cal["FETCH_SIZE"]
-            write = sum(w_vals) / len(w_vals) * 1024.0 / cal["WRITE_SIZE"]
-            algo = _algorithmic_bytes(wl)
-            path = os.path.join(out_dir, f"{tag}_hbm_traffic.md")
-            with open(path, "w") as fo:
-                fo.write(f"# {frag} on {wl}: HBM traffic per launch (rocprofv3 counters)\n\n")
-                fo.write(f"command: `{command}`\n\n")
-                fo.write("Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each taken in its "
-                         "own run and scaled by what the same counter reads for a copy of exactly "
-                         f"{CALIB_BYTES} bytes read and {CALIB_BYTES} bytes written "
-                         f"(factor FETCH {cal['FETCH_SIZE']:.4f}, WRITE "
-                         f"{cal['WRITE_SIZE']:.4f} counter bytes per byte).\n\n")
-                fo.write("| dispatches | fetch bytes | write bytes | total bytes | algorithmic "
-                         "bytes | total / algorithmic |\n|---|---|---|---|---|---|\n")
-                fo.write(f"| {len(f_vals)} | {fetch:.4g} | {write:.4g} | {fetch + write:.4g} | "
-                         f"{algo} | {(fetch + write) / algo:.3f} |\n\n")
-                fo.write(f"source_digest: {digest}\n")
-                fo.write(f"hbm_bytes_per_launch: {fetch + write:.6g}\n")
-            print("wrote", path)
+            fetch = write = 0.0
+            ndisp = []
+            for frag in frags:
+                f_vals = counters.get((frag, "FETCH_SIZE"))
+                w_vals = counters.get((frag, "WRITE_SIZE"))
+                if not f_vals or not w_vals:
+                    break
+                fetch += sum(f_vals) / len(f_vals) * 1024.0 / cal["FETCH_SIZE"]
+                write += sum(w_vals) / len(w_vals) * 1024.0 / cal["WRITE_SIZE"]
+                ndisp.append(str(len(f_vals)))
+            else:
+                algo = _algorithmic_bytes(wl)
+                path = os.path.join(out_dir, f"{tag}_hbm_traffic.md")
+                with open(path, "w") as fo:
+                    fo.write(f"# {', '.join(frags)} on {wl}: HBM traffic per call "
+                             "(rocprofv3 counters)\n\n")
+                    fo.write(f"command: `{command}`\n\n")
+                    fo.write("Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each taken "
+                             "in its own run and scaled by what the same counter reads for a copy "
+                             f"of exactly {CALIB_BYTES} bytes read and {CALIB_BYTES} bytes "
+                             f"written (factor FETCH {cal['FETCH_SIZE']:.4f}, WRITE "
+                             f"{cal['WRITE_SIZE']:.4f} counter bytes per byte); the per-dispatch "
+                             "means of the kernels of one call are added.\n\n")
+                    fo.write("| dispatches | fetch bytes | write bytes | total bytes | "
+                             "algorithmic bytes | total / algorithmic |\n"
+                             "|---|---|---|---|---|---|\n")
+                    fo.write(f"| {' + '.join(ndisp)} | {fetch:.4g} | {write:.4g} | "
+                             f"{fetch + write:.4g} | {algo} | {(fetch + write) / algo:.3f} |\n\n")
+                    fo.write(f"source_digest: {digest}\n")
+                    fo.write(f"hbm_bytes_per_launch: {fetch + write:.6g}\n")
+                print("wrote", path)
 
 
 def time_launches(fn, steps, warmup, stream):

@@ -46,8 +46,8 @@ __device__ __forceinline__ void store4<float>(float* p, const float x[4]) {
 template <>
 __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float x[4]) {
     uint2 y;
-    y.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
-    y.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+    y.x = pack_bf16x2(x[0], x[1]);
+    y.y = pack_bf16x2(x[2], x[3]);
     *reinterpret_cast<uint2*>(p) = y;
 }
 

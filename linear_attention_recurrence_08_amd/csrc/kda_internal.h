@@ -99,12 +99,30 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// round to nearest even; NaN stays NaN
+// Two float32 values to packed bfloat16 (low half = lo), rounding to nearest even, NaN kept a
+// NaN: one v_cvt_pk_bf16_f32.
+typedef float kda_fpair __attribute__((ext_vector_type(2)));
+typedef __bf16 kda_bfpair __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const kda_fpair v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, kda_bfpair));
+}
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<bf16_t>(u >> 16);
+    return static_cast<bf16_t>(pack_bf16x2(f, 0.f) & 0xffffu);
+}
+
+// Sum over each aligned group of 16 lanes, left in every lane of the group: a butterfly of DPP
+// moves within the 16-lane row (mirror, half-mirror, then swaps of neighbours and of pairs in
+// each quad), no LDS traffic.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float sum16(float x) {
+    x += dpp_mov<0x140>(x);   // row_mirror: lane i <- lane 15 - i
+    x += dpp_mov<0x141>(x);   // row_half_mirror: lane i <- lane 7 - i within each half
+    x += dpp_mov<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x += dpp_mov<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    return x;
 }
 
 template <typename T> struct io;
@@ -136,7 +154,7 @@ template <> struct Row8<bf16_t> {
         u32v4 u;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            u[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
+            u[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
         __builtin_nontemporal_store(u, reinterpret_cast<u32v4*>(p));
     }
 };

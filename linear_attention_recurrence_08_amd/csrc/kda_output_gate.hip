@@ -8,7 +8,7 @@
 //
 // The stage is HBM-bound (three dv-wide rows per (token, head), a few flops per element).  A group
 // of 16 lanes owns one row: lane j holds elements 8j .. 8j+7 (one 16-byte access for bf16, two
-// for float32), the sum of squares is reduced across the group with four xor shuffles, and the
+// for float32), the sum of squares is reduced across the group with four DPP steps, and the
 // row is written back once.  Lanes past dv / 8 hold nothing (dv is a multiple of 16, <= 128).
 // Each group takes eight rows and issues all their loads before the arithmetic, so every lane
 // keeps 256 bytes (bf16) in flight.
@@ -49,9 +49,7 @@ __global__ __launch_bounds__(256) void kda_output_gate_kernel(GateArgs a) {
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
-#pragma unroll
-        for (int m = 8; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 16);
-        const float rn = rsqrtf(ss / (float)a.dv + a.eps);
+        const float rn = __builtin_amdgcn_rsqf(sum16(ss) / (float)a.dv + a.eps);
         const int64_t row = row0 + r;
         if (row < a.rows && lane_on) {
             float y[8];
