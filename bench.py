@@ -152,13 +152,11 @@ SUMMARY_KERNELS = {
         "kda_decode_step_gated_decode_N256_H96_d128_bf16", "decode_gated_N256_H96_d128_bf16"),
     "kda_output_gate_kernel<unsigned short>": ("kda_output_gate_T4096_H96_d128_bf16",
                                                "output_gate_T4096_H96_d128_bf16"),
-    # the input stage runs as three kernels per call (q and k, v, the gates): one summary
-    "kda_frontend_conv_kernel<unsigned short, true, true>": ("kda_frontend_T4096_H96_d128_bf16",
-                                                             "frontend_T4096_H96_d128_bf16"),
-    "kda_frontend_conv_kernel<unsigned short, false, true>": ("kda_frontend_T4096_H96_d128_bf16",
-                                                              "frontend_T4096_H96_d128_bf16"),
-    "kda_frontend_gate_kernel<unsigned short, true>": ("kda_frontend_T4096_H96_d128_bf16",
+    # the input stage: one kernel streams q, k, v and the gates, a second saves the conv state
+    "kda_frontend_conv_kernel<unsigned short, true>": ("kda_frontend_T4096_H96_d128_bf16",
                                                        "frontend_T4096_H96_d128_bf16"),
+    "kda_frontend_state_kernel<unsigned short>": ("kda_frontend_T4096_H96_d128_bf16",
+                                                  "frontend_T4096_H96_d128_bf16"),
 }
 
 

@@ -11,25 +11,22 @@
 //     g = g_min * sigmoid(A_h (x_z + bias_c)),  beta = sigmoid(x_b),
 // with swish(y) = y sigmoid(y) and l2(y) = y / sqrt(sum_c y_c^2 + eps) over the head's dk values.
 //
-// The stage is HBM-bound (reads 3 dk + dv values and writes as many per (token, head)).  Three
-// kernels run per call, one per kind of tensor (q and k with the L2 norm, v, and z with beta), so
-// each executes compact code.  A group of 16 lanes owns a run of 16 consecutive packed tokens
-// (8 for float32) of one head; lane j holds channels 8j .. 8j+7, keeps the previous three inputs
-// in registers (a sliding window, so every input is read once) and requests all of its run's rows
-// before computing the first (16 bytes per token per lane in flight).  A full run inside one
-// sequence, the common case, is straight-line code; a run that crosses a sequence start (its
-// window restarts there from the saved state) or ends the input goes token by token.  The L2
-// norms are 16-lane DPP reductions.  A further kernel writes the saved convolution state (the last
-// three inputs of every sequence) after the others have read it, so the state may be updated in
-// place.
+// The stage is HBM-bound (reads 3 dk + dv values and writes as many per (token, head)).  One
+// launch streams all four tensors (blockIdx.y: q, k, v, z), a second writes the saved
+// convolution state.  A group of 16 lanes owns a chunk of 32 consecutive packed tokens of one
+// head; lane j holds channels 8j .. 8j+7 and, for the convolved tensors, keeps the previous three
+// inputs in registers (a sliding window, so every input is read once).  The four groups of a
+// wave take four consecutive chunks of one head, so their rows are addressed through one
+// wave-uniform buffer resource.  A chunk inside one sequence, the common case, streams through
+// two register sets of a few tokens each, the next set's rows in flight while the current one is
+// computed; a chunk that crosses a sequence start (its window restarts there from the saved
+// state) or ends the input goes token by token.  The L2 norms are 16-lane DPP reductions.  The
+// state kernel writes the last three inputs of every sequence after the first kernel has read
+// the saved state, so the state may be updated in place.
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
-
-// tokens per lane group: all of a run's rows are requested before the first is used
-template <typename Tin> constexpr int run_of() { return sizeof(Tin) == 2 ? 16 : 8; }
-constexpr int GROUPS = 16;       // lane groups per 256-thread block
 
 // logistic sigmoid with the hardware reciprocal (v_rcp_f32, 1 ulp)
 __device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
@@ -51,86 +48,163 @@ __device__ __forceinline__ int64_t seq_end(const FrontArgs& a, int64_t n) {
     return a.cu ? (int64_t)a.cu[n + 1] : (n + 1) * a.T;
 }
 
-// g = g_min sigmoid(A_h (z + bias)) and beta = sigmoid(x_b): elementwise.  One 16-lane group per
-// run of RUN packed tokens of head h; lane j holds channels 8j .. 8j+7 (FULL: dk = 128, every
-// lane holds channels).
-template <typename Tin, bool FULL>
-__global__ __launch_bounds__(256) void kda_frontend_gate_kernel(FrontArgs a) {
-    constexpr int RUN = run_of<Tin>();
-    const int tid = threadIdx.x;
-    const int j = tid & 15;
-    const int64_t unit = (int64_t)blockIdx.x * GROUPS + (tid >> 4);
-    const int64_t nruns = (a.Ttot + RUN - 1) / RUN;
-    if (unit >= nruns * a.H) return;     // whole 16-lane groups leave together
-    const int64_t H = a.H, d = a.dk;
-    const int64_t h = unit % H, run = unit / H;
-    const int64_t t0 = run * RUN, t1 = min(t0 + RUN, a.Ttot);
-    const bool on = FULL || 8 * j < d;
-    const int64_t c0 = h * d + 8 * j;
-    const int64_t tstride = H * d;
-    const Tin* xrow = static_cast<const Tin*>(a.xz) + t0 * tstride + c0;
-    Tin* orow = static_cast<Tin*>(a.g) + t0 * tstride + c0;
-    float zb[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) zb[c] = on ? a.zbias[c0 + c] : 0.f;
-    const float Ah = a.A[h];
-    Raw8<Tin> rows[RUN];
-#pragma unroll
-    for (int i = 0; i < RUN; ++i) {
-        if (on && t0 + i < t1) rows[i].load(xrow + i * tstride);
-        else rows[i].zero();
-    }
-#pragma unroll
-    for (int i = 0; i < RUN; ++i) {
-        if (t0 + i >= t1) break;
-        float z[8], g8[8];
-        rows[i].unpack(z);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) g8[c] = a.g_min * sigm(Ah * (z[c] + zb[c]));
-        if (on) Row8<Tin>::store(orow + i * tstride, g8);
-    }
-    // beta: lane j of the group takes token t0 + j
-    if (t0 + j < t1) {
-        const int64_t t = t0 + j;
-        const float bl = io<Tin>::load(static_cast<const Tin*>(a.xb) + t * H + h);
-        io<Tin>::store(static_cast<Tin*>(a.beta) + t * H + h, sigm(bl));
-    }
-}
-
-// The convolved tensors: blockIdx.y picks q or k (NORM, with the L2 normalisation) or is v (no
-// normalisation).  One 16-lane group per run of RUN packed tokens of head h; lane j holds
+// The convolved tensors: blockIdx.y picks q, k (both with the L2 normalisation) or v (without).
+// One 16-lane group per chunk of CONV_CHUNK packed tokens of head h; lane j holds
 // channels 8j .. 8j+7 with their four taps and the previous three inputs (FULL: 128 channels,
-// every lane holds channels).
-template <typename Tin, bool NORM, bool FULL>
+// every lane holds channels).  The four groups of a wave take four consecutive chunks of one head,
+// so a wave-uniform buffer resource addresses their rows (the row offset is a scalar; each lane
+// keeps one 32-bit offset).  A chunk inside one sequence streams through two register sets of
+// SUB tokens each: the rows of the next sub-run are in flight while the current one is computed.
+template <typename Tin> constexpr int sub_of() { return sizeof(Tin) == 2 ? 8 : 4; }
+constexpr int CONV_CHUNK = 32;
+constexpr int kBufNT = 2;                    // buffer cache policy: non-temporal (streaming)
+
+// eight consecutive elements through a buffer resource: one 16-byte access for bf16, two for f32
+template <typename Tin> struct BufRow;
+template <> struct BufRow<bf16_t> {
+    static __device__ __forceinline__ void load(Raw8<bf16_t>& r, __amdgpu_buffer_rsrc_t rs,
+                                                uint32_t voff, uint32_t soff) {
+        r.u = __builtin_bit_cast(u32v4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff,
+                                                                              kBufNT));
+    }
+    static __device__ __forceinline__ void store(const float y[8], __amdgpu_buffer_rsrc_t rs,
+                                                 uint32_t voff, uint32_t soff) {
+        const u32v4 u = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                         pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32v4, u), rs, voff, soff,
+                                               kBufNT);
+    }
+};
+template <> struct BufRow<float> {
+    static __device__ __forceinline__ void load(Raw8<float>& r, __amdgpu_buffer_rsrc_t rs,
+                                                uint32_t voff, uint32_t soff) {
+        r.a = __builtin_bit_cast(f32v4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff,
+                                                                              kBufNT));
+        r.b = __builtin_bit_cast(f32v4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, soff,
+                                                                              kBufNT));
+    }
+    static __device__ __forceinline__ void store(const float y[8], __amdgpu_buffer_rsrc_t rs,
+                                                 uint32_t voff, uint32_t soff) {
+        const f32v4 lo = {y[0], y[1], y[2], y[3]}, hi = {y[4], y[5], y[6], y[7]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32v4, lo), rs, voff, soff,
+                                               kBufNT);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32v4, hi), rs, voff + 16,
+                                               soff, kBufNT);
+    }
+};
+
+template <typename Tin, bool FULL>
 __global__ __launch_bounds__(256) void kda_frontend_conv_kernel(FrontArgs a) {
-    constexpr int RUN = run_of<Tin>();
+    constexpr int SUB = sub_of<Tin>();
+    constexpr int NSUB = CONV_CHUNK / SUB;
     const int tid = threadIdx.x;
-    const int j = tid & 15;
-    const int64_t unit = (int64_t)blockIdx.x * GROUPS + (tid >> 4);
-    const int64_t nruns = (a.Ttot + RUN - 1) / RUN;
-    if (unit >= nruns * a.H) return;     // whole 16-lane groups leave together
-    const int kind = NORM ? (int)blockIdx.y : 2;      // 0 = q, 1 = k, 2 = v
-    const int64_t H = a.H, Cq = H * a.dk, C = H * (2 * a.dk + a.dv);
-    const int64_t d = NORM ? a.dk : a.dv;
-    const int64_t h = unit % H, run = unit / H;
-    const int64_t t0 = run * RUN, t1 = min(t0 + RUN, a.Ttot);
+    const int j = tid & 15, grp = (tid >> 4) & 3;
+    const int64_t H = a.H;
+    const int64_t nchunks = (a.Ttot + CONV_CHUNK - 1) / CONV_CHUNK;
+    const int64_t wv = (int64_t)blockIdx.x * 4 + (tid >> 6);   // wave: one head, four chunks
+    const int64_t h = wv % H, chunk0 = (wv / H) * 4;
+    if (chunk0 >= nchunks) return;                              // the whole wave leaves
+    const int64_t chunk = chunk0 + grp;
+    if (chunk >= nchunks) return;                               // whole 16-lane groups leave
+    const int kind = (int)blockIdx.y;                  // 0 = q, 1 = k, 2 = v, 3 = z (gates)
+    const bool norm = kind < 2;                        // uniform per block
+    const int64_t Cq = H * a.dk, C = H * (2 * a.dk + a.dv);
+    const int64_t d = kind == 2 ? a.dv : a.dk;
+    const int64_t t0 = chunk * CONV_CHUNK, t1 = min(t0 + CONV_CHUNK, a.Ttot);
     const bool on = FULL || 8 * j < d;
-    const Tin* x = static_cast<const Tin*>(kind == 0 ? a.xq : kind == 1 ? a.xk : a.xv);
-    Tin* out = static_cast<Tin*>(kind == 0 ? a.q : kind == 1 ? a.k : a.v);
-    const float* wsrc = kind == 0 ? a.wq : kind == 1 ? a.wk : a.wv;
+    const Tin* x = static_cast<const Tin*>(kind == 0 ? a.xq : kind == 1 ? a.xk :
+                                           kind == 2 ? a.xv : a.xz);
+    Tin* out = static_cast<Tin*>(kind == 0 ? a.q : kind == 1 ? a.k : kind == 2 ? a.v : a.g);
     const int64_t c0 = h * d + 8 * j;                  // first channel within the tensor
-    const int64_t scol = (kind == 0 ? 0 : kind == 1 ? Cq : 2 * Cq) + c0;   // state column
     const int64_t tstride = H * d;                     // elements between consecutive tokens
     const Tin* xrow = x + t0 * tstride + c0;           // this lane's slice of token t0
     Tin* orow = out + t0 * tstride + c0;
-    const Tin* cin = static_cast<const Tin*>(a.conv_in);
 
-    Raw8<Tin> rows[RUN];
+    // buffer resources over the wave's four chunks of head h (wave-uniform bases); a lane's
+    // offset is its chunk's start plus its channels, a row's offset a scalar
+    const int64_t wbase = chunk0 * CONV_CHUNK * tstride + h * d;        // elements
+    // records: the wave's four chunks, cut at the end of the tensor
+    const int64_t wlen = min(4 * CONV_CHUNK * tstride, a.Ttot * tstride - wbase);
+    const uint32_t nrec = (uint32_t)(wlen * (int64_t)sizeof(Tin));
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + wbase), (short)0, (int)nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(out + wbase), (short)0, (int)nrec, 0x00020000);
+    const uint32_t voff = (uint32_t)(((int64_t)grp * CONV_CHUNK * tstride + 8 * j) *
+                                     (int64_t)sizeof(Tin));
+    const uint32_t rowb = (uint32_t)(tstride * (int64_t)sizeof(Tin));  // bytes per token
+
+    Raw8<Tin> ra[SUB], rb[SUB];
+    auto load_sub = [&](Raw8<Tin> (&r)[SUB], int sub) {
 #pragma unroll
-    for (int i = 0; i < RUN; ++i) {
-        if (on && t0 + i < t1) rows[i].load(xrow + i * tstride);
-        else rows[i].zero();
+        for (int i = 0; i < SUB; ++i) {
+            if (on) BufRow<Tin>::load(r[i], rx, voff, (uint32_t)(sub * SUB + i) * rowb);
+            else r[i].zero();
+        }
+    };
+    // streams a whole chunk through the two register sets (the next sub-run's rows in flight
+    // while the current one is computed); f(row, y) makes a token's output row
+    auto stream_chunk = [&](auto&& f) {
+        load_sub(ra, 0);
+        load_sub(rb, 1);
+        auto run_sub = [&](const Raw8<Tin> (&r)[SUB], int sub) {
+#pragma unroll
+            for (int i = 0; i < SUB; ++i) {
+                float y[8];
+                f(r[i], y);
+                if (on) BufRow<Tin>::store(y, ro, voff, (uint32_t)(sub * SUB + i) * rowb);
+            }
+        };
+#pragma unroll 1
+        for (int sub = 0; sub < NSUB; sub += 2) {
+            run_sub(ra, sub);
+            if (sub + 2 < NSUB) load_sub(ra, sub + 2);
+            run_sub(rb, sub + 1);
+            if (sub + 3 < NSUB) load_sub(rb, sub + 3);
+        }
+    };
+
+    if (kind == 3) {
+        // g = g_min sigmoid(A_h (z + bias)), elementwise; beta = sigmoid(x_b)
+        float zb[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) zb[c] = on ? a.zbias[c0 + c] : 0.f;
+        const float Ah = a.A[h];
+        auto gate = [&](const Raw8<Tin>& row, float y[8]) {
+            float z[8];
+            row.unpack(z);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) y[c] = a.g_min * sigm(Ah * (z[c] + zb[c]));
+        };
+        if (t1 - t0 == CONV_CHUNK) {
+            stream_chunk(gate);
+        } else {
+#pragma unroll 1
+            for (int i = 0; i < (int)(t1 - t0); ++i) {
+                Raw8<Tin> row;
+                if (on) row.load(xrow + i * tstride);
+                else row.zero();
+                float y[8];
+                gate(row, y);
+                if (on) Row8<Tin>::store(orow + i * tstride, y);
+            }
+        }
+        // lane j of the group takes tokens t0 + j, t0 + j + 16, ...
+        for (int64_t t = t0 + j; t < t1; t += 16) {
+            const float bl = io<Tin>::load(static_cast<const Tin*>(a.xb) + t * H + h);
+            io<Tin>::store(static_cast<Tin*>(a.beta) + t * H + h, sigm(bl));
+        }
+        return;
     }
+
+    const float* wsrc = kind == 0 ? a.wq : kind == 1 ? a.wk : a.wv;
+    const int64_t scol = (kind == 0 ? 0 : kind == 1 ? Cq : 2 * Cq) + c0;   // state column
+    const Tin* cin = static_cast<const Tin*>(a.conv_in);
+    int64_t n = seq_of(a, t0);
+    const int64_t bos0 = seq_start(a, n);
+    int64_t eos = seq_end(a, n);
+    const bool fast = t1 - t0 == CONV_CHUNK && eos >= t1;   // a whole chunk inside one sequence
+
     float w[8][4];
 #pragma unroll
     for (int c = 0; c < 8; ++c)
@@ -138,10 +212,7 @@ __global__ __launch_bounds__(256) void kda_frontend_conv_kernel(FrontArgs a) {
         for (int i = 0; i < 4; ++i) w[c][i] = on ? wsrc[(c0 + c) * 4 + i] : 0.f;
 
     float win[3][8];                    // inputs at t-3, t-2, t-1
-    int64_t n = seq_of(a, t0);
-    const int64_t bos0 = seq_start(a, n);
-    int64_t eos = seq_end(a, n);
-    // window of the run's first token: positions t0-bos-3 .. t0-bos-1 of its sequence, the
+    // window of the chunk's first token: positions t0-bos-3 .. t0-bos-1 of its sequence, the
     // negative ones from the saved state (or zeros)
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
@@ -154,10 +225,10 @@ __global__ __launch_bounds__(256) void kda_frontend_conv_kernel(FrontArgs a) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) win[s][c] = v8[c];
     }
-    // one token: convolution over the window and the current input, Swish, the optional L2
-    // normalisation, the store; the window slides by one
-    auto token = [&](const Raw8<Tin>& row, Tin* dst) {
-        float xc[8], y[8], ss = 0.f;
+    // one token: convolution over the window and the current input, Swish, the L2 normalisation
+    // for q and k; the window slides by one
+    auto token = [&](const Raw8<Tin>& row, float y[8]) {
+        float xc[8], ss = 0.f;
         row.unpack(xc);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -169,21 +240,17 @@ __global__ __launch_bounds__(256) void kda_frontend_conv_kernel(FrontArgs a) {
             win[1][c] = win[2][c];
             win[2][c] = xc[c];
         }
-        if (NORM) {
+        if (norm) {
             const float r = __builtin_amdgcn_rsqf(sum16(ss) + a.eps);
 #pragma unroll
             for (int c = 0; c < 8; ++c) y[c] *= r;
         }
-        if (on) Row8<Tin>::store(dst, y);
     };
-    if (t1 - t0 == RUN && eos >= t1) {
-        // the common case: a full run inside one sequence, straight-line code
-#pragma unroll
-        for (int i = 0; i < RUN; ++i) token(rows[i], orow + i * tstride);
+    if (fast) {
+        stream_chunk(token);
         return;
     }
-    // otherwise (the run crosses a sequence start, or is the last, partial one) token by token,
-    // reloading each row
+    // otherwise (the chunk crosses a sequence start, or is the last, partial one) token by token
 #pragma unroll 1
     for (int i = 0; i < (int)(t1 - t0); ++i) {
         const int64_t t = t0 + i;
@@ -203,7 +270,9 @@ __global__ __launch_bounds__(256) void kda_frontend_conv_kernel(FrontArgs a) {
         Raw8<Tin> row;
         if (on) row.load(xrow + i * tstride);
         else row.zero();
-        token(row, orow + i * tstride);
+        float y[8];
+        token(row, y);
+        if (on) Row8<Tin>::store(orow + i * tstride, y);
     }
 }
 
@@ -238,13 +307,11 @@ __global__ __launch_bounds__(256) void kda_frontend_state_kernel(FrontArgs a) {
 
 template <typename Tin, bool FULL>
 hipError_t launch_frontend_t(const FrontArgs& a, hipStream_t s) {
-    const int64_t units = (a.Ttot + run_of<Tin>() - 1) / run_of<Tin>() * a.H;
-    const unsigned blocks = (unsigned)((units + GROUPS - 1) / GROUPS);
-    hipLaunchKernelGGL((kda_frontend_conv_kernel<Tin, true, FULL>), dim3(blocks, 2), dim3(256), 0,
-                       s, a);
-    hipLaunchKernelGGL((kda_frontend_conv_kernel<Tin, false, FULL>), dim3(blocks), dim3(256), 0,
-                       s, a);
-    hipLaunchKernelGGL((kda_frontend_gate_kernel<Tin, FULL>), dim3(blocks), dim3(256), 0, s, a);
+    // conv kernels: a wave per (head, four consecutive chunks), four waves per block
+    const int64_t waves = (a.Ttot + 4 * CONV_CHUNK - 1) / (4 * CONV_CHUNK) * a.H;
+    const unsigned cblocks = (unsigned)((waves + 3) / 4);
+    hipLaunchKernelGGL((kda_frontend_conv_kernel<Tin, FULL>), dim3(cblocks, 4), dim3(256), 0, s,
+                       a);
     return hipGetLastError();
 }
 
