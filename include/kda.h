@@ -40,7 +40,9 @@
  *
  * Supported sizes.  dk and dv: multiples of 16 from 16 to 128 (any combination).  The fast
  * matrix-core path is used for dtype KDA_BF16 with dk = dv = 128; every other supported
- * combination runs the general float32 tile path.  H >= 1; B, T, N >= 0 (empty input is a no-op
+ * combination runs the general float32 tile path.  H >= 1 with H * max(dk, dv) <= 2^20 (one
+ * token's row of a tensor; larger rows return KDA_ERR_SHAPE, since the streaming kernels address
+ * a few dozen consecutive rows with 32-bit byte offsets); B, T, N >= 0 (empty input is a no-op
  * that still copies h0 to hT).
  */
 #ifndef KDA_H
@@ -59,7 +61,7 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 enum {
     KDA_OK = 0,
     KDA_ERR_NULL = -1,        /* a required pointer is NULL */
-    KDA_ERR_SHAPE = -2,       /* negative or inconsistent sizes */
+    KDA_ERR_SHAPE = -2,       /* negative or inconsistent sizes, or H * max(dk, dv) > 2^20 */
     KDA_ERR_DTYPE = -3,       /* dtype not KDA_BF16 / KDA_F32 */
     KDA_ERR_UNSUPPORTED = -4, /* dk or dv not a multiple of 16 in [16, 128] */
     KDA_ERR_SEQLENS = -5,     /* cu_seqlens with B != 1, or (KDA_VALIDATE) bad contents */

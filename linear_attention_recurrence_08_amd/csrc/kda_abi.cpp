@@ -16,6 +16,12 @@ namespace {
 
 bool supported_dim(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
 
+// One token's row of a tensor (H * d elements) is at most 2^20 elements: the streaming kernels
+// address a few dozen consecutive rows with 32-bit byte offsets.
+bool rows_ok(int H, int dk, int dv) {
+    return static_cast<int64_t>(H) * (dk > dv ? dk : dv) <= (int64_t{1} << 20);
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool validate_enabled() {
@@ -67,6 +73,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, c
     if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
     if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
     if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!rows_ok(H, dk, dv)) return KDA_ERR_SHAPE;
     if (snap_stride < 0 || snap_stride % 16 != 0) return KDA_ERR_STRIDE;
     const bool want_snaps = snap_stride > 0;
     int64_t N, Ttot;
@@ -139,7 +146,7 @@ const char* kda_status_string(int status) {
     switch (status) {
         case KDA_OK: return "ok";
         case KDA_ERR_NULL: return "a required pointer is NULL";
-        case KDA_ERR_SHAPE: return "negative or inconsistent sizes";
+        case KDA_ERR_SHAPE: return "negative or inconsistent sizes, or H * max(dk, dv) > 2^20";
         case KDA_ERR_DTYPE: return "dtype must be KDA_BF16 or KDA_F32";
         case KDA_ERR_UNSUPPORTED: return "dk and dv must be multiples of 16 in [16, 128]";
         case KDA_ERR_SEQLENS: return "bad cu_seqlens (needs B == 1; non-decreasing from 0 to T)";
@@ -182,6 +189,7 @@ int kda_output_gate(const void* o, const void* gate, const float* weight, float 
     if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
     if (Ttot < 0 || H <= 0) return KDA_ERR_SHAPE;
     if (!supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!rows_ok(H, dv, dv)) return KDA_ERR_SHAPE;
     if (!(eps >= 0.f) || !std::isfinite(eps)) return KDA_ERR_RANGE;
     if (Ttot == 0) return KDA_OK;
     if (!o || !gate || !y) return KDA_ERR_NULL;
@@ -201,6 +209,7 @@ int decode_impl(const void* q, const void* k, const void* v, const void* g, cons
     if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
     if (N < 0 || H <= 0) return KDA_ERR_SHAPE;
     if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!rows_ok(H, dk, dv)) return KDA_ERR_SHAPE;
     if (N == 0) return KDA_OK;
     if (!q || !k || !v || !g || !beta || !S || !o) return KDA_ERR_NULL;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -245,6 +254,7 @@ int kda_decode_step_gated(const void* q, const void* k, const void* v, const voi
     if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
     if (N < 0 || H <= 0) return KDA_ERR_SHAPE;
     if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!rows_ok(H, dk, dv)) return KDA_ERR_SHAPE;
     if (!(eps >= 0.f) || !std::isfinite(eps)) return KDA_ERR_RANGE;
     if (N == 0) return KDA_OK;
     if (!gate || !y) return KDA_ERR_NULL;
@@ -266,6 +276,7 @@ int kda_frontend(const void* x_q, const void* x_k, const void* x_v, const void* 
     if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
     if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
     if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
+    if (!rows_ok(H, dk, dv)) return KDA_ERR_SHAPE;
     if (!(g_min < 0.f) || !std::isfinite(g_min) || !(eps >= 0.f) || !std::isfinite(eps))
         return KDA_ERR_RANGE;
     int64_t N, Ttot;

@@ -86,6 +86,8 @@ def _decode(lib, **kw):
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(g=None), -1),
     (dict(beta=None), -1), (dict(o=None), -1),
     (dict(cu=FAKE, B=2, num_seqs=3), -5),
+    # one token's row may hold at most 2^20 elements (H * max(dk, dv))
+    (dict(H=8193), -2), (dict(H=65537, dk=16, dv=16), -2),
 ])
 def test_prefill_argument_errors(lib, kw, code):
     assert _prefill(lib, **kw) == code
@@ -118,7 +120,7 @@ def test_snapshot_empty_is_noop(lib):
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=3), -3), (dict(N=-1), -2), (dict(H=0), -2), (dict(dk=100), -4),
     (dict(dv=256), -4), (dict(q=None), -1), (dict(S=None), -1), (dict(o=None), -1),
-    (dict(beta=None), -1),
+    (dict(beta=None), -1), (dict(H=8193), -2),
 ])
 def test_decode_argument_errors(lib, kw, code):
     assert _decode(lib, **kw) == code
@@ -151,6 +153,7 @@ def _gate(lib, **kw):
     (dict(eps=-1.0), -6), (dict(eps=float("nan")), -6), (dict(eps=float("inf")), -6),
     (dict(o=None), -1), (dict(gate=None), -1), (dict(y=None), -1),
     (dict(o=UNALIGNED), -9), (dict(gate=UNALIGNED), -9), (dict(y=UNALIGNED), -9),
+    (dict(H=8193), -2),
 ])
 def test_output_gate_argument_errors(lib, kw, code):
     assert _gate(lib, **kw) == code
@@ -174,6 +177,7 @@ def _decode_gated(lib, **kw):
     (dict(gate=None), -1), (dict(y=None), -1), (dict(o=None), -1), (dict(S=None), -1),
     # the unfused fallback (64 x 64 heads) needs 16-byte aligned output-stage rows
     (dict(y=UNALIGNED), -9), (dict(gate=UNALIGNED), -9),
+    (dict(H=16385), -2),
 ])
 def test_decode_gated_argument_errors(lib, kw, code):
     assert _decode_gated(lib, **kw) == code
@@ -196,6 +200,7 @@ def _front(lib, **kw):
     (dict(cu=FAKE, B=2, num_seqs=1), -5),
     (dict(xq=None), -1), (dict(wv=None), -1), (dict(A=None), -1), (dict(beta=None), -1),
     (dict(q=UNALIGNED), -9), (dict(xv=UNALIGNED), -9), (dict(cin=UNALIGNED), -9),
+    (dict(H=8193), -2),
 ])
 def test_frontend_argument_errors(lib, kw, code):
     assert _front(lib, **kw) == code
