@@ -3,7 +3,13 @@ in the library's HIP kernels.  PyTorch supplies device memory and the current st
 
     kda_chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, output_final_state=True)
         -> (o, hT)
+    kda_chunk_fwd_chunk64(...)   the same with 64-token chunks of four 16-token sub-tiles
+    kda_chunk_fwd_snapshots(q, k, v, g, beta, snap_stride, ...) -> (o, hT, snaps, snap_offsets)
     kda_decode_step(q, k, v, g, beta, S) -> o         (S is updated in place)
+    kda_decode_step_gated(q, k, v, g, beta, S, gate, weight=None, eps=...) -> (o, y)
+    kda_output_gate(o, gate, weight=None, eps=...) -> y
+    kda_frontend(x_q, x_k, x_v, x_z, x_b, w_q, w_k, w_v, z_bias, A, ...)
+        -> (q, k, v, g, beta, conv_state)
     kda_status_string(code) -> str
 
 Layouts (see include/kda.h): q, k, g [B, T, H, dk] or packed [Ttot, H, dk]; v [.., H, dv];
