@@ -72,15 +72,24 @@ def decode_bytes(d) -> int:
     return d.B * d.H * per
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the HIP sources and the build script (which holds the code-generation options):
-    identifies the kernels measured."""
-    h = hashlib.sha256()
+# The sources that make each measured kernel's code: its own file, the shared device helpers and
+# the build script (which holds the code-generation options).
+KERNEL_SOURCES = {
+    "kda_chunk_fwd": "kda_prefill_mfma.hip",
+    "kda_decode": "kda_decode.hip",
+    "kda_output_gate": "kda_output_gate.hip",
+    "kda_frontend": "kda_frontend.hip",
+}
+
+
+def kernel_source_digest(kernel_tag: str) -> str:
+    """sha256 over the sources of the kernel a summary tag names: identifies the code measured."""
     pkg = os.path.join(ROOT, "linear_attention_recurrence_08_amd")
-    csrc = os.path.join(pkg, "csrc")
-    files = [os.path.join(csrc, n) for n in sorted(os.listdir(csrc))]
-    files.append(os.path.join(pkg, "build.py"))
-    for path in files:
+    src = next(f for prefix, f in sorted(KERNEL_SOURCES.items(), key=lambda kv: -len(kv[0]))
+               if kernel_tag.startswith(prefix))
+    h = hashlib.sha256()
+    for path in (os.path.join(pkg, "csrc", src), os.path.join(pkg, "csrc", "kda_internal.h"),
+                 os.path.join(pkg, "build.py")):
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -95,7 +104,7 @@ def recorded_traffic(kernel_tag: str):
     txt = open(path).read()
     m_d = re.search(r"source_digest:\s*([0-9a-f]+)", txt)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m_d or not m_b or m_d.group(1) != kernel_source_digest():
+    if not m_d or not m_b or m_d.group(1) != kernel_source_digest(kernel_tag):
         return None
     return float(m_b.group(1))
 
@@ -186,7 +195,6 @@ def summarize(dirs, command):
     import glob
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
-    digest = kernel_source_digest()
     tags = {}
     for frag, (tag, wl) in SUMMARY_KERNELS.items():
         tags.setdefault(tag, (wl, []))[1].append(frag)
@@ -227,7 +235,7 @@ def summarize(dirs, command):
             if len(rows) > 1:
                 fo.write(f"| sum per call | | "
                          f"{sum(float(r['AverageNs']) for _, r in rows):.0f} | | | |\n")
-            fo.write(f"\nsource_digest: {digest}\n")
+            fo.write(f"\nsource_digest: {kernel_source_digest(tag)}\n")
         print("wrote", path)
     if counters:
         cal = {}
@@ -266,7 +274,7 @@ def summarize(dirs, command):
                              "|---|---|---|---|---|---|\n")
                     fo.write(f"| {' + '.join(ndisp)} | {fetch:.4g} | {write:.4g} | "
                              f"{fetch + write:.4g} | {algo} | {(fetch + write) / algo:.3f} |\n\n")
-                    fo.write(f"source_digest: {digest}\n")
+                    fo.write(f"source_digest: {kernel_source_digest(tag)}\n")
                     fo.write(f"hbm_bytes_per_launch: {fetch + write:.6g}\n")
                 print("wrote", path)
 
@@ -368,7 +376,7 @@ def main():
         # fraction of the attainable roofline: the faster of the HBM and matrix-core bounds
         "attainable_frac": round(max(nbytes / (HBM_PEAK_GBS * 1e9),
                                      flops / (MFMA_BF16_PEAK_TFS * 1e12)) / (ms * 1e-3), 4),
-        "source_digest": kernel_source_digest(),
+        "source_digest": kernel_source_digest("kda_chunk_fwd"),
     }
 
     result = {
