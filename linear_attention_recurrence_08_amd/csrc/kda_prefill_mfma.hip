@@ -168,6 +168,7 @@ struct Shared {
     float ec[8][D];            // e^{Gam_C} (stage A -> stage S, tile % 8)
 };
 
+template <bool PRIO_A>
 __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     __shared__ Shared sh;
 
@@ -447,6 +448,10 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     // unchanged and store nothing.
     const int64_t nsteps = ntiles + (ntiles & 1);
     if (role == 1) {
+        // with most CUs busy, stage A paces the period (its loads and exponentials start each
+        // tile): its waves then win issue ties against the other two roles on their SIMD (for a
+        // few workgroups the chain through stage B paces it instead, and this would slow it)
+        if (PRIO_A) __builtin_amdgcn_s_setprio(1);
         Raw R0, R1;
         load_tile(R0);     // tile 0
         load_tile(R1);     // tile 1
@@ -536,7 +541,11 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s) {
     const int64_t grid = a.N * a.H * (D / BV);
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kda_prefill_mfma_kernel, dim3((unsigned)grid), dim3(NT), 0, s, a);
+    if (grid >= 128)       // at least half of the 256 CUs hold a workgroup
+        hipLaunchKernelGGL(kda_prefill_mfma_kernel<true>, dim3((unsigned)grid), dim3(NT), 0, s, a);
+    else
+        hipLaunchKernelGGL(kda_prefill_mfma_kernel<false>, dim3((unsigned)grid), dim3(NT), 0, s,
+                           a);
     return hipGetLastError();
 }
 
