@@ -444,6 +444,9 @@ def _check_front(out, ref, dt, label):
     ([40, 40], 2, 64, 32, "f32", True),
     ([17, 1, 30], 2, 16, 48, "f32", False),
     ([3, 50], 4, 128, 64, "f32", True),
+    # full-width heads in float32 (four-token register sets), and bf16 with dk != dv
+    ([70, 33, 0, 64], 2, 128, 128, "f32", True),
+    ([96, 7, 64], 3, 64, 128, "bf16", False),
 ])
 def test_frontend_small(oracle_mod, lens, H, dk, dv, dt, state):
     dev = _dev()
