@@ -12,7 +12,9 @@ replace).  An `output_gate` object times the output stage (per-head RMSNorm time
 gate; 3 x 256 B per (token, head) in bf16) on the same [4096, 96, 128] shape, and
 `decode.gated` the decode step with that stage fused.  A `frontend` object times the input stage
 (short convolution, Swish, L2 norm, sigmoid beta, bounded log-decay: reads 3 dk + dv values and
-beta's logit, writes as many per (token, head)) on the same token and head count.
+beta's logit, writes as many per (token, head)) on the same token and head count.  A `varlen`
+object times the prefill on the variable-length batch (16 sequences of 1,024-16,384 tokens with
+initial states, packed with cu_seqlens).
 
 Roofline: algorithmic bytes per launch divided by the kernel's average duration, measured with
 HIP events recorded on the stream the kernels are launched on, against MI355X's 8 TB/s HBM.
@@ -47,6 +49,7 @@ CHUNK = 16
 PREFILL_WORKLOADS = ("prefill_T4096_H96_d128_bf16", "varlen_16seq_H96_d128_bf16",
                      "long_T131072_H96_d128_bf16", "tiny_T64_H2_d32_f32")
 DECODE_WORKLOAD = "decode_N256_H96_d128_bf16"
+VARLEN_WORKLOAD = "varlen_16seq_H96_d128_bf16"
 
 
 def _esize(dtype):
@@ -310,6 +313,7 @@ def main():
     ap.add_argument("--no-output-gate", action="store_true")
     ap.add_argument("--no-frontend", action="store_true")
     ap.add_argument("--no-chunk64", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="run a 1 GiB calibration copy and 3 launches of each kernel (for "
@@ -429,6 +433,34 @@ def main():
                          "algorithmic_bytes_per_launch": nbytes},
         }
         del o_c, hT_c
+
+    # ---------------- variable-length batch: 16 sequences of 1,024-16,384 tokens ----------------
+    if not args.no_varlen and args.workload != VARLEN_WORKLOAD:
+        xv = inputs.make_workload(VARLEN_WORKLOAD)
+        xvd = xv.to(dev)
+        vviews = xvd.call_views()
+        ov = torch.empty_like(xvd.v)
+        hTv = torch.empty((xv.num_seqs, xv.H, xv.dk, xv.dv), dtype=torch.float32, device=dev)
+
+        def prefill_varlen():
+            kda_chunk_fwd(*vviews, h0=xvd.h0, cu_seqlens=xvd.cu_seqlens, o=ov, hT=hTv)
+
+        vsteps = max(3, args.steps // 10)
+        vms, _ = time_launches(prefill_varlen, vsteps, 1, stream)
+        vbytes = prefill_bytes(xv)
+        lens = [e - s for s, e in xv.seq_bounds()]
+        result["varlen"] = {
+            "workload": VARLEN_WORKLOAD, "num_seqs": xv.num_seqs, "total_tokens": xv.total_tokens,
+            "min_len": min(lens), "max_len": max(lens), "steps": vsteps,
+            "ms_per_step": round(vms, 4), "value": round(xv.total_tokens / (vms * 1e-3), 1),
+            "unit": "tokens/s",
+            "roofline": {"bound": "hbm", "achieved": round(vbytes / (vms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(vbytes / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": vbytes},
+        }
+        del xv, xvd, vviews, ov, hTv
+        torch.cuda.empty_cache()
 
     # ---------------- prefill with state snapshots ----------------
     if not args.no_snapshots:

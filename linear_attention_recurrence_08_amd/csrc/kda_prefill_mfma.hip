@@ -18,7 +18,8 @@
 //
 // Mapping to gfx950.  One workgroup of 12 waves owns one (sequence, head, 64-column slice of dv);
 // the two slices of a head are dispatched to the same XCD so their shared q/k/g reads meet in
-// that XCD's L2.  Each wave keeps one role for the whole sequence, and the work of a tile runs
+// that XCD's L2, and in a variable-length batch of up to 64 sequences the longest sequences are
+// dispatched first (the short ones fill the tail).  Each wave keeps one role for the whole sequence, and the work of a tile runs
 // as a software pipeline with a single workgroup barrier per period; period q holds
 //   stage A (waves 4-7) for tile q: wave s loads key channels [32s, 32s+32) of q, k, g and value
 //      columns [16s, 16s+16) of the slice through buffer resources, runs the cumulative
@@ -57,6 +58,7 @@ constexpr int C = 16;      // tile tokens
 constexpr int D = 128;     // dk = dv
 constexpr int BV = 64;     // dv columns per workgroup
 constexpr int NT = 768;    // threads per workgroup (12 waves: 4 per stage)
+constexpr int kLptMaxSeqs = 64;   // varlen batches up to this many sequences run longest first
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float L2E_HI = 1.4453125f;          // bf16(log2 e)
 constexpr float L2E_LO = -0.00262451171875f;  // bf16(log2 e - L2E_HI)
@@ -182,7 +184,26 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     int64_t p;
     int slice;
     map_workgroup(blockIdx.x, a.N * H, p, slice);
-    const int64_t n = p / H, h = p % H;
+    const int64_t h = p % H;
+    int64_t n = p / H;
+    if (a.cu && a.N > 1 && a.N <= kLptMaxSeqs) {
+        // longest first: pair index p / H is a rank in the order of decreasing length (ties by
+        // index), so the longest sequences are dispatched first and the short ones fill the tail
+        __shared__ int lpt_seq;
+        const int N = (int)a.N, r = (int)n;
+        for (int i = tid; i < N; i += NT) {
+            const int li = a.cu[i + 1] - a.cu[i];
+            int rank = 0;
+            for (int jx = 0; jx < N; ++jx) {
+                const int lj = a.cu[jx + 1] - a.cu[jx];
+                rank += (lj > li || (lj == li && jx < i)) ? 1 : 0;
+            }
+            if (rank == r) lpt_seq = i;
+        }
+        __syncthreads();
+        n = lpt_seq;
+        p = n * H + h;                                   // the state's (sequence, head) index
+    }
     int64_t bos, eos;
     if (a.cu) { bos = a.cu[n]; eos = a.cu[n + 1]; }
     else { bos = n * a.T; eos = bos + a.T; }
