@@ -56,7 +56,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int C = 16;      // tile tokens
 constexpr int D = 128;     // dk = dv
-constexpr int BV = 64;     // dv columns per workgroup
 constexpr int NT = 768;    // threads per workgroup (12 waves: 4 per stage)
 constexpr int kLptMaxSeqs = 64;   // varlen batches up to this many sequences run longest first
 constexpr float LOG2E = 1.4426950408889634f;
@@ -118,8 +117,14 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // (workgroup index) -> (pair index p = n * H + head, slice) with both slices of a pair on one XCD
-// (workgroups are dealt to the 8 XCDs round-robin by index).
-__device__ __forceinline__ void map_workgroup(int64_t b, int64_t pairs, int64_t& p, int& slice) {
+// (workgroups are dealt to the 8 XCDs round-robin by index); one slice per pair: p = b.
+__device__ __forceinline__ void map_workgroup(int64_t b, int64_t pairs, int nslice, int64_t& p,
+                                              int& slice) {
+    if (nslice == 1) {
+        p = b;
+        slice = 0;
+        return;
+    }
     const int64_t full = (pairs / 8) * 16;
     if (b < full) {
         const int64_t xcd = b % 8, j = b / 8;
@@ -133,46 +138,53 @@ __device__ __forceinline__ void map_workgroup(int64_t b, int64_t pairs, int64_t&
 }
 
 // Raw inputs of one tile for one stage-A lane: token ln, key channels 32s + 16hh + 4lg + r,
-// value columns 16s + 4lg + r of the slice, beta of token ln.  They are read through buffer
+// value columns 64m + 16s + 4lg + r of the slice (m < slice width / 64), beta of token ln.  They are read through buffer
 // resources whose record count ends at the sequence's last token, so a token past the end (and
 // every token of a tile past the end) reads as zero: with beta = 0 and k = v = 0 it neither
 // writes the state nor reaches a stored output, and with g = 0 it does not decay the state.
 struct Raw {
-    uint2 q0, q1, k0, k1, g0, g1, v;
+    uint2 q0, q1, k0, k1, g0, g1, v[2];
     uint32_t b;   // raw bf16 bits of beta in the low half
 };
 
 // Stage-to-stage buffers, grouped by hand-off so that one dynamic base address reaches every
-// member of a group.
+// member of a group.  NS = slice width / 64 strips of 16 columns per stage-S wave; with two, P Ut
+// travels as bf16 so that LDS still holds the pipeline (it is added to o, which is bf16 anyway).
+template <int NS> struct PutOf { typedef f32x4 T; };
+template <> struct PutOf<2> { typedef uint2 T; };
+template <int NS>
 struct FromA {                 // stage A -> stages B1 and B2 (indexed by tile % 4)
     bf16x8 kp[4][64];          // token-major Kp per 32-channel k-step (operand fragments)
     bf16x8 kd[4][64];          // token-major Kd
     bf16x8 qp[4][64];          // token-major Qp
     f32x4 qpf[8][64];          // Qp in float32 as acc(Qp^T) per 16-channel block (C input)
-    uint2 vraw[4][64];         // token-major V per 16-column strip (A operand of the transpose)
+    uint2 vraw[4 * NS][64];    // token-major V per 16-column strip (A operand of the transpose)
     float beta[C];
 };
 struct FromB1 {                // stage B1 -> stage B2 (indexed by tile % 2)
     uint2 tbt[64];             // acc((T Diag(beta))^T) as bf16
     uint2 y3[64];              // acc((P T Diag(beta))^T) as bf16
 };
+template <int NS>
 struct FromB {                 // stage B2 -> stage S (indexed by tile % 2)
     uint2 kdc[8][64];          // channel-major Kd per block (A operand of Kd^T U)
     bf16x8 w[4][64];           // A operands of W per 32-channel k-step
     bf16x8 qpp[4][64];         // A operands of Qpp per 32-channel k-step
-    f32x4 ut[4][64];           // Ut per strip (accumulator fragments)
-    f32x4 put[4][64];          // P Ut per strip
+    f32x4 ut[4 * NS][64];      // Ut per strip (accumulator fragments)
+    typename PutOf<NS>::T put[4 * NS][64];   // P Ut per strip
 };
+template <int NS>
 struct Shared {
-    FromA a[4];
-    FromB b[2];
+    FromA<NS> a[4];
+    FromB<NS> b[2];
     FromB1 b1[2];
     float ec[8][D];            // e^{Gam_C} (stage A -> stage S, tile % 8)
 };
 
-template <bool PRIO_A>
+template <bool PRIO_A, int BVT>
 __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
-    __shared__ Shared sh;
+    constexpr int NS = BVT / 64;       // 16-column strips per stage-S wave
+    __shared__ Shared<NS> sh;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -183,7 +195,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
 
     int64_t p;
     int slice;
-    map_workgroup(blockIdx.x, a.N * H, p, slice);
+    map_workgroup(blockIdx.x, a.N * H, D / BVT, p, slice);
     const int64_t h = p % H;
     int64_t n = p / H;
     if (a.cu && a.N > 1 && a.N <= kLptMaxSeqs) {
@@ -235,26 +247,37 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     bf16x4 onesA;    // all ones (A operand): column c of the product is Gam_C of channel c
     for (int j = 0; j < 4; ++j) onesA[j] = (__bf16)1.f;
 
-    // ---- stage S state: rows 16 mb + 4 lg + r, column col of this workgroup's slice ----
-    const int64_t col = (int64_t)slice * BV + 16 * s + ln;
+    // ---- stage S state: strip m holds rows 16 mb + 4 lg + r, column col + 64 m of this
+    //      workgroup's slice ----
+    const int64_t col = (int64_t)slice * BVT + 16 * s + ln;
     const int64_t sbase = p * (int64_t)(D * D);
-    f32x4 S[8];
+    // (declared here, set and used by the stage-S waves only, so that it occupies registers in
+    // their branch alone)
+    f32x4 S[NS][8];
+    // the state strips to or from a [dk, dv] float32 matrix (src == nullptr: zeros)
+    auto state_in = [&](const float* src) {
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) S[mb] = zero4();
-    if (role == 0 && a.h0) {
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[mb][r] = a.h0[sbase + (int64_t)(16 * mb + 4 * lg + r) * D + col];
-    }
-    if (ntiles == 0) {
-        if (role == 0 && a.hT) {
+        for (int m = 0; m < NS; ++m)
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    a.hT[sbase + (int64_t)(16 * mb + 4 * lg + r) * D + col] = S[mb][r];
+                    S[m][mb][r] = src ? src[(int64_t)(16 * mb + 4 * lg + r) * D + col + 64 * m]
+                                      : 0.f;
+    };
+    auto state_out = [&](float* dst) {
+#pragma unroll
+        for (int m = 0; m < NS; ++m)
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dst[(int64_t)(16 * mb + 4 * lg + r) * D + col + 64 * m] = S[m][mb][r];
+    };
+    if (ntiles == 0) {
+        if (role == 0 && a.hT) {
+            state_in(a.h0 ? a.h0 + sbase : nullptr);
+            state_out(a.hT + sbase);
         }
         return;
     }
@@ -263,7 +286,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     //      resources start at that token's head row (scalar base) and end after the last token
     //      of the sequence that the tile holds; lanes add a fixed byte offset ----
     const int64_t chan0 = 32 * s + 4 * lg;
-    const int64_t vcol0 = (int64_t)slice * BV + 16 * s + 4 * lg;
+    const int64_t vcol0 = (int64_t)slice * BVT + 16 * s + 4 * lg;
     const int64_t len = eos - bos;
     const int64_t row_bytes = H * D * 2;                       // one token, all heads
     const uint32_t vo_qkg = (uint32_t)(ln * row_bytes + chan0 * 2);
@@ -296,20 +319,21 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         R.k1 = ld8(rk, vo_qkg + 32);
         R.g0 = ld8(rg, vo_qkg);
         R.g1 = ld8(rg, vo_qkg + 32);
-        R.v = ld8(rv, vo_v);
+#pragma unroll
+        for (int m = 0; m < NS; ++m) R.v[m] = ld8(rv, vo_v + 128 * m);
         R.b = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, vo_b, 0, 0);
         ++ld_tile;
     };
 
     // Buffer indices of a tile: FromA by tile % 4, FromB and FromB1 by tile % 2, ec by tile % 8.
-    auto fa = [&](int64_t tile) -> FromA& { return sh.a[(uint32_t)tile & 3u]; };
-    auto fb = [&](int64_t tile) -> FromB& { return sh.b[(uint32_t)tile & 1u]; };
+    auto fa = [&](int64_t tile) -> FromA<NS>& { return sh.a[(uint32_t)tile & 3u]; };
+    auto fb = [&](int64_t tile) -> FromB<NS>& { return sh.b[(uint32_t)tile & 1u]; };
     auto fb1 = [&](int64_t tile) -> FromB1& { return sh.b1[(uint32_t)tile & 1u]; };
     auto ecb = [&](int64_t tile) -> float* { return sh.ec[(uint32_t)tile & 7u]; };
 
     // stage A for tile `tile`
     auto stage_a = [&](int64_t tile, const Raw& R) {
-        FromA& A = fa(tile);
+        FromA<NS>& A = fa(tile);
         float* ec = ecb(tile);
         const float bt = __uint_as_float(R.b << 16);
         const bf16x8 ga = cat8(as_bf4(R.g0), as_bf4(R.g1));
@@ -346,7 +370,8 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         A.kp[s][lane] = cat8(Kpb[0], Kpb[1]);
         A.qp[s][lane] = cat8(Qpb[0], Qpb[1]);
         A.kd[s][lane] = cat8(Kdb[0], Kdb[1]);
-        A.vraw[s][lane] = R.v;
+#pragma unroll
+        for (int m = 0; m < NS; ++m) A.vraw[s + 4 * m][lane] = R.v[m];
     };
 
     // stage B1 for tile `tile`: A, A^T, P^T over all 128 channels and the inverse T, in two
@@ -355,7 +380,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     // per period; the two waves of a pair compute identical results.
     struct B1Carry { f32x4 N4, N4t, Gt, Pt, brow; float bcol; };
     auto stage_b1a = [&](int64_t tile) -> B1Carry {
-        const FromA& A = fa(tile);
+        const FromA<NS>& A = fa(tile);
         f32x4 Am = zero4(), At = zero4(), Pt = zero4();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -409,8 +434,8 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     // stage B2 for tile `tile`, wave 8 + s: W and Qpp for channels [32s, 32s+32), Ut and PUt for
     // columns [16s, 16s+16), and the channel-major Kd blocks of those channels
     auto stage_b2 = [&](int64_t tile) {
-        const FromA& A = fa(tile);
-        FromB& B = fb(tile);
+        const FromA<NS>& A = fa(tile);
+        FromB<NS>& B = fb(tile);
         const uint2 tbu = fb1(tile).tbt[lane], y3u = fb1(tile).y3[lane];
         const bf16x4 TbTb = as_bf4(tbu), Y3b = as_bf4(y3u);
         const bf16x4 nY3b = as_bf4(make_uint2(y3u.x ^ 0x80008000u, y3u.y ^ 0x80008000u));
@@ -429,36 +454,64 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         }
         B.w[s][lane] = cat8(Wf[0], Wf[1]);
         B.qpp[s][lane] = cat8(Qf[0], Qf[1]);
-        const bf16x4 vcs = lds_tr16(&A.vraw[s][src]);  // column-major V
-        B.ut[s][lane] = mma16(TbTb, vcs, zero4());     // Tb V
-        B.put[s][lane] = mma16(Y3b, vcs, zero4());     // P Tb V
+#pragma unroll
+        for (int m = 0; m < NS; ++m) {
+            const bf16x4 vcs = lds_tr16(&A.vraw[s + 4 * m][src]);  // column-major V
+            B.ut[s + 4 * m][lane] = mma16(TbTb, vcs, zero4());     // Tb V
+            const f32x4 pu = mma16(Y3b, vcs, zero4());             // P Tb V
+            if constexpr (NS == 1) B.put[s][lane] = pu;
+            else B.put[s + 4 * m][lane] = as_u2(bf4(pu));
+        }
     };
 
-    // stage S for tile `tile`: strip s; returns the token-major o fragment (stored by the caller)
-    auto stage_s = [&](int64_t tile) -> bf16x4 {
-        const FromB& B = fb(tile);
+    // stage S for tile `tile`: strips s + 4 m; leaves the token-major o fragments in Ot
+    auto stage_s = [&](int64_t tile, bf16x4 (&Ot)[NS]) {
+        const FromB<NS>& B = fb(tile);
         const float* ec = ecb(tile);
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-            S[mb] *= *reinterpret_cast<const f32x4*>(&ec[16 * mb + 4 * lg]);   // St
-        f32x4 XW = zero4(), XQ = zero4();
+        for (int mb = 0; mb < 8; ++mb) {
+            const f32x4 e = *reinterpret_cast<const f32x4*>(&ec[16 * mb + 4 * lg]);
+#pragma unroll
+            for (int m = 0; m < NS; ++m) S[m][mb] *= e;                         // St
+        }
+        // k-steps outside, strips inside: one W / Qpp fragment pair is live at a time
+        f32x4 XW[NS], XQ[NS];
+#pragma unroll
+        for (int m = 0; m < NS; ++m) XW[m] = XQ[m] = zero4();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 sb = cat8(bf4(S[2 * ks]), bf4(S[2 * ks + 1]));
-            XW = mma32(B.w[ks][lane], sb, XW);
-            XQ = mma32(B.qpp[ks][lane], sb, XQ);
-        }
-        const f32x4 U = B.ut[s][lane] - XW;
-        const f32x4 O = XQ + B.put[s][lane];
-        const bf16x4 Ub = bf4(U);
+            const bf16x8 wf = B.w[ks][lane], qf = B.qpp[ks][lane];
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb) S[mb] = mma16(as_bf4(B.kdc[mb][lane]), Ub, S[mb]);
-        return bf4(mma16(bf4(O), eye, zero4()));    // token-major o
+            for (int m = 0; m < NS; ++m) {
+                const bf16x8 sb = cat8(bf4(S[m][2 * ks]), bf4(S[m][2 * ks + 1]));
+                XW[m] = mma32(wf, sb, XW[m]);
+                XQ[m] = mma32(qf, sb, XQ[m]);
+            }
+        }
+        bf16x4 Ub[NS];
+#pragma unroll
+        for (int m = 0; m < NS; ++m) {
+            Ub[m] = bf4(B.ut[s + 4 * m][lane] - XW[m]);                          // U
+            f32x4 O;
+            if constexpr (NS == 1) O = XQ[m] + B.put[s][lane];
+            else O = XQ[m] + unpack4(B.put[s + 4 * m][lane]);
+            Ot[m] = bf4(mma16(bf4(O), eye, zero4()));    // token-major o
+        }
+        // S <- St + Kd^T U, blocks outside and strips inside: each Kd fragment serves both strips
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+            const bf16x4 kdf = as_bf4(B.kdc[mb][lane]);
+#pragma unroll
+            for (int m = 0; m < NS; ++m) S[m][mb] = mma16(kdf, Ub[m], S[m][mb]);
+        }
     };
-    auto store_o = [&](int64_t tile, bf16x4 Ot, bool masked) {
+    auto store_o = [&](int64_t tile, const bf16x4 (&Ot)[NS], bool masked) {
         const int64_t t0 = bos + tile * C;
         bf16_t* dst = o + ((t0 + ln) * H + h) * D + vcol0;
-        if (!masked || t0 + ln < eos) *reinterpret_cast<uint2*>(dst) = as_u2(Ot);
+        if (!masked || t0 + ln < eos) {
+#pragma unroll
+            for (int m = 0; m < NS; ++m) *reinterpret_cast<uint2*>(dst + 64 * m) = as_u2(Ot[m]);
+        }
     };
 
     // Period q (one barrier after each) runs A(q), the first half of B1(q-1), the second half of
@@ -517,6 +570,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             lds_barrier();
         }
     } else {
+        state_in(a.h0 ? a.h0 + sbase : nullptr);
         lds_barrier();
         lds_barrier();
         lds_barrier();
@@ -528,45 +582,43 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         // tiles whose 16 tokens all lie inside the sequence store without a mask
         const int64_t nfull = (eos - bos) / C;
         int64_t i = 0;
+        bf16x4 Ot[NS];
         for (; i < nfull; ++i) {
-            store_o(i, stage_s(i), false);
+            stage_s(i, Ot);
+            store_o(i, Ot, false);
             if (i + 1 == snap_at) {
-                float* dst = a.snaps + (snap_idx * H + h) * (int64_t)(D * D);
-#pragma unroll
-                for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        dst[(int64_t)(16 * mb + 4 * lg + r) * D + col] = S[mb][r];
+                state_out(a.snaps + (snap_idx * H + h) * (int64_t)(D * D));
                 ++snap_idx;
                 snap_at += a.snap_tiles;
             }
             lds_barrier();
         }
         for (; i < nsteps; ++i) {
-            store_o(i, stage_s(i), true);
+            stage_s(i, Ot);
+            store_o(i, Ot, true);
             lds_barrier();
         }
-    }
-
-    if (role == 0 && a.hT) {
-#pragma unroll
-        for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                a.hT[sbase + (int64_t)(16 * mb + 4 * lg + r) * D + col] = S[mb][r];
+        if (a.hT) state_out(a.hT + sbase);
     }
 }
 
 }  // namespace
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s) {
-    const int64_t grid = a.N * a.H * (D / BV);
-    if (grid <= 0) return hipSuccess;
-    if (grid >= 128)       // at least half of the 256 CUs hold a workgroup
-        hipLaunchKernelGGL(kda_prefill_mfma_kernel<true>, dim3((unsigned)grid), dim3(NT), 0, s, a);
-    else
-        hipLaunchKernelGGL(kda_prefill_mfma_kernel<false>, dim3((unsigned)grid), dim3(NT), 0, s,
-                           a);
+    const int64_t pairs = a.N * a.H;
+    if (pairs <= 0) return hipSuccess;
+    if (pairs >= 256) {
+        // every CU is busy with one workgroup per (sequence, head): a workgroup takes all 128
+        // columns, so stages A and B1 run once per head instead of once per 64-column half
+        hipLaunchKernelGGL((kda_prefill_mfma_kernel<true, 128>), dim3((unsigned)pairs), dim3(NT),
+                           0, s, a);
+    } else if (2 * pairs >= 128) {   // at least half of the 256 CUs hold a workgroup
+        hipLaunchKernelGGL((kda_prefill_mfma_kernel<true, 64>), dim3((unsigned)(2 * pairs)),
+                           dim3(NT), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((kda_prefill_mfma_kernel<false, 64>), dim3((unsigned)(2 * pairs)),
+                           dim3(NT), 0, s, a);
+    }
     return hipGetLastError();
 }
 

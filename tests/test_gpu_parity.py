@@ -81,6 +81,9 @@ SMALL = [
     ([33, 19], 2, 16, 128, "bf16", 0.1, "sigmoid_shiftm1", True),
     ([64], 2, 32, 32, "f32", None, "sigmoid", False),
     ([29], 1, 112, 48, "f32", 0.1, "sigmoid", False),
+    # 256 or more (sequence, head) pairs: one workgroup per head takes all 128 columns
+    ([37, 0, 16, 5, 81, 1, 130, 64], 32, 128, 128, "bf16", 0.1, "sigmoid", True),
+    ([64, 64, 64, 64], 64, 128, 128, "bf16", None, "sigmoid", False),
 ]
 
 
@@ -275,6 +278,7 @@ SNAP_CASES = [
     ([70, 33, 160], 2, 128, 128, "f32", 32, True),
     ([100, 64], 2, 64, 32, "f32", 16, True),
     ([128], 2, 32, 96, "bf16", 64, False),
+    ([37, 0, 64, 15, 130, 128, 33, 48], 32, 128, 128, "bf16", 16, True),   # 256 pairs
 ]
 
 
