@@ -17,10 +17,13 @@
 // as the finite product (I - N)(I + N^2)(I + N^4)(I + N^8) with N = Diag(beta) A (N^16 = 0).
 //
 // Mapping to gfx950.  One workgroup of 12 waves owns one (sequence, head, 64-column slice of dv);
-// the two slices of a head are dispatched to the same XCD so their shared q/k/g reads meet in
+// when the (sequence, head) pairs alone fill the chip, one workgroup owns a whole head (a
+// 128-column slice: each stage-S wave carries two strips, and stages A and B1 run once per head).
+// The two slices of a head are dispatched to the same XCD so their shared q/k/g reads meet in
 // that XCD's L2, and in a variable-length batch of up to 64 sequences the longest sequences are
-// dispatched first (the short ones fill the tail).  Each wave keeps one role for the whole sequence, and the work of a tile runs
-// as a software pipeline with a single workgroup barrier per period; period q holds
+// dispatched first (the short ones fill the tail).  Each wave keeps one role for the whole
+// sequence, and the work of a tile runs as a software pipeline with a single workgroup barrier
+// per period; period q holds
 //   stage A (waves 4-7) for tile q: wave s loads key channels [32s, 32s+32) of q, k, g and value
 //      columns [16s, 16s+16) of the slice through buffer resources, runs the cumulative
 //      log-decay as a product with a triangular 0/1 matrix, and forms the decayed operands Kp,
@@ -30,8 +33,9 @@
 //      10-11 odd ones, so each SIMD carries half an inverse per period;
 //   stage B2 (waves 8-11, beside B1) for tile q-3: W and Qpp for key channels [32s, 32s+32), Ut
 //      and PUt for columns [16s, 16s+16), and the channel-major Kd blocks the carry consumes;
-//   stage S (waves 0-3) for tile q-4: wave s carries its 128 x 16 strip of S, which lives in
-//      registers as eight 16x16 float32 accumulator blocks for the whole sequence, and writes o.
+//   stage S (waves 0-3) for tile q-4: wave s carries its 128 x 16 strip of S (two strips in the
+//      128-column slice), which lives in registers as eight 16x16 float32 accumulator blocks per
+//      strip for the whole sequence, and writes o.
 // Three waves share each SIMD.  Loads run two tiles ahead of their use.  All products use
 // v_mfma_f32_16x16x{16,32}_bf16.  Token-major -> channel-major changes of layout are LDS transpose
 // reads where the data already sits in LDS, and products with 0/1 selector matrices on the
