@@ -185,7 +185,8 @@ struct Shared {
     float ec[8][D];            // e^{Gam_C} (stage A -> stage S, tile % 8)
 };
 
-template <bool PRIO_A, int BVT>
+// PRIO_ROLE: the role whose waves win issue ties on their SIMD (1: stage A, 2: stage B).
+template <int PRIO_ROLE, int BVT>
 __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     constexpr int NS = BVT / 64;       // 16-column strips per stage-S wave
     __shared__ Shared<NS> sh;
@@ -527,9 +528,8 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     const int64_t nsteps = ntiles + (ntiles & 1);
     if (role == 1) {
         // with most CUs busy, stage A paces the period (its loads and exponentials start each
-        // tile): its waves then win issue ties against the other two roles on their SIMD (for a
-        // few workgroups the chain through stage B paces it instead, and this would slow it)
-        if (PRIO_A) __builtin_amdgcn_s_setprio(1);
+        // tile), and its waves then win issue ties against the other two roles on their SIMD
+        if (PRIO_ROLE == 1) __builtin_amdgcn_s_setprio(1);
         Raw R0, R1;
         load_tile(R0);     // tile 0
         load_tile(R1);     // tile 1
@@ -550,6 +550,8 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         lds_barrier();
         lds_barrier();
     } else if (role == 2) {
+        // with few workgroups the chain through stage B paces the period instead
+        if (PRIO_ROLE == 2) __builtin_amdgcn_s_setprio(1);
         // every stage-B wave runs B2 of period q (tile q - 3) for its channel group, and its pair
         // alternates the two halves of B1 for the tiles of its parity
         const int par = s >> 1;            // tiles of this parity
@@ -614,13 +616,13 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s) {
     if (pairs >= 256) {
         // every CU is busy with one workgroup per (sequence, head): a workgroup takes all 128
         // columns, so stages A and B1 run once per head instead of once per 64-column half
-        hipLaunchKernelGGL((kda_prefill_mfma_kernel<true, 128>), dim3((unsigned)pairs), dim3(NT),
-                           0, s, a);
+        hipLaunchKernelGGL((kda_prefill_mfma_kernel<1, 128>), dim3((unsigned)pairs), dim3(NT), 0,
+                           s, a);
     } else if (2 * pairs >= 128) {   // at least half of the 256 CUs hold a workgroup
-        hipLaunchKernelGGL((kda_prefill_mfma_kernel<true, 64>), dim3((unsigned)(2 * pairs)),
+        hipLaunchKernelGGL((kda_prefill_mfma_kernel<1, 64>), dim3((unsigned)(2 * pairs)),
                            dim3(NT), 0, s, a);
     } else {
-        hipLaunchKernelGGL((kda_prefill_mfma_kernel<false, 64>), dim3((unsigned)(2 * pairs)),
+        hipLaunchKernelGGL((kda_prefill_mfma_kernel<2, 64>), dim3((unsigned)(2 * pairs)),
                            dim3(NT), 0, s, a);
     }
     return hipGetLastError();
