@@ -1,0 +1,72 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU contract, per-kernel source digests and the
+rocprofv3 summaries it writes from counter CSVs."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=ROOT)
+    assert r.returncode != 0
+    assert "one GPU" in r.stdout + r.stderr
+
+
+def test_source_digests_are_per_kernel():
+    tags = ["kda_chunk_fwd_prefill_T4096_H96_d128_bf16", "kda_decode_decode_N256_H96_d128_bf16",
+            "kda_decode_step_gated_decode_N256_H96_d128_bf16",
+            "kda_output_gate_T4096_H96_d128_bf16", "kda_frontend_T4096_H96_d128_bf16"]
+    d = {t: bench.kernel_source_digest(t) for t in tags}
+    # the gated decode is the decode kernel; the others are distinct sources
+    assert d[tags[1]] == d[tags[2]]
+    assert len({d[tags[0]], d[tags[1]], d[tags[3]], d[tags[4]]}) == 4
+    assert all(len(v) == 16 for v in d.values())
+
+
+def _write_counters(path, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_summaries_scale_by_the_copy_and_add_kernels_of_a_call(tmp_path, monkeypatch):
+    # counters in KiB per dispatch: the 1 GiB calibration copy reads 2 GiB worth of FETCH_SIZE
+    # (factor 2) and 1 GiB of WRITE_SIZE (factor 1); the input stage's two kernels are summed
+    gib_kib = (1 << 30) / 1024.0
+    conv = "void kda::(anonymous namespace)::kda_frontend_conv_kernel<unsigned short, true>(x)"
+    state = "void kda::(anonymous namespace)::kda_frontend_state_kernel<unsigned short>(x)"
+    fetch = [{"Kernel_Name": "elementwise_kernel", "Counter_Name": "FETCH_SIZE",
+              "Counter_Value": 2 * gib_kib}]
+    fetch += [{"Kernel_Name": conv, "Counter_Name": "FETCH_SIZE", "Counter_Value": 2000.0}] * 3
+    fetch += [{"Kernel_Name": state, "Counter_Name": "FETCH_SIZE", "Counter_Value": 20.0}] * 3
+    write = [{"Kernel_Name": "elementwise_kernel", "Counter_Name": "WRITE_SIZE",
+              "Counter_Value": gib_kib}]
+    write += [{"Kernel_Name": conv, "Counter_Name": "WRITE_SIZE", "Counter_Value": 500.0}] * 3
+    write += [{"Kernel_Name": state, "Counter_Name": "WRITE_SIZE", "Counter_Value": 5.0}] * 3
+    _write_counters(str(tmp_path / "f" / "fetch_counter_collection.csv"), fetch)
+    _write_counters(str(tmp_path / "w" / "write_counter_collection.csv"), write)
+    out = tmp_path / "repo"
+    (out / "profiles").mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(out))
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda tag: "0123456789abcdef")
+    bench.summarize([str(tmp_path / "f"), str(tmp_path / "w")], "test command")
+    txt = open(out / "profiles" / "kda_frontend_T4096_H96_d128_bf16_hbm_traffic.md").read()
+    want = (2000.0 + 20.0) * 1024 / 2 + (500.0 + 5.0) * 1024 / 1
+    line = [l for l in txt.splitlines() if l.startswith("hbm_bytes_per_launch:")][0]
+    assert float(line.split(":")[1]) == pytest.approx(want, rel=1e-5)
+    assert "command: `test command`" in txt
+    # a summary is used only while its digest matches the current sources
+    assert bench.recorded_traffic("kda_frontend_T4096_H96_d128_bf16") == pytest.approx(
+        want, rel=1e-5)
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda tag: "fedcba9876543210")
+    assert bench.recorded_traffic("kda_frontend_T4096_H96_d128_bf16") is None
