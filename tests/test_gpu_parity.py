@@ -84,10 +84,20 @@ SMALL = [
     # 256 or more (sequence, head) pairs: one workgroup per head takes all 128 columns
     ([37, 0, 16, 5, 81, 1, 130, 64], 32, 128, 128, "bf16", 0.1, "sigmoid", True),
     ([64, 64, 64, 64], 64, 128, 128, "bf16", None, "sigmoid", False),
+    # varlen batches around the 64-sequence limit of the longest-first dispatch (lengths 0..40
+    # with ties): 70 sequences dispatch in index order, 64 by length rank
+    ([(7 * i) % 41 for i in range(70)], 4, 128, 128, "bf16", 0.1, "sigmoid", True),
+    ([(5 * i + 3) % 37 for i in range(64)], 4, 128, 128, "bf16", 0.1, "sigmoid", True),
+    ([(7 * i) % 41 for i in range(70)], 1, 128, 128, "bf16", 0.1, "sigmoid", True),
 ]
 
 
-@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-H{c[1]}-{c[2]}x{c[3]}-{c[4]}-{c[6]}")
+def _small_id(c):
+    lens = str(c[0]) if len(c[0]) <= 8 else f"{len(c[0])}seqs"
+    return f"{lens}-H{c[1]}-{c[2]}x{c[3]}-{c[4]}-{c[6]}"
+
+
+@pytest.mark.parametrize("case", SMALL, ids=_small_id)
 def test_small_prefill(oracle_mod, case):
     dev = _dev()
     from linear_attention_recurrence_08_amd import inputs
@@ -279,10 +289,12 @@ SNAP_CASES = [
     ([100, 64], 2, 64, 32, "f32", 16, True),
     ([128], 2, 32, 96, "bf16", 64, False),
     ([37, 0, 64, 15, 130, 128, 33, 48], 32, 128, 128, "bf16", 16, True),   # 256 pairs
+    ([(7 * i) % 41 for i in range(70)], 4, 128, 128, "bf16", 16, True),    # 70 sequences
 ]
 
 
-@pytest.mark.parametrize("case", SNAP_CASES, ids=lambda c: f"{c[0]}-{c[2]}x{c[3]}-{c[4]}-s{c[5]}")
+@pytest.mark.parametrize("case", SNAP_CASES, ids=lambda c: (
+    f"{c[0] if len(c[0]) <= 8 else f'{len(c[0])}seqs'}-{c[2]}x{c[3]}-{c[4]}-s{c[5]}"))
 def test_snapshots_small(oracle_mod, case):
     dev = _dev()
     from linear_attention_recurrence_08_amd import inputs
