@@ -69,7 +69,9 @@ enum {
     KDA_ERR_HIP = -7,         /* a HIP runtime call or kernel launch failed */
     KDA_ERR_STRIDE = -8,      /* snapshot stride not a positive multiple of 16, or (KDA_VALIDATE)
                                  snap_offsets inconsistent with the sequence lengths */
-    KDA_ERR_ALIGN = -9        /* a buffer of the output stage is not 16-byte aligned */
+    KDA_ERR_ALIGN = -9,       /* a buffer of the output stage is not 16-byte aligned */
+    KDA_ERR_WORKSPACE = -10   /* workspace NULL, smaller than the size query returns, or not
+                                 256-byte aligned */
 };
 
 /*
@@ -105,18 +107,35 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
 /*
  * kda_chunk_fwd_chunk64 -- kda_chunk_fwd computed with 64-token chunks made of four 16-token
  * sub-tiles: the state is carried once per chunk, and the chunk's 64x64 triangular system is
- * solved by blocks, the diagonal sub-tiles by forward substitution and the coupling between
- * sub-tiles as separate off-diagonal products ("What's new in Kimi K3", section "KDA in one page":
- * the per-token cost is quoted at chunk size 64; "Kimi K3's hybrid block, from first principles",
+ * solved by blocks, the diagonal sub-tiles on their own and the coupling between sub-tiles as
+ * separate off-diagonal products ("What's new in Kimi K3", section "KDA in one page": the
+ * per-token cost is quoted at chunk size 64; "Kimi K3's hybrid block, from first principles",
  * section "From linear attention to the delta rule": the cumulative log-decay over 16 tokens
  * stays within (-80, 0), so every exponent is kept within one sub-tile or made non-positive).
- * Float32 arithmetic on the vector ALUs for every supported dtype and head size; same arguments,
- * layouts, results (up to rounding) and errors as kda_chunk_fwd.
+ * bf16 with dk = dv = 128 runs on the matrix cores in two kernels: the state-independent part of
+ * every (chunk, head) in parallel, written to the workspace, then the serial carry per (sequence,
+ * head).  Other dtypes and head sizes run in float32 on the vector ALUs and need no workspace.
+ * Same arguments, layouts, results (up to rounding) and errors as kda_chunk_fwd, plus
+ *   workspace        device memory of at least kda_chunk_fwd_chunk64_workspace_bytes(...) bytes,
+ *                    256-byte aligned, owned by the caller; its contents on entry do not matter
+ *                    and are undefined on return; it may be NULL when that size is 0
+ *   workspace_bytes  its size
+ * KDA_ERR_WORKSPACE when the workspace is missing, too small or misaligned.
  */
 int kda_chunk_fwd_chunk64(const void* q, const void* k, const void* v, const void* g,
                           const void* beta, const float* h0, const int32_t* cu_seqlens,
                           int num_seqs, void* o, float* hT,
-                          int B, int T, int H, int dk, int dv, int dtype, void* stream);
+                          int B, int T, int H, int dk, int dv, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_fwd_chunk64_workspace_bytes -- bytes of workspace kda_chunk_fwd_chunk64 needs for
+ * these arguments (only whether cu_seqlens is NULL matters; its contents are not read): 0 for the
+ * float32 path; for the matrix-core path, 97 KiB per (64-token chunk, head) plus the chunk
+ * offsets of a variable-length batch.  0 as well for arguments kda_chunk_fwd_chunk64 rejects.
+ */
+size_t kda_chunk_fwd_chunk64_workspace_bytes(const int32_t* cu_seqlens, int num_seqs, int B,
+                                             int T, int H, int dk, int dv, int dtype);
 
 /*
  * kda_chunk_fwd_snapshots -- kda_chunk_fwd that also saves the state at every multiple of

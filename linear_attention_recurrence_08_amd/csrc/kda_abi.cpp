@@ -12,9 +12,25 @@
 
 #include "kda_internal.h"
 
+namespace kda {
+// the 64-token-chunk matrix-core path (bf16, dk = dv = 128)
+size_t c64_mfma_workspace_bytes(int64_t nchunks, int64_t N, int64_t H);
+hipError_t launch_prefill_c64_mfma(const PrefillArgs& a, void* workspace, int64_t nchunks,
+                                   hipStream_t s);
+}  // namespace kda
+
 namespace {
 
 bool supported_dim(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
+
+bool force_general() { return std::getenv("KDA_FORCE_GENERAL") != nullptr; }
+
+// chunks the 64-token-chunk matrix-core path provisions for (an upper bound on the sum over
+// sequences of ceil(len / 64)); -1 when the float32 path applies
+int64_t c64_mfma_chunks(bool varlen, int64_t N, int64_t B, int64_t T, int dk, int dv, int dtype) {
+    if (dtype != KDA_BF16 || dk != 128 || dv != 128 || force_general()) return -1;
+    return varlen ? T / 64 + N : B * ((T + 63) / 64);
+}
 
 // One token's row of a tensor (H * d elements) is at most 2^20 elements: the streaming kernels
 // address a few dozen consecutive rows with 32-bit byte offsets.
@@ -69,7 +85,8 @@ int check_gate_range(const void* g, int64_t count, int dtype, hipStream_t s) {
 int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
                    const float* h0, const int32_t* cu_seqlens, int num_seqs, void* o, float* hT,
                    float* snaps, const int32_t* snap_offsets, int snap_stride, int B, int T,
-                   int H, int dk, int dv, int dtype, void* stream, bool chunk64 = false) {
+                   int H, int dk, int dv, int dtype, void* stream, bool chunk64 = false,
+                   void* workspace = nullptr, size_t workspace_bytes = 0) {
     if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
     if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
     if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
@@ -91,6 +108,14 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, c
     if (want_snaps && !snaps && !cu_seqlens && N > 0 && T >= snap_stride) return KDA_ERR_NULL;
     if (N == 0 || (Ttot == 0 && !hT)) return KDA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    int64_t c64_chunks = -1;   // >= 0: the 64-token-chunk matrix-core path, with this many chunks
+    if (chunk64) {
+        c64_chunks = c64_mfma_chunks(cu_seqlens != nullptr, N, B, T, dk, dv, dtype);
+        if (c64_chunks >= 0 &&
+            (!workspace || workspace_bytes < kda::c64_mfma_workspace_bytes(c64_chunks, N, H) ||
+             (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
+            return KDA_ERR_WORKSPACE;
+    }
 
     if (validate_enabled()) {
         std::vector<int32_t> cu;
@@ -128,8 +153,9 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, c
 
     hipError_t e;
     if (chunk64)
-        e = kda::launch_prefill_c64(a, s);
-    else if (dtype == KDA_BF16 && dk == 128 && dv == 128 && !std::getenv("KDA_FORCE_GENERAL"))
+        e = c64_chunks >= 0 ? kda::launch_prefill_c64_mfma(a, workspace, c64_chunks, s)
+                            : kda::launch_prefill_c64(a, s);
+    else if (dtype == KDA_BF16 && dk == 128 && dv == 128 && !force_general())
         e = kda::launch_prefill_mfma(a, s);
     else
         e = kda::launch_prefill_general(a, s);
@@ -155,6 +181,9 @@ const char* kda_status_string(int status) {
         case KDA_ERR_STRIDE:
             return "snapshot stride must be a positive multiple of 16, with matching snap_offsets";
         case KDA_ERR_ALIGN: return "output-stage buffers must be 16-byte aligned";
+        case KDA_ERR_WORKSPACE:
+            return "workspace missing, smaller than kda_chunk_fwd_chunk64_workspace_bytes, or not "
+                   "256-byte aligned";
         default: return "unknown status";
     }
 }
@@ -169,9 +198,21 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
 int kda_chunk_fwd_chunk64(const void* q, const void* k, const void* v, const void* g,
                           const void* beta, const float* h0, const int32_t* cu_seqlens,
                           int num_seqs, void* o, float* hT,
-                          int B, int T, int H, int dk, int dv, int dtype, void* stream) {
+                          int B, int T, int H, int dk, int dv, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
     return chunk_fwd_impl(q, k, v, g, beta, h0, cu_seqlens, num_seqs, o, hT, nullptr, nullptr, 0,
-                          B, T, H, dk, dv, dtype, stream, true);
+                          B, T, H, dk, dv, dtype, stream, true, workspace, workspace_bytes);
+}
+
+size_t kda_chunk_fwd_chunk64_workspace_bytes(const int32_t* cu_seqlens, int num_seqs, int B,
+                                             int T, int H, int dk, int dv, int dtype) {
+    if ((dtype != KDA_BF16 && dtype != KDA_F32) || B < 0 || T < 0 || H <= 0 || num_seqs < 0 ||
+        !supported_dim(dk) || !supported_dim(dv) || !rows_ok(H, dk, dv) ||
+        (cu_seqlens && B != 1))
+        return 0;
+    const int64_t N = cu_seqlens ? num_seqs : B;
+    const int64_t chunks = c64_mfma_chunks(cu_seqlens != nullptr, N, B, T, dk, dv, dtype);
+    return chunks < 0 || N == 0 ? 0 : kda::c64_mfma_workspace_bytes(chunks, N, H);
 }
 
 int kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const void* g,

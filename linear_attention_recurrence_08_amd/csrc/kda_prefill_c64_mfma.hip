@@ -1,0 +1,679 @@
+// KDA prefill with 64-token chunks on the CDNA4 matrix cores: bf16 inputs, dk = dv = 128,
+// float32 state.
+//
+// Method ("What's new in Kimi K3", section "KDA in one page": the per-token cost is quoted for
+// chunks of 64, length-independent; "Kimi K3's hybrid block, from first principles", section "From
+// linear attention to the delta rule": parallel inside a chunk, recurrent across chunks, and the
+// cumulative log-decay over 16 tokens stays within (-80, 0)).  For a chunk of L = 64 tokens with
+// entering state S and Gam_t the inclusive per-channel cumsum of g from the chunk start:
+//     Kg = K.e^{Gam},  Qg = Q.e^{Gam},  Kl = K.e^{Gam_L - Gam}            (every factor <= 1)
+//     A = strict_lower(A_ij = sum_c k_ic k_jc e^{Gam_ic - Gam_jc}),  P = lower(same with q_i)
+//     Tb = (I + Diag(beta) A)^-1 Diag(beta)                              (64 x 64, unit lower)
+//     W = Tb Kg,  Ut = Tb V,  Qpp = Qg - P W,  Z = P Ut                  (independent of S)
+//     U = Ut - W S,   O = Qpp S + Z,   S <- Diag(e^{Gam_L}) S + Kl^T U   (the serial carry)
+// which is the token recurrence S_t = (I - b k k^T) Diag(e^g) S_{t-1} + b k v^T, o_t = S_t^T q_t
+// unrolled over the chunk.  Over 64 tokens Gam reaches -320, beyond float32's range for e^{-Gam},
+// so A and P are formed by 16-token sub-tile blocks: the diagonal block (s, s) with the reference
+// point at the sub-tile end (factors e^{Gam_i - Gam_end(s)} <= e^80 and e^{Gam_end(s) - Gam_j} <= 1),
+// an off-diagonal block (s, r < s) as (K_s e^{Gam - Gam_end(r)}) (K_r e^{Gam_end(r) - Gam})^T with both
+// factors <= 1.  The inverse runs by blocks: the diagonal blocks as the finite product
+// (I - N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0), the off-diagonal ones by block substitution
+//     Tb_sr = -Tb_ss sum_{r <= j < s} A_sj Tb_jr.
+//
+// Mapping to gfx950.  Everything independent of the state runs in a prep kernel, one 4-wave
+// workgroup per (chunk, head), all chunks in parallel; it leaves W, Qpp, Ut, Z, Kl and e^{Gam_L} of
+// each (chunk, head) in a workspace, laid out as the matrix-core fragments the carry kernel reads.
+// The carry kernel runs one 4-wave workgroup per (sequence, head): wave w keeps two 16-column
+// strips of S (columns 16w and 64 + 16w) in registers for the whole sequence; per chunk it stages
+// W, Qpp and Kl in LDS (double-buffered, the next chunk's copy in flight) and runs U, O and the
+// update, the latter as K = 32 products over pairs of sub-tiles.  Fragment conventions as in the
+// 16-token kernel: acc(X) register r holds X[4 lg + r][ln]; the A operand of Z = X Y is acc(X^T),
+// the B operand acc(Y); for K = 32, slot j of lane group lg stands for index 16 (j / 4) + 4 lg +
+// (j % 4).
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CL = 64;     // chunk tokens
+constexpr int ST = 16;     // sub-tile tokens
+constexpr int NSUB = 4;    // sub-tiles per chunk
+constexpr int D = 128;     // dk = dv
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float L2E_HI = 1.4453125f;          // bf16(log2 e)
+constexpr float L2E_LO = -0.00262451171875f;  // bf16(log2 e - L2E_HI)
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ bf16x4 bf4(f32x4 x) {
+    const u32x2 u = {pk2(x[0], x[1]), pk2(x[2], x[3])};
+    return __builtin_bit_cast(bf16x4, u);
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x4 zero4() { return (f32x4){0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ bf16x4 as_bf4(uint2 u) { return __builtin_bit_cast(bf16x4, u); }
+__device__ __forceinline__ uint2 as_u2(bf16x4 b) { return __builtin_bit_cast(uint2, b); }
+__device__ __forceinline__ bf16x4 zb4() { return as_bf4(make_uint2(0u, 0u)); }
+__device__ __forceinline__ bf16x4 neg4(bf16x4 b) {   // exact sign flip of four bf16 values
+    const uint2 u = as_u2(b);
+    return as_bf4(make_uint2(u.x ^ 0x80008000u, u.y ^ 0x80008000u));
+}
+__device__ __forceinline__ f32x4 unpack4(uint2 u) {  // bf16 x4 -> float32 x4 (exact)
+    return (f32x4){__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                   __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+}
+// LDS transpose read (ds_read_b64_tr_b16): with lane 16q + 4r + a addressing the four values
+// (row 4q + r, columns 4a .. 4a+3) of a row-major 16 x 16 bf16 block, lane 16q + i receives column i
+// of rows 4q .. 4q+3, i.e. the accumulator layout of the block.
+__device__ __forceinline__ bf16x4 lds_tr16(const void* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+}
+__device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+// index of block (s, r), r <= s, of a 4 x 4 block lower triangle
+__device__ __forceinline__ constexpr int tri(int s, int r) { return s * (s + 1) / 2 + r; }
+
+// ---- workspace: one record per (chunk, head) ----
+struct C64Work {
+    bf16x8 w[NSUB][4][64];     // [sub-tile][32-channel group][lane]: A operands of W (token-major)
+    bf16x8 qpp[NSUB][4][64];   // the same for Qpp
+    uint2 kl[NSUB][8][64];     // [sub-tile][16-channel block][lane]: acc(Kl block), bf16
+    f32x4 ut[NSUB][8][64];     // [sub-tile][16-column block][lane]: acc(Ut block)
+    uint2 z[NSUB][8][64];      // acc(Z block), bf16
+    float el[D];               // e^{Gam_L} per channel
+};
+static_assert(sizeof(C64Work) % 256 == 0, "workspace records stay 256-byte aligned");
+
+// ---- prep kernel ----
+struct PrepShared {
+    bf16x8 kd[NSUB][4][64];    // token-major K e^{Gam_end(s) - Gam} per sub-tile (B operand of A, P)
+    bf16x8 kg[NSUB][4][64];    // token-major Kg (transposed reads)
+    bf16x8 kl[NSUB][4][64];    // token-major Kl (transposed reads)
+    uint2 vr[NSUB][8][64];     // token-major V per 16-column block (transposed reads)
+    f32x4 qg[NSUB][8][64];     // Qg in float32, acc(Qg^T) per 16-channel block (C input of Qpp)
+    uint2 at[10][64];          // acc(A_sr^T), bf16 (r <= s; strict lower on the diagonal)
+    uint2 pt[10][64];          // acc(P_sr^T), bf16 (lower on the diagonal)
+    uint2 tb[10][64];          // acc(Tb_sr), bf16
+    uint2 tbt[10][64];         // acc(Tb_sr^T), bf16
+    uint2 y3t[10][64];         // acc((P Tb)_sr^T), bf16
+    float G[NSUB][D];          // total log-decay of each sub-tile per channel
+    float beta[CL];
+};
+
+__global__ __launch_bounds__(256) void kda_c64_prep_kernel(PrefillArgs a, C64Work* __restrict__ ws,
+                                                           const int* __restrict__ coff,
+                                                           int64_t nrec_chunks) {
+    __shared__ PrepShared sh;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int64_t j = blockIdx.x, h = blockIdx.y, H = a.H;
+
+    // chunk j -> (sequence n, chunk c of n)
+    int64_t n, c;
+    if (a.cu) {
+        if (j >= coff[a.N]) return;
+        int64_t lo = 0, hi = a.N;                    // coff[lo] <= j < coff[hi]
+        while (hi - lo > 1) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (coff[mid] <= j) lo = mid; else hi = mid;
+        }
+        n = lo;
+        c = j - coff[n];
+    } else {
+        const int64_t per = (a.T + CL - 1) / CL;
+        n = j / per;
+        c = j % per;
+        if (n >= a.N) return;
+    }
+    int64_t bos, eos;
+    if (a.cu) { bos = a.cu[n]; eos = a.cu[n + 1]; }
+    else { bos = n * a.T; eos = bos + a.T; }
+    const int64_t t0 = bos + c * CL;
+    const int ntok = (int)min<int64_t>(CL, eos - t0);
+
+    const bf16_t* q = static_cast<const bf16_t*>(a.q);
+    const bf16_t* k = static_cast<const bf16_t*>(a.k);
+    const bf16_t* v = static_cast<const bf16_t*>(a.v);
+    const bf16_t* g = static_cast<const bf16_t*>(a.g);
+    const bf16_t* beta = static_cast<const bf16_t*>(a.beta);
+
+    // ---- constant fragments (as in the 16-token kernel) ----
+    bf16x8 sel[2];   // selector: channel-major transpose of 32-channel-group half hh
+    for (int hh = 0; hh < 2; ++hh)
+        for (int jx = 0; jx < 8; ++jx)
+            sel[hh][jx] = (__bf16)((lg == (ln >> 2) && jx == 4 * hh + (ln & 3)) ? 1.f : 0.f);
+    bf16x4 scanHi, scanLo;   // -log2(e) above the diagonal, two-term bf16 split
+    for (int jx = 0; jx < 4; ++jx) {
+        const bool up = 4 * lg + jx > ln;
+        scanHi[jx] = (__bf16)(up ? -L2E_HI : 0.f);
+        scanLo[jx] = (__bf16)(up ? -L2E_LO : 0.f);
+    }
+    const bf16x8 scanHL = cat8(scanHi, scanLo);
+    bf16x4 onesA;
+    for (int jx = 0; jx < 4; ++jx) onesA[jx] = (__bf16)1.f;
+
+    // ---- 1. wave s loads sub-tile s: token ln, channels / columns 16 cb + 4 lg + r ----
+    const int s = wave;
+    const int nv = min(max(ntok - ST * s, 0), ST);
+    const int64_t row_bytes = H * D * 2;
+    const int nrec = max((nv - 1) * (int)row_bytes + D * 2, 0);
+    const int nrec_b = max((nv - 1) * (int)(H * 2) + 2, 0);
+    const int64_t ts = t0 + ST * s;
+    const int64_t e0 = (ts * H + h) * D;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + e0), (short)0,
+                                                                        nrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + e0), (short)0,
+                                                                        nrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc((void*)(g + e0), (short)0,
+                                                                        nrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + e0), (short)0,
+                                                                        nrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(beta + (ts * H + h)), (short)0, nrec_b, kBufferFlags);
+    const uint32_t vo = (uint32_t)(ln * row_bytes + 8 * lg);
+    uint2 kr[8], qr[8], gr[8], vr[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+        kr[cb] = ld8(rk, vo + 32 * cb);
+        qr[cb] = ld8(rq, vo + 32 * cb);
+        gr[cb] = ld8(rg, vo + 32 * cb);
+        vr[cb] = ld8(rv, vo + 32 * cb);
+    }
+    const uint32_t braw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, ln * H * 2, 0, 0);
+
+    // ---- 2. log-decay within the sub-tile: X = log2(e) (Gam_i - Gam_end(s)) <= 0 ... as
+    //         -sum_{j>i} g_j, token-major; the sub-tile total per channel ----
+    f32x4 X[8];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+        const bf16x8 ga = cat8(as_bf4(gr[2 * gi]), as_bf4(gr[2 * gi + 1]));
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const bf16x4 gc = bf4(mma32(ga, sel[hh], zero4()));   // channel-major g (exact)
+            X[2 * gi + hh] = mma32(cat8(gc, gc), scanHL, zero4());
+            const f32x4 gsum = mma16(onesA, gc, zero4());
+            sh.G[s][32 * gi + 16 * hh + ln] = gsum[0];           // all lane groups agree
+        }
+    }
+    sh.beta[ST * s + ln] = __uint_as_float(braw << 16);
+    // X holds log2(e) * Gp with Gp_i = Gam_i - Gam_end(s) = -sum_{j>i} g_j >= 0
+    f32x4 kf[8], qf[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+        kf[cb] = unpack4(kr[cb]);
+        qf[cb] = unpack4(qr[cb]);
+    }
+    // Kd_s = K e^{-Gp} (<= 1): the column operand of every block (s', s), s' >= s
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+        f32x4 d0, d1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            d0[r] = kf[2 * gi][r] * __builtin_amdgcn_exp2f(-X[2 * gi][r]);
+            d1[r] = kf[2 * gi + 1][r] * __builtin_amdgcn_exp2f(-X[2 * gi + 1][r]);
+        }
+        sh.kd[s][gi][lane] = cat8(bf4(d0), bf4(d1));
+    }
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) sh.vr[s][cb][lane] = vr[cb];
+    __syncthreads();
+
+    // ---- 3. chunk-level operands, per 16-channel block cb (lane channels 16 cb + 4 lg + r), with
+    //         Gam_end(s') = G_0 + .. + G_s' the chunk-relative log-decay at the end of sub-tile s':
+    //         Kg, Qg take the exponent X + log2(e) Gam_end(s), Kl the exponent
+    //         -X + log2(e) (Gam_L - Gam_end(s)); every exponent is <= 0 ----
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+        f32x4 kg2[2], qg2[2], kl2[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int cb = 2 * gi + hh;
+            f32x4 es = zero4(), eL = zero4();
+#pragma unroll
+            for (int sp = 0; sp < NSUB; ++sp) {
+                const f32x4 gsp = *reinterpret_cast<const f32x4*>(&sh.G[sp][16 * cb + 4 * lg]);
+                eL += gsp;
+                if (sp <= s) es += gsp;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = X[cb][r];
+                const float fg = __builtin_amdgcn_exp2f(x + es[r] * LOG2E);
+                kg2[hh][r] = kf[cb][r] * fg;
+                qg2[hh][r] = qf[cb][r] * fg;
+                kl2[hh][r] = kf[cb][r] * __builtin_amdgcn_exp2f(-x + (eL[r] - es[r]) * LOG2E);
+            }
+            sh.qg[s][cb][lane] = qg2[hh];
+        }
+        sh.kg[s][gi][lane] = cat8(bf4(kg2[0]), bf4(kg2[1]));
+        sh.kl[s][gi][lane] = cat8(bf4(kl2[0]), bf4(kl2[1]));
+    }
+
+    // ---- 4. blocks (s, r <= s) of A^T and P^T; the diagonal inverse ----
+    const float bcol = sh.beta[ST * s + ln];
+    const f32x4 brow = *reinterpret_cast<const f32x4*>(&sh.beta[ST * s + 4 * lg]);
+    f32x4 Am = zero4();
+#pragma unroll
+    for (int r = 0; r < NSUB; ++r) {
+        if (r > s) break;
+        f32x4 At = zero4(), Pt = zero4();
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+            // row operands of block (s, r): exponent X + log2(e) (Gam_end(s) - Gam_end(r)) for r < s
+            // (<= 0), X itself on the diagonal (the sub-tile-end reference)
+            f32x4 rk2[2], rq2[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int cb = 2 * gi + hh;
+                f32x4 off = zero4();
+#pragma unroll
+                for (int sp = 0; sp < NSUB; ++sp)
+                    if (sp > r && sp <= s)
+                        off += *reinterpret_cast<const f32x4*>(&sh.G[sp][16 * cb + 4 * lg]);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const float f = __builtin_amdgcn_exp2f(X[cb][rr] + off[rr] * LOG2E);
+                    rk2[hh][rr] = kf[cb][rr] * f;
+                    rq2[hh][rr] = qf[cb][rr] * f;
+                }
+            }
+            const bf16x8 rk8 = cat8(bf4(rk2[0]), bf4(rk2[1]));
+            const bf16x8 rq8 = cat8(bf4(rq2[0]), bf4(rq2[1]));
+            const bf16x8 kd8 = sh.kd[r][gi][lane];
+            if (r == s) Am = mma32(rk8, kd8, Am);    // A_ss
+            At = mma32(kd8, rk8, At);                // A_sr^T
+            Pt = mma32(kd8, rq8, Pt);                // P_sr^T
+        }
+        if (r == s) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int i = 4 * lg + rr;
+                At[rr] = (i < ln) ? At[rr] : 0.f;    // A^T[i][ln] = A[ln][i], strict lower
+                Pt[rr] = (i <= ln) ? Pt[rr] : 0.f;   // P^T[i][ln] = P[ln][i], lower
+            }
+        }
+        sh.at[tri(s, r)][lane] = as_u2(bf4(At));
+        sh.pt[tri(s, r)][lane] = as_u2(bf4(Pt));
+        if (r == s) {
+            // T_ss = (I - N)(I + N^2)(I + N^4)(I + N^8), N = Diag(beta) A_ss (16 x 16)
+            f32x4 N, Nt, F1t, id;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int i = 4 * lg + rr;
+                N[rr] = (ln < i) ? brow[rr] * Am[rr] : 0.f;     // N[i][ln]
+                Nt[rr] = bcol * At[rr];                          // N^T[i][ln] (At masked)
+                F1t[rr] = ((i == ln) ? 1.f : 0.f) - Nt[rr];      // (I - N)^T
+                id[rr] = (i == ln) ? 1.f : 0.f;
+            }
+            const bf16x4 Nb = bf4(N), Ntb = bf4(Nt);
+            const f32x4 N2 = mma16(Ntb, Nb, zero4()), N2t = mma16(Nb, Ntb, zero4());
+            const bf16x4 N2b = bf4(N2), N2tb = bf4(N2t);
+            const f32x4 N4 = mma16(N2tb, N2b, zero4());
+            const f32x4 N4t = mma16(N2b, N2tb, zero4());
+            const f32x4 Gt = mma16(N2b, bf4(F1t), F1t);                  // ((I - N)(I + N^2))^T
+            const f32x4 F8 = mma16(bf4(N4t), bf4(N4), id);               // I + N^8
+            const f32x4 Ht = mma16(bf4(N4), bf4(Gt), Gt);                // (.. (I + N^4))^T
+            const bf16x4 Htb = bf4(Ht), F8b = bf4(F8);
+            const f32x4 Tm = mma16(Htb, F8b, zero4());                   // T_ss
+            const f32x4 Tt = mma16(F8b, Htb, zero4());                   // T_ss^T
+            f32x4 TbT, Tb;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                TbT[rr] = brow[rr] * Tt[rr];    // (T Diag(beta))^T
+                Tb[rr] = bcol * Tm[rr];         // T Diag(beta)
+            }
+            sh.tbt[tri(s, s)][lane] = as_u2(bf4(TbT));
+            sh.tb[tri(s, s)][lane] = as_u2(bf4(Tb));
+        }
+    }
+    __syncthreads();
+
+    // ---- 5. off-diagonal blocks of Tb, row by row: Tb_kr = -Tb_kk sum_{r <= jj < k} A_kj Tb_jr ----
+#pragma unroll
+    for (int kk = 1; kk < NSUB; ++kk) {
+        if (s == kk) {
+            const bf16x4 tkkT = as_bf4(sh.tbt[tri(kk, kk)][lane]);   // acc(Tb_kk^T)
+#pragma unroll
+            for (int r = 0; r < NSUB - 1; ++r) {
+                if (r >= kk) break;
+                f32x4 Cm = zero4();
+#pragma unroll
+                for (int jj = 0; jj < NSUB - 1; ++jj) {
+                    if (jj < r || jj >= kk) continue;
+                    const bf16x4 akj = as_bf4(sh.at[tri(kk, jj)][lane]);   // acc(A_kj^T)
+                    const bf16x4 tjr = as_bf4(sh.tb[tri(jj, r)][lane]);    // acc(Tb_jr)
+                    Cm = mma16(akj, tjr, Cm);     // C = sum A_kj Tb_jr
+                }
+                const bf16x4 nC = neg4(bf4(Cm));  // acc(-C)
+                sh.tb[tri(kk, r)][lane] = as_u2(bf4(mma16(tkkT, nC, zero4())));    // -Tb_kk C
+                sh.tbt[tri(kk, r)][lane] = as_u2(bf4(mma16(nC, tkkT, zero4())));   // (-Tb_kk C)^T
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- 6. Y3 = P Tb by blocks (s, r <= s): Y3_sr^T = sum_{r <= jj <= s} Tb_jr^T P_sj^T ----
+#pragma unroll
+    for (int r = 0; r < NSUB; ++r) {
+        if (r > s) break;
+        f32x4 Y = zero4();
+#pragma unroll
+        for (int jj = 0; jj < NSUB; ++jj) {
+            if (jj < r || jj > s) continue;
+            Y = mma16(as_bf4(sh.tb[tri(jj, r)][lane]), as_bf4(sh.pt[tri(s, jj)][lane]), Y);
+        }
+        sh.y3t[tri(s, r)][lane] = as_u2(bf4(Y));
+    }
+    __syncthreads();
+
+    // ---- 7. the chunk's products, wave w: channel blocks and value-column blocks 2w, 2w+1 ----
+    C64Work* out = ws + (j * H + h);
+    const int src = 4 * lg + (ln >> 2) + 16 * (ln & 3);   // transpose-read source lane
+    auto kg_acc = [&](int r, int cb) {                    // acc(Kg_r block cb)
+        return lds_tr16(reinterpret_cast<const char*>(&sh.kg[r][cb >> 1][src]) + 8 * (cb & 1));
+    };
+    auto kl_acc = [&](int r, int cb) {
+        return lds_tr16(reinterpret_cast<const char*>(&sh.kl[r][cb >> 1][src]) + 8 * (cb & 1));
+    };
+    auto v_acc = [&](int r, int vb) { return lds_tr16(&sh.vr[r][vb][src]); };
+    const int w = wave;
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+        // B operands over the tokens of sub-tile pairs (0, 1) and (2, 3); blocks above the
+        // diagonal are zero
+        // acc(Tb_sr^T) serves as the B operand of W^T = Kg^T Tb^T and as the A operand of
+        // Ut = Tb V; likewise acc(Y3_sr^T), negated for Qpp
+        auto tbt_at = [&](int r) { return r <= sb ? as_bf4(sh.tbt[tri(sb, r)][lane]) : zb4(); };
+        auto y3t_at = [&](int r) { return r <= sb ? as_bf4(sh.y3t[tri(sb, r)][lane]) : zb4(); };
+        bf16x8 tb8[2], y38[2], ny38[2];
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            tb8[pp] = cat8(tbt_at(2 * pp), tbt_at(2 * pp + 1));
+            y38[pp] = cat8(y3t_at(2 * pp), y3t_at(2 * pp + 1));
+            ny38[pp] = cat8(neg4(y3t_at(2 * pp)), neg4(y3t_at(2 * pp + 1)));
+        }
+        const int npairs = sb >= 2 ? 2 : 1;
+        bf16x4 Wb[2], Qb[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int cb = 2 * w + hh;
+            f32x4 Wt = zero4(), Qt = sh.qg[sb][cb][lane];
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                if (pp >= npairs) break;
+                const bf16x8 A8 = cat8(kg_acc(2 * pp, cb), kg_acc(2 * pp + 1, cb));
+                Wt = mma32(A8, tb8[pp], Wt);       // W^T
+                Qt = mma32(A8, ny38[pp], Qt);      // Qpp^T = Qg^T - Kg^T (P Tb)^T
+            }
+            Wb[hh] = bf4(Wt);
+            Qb[hh] = bf4(Qt);
+        }
+        out->w[sb][w][lane] = cat8(Wb[0], Wb[1]);
+        out->qpp[sb][w][lane] = cat8(Qb[0], Qb[1]);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int vb = 2 * w + hh;
+            f32x4 Ut = zero4(), Zt = zero4();
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                if (pp >= npairs) break;
+                const bf16x8 B8 = cat8(v_acc(2 * pp, vb), v_acc(2 * pp + 1, vb));
+                Ut = mma32(tb8[pp], B8, Ut);       // Ut = Tb V
+                Zt = mma32(y38[pp], B8, Zt);       // Z = P Tb V
+            }
+            out->ut[sb][vb][lane] = Ut;
+            out->z[sb][vb][lane] = as_u2(bf4(Zt));
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NSUB; ++r)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) out->kl[r][2 * w + hh][lane] = as_u2(kl_acc(r, 2 * w + hh));
+    if (w == 0) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int ch = lane + 64 * half;
+            const float gl = sh.G[0][ch] + sh.G[1][ch] + sh.G[2][ch] + sh.G[3][ch];
+            out->el[ch] = __builtin_amdgcn_exp2f(gl * LOG2E);
+        }
+    }
+}
+
+// ---- chunk offsets of a variable-length batch: coff[n] = sum_{m < n} ceil(len_m / 64) ----
+__global__ __launch_bounds__(256) void kda_c64_offsets_kernel(const int32_t* __restrict__ cu,
+                                                              int N, int* __restrict__ coff) {
+    __shared__ int part[256];
+    const int tid = threadIdx.x;
+    const int per = (N + 255) / 256;
+    const int lo = min(tid * per, N), hi = min(lo + per, N);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) sum += (max(cu[i + 1] - cu[i], 0) + CL - 1) / CL;
+    part[tid] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int i = 0; i < 256; ++i) {
+            const int t = part[i];
+            part[i] = acc;
+            acc += t;
+        }
+    }
+    __syncthreads();
+    int acc = part[tid];
+    for (int i = lo; i < hi; ++i) {
+        coff[i] = acc;
+        acc += (max(cu[i + 1] - cu[i], 0) + CL - 1) / CL;
+    }
+    if (tid == 255) coff[N] = acc;
+}
+
+// ---- carry kernel ----
+struct CarryBuf {
+    bf16x8 w[NSUB][4][64];
+    bf16x8 qpp[NSUB][4][64];
+    uint2 kl[NSUB][8][64];
+    float el[D];
+};
+constexpr int kCarryU4 = (int)(sizeof(CarryBuf) / 16);        // 16-byte units per chunk
+static_assert(sizeof(CarryBuf) % 16 == 0, "copied in 16-byte units");
+constexpr int kCarryPer = (kCarryU4 + 255) / 256;             // units per thread
+
+__global__ __launch_bounds__(256) void kda_c64_carry_kernel(PrefillArgs a,
+                                                            const C64Work* __restrict__ ws,
+                                                            const int* __restrict__ coff,
+                                                            int64_t nrec_chunks) {
+    __shared__ CarryBuf buf[2];
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int64_t H = a.H;
+    const int64_t p = blockIdx.x, n = p / H, h = p % H;
+    int64_t bos, eos, j0;
+    if (a.cu) { bos = a.cu[n]; eos = a.cu[n + 1]; j0 = coff[n]; }
+    else { bos = n * a.T; eos = bos + a.T; j0 = n * ((a.T + CL - 1) / CL); }
+    int64_t nch = eos > bos ? (eos - bos + CL - 1) / CL : 0;
+    nch = max<int64_t>(min<int64_t>(nch, nrec_chunks - j0), 0);   // malformed offsets stay in bounds
+
+    // state strips m = 0, 1: rows 16 mb + 4 lg + r, column 16 w + 64 m + ln
+    const int64_t sbase = p * (int64_t)(D * D);
+    f32x4 S[2][8];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[m][mb][r] = a.h0 ? a.h0[sbase + (int64_t)(16 * mb + 4 * lg + r) * D + 16 * w +
+                                          64 * m + ln]
+                                   : 0.f;
+
+    bf16x4 eye;
+    for (int jx = 0; jx < 4; ++jx) eye[jx] = (__bf16)((4 * lg + jx == ln) ? 1.f : 0.f);
+
+    // the shared part of chunk jx (W, Qpp, Kl, e^{Gam_L}) in flight in registers
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 pre[kCarryPer];
+    auto fetch = [&](int64_t jx) {
+        const C64Work* wk = ws + (jx * H + h);
+        const u32x4* s0 = reinterpret_cast<const u32x4*>(&wk->w[0][0][0]);
+        const u32x4* s1 = reinterpret_cast<const u32x4*>(&wk->el[0]);
+        constexpr int n0 = (int)((sizeof(bf16x8) * 2 * NSUB * 4 * 64 + sizeof(uint2) * NSUB * 8 * 64) / 16);
+#pragma unroll
+        for (int i = 0; i < kCarryPer; ++i) {
+            const int u = tid + 256 * i;
+            if (u < n0) pre[i] = s0[u];
+            else if (u < kCarryU4) pre[i] = s1[u - n0];
+        }
+    };
+    auto stash = [&](int b) {
+        u32x4* d = reinterpret_cast<u32x4*>(&buf[b]);
+#pragma unroll
+        for (int i = 0; i < kCarryPer; ++i) {
+            const int u = tid + 256 * i;
+            if (u < kCarryU4) d[u] = pre[i];
+        }
+    };
+    bf16_t* o = static_cast<bf16_t*>(a.o);
+
+    // this wave's columns of a chunk: Ut and Z of strips m (16-column blocks w + 4 m)
+    struct Own { f32x4 ut[NSUB][2]; uint2 z[NSUB][2]; };
+    auto fetch_own = [&](int64_t jx, Own& d) {
+        const C64Work* wk = ws + (jx * H + h);
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                d.ut[sb][m] = wk->ut[sb][w + 4 * m][lane];
+                d.z[sb][m] = wk->z[sb][w + 4 * m][lane];
+            }
+    };
+    // chunk c from LDS buffer c % 2 and the wave's own registers; the next chunk's data in flight
+    auto chunk = [&](int64_t c, const Own& cur, Own& nxt) {
+        const int b = (int)(c & 1);
+        if (c + 1 < nch) {
+            fetch(j0 + c + 1);
+            fetch_own(j0 + c + 1, nxt);
+        }
+        const CarryBuf& B = buf[b];
+        // bf16 copy of the chunk-start state (B operands over 32-channel groups)
+        bf16x8 Sb[2][4];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi)
+                Sb[m][gi] = cat8(bf4(S[m][2 * gi]), bf4(S[m][2 * gi + 1]));
+        bf16x4 Ub[NSUB][2];
+        const int64_t t0 = bos + c * CL;
+#pragma unroll
+        for (int sb = 0; sb < NSUB; ++sb) {
+            f32x4 XW[2] = {zero4(), zero4()}, XQ[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const bf16x8 wf = B.w[sb][gi][lane], qf = B.qpp[sb][gi][lane];
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    XW[m] = mma32(wf, Sb[m][gi], XW[m]);
+                    XQ[m] = mma32(qf, Sb[m][gi], XQ[m]);
+                }
+            }
+            const int64_t tok = t0 + ST * sb + ln;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                Ub[sb][m] = bf4(cur.ut[sb][m] - XW[m]);                           // U
+                const f32x4 O = XQ[m] + unpack4(cur.z[sb][m]);                    // O
+                const bf16x4 Ot = bf4(mma16(bf4(O), eye, zero4()));              // token-major
+                if (tok < eos)
+                    *reinterpret_cast<uint2*>(o + (tok * H + h) * D + 16 * w + 64 * m + 4 * lg) =
+                        as_u2(Ot);
+            }
+        }
+        // S <- Diag(e^{Gam_L}) S + Kl^T U, contracted over sub-tile pairs
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+            const f32x4 e = *reinterpret_cast<const f32x4*>(&B.el[16 * mb + 4 * lg]);
+            const bf16x8 k01 = cat8(as_bf4(B.kl[0][mb][lane]), as_bf4(B.kl[1][mb][lane]));
+            const bf16x8 k23 = cat8(as_bf4(B.kl[2][mb][lane]), as_bf4(B.kl[3][mb][lane]));
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                f32x4 acc = S[m][mb] * e;
+                acc = mma32(k01, cat8(Ub[0][m], Ub[1][m]), acc);
+                acc = mma32(k23, cat8(Ub[2][m], Ub[3][m]), acc);
+                S[m][mb] = acc;
+            }
+        }
+        if (c + 1 < nch) stash(b ^ 1);
+        __syncthreads();
+    };
+
+    Own own0, own1;
+    if (nch > 0) {
+        fetch(j0);
+        stash(0);
+        fetch_own(j0, own0);
+    }
+    __syncthreads();
+    // unrolled by two so that the register sets alternate without copies
+    for (int64_t c = 0; c < nch; c += 2) {
+        chunk(c, own0, own1);
+        if (c + 1 < nch) chunk(c + 1, own1, own0);
+    }
+    if (a.hT) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    a.hT[sbase + (int64_t)(16 * mb + 4 * lg + r) * D + 16 * w + 64 * m + ln] =
+                        S[m][mb][r];
+    }
+}
+
+}  // namespace
+
+// Workspace bytes of the 64-token-chunk matrix-core path: chunk offsets, then one record per
+// (chunk, head).  nchunks bounds the chunk count (sum over sequences of ceil(len / 64)).
+size_t c64_mfma_workspace_bytes(int64_t nchunks, int64_t N, int64_t H) {
+    const size_t off = ((size_t)(N + 1) * sizeof(int) + 255) / 256 * 256;
+    return off + (size_t)nchunks * (size_t)H * sizeof(C64Work);
+}
+
+hipError_t launch_prefill_c64_mfma(const PrefillArgs& a, void* workspace, int64_t nchunks,
+                                   hipStream_t s) {
+    if (a.N <= 0 || a.H <= 0) return hipSuccess;
+    int* coff = static_cast<int*>(workspace);
+    const size_t off = ((size_t)(a.N + 1) * sizeof(int) + 255) / 256 * 256;
+    C64Work* ws = reinterpret_cast<C64Work*>(static_cast<char*>(workspace) + off);
+    if (a.cu)
+        hipLaunchKernelGGL(kda_c64_offsets_kernel, dim3(1), dim3(256), 0, s, a.cu, (int)a.N, coff);
+    if (nchunks > 0)
+        hipLaunchKernelGGL(kda_c64_prep_kernel, dim3((unsigned)nchunks, (unsigned)a.H), dim3(256),
+                           0, s, a, ws, coff, nchunks);
+    hipLaunchKernelGGL(kda_c64_carry_kernel, dim3((unsigned)(a.N * a.H)), dim3(256), 0, s, a, ws,
+                       coff, nchunks);
+    return hipGetLastError();
+}
+
+}  // namespace kda

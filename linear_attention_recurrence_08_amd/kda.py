@@ -52,8 +52,12 @@ def load_library():
                                       i32, i32, i32, i32, i32, i32, vp]
         lib.kda_chunk_fwd.restype = i32
         lib.kda_chunk_fwd_chunk64.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
-                                              i32, i32, i32, i32, i32, i32, vp]
+                                              i32, i32, i32, i32, i32, i32, vp, ctypes.c_size_t,
+                                              vp]
         lib.kda_chunk_fwd_chunk64.restype = i32
+        lib.kda_chunk_fwd_chunk64_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32,
+                                                              i32]
+        lib.kda_chunk_fwd_chunk64_workspace_bytes.restype = ctypes.c_size_t
         lib.kda_chunk_fwd_snapshots.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                                 i32, i32, i32, i32, i32, i32, i32, vp]
         lib.kda_chunk_fwd_snapshots.restype = i32
@@ -169,19 +173,33 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     return o, hT
 
 
+def kda_chunk_fwd_chunk64_workspace_bytes(q: torch.Tensor, cu_seqlens: Optional[torch.Tensor],
+                                          num_seqs: int, B: int, T: int, H: int, dk: int,
+                                          dv: int) -> int:
+    """Workspace bytes kda_chunk_fwd_chunk64 needs for these arguments (0: none)."""
+    return int(load_library().kda_chunk_fwd_chunk64_workspace_bytes(
+        _ptr(cu_seqlens), num_seqs, B, T, H, dk, dv, _dtype_code(q)))
+
+
 def kda_chunk_fwd_chunk64(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                           beta: torch.Tensor, h0: Optional[torch.Tensor] = None,
                           cu_seqlens: Optional[torch.Tensor] = None,
                           output_final_state: bool = True, o: Optional[torch.Tensor] = None,
-                          hT: Optional[torch.Tensor] = None
+                          hT: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None
                           ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """kda_chunk_fwd computed with 64-token chunks of four 16-token sub-tiles (one state carry per
-    chunk; float32 vector arithmetic).  Same arguments and results as kda_chunk_fwd."""
+    chunk).  Same arguments and results as kda_chunk_fwd; `workspace` (a contiguous device tensor
+    of at least kda_chunk_fwd_chunk64_workspace_bytes bytes) is allocated here when not given."""
     dev, B, T, H, dk, dv, N, o, hT = _prefill_args(q, k, v, g, beta, h0, cu_seqlens,
                                                    output_final_state, o, hT)
+    need = kda_chunk_fwd_chunk64_workspace_bytes(q, cu_seqlens, N, B, T, H, dk, dv)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().kda_chunk_fwd_chunk64(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), N,
-        _ptr(o), _ptr(hT), B, T, H, dk, dv, _dtype_code(q), _stream(dev))
+        _ptr(o), _ptr(hT), B, T, H, dk, dv, _dtype_code(q), _ptr(workspace), nbytes, _stream(dev))
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd_chunk64")
     return o, hT

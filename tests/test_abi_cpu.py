@@ -29,6 +29,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_chunk64",
+                                     "kda_chunk_fwd_chunk64_workspace_bytes",
                                      "kda_chunk_fwd_snapshots",
                                      "kda_decode_step", "kda_decode_step_gated", "kda_frontend",
                                      "kda_output_gate", "kda_status_string", "kda_version"]
@@ -42,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     from linear_attention_recurrence_08_amd.kda import kda_status_string
     assert kda_status_string(0) == "ok"
-    for code in range(-9, 0):
+    for code in range(-10, 0):
         s = kda_status_string(code)
         assert s and s != "unknown status"
     assert kda_status_string(-99) == "unknown status"
@@ -91,6 +92,52 @@ def _decode(lib, **kw):
 ])
 def test_prefill_argument_errors(lib, kw, code):
     assert _prefill(lib, **kw) == code
+
+
+def _chunk64(lib, ws=None, ws_bytes=0, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, num_seqs=0, o=FAKE,
+             hT=FAKE, B=1, T=16, H=2, dk=128, dv=128, dtype=0)
+    a.update(kw)
+    return lib.kda_chunk_fwd_chunk64(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"],
+                                     a["num_seqs"], a["o"], a["hT"], a["B"], a["T"], a["H"],
+                                     a["dk"], a["dv"], a["dtype"], ws, ws_bytes, None)
+
+
+def _ws_bytes(lib, cu=None, num_seqs=0, B=1, T=16, H=2, dk=128, dv=128, dtype=0):
+    return lib.kda_chunk_fwd_chunk64_workspace_bytes(cu, num_seqs, B, T, H, dk, dv, dtype)
+
+
+RECORD = 98816      # workspace bytes per (64-token chunk, head) of the matrix-core path
+
+
+def test_chunk64_workspace_size(lib):
+    # bf16 with dk = dv = 128: chunk offsets (rounded to 256 bytes), then one record per
+    # (chunk, head); equal lengths provision B * ceil(T / 64) chunks
+    assert _ws_bytes(lib, B=3, T=130, H=5) == 256 + 3 * 3 * 5 * RECORD
+    assert _ws_bytes(lib, B=2, T=64, H=1) == 256 + 2 * 1 * RECORD
+    # a variable-length batch provisions Ttot // 64 + N chunks (sum of ceil(len / 64) <= that)
+    assert _ws_bytes(lib, cu=FAKE, num_seqs=3, B=1, T=200, H=4) == 256 + (3 + 3) * 4 * RECORD
+    assert _ws_bytes(lib, cu=FAKE, num_seqs=100, B=1, T=64, H=1) == \
+        (101 * 4 + 255) // 256 * 256 + 101 * RECORD
+    # the float32 path (other dtype or head size) needs none; nor do rejected arguments
+    assert _ws_bytes(lib, dtype=1) == 0
+    assert _ws_bytes(lib, dk=64) == 0
+    assert _ws_bytes(lib, dtype=5) == 0 and _ws_bytes(lib, H=0) == 0
+    assert _ws_bytes(lib, cu=FAKE, B=2, num_seqs=2) == 0
+    assert _ws_bytes(lib, B=0) == 0
+
+
+def test_chunk64_workspace_errors(lib):
+    need = _ws_bytes(lib)
+    aligned = ctypes.c_void_p(0x10000)   # never dereferenced: the calls fail validation first
+    assert _chunk64(lib) == -10                                   # missing
+    assert _chunk64(lib, ws=aligned, ws_bytes=need - 1) == -10    # too small
+    assert _chunk64(lib, ws=ctypes.c_void_p(0x10010), ws_bytes=need) == -10   # misaligned
+    # argument errors come first, as in kda_chunk_fwd
+    assert _chunk64(lib, dtype=2) == -3 and _chunk64(lib, q=None) == -1
+    # the float32 path takes no workspace: its argument errors come through without one
+    assert _chunk64(lib, dtype=1, dk=96, q=None) == -1
+    assert _chunk64(lib, B=0) == 0
 
 
 def test_prefill_empty_is_noop(lib):
