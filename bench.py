@@ -79,6 +79,7 @@ def decode_bytes(d) -> int:
 # the build script (which holds the code-generation options).
 KERNEL_SOURCES = {
     "kda_chunk_fwd": "kda_prefill_mfma.hip",
+    "kda_chunk_fwd_chunk64": "kda_prefill_c64_mfma.hip",
     "kda_decode": "kda_decode.hip",
     "kda_output_gate": "kda_output_gate.hip",
     "kda_frontend": "kda_frontend.hip",
@@ -116,8 +117,8 @@ CALIB_BYTES = 1 << 30   # calibration copy: reads and writes exactly this many b
 
 
 def traffic_pass(dev):
-    """A plain copy of known size (y = x * 1 over 1 GiB of float32), then 3 launches of the
-    prefill and the decode kernels on their benchmark workloads."""
+    """A plain copy of known size (y = x * 1 over 1 GiB of float32), then 3 launches of each
+    entry point the bench line times, on its benchmark workload."""
     import torch
     from linear_attention_recurrence_08_amd import (inputs, kda_chunk_fwd, kda_chunk_fwd_snapshots,
                                                     kda_decode_step, kda_decode_step_gated,
@@ -130,6 +131,9 @@ def traffic_pass(dev):
     w = inputs.make_workload("prefill_T4096_H96_d128_bf16").to(dev)
     for _ in range(3):
         kda_chunk_fwd(*w.call_views(), h0=w.h0, cu_seqlens=w.cu_seqlens)
+    from linear_attention_recurrence_08_amd import kda_chunk_fwd_chunk64
+    for _ in range(3):
+        kda_chunk_fwd_chunk64(*w.call_views(), h0=w.h0, cu_seqlens=w.cu_seqlens)
     torch.cuda.synchronize()
     del w
     d = inputs.make_workload(DECODE_WORKLOAD)
@@ -157,6 +161,11 @@ def traffic_pass(dev):
 SUMMARY_KERNELS = {
     # kernel name fragment (as rocprofv3 records it) -> (summary tag, workload)
     "kda_prefill_mfma_kernel": ("kda_chunk_fwd_prefill_T4096_H96_d128_bf16",
+                                "prefill_T4096_H96_d128_bf16"),
+    # 64-token chunks: the state-independent prep kernel, then the carry (one head in two halves)
+    "kda_c64_prep_kernel": ("kda_chunk_fwd_chunk64_prefill_T4096_H96_d128_bf16",
+                            "prefill_T4096_H96_d128_bf16"),
+    "kda_c64_carry_kernel<1>": ("kda_chunk_fwd_chunk64_prefill_T4096_H96_d128_bf16",
                                 "prefill_T4096_H96_d128_bf16"),
     "kda_decode_d128_kernel<unsigned short, 2, false>": ("kda_decode_decode_N256_H96_d128_bf16",
                                                          "decode_N256_H96_d128_bf16"),
@@ -403,36 +412,59 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
 
-    # ---------------- 64-token chunks (float32 vector path) beside 16-token tiles ----------------
+    # ---------------- 64-token chunks beside 16-token tiles ----------------
     if not args.no_chunk64:
         from linear_attention_recurrence_08_amd import kda_chunk_fwd_chunk64
+        from linear_attention_recurrence_08_amd.kda import kda_chunk_fwd_chunk64_workspace_bytes
 
         o_c, hT_c = torch.empty_like(o), torch.empty_like(hT)   # leave the prefill's o intact
+        q0 = args_views[0]
+        cB, cT = (1, q0.shape[0]) if q0.dim() == 3 else (q0.shape[0], q0.shape[1])
+        ws_bytes = kda_chunk_fwd_chunk64_workspace_bytes(q0, xd.cu_seqlens, x.num_seqs, cB, cT,
+                                                         x.H, x.dk, x.dv)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
         def prefill_c64():
-            kda_chunk_fwd_chunk64(*args_views, h0=xd.h0, cu_seqlens=xd.cu_seqlens, o=o_c, hT=hT_c)
+            kda_chunk_fwd_chunk64(*args_views, h0=xd.h0, cu_seqlens=xd.cu_seqlens, o=o_c, hT=hT_c,
+                                  workspace=ws)
 
-        def prefill_c16_general():
-            os.environ["KDA_FORCE_GENERAL"] = "1"
-            try:
-                kda_chunk_fwd(*args_views, h0=xd.h0, cu_seqlens=xd.cu_seqlens, o=o_c, hT=hT_c)
-            finally:
-                del os.environ["KDA_FORCE_GENERAL"]
+        def forced_float32(fn):
+            def run():
+                os.environ["KDA_FORCE_GENERAL"] = "1"
+                try:
+                    fn()
+                finally:
+                    del os.environ["KDA_FORCE_GENERAL"]
+            return run
 
-        csteps = max(3, args.steps // 10)
-        c64ms, _ = time_launches(prefill_c64, csteps, 1, stream)
-        c16ms, _ = time_launches(prefill_c16_general, csteps, 1, stream)
+        def prefill_c16():
+            kda_chunk_fwd(*args_views, h0=xd.h0, cu_seqlens=xd.cu_seqlens, o=o_c, hT=hT_c)
+
+        c64ms, _ = time_launches(prefill_c64, max(5, args.steps // 2), 2, stream)
+        fsteps = max(3, args.steps // 10)
+        f64ms, _ = time_launches(forced_float32(prefill_c64), fsteps, 1, stream)
+        f16ms, _ = time_launches(forced_float32(prefill_c16), fsteps, 1, stream)
+        # the workspace round trip: every (chunk, head) record written once and read back
+        ws_traffic = 2 * ws_bytes
         result["chunk64"] = {
-            "kernel": "kda_prefill_c64 (float32 vector ALUs)", "steps": csteps,
+            "kernel": "kda_c64_prep + kda_c64_carry (matrix cores)" if ws_bytes else
+                      "kda_prefill_c64 (float32 vector ALUs)",
+            "steps": max(5, args.steps // 2),
             "ms_per_step": round(c64ms, 4), "value": round(tokens / (c64ms * 1e-3), 1),
-            "unit": "tokens/s",
-            "chunk16_general_ms_per_step": round(c16ms, 4),
+            "unit": "tokens/s", "vs_chunk16": round(ms / c64ms, 4),
+            "workspace_bytes": ws_bytes,
             "roofline": {"bound": "hbm", "achieved": round(nbytes / (c64ms * 1e-3) / 1e9, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(nbytes / (c64ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "algorithmic_bytes_per_launch": nbytes},
+                         "algorithmic_bytes_per_launch": nbytes,
+                         "with_workspace_bytes_per_launch": nbytes + ws_traffic,
+                         "with_workspace_frac": round((nbytes + ws_traffic) / (c64ms * 1e-3) /
+                                                      1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": recorded_traffic("kda_chunk_fwd_chunk64_" + args.workload)},
+            "float32_vector_ms_per_step": round(f64ms, 4),
+            "chunk16_float32_vector_ms_per_step": round(f16ms, 4),
         }
-        del o_c, hT_c
+        del o_c, hT_c, ws
 
     # ---------------- variable-length batch: 16 sequences of 1,024-16,384 tokens ----------------
     if not args.no_varlen and args.workload != VARLEN_WORKLOAD:

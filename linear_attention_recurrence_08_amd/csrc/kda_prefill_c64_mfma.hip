@@ -106,22 +106,32 @@ struct C64Work {
 static_assert(sizeof(C64Work) % 256 == 0, "workspace records stay 256-byte aligned");
 
 // ---- prep kernel ----
+// 70 KB, so that two workgroups share a CU and one's loads overlap the other's arithmetic;
+// arrays whose lifetimes do not overlap share storage
 struct PrepShared {
-    bf16x8 kd[NSUB][4][64];    // token-major K e^{Gam_end(s) - Gam} per sub-tile (B operand of A, P)
+    union {
+        bf16x8 kd[NSUB][4][64];   // token-major K e^{Gam_end(s) - Gam} (B operand of A, P blocks)
+        bf16x8 kl[NSUB][4][64];   // then token-major Kl (transposed reads)
+    };
     bf16x8 kg[NSUB][4][64];    // token-major Kg (transposed reads)
-    bf16x8 kl[NSUB][4][64];    // token-major Kl (transposed reads)
     uint2 vr[NSUB][8][64];     // token-major V per 16-column block (transposed reads)
-    f32x4 qg[NSUB][8][64];     // Qg in float32, acc(Qg^T) per 16-channel block (C input of Qpp)
-    uint2 at[10][64];          // acc(A_sr^T), bf16 (r <= s; strict lower on the diagonal)
+    union {
+        uint2 at[10][64];      // acc(A_sr^T), bf16 (r <= s; strict lower on the diagonal)
+        uint2 y3t[10][64];     // then acc((P Tb)_sr^T), bf16
+    };
     uint2 pt[10][64];          // acc(P_sr^T), bf16 (lower on the diagonal)
     uint2 tb[10][64];          // acc(Tb_sr), bf16
     uint2 tbt[10][64];         // acc(Tb_sr^T), bf16
-    uint2 y3t[10][64];         // acc((P Tb)_sr^T), bf16
     float G[NSUB][D];          // total log-decay of each sub-tile per channel
+    float F[14][D];            // per-channel decay factors, all <= 1 (see kF*)
     float beta[CL];
 };
+// rows of PrepShared::F, with Gam_end(s) the chunk-relative log-decay at the end of sub-tile s:
+constexpr int kFg = 0;         // kFg + s:  e^{Gam_end(s)}
+constexpr int kFl = 4;         // kFl + s:  e^{Gam_L - Gam_end(s)}
+constexpr int kFo = 8;         // kFo + s (s - 1) / 2 + r, r < s:  e^{Gam_end(s) - Gam_end(r)}
 
-__global__ __launch_bounds__(256) void kda_c64_prep_kernel(PrefillArgs a, C64Work* __restrict__ ws,
+__global__ __launch_bounds__(256, 2) void kda_c64_prep_kernel(PrefillArgs a, C64Work* __restrict__ ws,
                                                            const int* __restrict__ coff,
                                                            int64_t nrec_chunks) {
     __shared__ PrepShared sh;
@@ -203,8 +213,8 @@ __global__ __launch_bounds__(256) void kda_c64_prep_kernel(PrefillArgs a, C64Wor
     }
     const uint32_t braw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, ln * H * 2, 0, 0);
 
-    // ---- 2. log-decay within the sub-tile: X = log2(e) (Gam_i - Gam_end(s)) <= 0 ... as
-    //         -sum_{j>i} g_j, token-major; the sub-tile total per channel ----
+    // ---- 2. log-decay within the sub-tile, X = log2(e) Gp with Gp_i = Gam_i - Gam_end(s) =
+    //         -sum_{j>i} g_j >= 0 (token-major), and the sub-tile total per channel ----
     f32x4 X[8];
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
@@ -218,57 +228,70 @@ __global__ __launch_bounds__(256) void kda_c64_prep_kernel(PrefillArgs a, C64Wor
         }
     }
     sh.beta[ST * s + ln] = __uint_as_float(braw << 16);
-    // X holds log2(e) * Gp with Gp_i = Gam_i - Gam_end(s) = -sum_{j>i} g_j >= 0
-    f32x4 kf[8], qf[8];
+    // Kp = K e^{Gp} (>= 1, at most e^80), Qp = Q e^{Gp}, Kd = K e^{-Gp} (<= 1); Kd_s is the column
+    // operand of every block (s', s), s' >= s
+    f32x4 Kp[8], Qp[8], Kd[8];
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
-        kf[cb] = unpack4(kr[cb]);
-        qf[cb] = unpack4(qr[cb]);
-    }
-    // Kd_s = K e^{-Gp} (<= 1): the column operand of every block (s', s), s' >= s
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-        f32x4 d0, d1;
+        const f32x4 kf = unpack4(kr[cb]), qf = unpack4(qr[cb]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            d0[r] = kf[2 * gi][r] * __builtin_amdgcn_exp2f(-X[2 * gi][r]);
-            d1[r] = kf[2 * gi + 1][r] * __builtin_amdgcn_exp2f(-X[2 * gi + 1][r]);
+            const float e = __builtin_amdgcn_exp2f(X[cb][r]);
+            const float d = __builtin_amdgcn_exp2f(-X[cb][r]);
+            Kp[cb][r] = kf[r] * e;
+            Qp[cb][r] = qf[r] * e;
+            Kd[cb][r] = kf[r] * d;
         }
-        sh.kd[s][gi][lane] = cat8(bf4(d0), bf4(d1));
     }
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) sh.kd[s][gi][lane] = cat8(bf4(Kd[2 * gi]), bf4(Kd[2 * gi + 1]));
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) sh.vr[s][cb][lane] = vr[cb];
     __syncthreads();
 
-    // ---- 3. chunk-level operands, per 16-channel block cb (lane channels 16 cb + 4 lg + r), with
-    //         Gam_end(s') = G_0 + .. + G_s' the chunk-relative log-decay at the end of sub-tile s':
-    //         Kg, Qg take the exponent X + log2(e) Gam_end(s), Kl the exponent
-    //         -X + log2(e) (Gam_L - Gam_end(s)); every exponent is <= 0 ----
+    // per-channel factors: every chunk-level operand is a sub-tile operand times one of them (a
+    // factor underflows only where the product it scales is below e^{80 - 103})
+    {
+        const int ch = tid & 127, half = tid >> 7;
+        float E[NSUB], acc = 0.f;
+#pragma unroll
+        for (int sp = 0; sp < NSUB; ++sp) {
+            acc += sh.G[sp][ch];
+            E[sp] = acc;
+        }
+        if (half == 0) {
+#pragma unroll
+            for (int sp = 0; sp < NSUB; ++sp) {
+                sh.F[kFg + sp][ch] = __builtin_amdgcn_exp2f(E[sp] * LOG2E);
+                sh.F[kFl + sp][ch] = __builtin_amdgcn_exp2f((E[NSUB - 1] - E[sp]) * LOG2E);
+            }
+        } else {
+#pragma unroll
+            for (int sp = 1; sp < NSUB; ++sp)
+#pragma unroll
+                for (int r = 0; r < sp; ++r)
+                    sh.F[kFo + sp * (sp - 1) / 2 + r][ch] =
+                        __builtin_amdgcn_exp2f((E[sp] - E[r]) * LOG2E);
+        }
+    }
+    __syncthreads();
+    auto fac = [&](int row, int cb) {   // the factors of this lane's channels 16 cb + 4 lg + r
+        return *reinterpret_cast<const f32x4*>(&sh.F[row][16 * cb + 4 * lg]);
+    };
+
+    // ---- 3. chunk-level operands Kg = Kp e^{Gam_end(s)}, Qg = Qp e^{Gam_end(s)} ----
+    f32x4 qgr[8];          // Qg in float32, acc(Qg^T) per 16-channel block: C input of Qpp^T
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
-        f32x4 kg2[2], qg2[2], kl2[2];
+        f32x4 kg2[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int cb = 2 * gi + hh;
-            f32x4 es = zero4(), eL = zero4();
-#pragma unroll
-            for (int sp = 0; sp < NSUB; ++sp) {
-                const f32x4 gsp = *reinterpret_cast<const f32x4*>(&sh.G[sp][16 * cb + 4 * lg]);
-                eL += gsp;
-                if (sp <= s) es += gsp;
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float x = X[cb][r];
-                const float fg = __builtin_amdgcn_exp2f(x + es[r] * LOG2E);
-                kg2[hh][r] = kf[cb][r] * fg;
-                qg2[hh][r] = qf[cb][r] * fg;
-                kl2[hh][r] = kf[cb][r] * __builtin_amdgcn_exp2f(-x + (eL[r] - es[r]) * LOG2E);
-            }
-            sh.qg[s][cb][lane] = qg2[hh];
+            const f32x4 fg = fac(kFg + s, cb);
+            kg2[hh] = Kp[cb] * fg;
+            qgr[cb] = Qp[cb] * fg;
         }
         sh.kg[s][gi][lane] = cat8(bf4(kg2[0]), bf4(kg2[1]));
-        sh.kl[s][gi][lane] = cat8(bf4(kl2[0]), bf4(kl2[1]));
     }
 
     // ---- 4. blocks (s, r <= s) of A^T and P^T; the diagonal inverse ----
@@ -281,22 +304,19 @@ __global__ __launch_bounds__(256) void kda_c64_prep_kernel(PrefillArgs a, C64Wor
         f32x4 At = zero4(), Pt = zero4();
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
-            // row operands of block (s, r): exponent X + log2(e) (Gam_end(s) - Gam_end(r)) for r < s
-            // (<= 0), X itself on the diagonal (the sub-tile-end reference)
+            // row operands of block (s, r): Kp, Qp on the diagonal (the sub-tile-end reference),
+            // times e^{Gam_end(s) - Gam_end(r)} for r < s (then every factor is <= 1)
             f32x4 rk2[2], rq2[2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int cb = 2 * gi + hh;
-                f32x4 off = zero4();
-#pragma unroll
-                for (int sp = 0; sp < NSUB; ++sp)
-                    if (sp > r && sp <= s)
-                        off += *reinterpret_cast<const f32x4*>(&sh.G[sp][16 * cb + 4 * lg]);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const float f = __builtin_amdgcn_exp2f(X[cb][rr] + off[rr] * LOG2E);
-                    rk2[hh][rr] = kf[cb][rr] * f;
-                    rq2[hh][rr] = qf[cb][rr] * f;
+                if (r == s) {
+                    rk2[hh] = Kp[cb];
+                    rq2[hh] = Qp[cb];
+                } else {
+                    const f32x4 f = fac(kFo + s * (s - 1) / 2 + r, cb);
+                    rk2[hh] = Kp[cb] * f;
+                    rq2[hh] = Qp[cb] * f;
                 }
             }
             const bf16x8 rk8 = cat8(bf4(rk2[0]), bf4(rk2[1]));
@@ -350,6 +370,12 @@ __global__ __launch_bounds__(256) void kda_c64_prep_kernel(PrefillArgs a, C64Wor
     }
     __syncthreads();
 
+    // Kl = Kd e^{Gam_L - Gam_end(s)}, into the storage of Kd (no longer read)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
+        sh.kl[s][gi][lane] = cat8(bf4(Kd[2 * gi] * fac(kFl + s, 2 * gi)),
+                                  bf4(Kd[2 * gi + 1] * fac(kFl + s, 2 * gi + 1)));
+
     // ---- 5. off-diagonal blocks of Tb, row by row: Tb_kr = -Tb_kk sum_{r <= jj < k} A_kj Tb_jr ----
 #pragma unroll
     for (int kk = 1; kk < NSUB; ++kk) {
@@ -388,7 +414,7 @@ __global__ __launch_bounds__(256) void kda_c64_prep_kernel(PrefillArgs a, C64Wor
     }
     __syncthreads();
 
-    // ---- 7. the chunk's products, wave w: channel blocks and value-column blocks 2w, 2w+1 ----
+    // ---- 7. the chunk's products ----
     C64Work* out = ws + (j * H + h);
     const int src = 4 * lg + (ln >> 2) + 16 * (ln & 3);   // transpose-read source lane
     auto kg_acc = [&](int r, int cb) {                    // acc(Kg_r block cb)
@@ -399,49 +425,61 @@ __global__ __launch_bounds__(256) void kda_c64_prep_kernel(PrefillArgs a, C64Wor
     };
     auto v_acc = [&](int r, int vb) { return lds_tr16(&sh.vr[r][vb][src]); };
     const int w = wave;
-#pragma unroll
-    for (int sb = 0; sb < NSUB; ++sb) {
-        // B operands over the tokens of sub-tile pairs (0, 1) and (2, 3); blocks above the
-        // diagonal are zero
-        // acc(Tb_sr^T) serves as the B operand of W^T = Kg^T Tb^T and as the A operand of
-        // Ut = Tb V; likewise acc(Y3_sr^T), negated for Qpp
+    // acc(Tb_sr^T) serves as the B operand of W^T = Kg^T Tb^T and as the A operand of Ut = Tb V;
+    // likewise acc(Y3_sr^T), negated for Qpp.  Operands over the tokens of sub-tile pairs (0, 1)
+    // and (2, 3); blocks above the diagonal are zero.
+    struct PairOps { bf16x8 tb8[2], y38[2], ny38[2]; int npairs; };
+    auto pair_ops = [&](int sb) {
+        PairOps po;
         auto tbt_at = [&](int r) { return r <= sb ? as_bf4(sh.tbt[tri(sb, r)][lane]) : zb4(); };
         auto y3t_at = [&](int r) { return r <= sb ? as_bf4(sh.y3t[tri(sb, r)][lane]) : zb4(); };
-        bf16x8 tb8[2], y38[2], ny38[2];
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
-            tb8[pp] = cat8(tbt_at(2 * pp), tbt_at(2 * pp + 1));
-            y38[pp] = cat8(y3t_at(2 * pp), y3t_at(2 * pp + 1));
-            ny38[pp] = cat8(neg4(y3t_at(2 * pp)), neg4(y3t_at(2 * pp + 1)));
+            po.tb8[pp] = cat8(tbt_at(2 * pp), tbt_at(2 * pp + 1));
+            po.y38[pp] = cat8(y3t_at(2 * pp), y3t_at(2 * pp + 1));
+            po.ny38[pp] = cat8(neg4(y3t_at(2 * pp)), neg4(y3t_at(2 * pp + 1)));
         }
-        const int npairs = sb >= 2 ? 2 : 1;
-        bf16x4 Wb[2], Qb[2];
+        po.npairs = sb >= 2 ? 2 : 1;
+        return po;
+    };
+    // W^T and Qpp^T of this wave's sub-tile, every channel block (Qg^T from registers)
+    {
+        const PairOps po = pair_ops(s);
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int cb = 2 * w + hh;
-            f32x4 Wt = zero4(), Qt = sh.qg[sb][cb][lane];
+        for (int gi = 0; gi < 4; ++gi) {
+            bf16x4 Wb[2], Qb[2];
 #pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
-                if (pp >= npairs) break;
-                const bf16x8 A8 = cat8(kg_acc(2 * pp, cb), kg_acc(2 * pp + 1, cb));
-                Wt = mma32(A8, tb8[pp], Wt);       // W^T
-                Qt = mma32(A8, ny38[pp], Qt);      // Qpp^T = Qg^T - Kg^T (P Tb)^T
+            for (int hh = 0; hh < 2; ++hh) {
+                const int cb = 2 * gi + hh;
+                f32x4 Wt = zero4(), Qt = qgr[cb];
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    if (pp >= po.npairs) break;
+                    const bf16x8 A8 = cat8(kg_acc(2 * pp, cb), kg_acc(2 * pp + 1, cb));
+                    Wt = mma32(A8, po.tb8[pp], Wt);       // W^T
+                    Qt = mma32(A8, po.ny38[pp], Qt);      // Qpp^T = Qg^T - Kg^T (P Tb)^T
+                }
+                Wb[hh] = bf4(Wt);
+                Qb[hh] = bf4(Qt);
             }
-            Wb[hh] = bf4(Wt);
-            Qb[hh] = bf4(Qt);
+            out->w[s][gi][lane] = cat8(Wb[0], Wb[1]);
+            out->qpp[s][gi][lane] = cat8(Qb[0], Qb[1]);
         }
-        out->w[sb][w][lane] = cat8(Wb[0], Wb[1]);
-        out->qpp[sb][w][lane] = cat8(Qb[0], Qb[1]);
+    }
+    // Ut and Z, value-column blocks 2w, 2w+1 of every sub-tile
+#pragma unroll
+    for (int sb = 0; sb < NSUB; ++sb) {
+        const PairOps po = pair_ops(sb);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int vb = 2 * w + hh;
             f32x4 Ut = zero4(), Zt = zero4();
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
-                if (pp >= npairs) break;
+                if (pp >= po.npairs) break;
                 const bf16x8 B8 = cat8(v_acc(2 * pp, vb), v_acc(2 * pp + 1, vb));
-                Ut = mma32(tb8[pp], B8, Ut);       // Ut = Tb V
-                Zt = mma32(y38[pp], B8, Zt);       // Z = P Tb V
+                Ut = mma32(po.tb8[pp], B8, Ut);       // Ut = Tb V
+                Zt = mma32(po.y38[pp], B8, Zt);       // Z = P Tb V
             }
             out->ut[sb][vb][lane] = Ut;
             out->z[sb][vb][lane] = as_u2(bf4(Zt));
@@ -500,6 +538,31 @@ constexpr int kCarryU4 = (int)(sizeof(CarryBuf) / 16);        // 16-byte units p
 static_assert(sizeof(CarryBuf) % 16 == 0, "copied in 16-byte units");
 constexpr int kCarryPer = (kCarryU4 + 255) / 256;             // units per thread
 
+// (workgroup index) -> (pair p = n * H + head, slice) with both slices of a pair on one XCD
+// (workgroups are dealt to the 8 XCDs round-robin by index), so that the second slice's reads of
+// the shared W, Qpp and Kl meet in that XCD's L2; one slice per pair: p = b
+__device__ __forceinline__ void map_pair(int64_t b, int64_t pairs, int nslice, int64_t& p,
+                                         int& slice) {
+    if (nslice == 1) {
+        p = b;
+        slice = 0;
+        return;
+    }
+    const int64_t full = (pairs / 8) * 16;
+    if (b < full) {
+        const int64_t xcd = b % 8, jx = b / 8;
+        slice = (int)(jx % 2);
+        p = (jx / 2) * 8 + xcd;
+    } else {
+        const int64_t t = b - full;
+        slice = (int)(t % 2);
+        p = (pairs / 8) * 8 + t / 2;
+    }
+}
+
+// NS: 16-column strips per wave; NS = 2 takes a whole head per workgroup, NS = 1 one 64-column
+// slice of it (two workgroups per head, for grids that would otherwise leave CUs idle)
+template <int NS>
 __global__ __launch_bounds__(256) void kda_c64_carry_kernel(PrefillArgs a,
                                                             const C64Work* __restrict__ ws,
                                                             const int* __restrict__ coff,
@@ -509,24 +572,28 @@ __global__ __launch_bounds__(256) void kda_c64_carry_kernel(PrefillArgs a,
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     const int64_t H = a.H;
-    const int64_t p = blockIdx.x, n = p / H, h = p % H;
+    int64_t p;
+    int slice;
+    map_pair(blockIdx.x, a.N * H, 2 / NS, p, slice);
+    const int64_t n = p / H, h = p % H;
+    auto vblk = [&](int m) { return 4 * slice + w + 4 * m; };   // 16-column block of strip m
     int64_t bos, eos, j0;
     if (a.cu) { bos = a.cu[n]; eos = a.cu[n + 1]; j0 = coff[n]; }
     else { bos = n * a.T; eos = bos + a.T; j0 = n * ((a.T + CL - 1) / CL); }
     int64_t nch = eos > bos ? (eos - bos + CL - 1) / CL : 0;
     nch = max<int64_t>(min<int64_t>(nch, nrec_chunks - j0), 0);   // malformed offsets stay in bounds
 
-    // state strips m = 0, 1: rows 16 mb + 4 lg + r, column 16 w + 64 m + ln
+    // state strips m: rows 16 mb + 4 lg + r, column 16 vblk(m) + ln
     const int64_t sbase = p * (int64_t)(D * D);
-    f32x4 S[2][8];
+    f32x4 S[NS][8];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < NS; ++m)
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                S[m][mb][r] = a.h0 ? a.h0[sbase + (int64_t)(16 * mb + 4 * lg + r) * D + 16 * w +
-                                          64 * m + ln]
+                S[m][mb][r] = a.h0 ? a.h0[sbase + (int64_t)(16 * mb + 4 * lg + r) * D +
+                                          16 * vblk(m) + ln]
                                    : 0.f;
 
     bf16x4 eye;
@@ -558,15 +625,15 @@ __global__ __launch_bounds__(256) void kda_c64_carry_kernel(PrefillArgs a,
     bf16_t* o = static_cast<bf16_t*>(a.o);
 
     // this wave's columns of a chunk: Ut and Z of strips m (16-column blocks w + 4 m)
-    struct Own { f32x4 ut[NSUB][2]; uint2 z[NSUB][2]; };
+    struct Own { f32x4 ut[NSUB][NS]; uint2 z[NSUB][NS]; };
     auto fetch_own = [&](int64_t jx, Own& d) {
         const C64Work* wk = ws + (jx * H + h);
 #pragma unroll
         for (int sb = 0; sb < NSUB; ++sb)
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                d.ut[sb][m] = wk->ut[sb][w + 4 * m][lane];
-                d.z[sb][m] = wk->z[sb][w + 4 * m][lane];
+            for (int m = 0; m < NS; ++m) {
+                d.ut[sb][m] = wk->ut[sb][vblk(m)][lane];
+                d.z[sb][m] = wk->z[sb][vblk(m)][lane];
             }
     };
     // chunk c from LDS buffer c % 2 and the wave's own registers; the next chunk's data in flight
@@ -578,34 +645,36 @@ __global__ __launch_bounds__(256) void kda_c64_carry_kernel(PrefillArgs a,
         }
         const CarryBuf& B = buf[b];
         // bf16 copy of the chunk-start state (B operands over 32-channel groups)
-        bf16x8 Sb[2][4];
+        bf16x8 Sb[NS][4];
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < NS; ++m)
 #pragma unroll
             for (int gi = 0; gi < 4; ++gi)
                 Sb[m][gi] = cat8(bf4(S[m][2 * gi]), bf4(S[m][2 * gi + 1]));
-        bf16x4 Ub[NSUB][2];
+        bf16x4 Ub[NSUB][NS];
         const int64_t t0 = bos + c * CL;
 #pragma unroll
         for (int sb = 0; sb < NSUB; ++sb) {
-            f32x4 XW[2] = {zero4(), zero4()}, XQ[2] = {zero4(), zero4()};
+            f32x4 XW[NS], XQ[NS];
+#pragma unroll
+            for (int m = 0; m < NS; ++m) XW[m] = XQ[m] = zero4();
 #pragma unroll
             for (int gi = 0; gi < 4; ++gi) {
                 const bf16x8 wf = B.w[sb][gi][lane], qf = B.qpp[sb][gi][lane];
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
+                for (int m = 0; m < NS; ++m) {
                     XW[m] = mma32(wf, Sb[m][gi], XW[m]);
                     XQ[m] = mma32(qf, Sb[m][gi], XQ[m]);
                 }
             }
             const int64_t tok = t0 + ST * sb + ln;
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
+            for (int m = 0; m < NS; ++m) {
                 Ub[sb][m] = bf4(cur.ut[sb][m] - XW[m]);                           // U
                 const f32x4 O = XQ[m] + unpack4(cur.z[sb][m]);                    // O
                 const bf16x4 Ot = bf4(mma16(bf4(O), eye, zero4()));              // token-major
                 if (tok < eos)
-                    *reinterpret_cast<uint2*>(o + (tok * H + h) * D + 16 * w + 64 * m + 4 * lg) =
+                    *reinterpret_cast<uint2*>(o + (tok * H + h) * D + 16 * vblk(m) + 4 * lg) =
                         as_u2(Ot);
             }
         }
@@ -616,7 +685,7 @@ __global__ __launch_bounds__(256) void kda_c64_carry_kernel(PrefillArgs a,
             const bf16x8 k01 = cat8(as_bf4(B.kl[0][mb][lane]), as_bf4(B.kl[1][mb][lane]));
             const bf16x8 k23 = cat8(as_bf4(B.kl[2][mb][lane]), as_bf4(B.kl[3][mb][lane]));
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
+            for (int m = 0; m < NS; ++m) {
                 f32x4 acc = S[m][mb] * e;
                 acc = mma32(k01, cat8(Ub[0][m], Ub[1][m]), acc);
                 acc = mma32(k23, cat8(Ub[2][m], Ub[3][m]), acc);
@@ -641,12 +710,12 @@ __global__ __launch_bounds__(256) void kda_c64_carry_kernel(PrefillArgs a,
     }
     if (a.hT) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < NS; ++m)
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    a.hT[sbase + (int64_t)(16 * mb + 4 * lg + r) * D + 16 * w + 64 * m + ln] =
+                    a.hT[sbase + (int64_t)(16 * mb + 4 * lg + r) * D + 16 * vblk(m) + ln] =
                         S[m][mb][r];
     }
 }
@@ -671,8 +740,13 @@ hipError_t launch_prefill_c64_mfma(const PrefillArgs& a, void* workspace, int64_
     if (nchunks > 0)
         hipLaunchKernelGGL(kda_c64_prep_kernel, dim3((unsigned)nchunks, (unsigned)a.H), dim3(256),
                            0, s, a, ws, coff, nchunks);
-    hipLaunchKernelGGL(kda_c64_carry_kernel, dim3((unsigned)(a.N * a.H)), dim3(256), 0, s, a, ws,
-                       coff, nchunks);
+    const int64_t pairs = a.N * a.H;
+    if (pairs >= 256)   // the pairs alone fill the chip: a whole head per workgroup
+        hipLaunchKernelGGL(kda_c64_carry_kernel<2>, dim3((unsigned)pairs), dim3(256), 0, s, a, ws,
+                           coff, nchunks);
+    else
+        hipLaunchKernelGGL(kda_c64_carry_kernel<1>, dim3((unsigned)(2 * pairs)), dim3(256), 0, s,
+                           a, ws, coff, nchunks);
     return hipGetLastError();
 }
 

@@ -524,8 +524,7 @@ C64_CASES = SMALL + [
 ]
 
 
-@pytest.mark.parametrize("case", C64_CASES,
-                         ids=lambda c: f"{c[0]}-H{c[1]}-{c[2]}x{c[3]}-{c[4]}-{c[6]}")
+@pytest.mark.parametrize("case", C64_CASES, ids=_small_id)
 def test_chunk64_small(oracle_mod, case):
     dev = _dev()
     from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd_chunk64
@@ -541,6 +540,58 @@ def test_chunk64_small(oracle_mod, case):
     _say(f"chunk64 {lens} {dk}x{dv} {dt} {gate}: error o={eo:.3e} hT={eh:.3e}")
     assert np.isfinite(to64(o)).all() and np.isfinite(to64(hT)).all()
     assert eo <= TOL[dt] and eh <= TOL[dt]
+
+
+@pytest.mark.parametrize("case", [
+    ([300], 2, 128, 128, "bf16", 0.05, "sigmoid", False),
+    ([130, 64, 65, 1, 0, 255], 3, 128, 128, "bf16", 0.1, "sigmoid_shiftm1", True),
+], ids=_small_id)
+def test_chunk64_float32_path_bf16(oracle_mod, case, monkeypatch):
+    """bf16 inputs through the float32 vector chunk-64 kernel (the matrix-core path switched off)."""
+    monkeypatch.setenv("KDA_FORCE_GENERAL", "1")
+    test_chunk64_small(oracle_mod, case)
+
+
+def test_chunk64_workspace_reuse():
+    """The workspace's contents on entry do not matter: a second call with a smaller input on the
+    first call's workspace matches a call on a fresh one bit for bit; a short one is refused."""
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import KDAError, inputs, kda_chunk_fwd_chunk64
+    from linear_attention_recurrence_08_amd.kda import kda_chunk_fwd_chunk64_workspace_bytes
+    big = inputs.make_inputs([200, 77, 130], 3, 128, 128, "bf16", seed=5, h0_sigma=0.1,
+                             packed=True).to(dev)
+    small = inputs.make_inputs([90, 33], 3, 128, 128, "bf16", seed=6, h0_sigma=0.1,
+                               packed=True).to(dev)
+
+    def need(x):
+        q = x.call_views()[0]
+        return kda_chunk_fwd_chunk64_workspace_bytes(q, x.cu_seqlens, x.num_seqs, 1, q.shape[0],
+                                                     x.H, x.dk, x.dv)
+    ws = torch.full((need(big),), 0xAB, dtype=torch.uint8, device=dev)
+    kda_chunk_fwd_chunk64(*big.call_views(), h0=big.h0, cu_seqlens=big.cu_seqlens, workspace=ws)
+    o1, h1 = kda_chunk_fwd_chunk64(*small.call_views(), h0=small.h0, cu_seqlens=small.cu_seqlens,
+                                   workspace=ws)
+    o2, h2 = kda_chunk_fwd_chunk64(*small.call_views(), h0=small.h0, cu_seqlens=small.cu_seqlens)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    short = torch.empty((need(small) - 256,), dtype=torch.uint8, device=dev)
+    with pytest.raises(KDAError):
+        kda_chunk_fwd_chunk64(*small.call_views(), h0=small.h0, cu_seqlens=small.cu_seqlens,
+                              workspace=short)
+
+
+def test_chunk64_varlen_16seq_H96(oracle_mod):
+    dev = _dev()
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd_chunk64
+    x = inputs.make_workload("varlen_16seq_H96_d128_bf16")
+    xd = x.to(dev)
+    o, hT = kda_chunk_fwd_chunk64(*xd.call_views(), h0=xd.h0, cu_seqlens=xd.cu_seqlens)
+    torch.cuda.synchronize()
+    heads = [5, 90]
+    o_ref, h_ref = oracle_prefill(oracle_mod, x, heads)
+    eo, eh = err(to64(o[:, heads]), o_ref), err(to64(hT[:, heads]), h_ref)
+    _say(f"chunk64 varlen H96: error o={eo:.3e} hT={eh:.3e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
 
 
 def test_chunk64_matches_chunk16_f32():
