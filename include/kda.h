@@ -131,7 +131,7 @@ int kda_chunk_fwd_chunk64(const void* q, const void* k, const void* v, const voi
 /*
  * kda_chunk_fwd_chunk64_workspace_bytes -- bytes of workspace kda_chunk_fwd_chunk64 needs for
  * these arguments (only whether cu_seqlens is NULL matters; its contents are not read): 0 for the
- * float32 path; for the matrix-core path, 97 KiB per (64-token chunk, head) plus the chunk
+ * float32 path; for the matrix-core path, 80.5 KiB per (64-token chunk, head) plus the chunk
  * offsets of a variable-length batch.  0 as well for arguments kda_chunk_fwd_chunk64 rejects.
  */
 size_t kda_chunk_fwd_chunk64_workspace_bytes(const int32_t* cu_seqlens, int num_seqs, int B,

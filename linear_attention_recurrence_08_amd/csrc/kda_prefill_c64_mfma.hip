@@ -99,7 +99,7 @@ struct C64Work {
     bf16x8 w[NSUB][4][64];     // [sub-tile][32-channel group][lane]: A operands of W (token-major)
     bf16x8 qpp[NSUB][4][64];   // the same for Qpp
     uint2 kl[NSUB][8][64];     // [sub-tile][16-channel block][lane]: acc(Kl block), bf16
-    f32x4 ut[NSUB][8][64];     // [sub-tile][16-column block][lane]: acc(Ut block)
+    uint2 ut[NSUB][8][64];     // [sub-tile][16-column block][lane]: acc(Ut block), bf16
     uint2 z[NSUB][8][64];      // acc(Z block), bf16
     float el[D];               // e^{Gam_L} per channel
 };
@@ -481,7 +481,7 @@ __global__ __launch_bounds__(256, 2) void kda_c64_prep_kernel(PrefillArgs a, C64
                 Ut = mma32(po.tb8[pp], B8, Ut);       // Ut = Tb V
                 Zt = mma32(po.y38[pp], B8, Zt);       // Z = P Tb V
             }
-            out->ut[sb][vb][lane] = Ut;
+            out->ut[sb][vb][lane] = as_u2(bf4(Ut));
             out->z[sb][vb][lane] = as_u2(bf4(Zt));
         }
     }
@@ -625,7 +625,7 @@ __global__ __launch_bounds__(256) void kda_c64_carry_kernel(PrefillArgs a,
     bf16_t* o = static_cast<bf16_t*>(a.o);
 
     // this wave's columns of a chunk: Ut and Z of strips m (16-column blocks w + 4 m)
-    struct Own { f32x4 ut[NSUB][NS]; uint2 z[NSUB][NS]; };
+    struct Own { uint2 ut[NSUB][NS]; uint2 z[NSUB][NS]; };
     auto fetch_own = [&](int64_t jx, Own& d) {
         const C64Work* wk = ws + (jx * H + h);
 #pragma unroll
@@ -670,7 +670,7 @@ __global__ __launch_bounds__(256) void kda_c64_carry_kernel(PrefillArgs a,
             const int64_t tok = t0 + ST * sb + ln;
 #pragma unroll
             for (int m = 0; m < NS; ++m) {
-                Ub[sb][m] = bf4(cur.ut[sb][m] - XW[m]);                           // U
+                Ub[sb][m] = bf4(unpack4(cur.ut[sb][m]) - XW[m]);                  // U
                 const f32x4 O = XQ[m] + unpack4(cur.z[sb][m]);                    // O
                 const bf16x4 Ot = bf4(mma16(bf4(O), eye, zero4()));              // token-major
                 if (tok < eos)
