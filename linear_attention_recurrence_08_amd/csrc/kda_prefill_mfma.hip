@@ -38,8 +38,9 @@
 //      strip for the whole sequence, and writes o.
 // Three waves share each SIMD.  Loads run two tiles ahead of their use.  All products use
 // v_mfma_f32_16x16x{16,32}_bf16.  Token-major -> channel-major changes of layout are LDS transpose
-// reads where the data already sits in LDS, and products with 0/1 selector matrices on the
-// matrix cores otherwise (both exact for bf16 data).
+// reads where the data already sits in LDS, and a product with a 0/1 selector matrix on the
+// matrix cores for g (both exact for bf16 data).  The output and P Ut are formed as transposed
+// products (operands swapped), which leaves them token-major as o is stored.
 //
 // Fragment conventions for a 16x16 block, lane l = ln + 16 lg (ln = l % 16, lg = l / 16):
 //   accumulator  acc(X): register r holds X[4 lg + r][ln]
@@ -175,7 +176,7 @@ struct FromB {                 // stage B2 -> stage S (indexed by tile % 2)
     bf16x8 w[4][64];           // A operands of W per 32-channel k-step
     bf16x8 qpp[4][64];         // A operands of Qpp per 32-channel k-step
     f32x4 ut[4 * NS][64];      // Ut per strip (accumulator fragments)
-    typename PutOf<NS>::T put[4 * NS][64];   // P Ut per strip
+    typename PutOf<NS>::T put[4 * NS][64];   // (P Ut)^T per strip (token-major like o)
 };
 template <int NS>
 struct Shared {
@@ -238,8 +239,6 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     for (int hh = 0; hh < 2; ++hh)
         for (int j = 0; j < 8; ++j)
             sel[hh][j] = (__bf16)((lg == (ln >> 2) && j == 4 * hh + (ln & 3)) ? 1.f : 0.f);
-    bf16x4 eye;      // identity (B operand, K = 16)
-    for (int j = 0; j < 4; ++j) eye[j] = (__bf16)((4 * lg + j == ln) ? 1.f : 0.f);
     // M^T scaled by log2(e) as a two-term bf16 split (hi + lo = log2(e) to 5e-6 relative), with
     // M[i][j] = -1 for j > i: row i of M g gives -log2(e) sum_{j>i} g_j, the exponent in base 2
     bf16x4 scanHi, scanLo;
@@ -463,7 +462,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         for (int m = 0; m < NS; ++m) {
             const bf16x4 vcs = lds_tr16(&A.vraw[s + 4 * m][src]);  // column-major V
             B.ut[s + 4 * m][lane] = mma16(TbTb, vcs, zero4());     // Tb V
-            const f32x4 pu = mma16(Y3b, vcs, zero4());             // P Tb V
+            const f32x4 pu = mma16(vcs, Y3b, zero4());             // (P Tb V)^T
             if constexpr (NS == 1) B.put[s][lane] = pu;
             else B.put[s + 4 * m][lane] = as_u2(bf4(pu));
         }
@@ -490,7 +489,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             for (int m = 0; m < NS; ++m) {
                 const bf16x8 sb = cat8(bf4(S[m][2 * ks]), bf4(S[m][2 * ks + 1]));
                 XW[m] = mma32(wf, sb, XW[m]);
-                XQ[m] = mma32(qf, sb, XQ[m]);
+                XQ[m] = mma32(sb, qf, XQ[m]);   // (Qpp St)^T: o already token-major
             }
         }
         bf16x4 Ub[NS];
@@ -500,7 +499,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             f32x4 O;
             if constexpr (NS == 1) O = XQ[m] + B.put[s][lane];
             else O = XQ[m] + unpack4(B.put[s + 4 * m][lane]);
-            Ot[m] = bf4(mma16(bf4(O), eye, zero4()));    // token-major o
+            Ot[m] = bf4(O);
         }
         // S <- St + Kd^T U, blocks outside and strips inside: each Kd fragment serves both strips
 #pragma unroll
