@@ -29,7 +29,8 @@
 // update, the latter as K = 32 products over pairs of sub-tiles.  Fragment conventions as in the
 // 16-token kernel: acc(X) register r holds X[4 lg + r][ln]; the A operand of Z = X Y is acc(X^T),
 // the B operand acc(Y); for K = 32, slot j of lane group lg stands for index 16 (j / 4) + 4 lg +
-// (j % 4).
+// (j % 4).  Z and the output are formed as transposed products (operands swapped), so both come
+// out token-major, the layout o is stored in.
 #include "kda_internal.h"
 
 namespace kda {
@@ -100,7 +101,7 @@ struct C64Work {
     bf16x8 qpp[NSUB][4][64];   // the same for Qpp
     uint2 kl[NSUB][8][64];     // [sub-tile][16-channel block][lane]: acc(Kl block), bf16
     uint2 ut[NSUB][8][64];     // [sub-tile][16-column block][lane]: acc(Ut block), bf16
-    uint2 z[NSUB][8][64];      // acc(Z block), bf16
+    uint2 z[NSUB][8][64];      // acc(Z^T block), bf16 (token-major, as o is stored)
     float el[D];               // e^{Gam_L} per channel
 };
 static_assert(sizeof(C64Work) % 256 == 0, "workspace records stay 256-byte aligned");
@@ -479,7 +480,7 @@ __global__ __launch_bounds__(256, 2) void kda_c64_prep_kernel(PrefillArgs a, C64
                 if (pp >= po.npairs) break;
                 const bf16x8 B8 = cat8(v_acc(2 * pp, vb), v_acc(2 * pp + 1, vb));
                 Ut = mma32(po.tb8[pp], B8, Ut);       // Ut = Tb V
-                Zt = mma32(po.y38[pp], B8, Zt);       // Z = P Tb V
+                Zt = mma32(B8, po.y38[pp], Zt);       // Z^T = (P Tb V)^T
             }
             out->ut[sb][vb][lane] = as_u2(bf4(Ut));
             out->z[sb][vb][lane] = as_u2(bf4(Zt));
@@ -596,9 +597,6 @@ __global__ __launch_bounds__(256) void kda_c64_carry_kernel(PrefillArgs a,
                                           16 * vblk(m) + ln]
                                    : 0.f;
 
-    bf16x4 eye;
-    for (int jx = 0; jx < 4; ++jx) eye[jx] = (__bf16)((4 * lg + jx == ln) ? 1.f : 0.f);
-
     // the shared part of chunk jx (W, Qpp, Kl, e^{Gam_L}) in flight in registers
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     u32x4 pre[kCarryPer];
@@ -664,15 +662,14 @@ __global__ __launch_bounds__(256) void kda_c64_carry_kernel(PrefillArgs a,
 #pragma unroll
                 for (int m = 0; m < NS; ++m) {
                     XW[m] = mma32(wf, Sb[m][gi], XW[m]);
-                    XQ[m] = mma32(qf, Sb[m][gi], XQ[m]);
+                    XQ[m] = mma32(Sb[m][gi], qf, XQ[m]);   // (Qpp S)^T: token-major
                 }
             }
             const int64_t tok = t0 + ST * sb + ln;
 #pragma unroll
             for (int m = 0; m < NS; ++m) {
                 Ub[sb][m] = bf4(unpack4(cur.ut[sb][m]) - XW[m]);                  // U
-                const f32x4 O = XQ[m] + unpack4(cur.z[sb][m]);                    // O
-                const bf16x4 Ot = bf4(mma16(bf4(O), eye, zero4()));              // token-major
+                const bf16x4 Ot = bf4(XQ[m] + unpack4(cur.z[sb][m]));            // O^T
                 if (tok < eos)
                     *reinterpret_cast<uint2*>(o + (tok * H + h) * D + 16 * vblk(m) + 4 * lg) =
                         as_u2(Ot);
