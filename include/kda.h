@@ -138,6 +138,53 @@ size_t kda_chunk_fwd_chunk64_workspace_bytes(const int32_t* cu_seqlens, int num_
                                              int T, int H, int dk, int dv, int dtype);
 
 /*
+ * kda_chunk_fwd_split -- kda_chunk_fwd for equal-length sequences, with each sequence also cut
+ * into token ranges that run at the same time, for batches too small to fill the chip (one GPU's
+ * share of the heads at batch 1, for instance).  The recurrence is affine in the state ("Kimi K3's
+ * hybrid block, from first principles", section "From linear attention to the delta rule": a tile
+ * maps its entering state S to M S + B, so any run of tokens does too), so a segment that starts
+ * from an unknown state S_in has S_t = M_t S_in + B_t.  Segment 0 runs from h0; every later
+ * segment runs twice in the same launch, from a zero state with its values (B_t, outputs
+ * B_t^T q_t) and from the identity with v = 0 (M_t, outputs M_t^T q_t).  A composition step then
+ * chains S_in(s + 1) = M_s S_in(s) + B_s, writes hT, and adds S_in(s)^T (M_t^T q_t) to the outputs
+ * of segment s.  About twice the state work of the later segments buys a serial chain of T / P
+ * tokens instead of T.
+ *
+ * Arguments as kda_chunk_fwd without cu_seqlens (B sequences of length T), plus
+ *   segments         the number of token ranges P requested (at most 16); 0 lets the library
+ *                    choose (kda_chunk_fwd_split_segments).  Segments are a multiple of 64
+ *                    tokens, so fewer may be used than requested
+ *   workspace        device memory of at least kda_chunk_fwd_split_workspace_bytes(...) bytes,
+ *                    256-byte aligned, owned by the caller; contents on entry do not matter and
+ *                    are undefined on return; may be NULL when that size is 0
+ *   workspace_bytes  its size
+ * The split applies to KDA_BF16 with dk = dv = 128 and B * H <= 65535; otherwise, or when one
+ * segment results, the call is kda_chunk_fwd and needs no workspace.  Results equal
+ * kda_chunk_fwd's up to rounding (the outputs of later segments are rounded to bf16 twice).
+ * Returns KDA_OK, KDA_ERR_SHAPE for segments < 0, KDA_ERR_WORKSPACE, or kda_chunk_fwd's errors.
+ */
+int kda_chunk_fwd_split(const void* q, const void* k, const void* v, const void* g,
+                        const void* beta, const float* h0, void* o, float* hT,
+                        int B, int T, int H, int dk, int dv, int dtype, int segments,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_fwd_split_segments -- the number of segments kda_chunk_fwd_split uses for these
+ * arguments and request (1: no split).  With segments = 0 it is the largest P whose
+ * 2 (2 P - 1) B H matrix-core workgroups hold one of the 256 compute units each, with at least
+ * 256 tokens per segment, and 1 once 2 B H >= 128.
+ */
+int kda_chunk_fwd_split_segments(int B, int T, int H, int dk, int dv, int dtype, int segments);
+
+/*
+ * kda_chunk_fwd_split_workspace_bytes -- bytes of workspace kda_chunk_fwd_split needs: 0 without
+ * a split; else B T H 256 bytes (the M_t^T q_t outputs in bf16) rounded up to 256, plus
+ * P * 2 * B * H * 64 KiB (the final states of both runs of every segment).
+ */
+size_t kda_chunk_fwd_split_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype,
+                                           int segments);
+
+/*
  * kda_chunk_fwd_snapshots -- kda_chunk_fwd that also saves the state at every multiple of
  * snap_stride tokens of each sequence, for prefix caching.  A KDA layer keeps one state that
  * summarises the whole prefix, so a cached prefix can be resumed only from a state saved at

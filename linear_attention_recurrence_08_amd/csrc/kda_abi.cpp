@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -80,13 +81,55 @@ int check_gate_range(const void* g, int64_t count, int dtype, hipStream_t s) {
     return KDA_OK;
 }
 
+// Token-range split of equal-length sequences: P segments of seg_len tokens (P = 1: none).  It
+// applies to bf16 with dk = dv = 128.  requested = 0 picks the largest P whose 2 (2 P - 1) B H
+// workgroups hold one CU each (256 CUs), with at least 256 tokens per segment; a requested count
+// is capped at kMaxSplit.  seg_len is a multiple of 64 so that the output fix-up's 64-token blocks
+// never straddle two segments.
+constexpr int64_t kMaxSplit = 16;
+struct SplitPlan {
+    int64_t P = 1;
+    int64_t seg_len = 0;
+};
+SplitPlan split_plan(int B, int T, int H, int dk, int dv, int dtype, int requested) {
+    SplitPlan sp;
+    if (dtype != KDA_BF16 || dk != 128 || dv != 128 || force_general() || B <= 0 || T <= 0 ||
+        H <= 0 || requested < 0)
+        return sp;
+    const int64_t pairs = static_cast<int64_t>(B) * H;
+    if (pairs > 65535) return sp;          // the completion kernels put pairs on the grid's y
+    int64_t P = requested;
+    if (P == 0) {
+        if (2 * pairs >= 128) return sp;
+        P = std::min<int64_t>((128 / pairs + 1) / 2, T / 256);
+    }
+    P = std::min(P, kMaxSplit);
+    if (P <= 1) return sp;
+    const int64_t len = ((T + P - 1) / P + 63) / 64 * 64;
+    const int64_t used = (T + len - 1) / len;
+    if (used <= 1) return sp;
+    sp.P = used;
+    sp.seg_len = len;
+    return sp;
+}
+// workspace of a split: M_t^T q_t of every token [B T, H, 128] bf16, then the final states of
+// both parts of every segment [P, 2, B H, 128, 128] float32
+size_t split_om_bytes(int B, int T, int H) {
+    return (static_cast<size_t>(B) * T * H * 128 * 2 + 255) / 256 * 256;
+}
+size_t split_workspace_bytes(const SplitPlan& sp, int B, int T, int H) {
+    if (sp.P <= 1) return 0;
+    return split_om_bytes(B, T, H) + static_cast<size_t>(sp.P) * 2 * B * H * 128 * 128 * 4;
+}
+
 // Prefill with optional snapshots (snap_stride 0: none); chunk64 selects the 64-token-chunk
-// kernel (no snapshots).
+// kernel (no snapshots); split (P > 1) the token-range split of the matrix-core kernel.
 int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
                    const float* h0, const int32_t* cu_seqlens, int num_seqs, void* o, float* hT,
                    float* snaps, const int32_t* snap_offsets, int snap_stride, int B, int T,
                    int H, int dk, int dv, int dtype, void* stream, bool chunk64 = false,
-                   void* workspace = nullptr, size_t workspace_bytes = 0) {
+                   void* workspace = nullptr, size_t workspace_bytes = 0,
+                   const SplitPlan* split = nullptr) {
     if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
     if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
     if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
@@ -109,6 +152,10 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, c
     if (N == 0 || (Ttot == 0 && !hT)) return KDA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     int64_t c64_chunks = -1;   // >= 0: the 64-token-chunk matrix-core path, with this many chunks
+    const bool splitting = split && split->P > 1 && !cu_seqlens && !want_snaps && !chunk64;
+    if (splitting && (!workspace || workspace_bytes < split_workspace_bytes(*split, B, T, H) ||
+                      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
+        return KDA_ERR_WORKSPACE;
     if (chunk64) {
         c64_chunks = c64_mfma_chunks(cu_seqlens != nullptr, N, B, T, dk, dv, dtype);
         if (c64_chunks >= 0 &&
@@ -152,7 +199,15 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, c
     }
 
     hipError_t e;
-    if (chunk64)
+    if (splitting) {
+        a.split = split->P;
+        a.seg_len = split->seg_len;
+        a.oM = workspace;
+        a.seg_states = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                split_om_bytes(B, T, H));
+        e = kda::launch_prefill_mfma(a, s);
+        if (e == hipSuccess) e = kda::launch_split_finish(a, s);
+    } else if (chunk64)
         e = c64_chunks >= 0 ? kda::launch_prefill_c64_mfma(a, workspace, c64_chunks, s)
                             : kda::launch_prefill_c64(a, s);
     else if (dtype == KDA_BF16 && dk == 128 && dv == 128 && !force_general())
@@ -182,8 +237,9 @@ const char* kda_status_string(int status) {
             return "snapshot stride must be a positive multiple of 16, with matching snap_offsets";
         case KDA_ERR_ALIGN: return "output-stage buffers must be 16-byte aligned";
         case KDA_ERR_WORKSPACE:
-            return "workspace missing, smaller than kda_chunk_fwd_chunk64_workspace_bytes, or not "
-                   "256-byte aligned";
+            return "workspace missing, smaller than the size its query returns "
+                   "(kda_chunk_fwd_chunk64_workspace_bytes, kda_chunk_fwd_split_workspace_bytes), "
+                   "or not 256-byte aligned";
         default: return "unknown status";
     }
 }
@@ -213,6 +269,26 @@ size_t kda_chunk_fwd_chunk64_workspace_bytes(const int32_t* cu_seqlens, int num_
     const int64_t N = cu_seqlens ? num_seqs : B;
     const int64_t chunks = c64_mfma_chunks(cu_seqlens != nullptr, N, B, T, dk, dv, dtype);
     return chunks < 0 || N == 0 ? 0 : kda::c64_mfma_workspace_bytes(chunks, N, H);
+}
+
+int kda_chunk_fwd_split(const void* q, const void* k, const void* v, const void* g,
+                        const void* beta, const float* h0, void* o, float* hT,
+                        int B, int T, int H, int dk, int dv, int dtype, int segments,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (segments < 0) return KDA_ERR_SHAPE;
+    const SplitPlan sp = split_plan(B, T, H, dk, dv, dtype, segments);
+    return chunk_fwd_impl(q, k, v, g, beta, h0, nullptr, B, o, hT, nullptr, nullptr, 0, B, T, H,
+                          dk, dv, dtype, stream, false, workspace, workspace_bytes, &sp);
+}
+
+int kda_chunk_fwd_split_segments(int B, int T, int H, int dk, int dv, int dtype, int segments) {
+    return static_cast<int>(split_plan(B, T, H, dk, dv, dtype, segments).P);
+}
+
+size_t kda_chunk_fwd_split_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype,
+                                           int segments) {
+    if (B < 0 || T < 0 || H <= 0 || !rows_ok(H, dk, dv)) return 0;
+    return split_workspace_bytes(split_plan(B, T, H, dk, dv, dtype, segments), B, T, H);
 }
 
 int kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const void* g,

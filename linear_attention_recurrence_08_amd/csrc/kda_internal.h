@@ -26,6 +26,16 @@ struct PrefillArgs {
     int64_t T;            // per-sequence length when cu == nullptr
     int64_t H, dk, dv;
     int dtype;            // 0 = bf16, 1 = f32
+    // token-range split (split > 1; bf16, dk = dv = 128, cu == nullptr): every sequence is cut
+    // into `split` segments of seg_len tokens (a multiple of 64).  Segment 0 runs from h0 into o;
+    // each later segment runs as a part B (zero entering state, into o) and a part M (v = 0,
+    // identity entering state, its outputs M_t^T q_t into oM); every run's final state goes to
+    // seg_states.  launch_split_finish composes the entering states, writes hT and adds
+    // S_in^T (M_t^T q_t) to the outputs of the later segments.
+    int64_t split = 1;
+    int64_t seg_len = 0;
+    void* oM = nullptr;             // [Ttot, H, dk] bf16
+    float* seg_states = nullptr;    // [split, 2, N * H, dk, dv]
 };
 
 struct DecodeArgs {
@@ -86,6 +96,7 @@ struct FrontArgs {
 hipError_t launch_prefill_general(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);   // bf16, dk = dv = 128
 hipError_t launch_prefill_c64(const PrefillArgs& a, hipStream_t s);    // 64-token chunks
+hipError_t launch_split_finish(const PrefillArgs& a, hipStream_t s);   // after a split prefill
 hipError_t launch_decode_d128(const DecodeArgs& a, hipStream_t s);     // dk = dv = 128
 hipError_t launch_output_gate(const GateArgs& a, hipStream_t s);      // 16-byte aligned rows
 hipError_t launch_frontend(const FrontArgs& a, hipStream_t s);        // 16-byte aligned rows

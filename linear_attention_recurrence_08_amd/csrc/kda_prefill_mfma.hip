@@ -201,7 +201,14 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
 
     int64_t p;
     int slice;
-    map_workgroup(blockIdx.x, a.N * H, D / BVT, p, slice);
+    // with a token-range split, unit u of pair p is segment 0 (u = 0), the part B of segment u
+    // (0 < u < split) or the part M of segment u - split + 1; units of one pair share nothing
+    const int64_t units = a.split > 1 ? 2 * a.split - 1 : 1;
+    map_workgroup(blockIdx.x, a.N * H * units, D / BVT, p, slice);
+    const int64_t unit = p / (a.N * H);
+    p %= a.N * H;
+    const int seg = (int)(unit < a.split ? unit : unit - a.split + 1);
+    const bool part_m = unit >= a.split;   // the transition part: v = 0, identity entering state
     const int64_t h = p % H;
     int64_t n = p / H;
     if (a.cu && a.N > 1 && a.N <= kLptMaxSeqs) {
@@ -225,6 +232,11 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     int64_t bos, eos;
     if (a.cu) { bos = a.cu[n]; eos = a.cu[n + 1]; }
     else { bos = n * a.T; eos = bos + a.T; }
+    if (a.split > 1) {                     // the segment's tokens (seg_len is a multiple of 16)
+        bos += seg * a.seg_len;
+        eos = min(eos, bos + a.seg_len);
+        bos = min(bos, eos);
+    }
     const int64_t ntiles = (eos - bos + C - 1) / C;
 
     const bf16_t* __restrict__ q = static_cast<const bf16_t*>(a.q);
@@ -232,7 +244,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     const bf16_t* __restrict__ v = static_cast<const bf16_t*>(a.v);
     const bf16_t* __restrict__ g = static_cast<const bf16_t*>(a.g);
     const bf16_t* __restrict__ beta = static_cast<const bf16_t*>(a.beta);
-    bf16_t* __restrict__ o = static_cast<bf16_t*>(a.o);
+    bf16_t* __restrict__ o = static_cast<bf16_t*>(part_m ? a.oM : a.o);
 
     // ---- constant fragments ----
     bf16x8 sel[2];   // selector: channel-major transpose of 32-channel-group half hh (B, K = 32)
@@ -258,16 +270,19 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     // (declared here, set and used by the stage-S waves only, so that it occupies registers in
     // their branch alone)
     f32x4 S[NS][8];
-    // the state strips to or from a [dk, dv] float32 matrix (src == nullptr: zeros)
-    auto state_in = [&](const float* src) {
+    // the state strips to or from a [dk, dv] float32 matrix (src == nullptr: zeros, or the
+    // identity for the transition part of a split segment)
+    auto state_in = [&](const float* src, bool ident) {
 #pragma unroll
         for (int m = 0; m < NS; ++m)
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    S[m][mb][r] = src ? src[(int64_t)(16 * mb + 4 * lg + r) * D + col + 64 * m]
-                                      : 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t row = 16 * mb + 4 * lg + r;
+                    S[m][mb][r] = src ? src[row * D + col + 64 * m]
+                                      : (ident && row == col + 64 * m ? 1.f : 0.f);
+                }
     };
     auto state_out = [&](float* dst) {
 #pragma unroll
@@ -278,10 +293,19 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
                 for (int r = 0; r < 4; ++r)
                     dst[(int64_t)(16 * mb + 4 * lg + r) * D + col + 64 * m] = S[m][mb][r];
     };
+    // entering state and final-state destination of this run: with a split, segment 0 starts
+    // from h0, later segments from zero (part B) or the identity (part M), and every final state
+    // goes to the segment-state buffer [split, 2, N * H, dk, dv]
+    const float* h_in = a.h0 ? a.h0 + sbase : nullptr;
+    float* h_out = a.hT ? a.hT + sbase : nullptr;
+    if (a.split > 1) {
+        if (seg > 0) h_in = nullptr;
+        h_out = a.seg_states + ((2 * seg + (part_m ? 1 : 0)) * a.N * H + p) * (int64_t)(D * D);
+    }
     if (ntiles == 0) {
-        if (role == 0 && a.hT) {
-            state_in(a.h0 ? a.h0 + sbase : nullptr);
-            state_out(a.hT + sbase);
+        if (role == 0 && h_out) {
+            state_in(h_in, part_m);
+            state_out(h_out);
         }
         return;
     }
@@ -314,7 +338,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(g + e0), (short)0, nrec, kBufferFlags);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(v + e0), (short)0, nrec, kBufferFlags);
+            (void*)(v + e0), (short)0, part_m ? 0 : nrec, kBufferFlags);   // part M: v = 0
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(beta + (t0 * H + h)), (short)0, nrec_b, kBufferFlags);
         R.q0 = ld8(rq, vo_qkg);
@@ -575,7 +599,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             lds_barrier();
         }
     } else {
-        state_in(a.h0 ? a.h0 + sbase : nullptr);
+        state_in(h_in, part_m);
         lds_barrier();
         lds_barrier();
         lds_barrier();
@@ -603,14 +627,15 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             store_o(i, Ot, true);
             lds_barrier();
         }
-        if (a.hT) state_out(a.hT + sbase);
+        if (h_out) state_out(h_out);
     }
 }
 
 }  // namespace
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s) {
-    const int64_t pairs = a.N * a.H;
+    // with a token-range split every (sequence, head) pair runs 2 split - 1 units
+    const int64_t pairs = a.N * a.H * (a.split > 1 ? 2 * a.split - 1 : 1);
     if (pairs <= 0) return hipSuccess;
     if (pairs >= 256) {
         // every CU is busy with one workgroup per (sequence, head): a workgroup takes all 128

@@ -4,6 +4,9 @@ in the library's HIP kernels.  PyTorch supplies device memory and the current st
     kda_chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, output_final_state=True)
         -> (o, hT)
     kda_chunk_fwd_chunk64(...)   the same with 64-token chunks of four 16-token sub-tiles
+    kda_chunk_fwd_split(q, k, v, g, beta, h0=None, segments=0, ...) -> (o, hT)
+                                 the same for equal-length sequences, each also cut into token
+                                 ranges that run concurrently (small batches)
     kda_chunk_fwd_snapshots(q, k, v, g, beta, snap_stride, ...) -> (o, hT, snaps, snap_offsets)
     kda_decode_step(q, k, v, g, beta, S) -> o         (S is updated in place)
     kda_decode_step_gated(q, k, v, g, beta, S, gate, weight=None, eps=...) -> (o, y)
@@ -58,6 +61,13 @@ def load_library():
         lib.kda_chunk_fwd_chunk64_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32,
                                                               i32]
         lib.kda_chunk_fwd_chunk64_workspace_bytes.restype = ctypes.c_size_t
+        lib.kda_chunk_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                            i32, i32, i32, vp, ctypes.c_size_t, vp]
+        lib.kda_chunk_fwd_split.restype = i32
+        lib.kda_chunk_fwd_split_segments.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        lib.kda_chunk_fwd_split_segments.restype = i32
+        lib.kda_chunk_fwd_split_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        lib.kda_chunk_fwd_split_workspace_bytes.restype = ctypes.c_size_t
         lib.kda_chunk_fwd_snapshots.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                                 i32, i32, i32, i32, i32, i32, i32, vp]
         lib.kda_chunk_fwd_snapshots.restype = i32
@@ -202,6 +212,44 @@ def kda_chunk_fwd_chunk64(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: 
         _ptr(o), _ptr(hT), B, T, H, dk, dv, _dtype_code(q), _ptr(workspace), nbytes, _stream(dev))
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd_chunk64")
+    return o, hT
+
+
+def kda_chunk_fwd_split_segments(q: torch.Tensor, B: int, T: int, H: int, dk: int, dv: int,
+                                 segments: int = 0) -> int:
+    """Segments kda_chunk_fwd_split uses for these sizes and request (1: no split)."""
+    return int(load_library().kda_chunk_fwd_split_segments(B, T, H, dk, dv, _dtype_code(q),
+                                                           segments))
+
+
+def kda_chunk_fwd_split_workspace_bytes(q: torch.Tensor, B: int, T: int, H: int, dk: int,
+                                        dv: int, segments: int = 0) -> int:
+    """Workspace bytes kda_chunk_fwd_split needs for these sizes and request (0: none)."""
+    return int(load_library().kda_chunk_fwd_split_workspace_bytes(B, T, H, dk, dv,
+                                                                  _dtype_code(q), segments))
+
+
+def kda_chunk_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                        beta: torch.Tensor, h0: Optional[torch.Tensor] = None,
+                        output_final_state: bool = True, segments: int = 0,
+                        o: Optional[torch.Tensor] = None, hT: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None
+                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_chunk_fwd for B equal-length sequences with each sequence also cut into token ranges
+    that run concurrently (segments = 0: the library's choice).  Same results as kda_chunk_fwd;
+    `workspace` (a contiguous device tensor of at least kda_chunk_fwd_split_workspace_bytes bytes)
+    is allocated here when not given."""
+    dev, B, T, H, dk, dv, N, o, hT = _prefill_args(q, k, v, g, beta, h0, None,
+                                                   output_final_state, o, hT)
+    need = kda_chunk_fwd_split_workspace_bytes(q, B, T, H, dk, dv, segments)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().kda_chunk_fwd_split(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT), B, T, H,
+        dk, dv, _dtype_code(q), int(segments), _ptr(workspace), nbytes, _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd_split")
     return o, hT
 
 

@@ -463,6 +463,8 @@ def _check_front(out, ref, dt, label):
     # full-width heads in float32 (four-token register sets), and bf16 with dk != dv
     ([70, 33, 0, 64], 2, 128, 128, "f32", True),
     ([96, 7, 64], 3, 64, 128, "bf16", False),
+    # five heads: a wave's second group of four holds one head; chunks cross sequence starts
+    ([100, 29, 64, 1], 5, 128, 128, "bf16", True),
 ])
 def test_frontend_small(oracle_mod, lens, H, dk, dv, dt, state):
     dev = _dev()
@@ -619,3 +621,77 @@ def test_chunk64_T4096_H96(oracle_mod):
     eo, eh = err(to64(o[:, heads]), o_ref), err(to64(hT[:, heads]), h_ref)
     _say(f"chunk64 T4096 H96: error o={eo:.3e} hT={eh:.3e}")
     assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------------------------------------
+# token-range split (kda_chunk_fwd_split): later segments run from a zero state and from the
+# identity in the same launch; the composition step chains their entering states and corrects
+# their outputs
+# ------------------------------------------------------------------------------------------------
+SPLIT = [
+    # (equal seq_lens, H, h0_sigma, gate, segments requested; 0 = automatic)
+    ([300], 2, None, "sigmoid", 2),
+    ([1000], 3, 0.1, "sigmoid", 0),
+    ([1000, 1000], 2, 0.1, "bimodal", 5),
+    ([257], 1, 0.05, "zero", 4),             # alpha = 1; segments of 128, 128 and 1 tokens
+    ([700], 2, 0.1, "sigmoid_shiftm1", 11),  # 11 segments of 64 tokens, the last 60
+]
+
+
+def gpu_split(x, dev, segments, **kw):
+    from linear_attention_recurrence_08_amd import kda_chunk_fwd_split
+    xd = x.to(dev)
+    o, hT = kda_chunk_fwd_split(*xd.call_views(), h0=xd.h0, segments=segments, **kw)
+    torch.cuda.synchronize()
+    return o.reshape(x.total_tokens, x.H, x.dv), hT
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: f"{c[0]}-H{c[1]}-{c[3]}-P{c[4]}")
+def test_split_small(oracle_mod, case):
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd_split_segments
+    lens, H, sig, gate, segs = case
+    dev = _dev()
+    x = inputs.make_inputs(lens, H=H, dk=128, dv=128, dtype="bf16", seed=300 + len(lens) + H,
+                           gate=gate, h0_sigma=sig, packed=False)
+    P = kda_chunk_fwd_split_segments(x.q, x.B, x.T, H, 128, 128, segs)
+    assert P > 1
+    _say(f"split {lens} H={H} gate={gate}: {P} segments")
+    o, hT = gpu_split(x, dev, segs)
+    o_ref, h_ref = oracle_prefill(oracle_mod, x)
+    eo, eh = err(to64(o), o_ref), err(to64(hT), h_ref)
+    _say(f"split: error o={eo:.3e} hT={eh:.3e}")
+    assert np.isfinite(to64(o)).all() and np.isfinite(to64(hT)).all()
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
+
+
+def test_split_in_place_state():
+    # hT may be h0 itself: segment 0 reads h0 in the prefill, the composition writes hT after it
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd_split
+    dev = _dev()
+    x = inputs.make_inputs([640], H=2, dk=128, dv=128, dtype="bf16", seed=331, h0_sigma=0.1,
+                           packed=False)
+    xd = x.to(dev)
+    o_a, h_a = kda_chunk_fwd_split(*xd.call_views(), h0=xd.h0, segments=3)
+    S = xd.h0.clone()
+    o_b, h_b = kda_chunk_fwd_split(*xd.call_views(), h0=S, hT=S, segments=3)
+    torch.cuda.synchronize()
+    assert h_b.data_ptr() == S.data_ptr()
+    assert torch.equal(o_a, o_b) and torch.equal(h_a, S)
+
+
+def test_split_T4096_H12(oracle_mod):
+    # one GPU's share of K3's 96 heads under 8-way head sharding, at batch 1: the automatic split
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd_split_segments
+    dev = _dev()
+    x = inputs.make_inputs([4096], H=12, dk=128, dv=128, dtype="bf16", seed=340, packed=False)
+    assert kda_chunk_fwd_split_segments(x.q, 1, 4096, 12, 128, 128, 0) == 5
+    o, hT = gpu_split(x, dev, 0)
+    o1, h1 = gpu_prefill(x, dev)
+    d_o, d_h = err(to64(o), to64(o1)), err(to64(hT), to64(h1))
+    _say(f"split vs unsplit, all heads: o {d_o:.3e} hT {d_h:.3e}")
+    assert d_o <= TOL["bf16"] and d_h <= TOL["bf16"]
+    heads = [0, 11]
+    o_ref, h_ref = oracle_prefill(oracle_mod, x, heads)
+    eo, eh = err(to64(o[:, heads]), o_ref), err(to64(hT[:, heads]), h_ref)
+    _say(f"split T4096 H12 heads {heads}: error o={eo:.3e} hT={eh:.3e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
