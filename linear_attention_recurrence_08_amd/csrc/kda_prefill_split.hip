@@ -9,9 +9,10 @@
 // outputs are o_t = S_t^T q_t = B_t^T q_t + S_in^T (M_t^T q_t).  The prefill kernel leaves B_t^T q_t
 // in o, M_t^T q_t in oM and the final B and M of every segment in seg_states; here
 //   S_in(1) = final state of segment 0,   S_in(s + 1) = M_s S_in(s) + B_s,   hT = S_in(split),
-// then o_t += S_in(s)^T (M_t^T q_t) for every token of segment s >= 1.  Both steps run in float32
-// on the vector ALUs (the products are small: 128 x 128 per segment and head, and 128 x 128 per
-// token of the later segments).
+// then o_t += S_in(s)^T (M_t^T q_t) for every token of segment s >= 1.  Both are matrix-core
+// products whose float32 operands enter as hi + lo bf16 pairs (float32-accurate): one 128 x 128
+// product per segment and head on the serial chain of the composition, and one 128 x 128 product
+// per token of the later segments for the correction.
 #include "kda_internal.h"
 
 namespace kda {
@@ -19,95 +20,171 @@ namespace {
 
 constexpr int D = 128;
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t pk2(float x, float y) {
+    const f32x2 v = {x, y};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ float hi_of(uint32_t u, int half) {   // one bf16 of a pair, as float
+    return __uint_as_float(half ? (u & 0xffff0000u) : (u << 16));
+}
+// eight float32 values as hi and lo bf16 operands
+__device__ __forceinline__ void split8(const float x[8], bf16x8& hi, bf16x8& lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h[i] = pk2(x[2 * i], x[2 * i + 1]);
+        l[i] = pk2(x[2 * i] - hi_of(h[i], 0), x[2 * i + 1] - hi_of(h[i], 1));
+    }
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    hi = __builtin_bit_cast(bf16x8, (u32x4){h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]});
+}
+// K = 32 operand slot j of lane group lg stands for index 16 (j / 4) + 4 lg + (j % 4)
+__device__ __forceinline__ int kslot(int j, int lg) { return 16 * (j >> 2) + 4 * lg + (j & 3); }
+
 // One workgroup per (16-column block, pair): the columns of the state evolve independently under
-// the row maps M_s.  Thread (row r, columns c8 .. c8 + 7 of the block).  S_in(s) replaces B_s in
-// seg_states once B_s has been used (each thread overwrites only the entries it read).
+// the row maps M_s.  The block of the current entering state sits in LDS; wave w forms rows
+// [32 w, 32 w + 32) of M_s S_in(s) + B_s as two 16 x 16 matrix-core blocks, with both float32
+// operands split into hi + lo bf16 parts (hi hi + hi lo + lo hi: float32-accurate products).
+// S_in(s) replaces B_s in seg_states once B_s has been read (each lane overwrites only the
+// entries it read).
 __global__ __launch_bounds__(256) void kda_split_compose_kernel(PrefillArgs a) {
     __shared__ float sc[D][16];            // the column block of the current entering state
-    const int tid = threadIdx.x;
-    const int r = tid >> 1, c8 = (tid & 1) * 8;
-    const int64_t cbase = 16 * (int64_t)blockIdx.x + c8;
+    const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int w = tid >> 6;
+    const int64_t c0 = 16 * (int64_t)blockIdx.x;
     const int64_t p = blockIdx.y, pairs = a.N * a.H;
     auto slot = [&](int64_t seg, int part) {
         return a.seg_states + ((2 * seg + part) * pairs + p) * (int64_t)(D * D);
     };
-    {
-        const float* src = slot(0, 0) + r * D + cbase;      // S_in(1)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) sc[r][c8 + c] = src[c];
-    }
+    for (int i = tid; i < D * 16; i += 256) sc[i >> 4][i & 15] = slot(0, 0)[(i >> 4) * D + c0 + (i & 15)];
     __syncthreads();
     for (int64_t sg = 1; sg < a.split; ++sg) {
-        float* bs = slot(sg, 0) + r * D + cbase;            // B_s, row r
-        const float* ms = slot(sg, 1) + r * D;              // M_s, row r
-        float acc[8];
+        const float* ms = slot(sg, 1);
+        float* bs = slot(sg, 0);
+        // B operands: the entering state's block over channel steps ks (column ln)
+        bf16x8 bh[4], bl[4];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = bs[c];
-        for (int kk = 0; kk < D; kk += 4) {
-            const float4 m4 = *reinterpret_cast<const float4*>(ms + kk);
-            const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+        for (int ks = 0; ks < 4; ++ks) {
+            float x[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int c = 0; c < 8; ++c) acc[c] += mv[i] * sc[kk + i][c8 + c];
+            for (int j = 0; j < 8; ++j) x[j] = sc[32 * ks + kslot(j, lg)][ln];
+            split8(x, bh[ks], bl[ks]);
         }
+        f32x4 acc[2];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) bs[c] = sc[r][c8 + c];  // S_in(s) in B_s's place
+        for (int b = 0; b < 2; ++b) {
+            const int r0 = 32 * w + 16 * b;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[b][r] = bs[(r0 + 4 * lg + r) * D + c0 + ln];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                // A operand: row r0 + ln of M_s over the channels of step ks
+                const float* mrow = ms + (r0 + ln) * D + 32 * ks + 4 * lg;
+                const float4 m0 = *reinterpret_cast<const float4*>(mrow);
+                const float4 m1 = *reinterpret_cast<const float4*>(mrow + 16);
+                const float x[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+                bf16x8 ah, al;
+                split8(x, ah, al);
+                acc[b] = mma32(ah, bh[ks], acc[b]);
+                acc[b] = mma32(ah, bl[ks], acc[b]);
+                acc[b] = mma32(al, bh[ks], acc[b]);
+            }
+        }
+        // S_in(s) in B_s's place (the entries this lane read), then the new block into LDS
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 32 * w + 16 * b + 4 * lg + r;
+                bs[row * D + c0 + ln] = sc[row][ln];
+            }
         __syncthreads();
 #pragma unroll
-        for (int c = 0; c < 8; ++c) sc[r][c8 + c] = acc[c];
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[32 * w + 16 * b + 4 * lg + r][ln] = acc[b][r];
         __syncthreads();
     }
     if (a.hT) {
-        float* dst = a.hT + p * (int64_t)(D * D) + r * D + cbase;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) dst[c] = sc[r][c8 + c];
+        float* dst = a.hT + p * (int64_t)(D * D);
+        for (int i = tid; i < D * 16; i += 256) dst[(i >> 4) * D + c0 + (i & 15)] = sc[i >> 4][i & 15];
     }
 }
 
-// One workgroup per (64-token block of the later segments, pair); a block lies in one segment
-// because seg_len is a multiple of 64.  The block's M_t^T q_t rows are staged transposed in LDS as
-// float32; thread (column j, 32 tokens) accumulates sum_c S_in[c][j] (M_t^T q_t)[c] and adds it to
-// the bf16 output B_t^T q_t already in o.
+// One wave per (64-token block of the later segments, pair); a block lies in one segment because
+// seg_len is a multiple of 64.  The correction out^T = S_in^T (M_t^T q_t)^T is a matrix-core product
+// per 16 x 16 block (column block of S_in, 16 tokens): S_in's float32 values enter as a hi + lo
+// pair of bf16 operands (x = hi + lo to 2^-17 relative), M_t^T q_t as the bf16 values the prefill
+// stored; the transposed form leaves each lane 4 consecutive columns of one token, added to the
+// bf16 output B_t^T q_t already in o.
 constexpr int TB = 64;
 __global__ __launch_bounds__(256) void kda_split_fixup_kernel(PrefillArgs a) {
-    __shared__ float mt[D][TB];
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
     const int64_t p = blockIdx.y, H = a.H, n = p / H, h = p % H;
-    const int64_t trel = a.seg_len + (int64_t)blockIdx.x * TB;   // within the sequence
-    if (trel >= a.T) return;
+    const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t trel = a.seg_len + blk * TB;                   // within the sequence
+    if (trel >= a.T) return;                                     // the whole wave leaves
     const int nt = (int)min<int64_t>(TB, a.T - trel);
     const int64_t seg = trel / a.seg_len;
     const float* S = a.seg_states + (2 * seg * a.N * H + p) * (int64_t)(D * D);   // S_in(seg)
     const int64_t t0 = n * a.T + trel;                           // packed token index
     const bf16_t* om = static_cast<const bf16_t*>(a.oM);
     bf16_t* o = static_cast<bf16_t*>(a.o);
-    for (int i = tid; i < TB * D; i += 256) {
-        const int tk = i / D, c = i % D;
-        mt[c][tk] = tk < nt ? bf16_to_f32(om[((t0 + tk) * H + h) * D + c]) : 0.f;
-    }
-    __syncthreads();
-    const int j = tid & (D - 1), tq = (tid >> 7) * 32;
-    float acc[32];
+    // B operands: (M_t^T q_t)^T over channel steps ks, token ln of each 16-token sub-block tb
+    bf16x8 bm[4][4];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] = 0.f;
-    for (int c = 0; c < D; ++c) {
-        const float sv = S[c * D + j];
+    for (int tb = 0; tb < 4; ++tb) {
+        const int tok = 16 * tb + ln;
 #pragma unroll
-        for (int i = 0; i < 32; i += 4) {
-            const float4 m4 = *reinterpret_cast<const float4*>(&mt[c][tq + i]);
-            acc[i] += sv * m4.x;
-            acc[i + 1] += sv * m4.y;
-            acc[i + 2] += sv * m4.z;
-            acc[i + 3] += sv * m4.w;
+        for (int ks = 0; ks < 4; ++ks) {
+            uint2 u0 = make_uint2(0u, 0u), u1 = make_uint2(0u, 0u);
+            if (tok < nt) {
+                const bf16_t* row = om + ((t0 + tok) * H + h) * D + 32 * ks + 4 * lg;
+                u0 = *reinterpret_cast<const uint2*>(row);
+                u1 = *reinterpret_cast<const uint2*>(row + 16);
+            }
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            bm[tb][ks] = __builtin_bit_cast(bf16x8, (u32x4){u0.x, u0.y, u1.x, u1.y});
         }
     }
+#pragma unroll 1
+    for (int cb = 0; cb < D / 16; ++cb) {
+        // A operands: S_in^T rows (S_in columns 16 cb + ln) over the channels of step ks
+        bf16x8 ah[4], al[4];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const int tk = tq + i;
-        if (tk < nt) {
-            bf16_t* dst = o + ((t0 + tk) * H + h) * D + j;
-            *dst = f32_to_bf16(bf16_to_f32(*dst) + acc[i]);
+        for (int ks = 0; ks < 4; ++ks) {
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = S[(32 * ks + kslot(j, lg)) * D + 16 * cb + ln];
+            split8(x, ah[ks], al[ks]);
+        }
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                acc = mma32(ah[ks], bm[tb][ks], acc);
+                acc = mma32(al[ks], bm[tb][ks], acc);
+            }
+            // acc register r: column 16 cb + 4 lg + r of token 16 tb + ln
+            const int tok = 16 * tb + ln;
+            if (tok < nt) {
+                uint2* dst = reinterpret_cast<uint2*>(o + ((t0 + tok) * H + h) * D + 16 * cb +
+                                                      4 * lg);
+                const uint2 u = *dst;
+                *dst = make_uint2(pk2(hi_of(u.x, 0) + acc[0], hi_of(u.x, 1) + acc[1]),
+                                  pk2(hi_of(u.y, 0) + acc[2], hi_of(u.y, 1) + acc[3]));
+            }
         }
     }
 }
@@ -120,10 +197,12 @@ hipError_t launch_split_finish(const PrefillArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(kda_split_compose_kernel, dim3(D / 16, (unsigned)pairs), dim3(256), 0, s,
                        a);
     const int64_t later = a.T - a.seg_len;
-    if (later > 0)
-        hipLaunchKernelGGL(kda_split_fixup_kernel, dim3((unsigned)((later + TB - 1) / TB),
+    if (later > 0) {
+        const int64_t blocks = (later + TB - 1) / TB;            // one wave each, four per group
+        hipLaunchKernelGGL(kda_split_fixup_kernel, dim3((unsigned)((blocks + 3) / 4),
                                                         (unsigned)pairs),
                            dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 
