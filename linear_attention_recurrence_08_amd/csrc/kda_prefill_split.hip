@@ -20,6 +20,14 @@ namespace {
 
 constexpr int D = 128;
 
+// Workgroup barrier that orders LDS only: the global loads issued ahead stay in flight across it,
+// and the global stores need no ordering within the launch.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -67,9 +75,30 @@ __global__ __launch_bounds__(256) void kda_split_compose_kernel(PrefillArgs a) {
         return a.seg_states + ((2 * seg + part) * pairs + p) * (int64_t)(D * D);
     };
     for (int i = tid; i < D * 16; i += 256) sc[i >> 4][i & 15] = slot(0, 0)[(i >> 4) * D + c0 + (i & 15)];
-    __syncthreads();
-    for (int64_t sg = 1; sg < a.split; ++sg) {
+    lds_barrier();
+    // this wave's rows of M_s (A operands: row r0 + ln over the channels of step ks) and of B_s
+    // (the accumulator's start), loaded one step ahead so that the chain waits only on LDS and
+    // the matrix cores
+    float4 mr[2][4][2];
+    f32x4 br[2];
+    auto load_step = [&](int64_t sg) {
         const float* ms = slot(sg, 1);
+        const float* bs = slot(sg, 0);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int r0 = 32 * w + 16 * b;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const float* mrow = ms + (r0 + ln) * D + 32 * ks + 4 * lg;
+                mr[b][ks][0] = *reinterpret_cast<const float4*>(mrow);
+                mr[b][ks][1] = *reinterpret_cast<const float4*>(mrow + 16);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) br[b][r] = bs[(r0 + 4 * lg + r) * D + c0 + ln];
+        }
+    };
+    if (a.split > 1) load_step(1);
+    for (int64_t sg = 1; sg < a.split; ++sg) {
         float* bs = slot(sg, 0);
         // B operands: the entering state's block over channel steps ks (column ln)
         bf16x8 bh[4], bl[4];
@@ -80,26 +109,27 @@ __global__ __launch_bounds__(256) void kda_split_compose_kernel(PrefillArgs a) {
             for (int j = 0; j < 8; ++j) x[j] = sc[32 * ks + kslot(j, lg)][ln];
             split8(x, bh[ks], bl[ks]);
         }
+        bf16x8 mh[2][4], ml[2][4];
         f32x4 acc[2];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            const int r0 = 32 * w + 16 * b;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[b][r] = bs[(r0 + 4 * lg + r) * D + c0 + ln];
+            acc[b] = br[b];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                // A operand: row r0 + ln of M_s over the channels of step ks
-                const float* mrow = ms + (r0 + ln) * D + 32 * ks + 4 * lg;
-                const float4 m0 = *reinterpret_cast<const float4*>(mrow);
-                const float4 m1 = *reinterpret_cast<const float4*>(mrow + 16);
+                const float4 m0 = mr[b][ks][0], m1 = mr[b][ks][1];
                 const float x[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-                bf16x8 ah, al;
-                split8(x, ah, al);
-                acc[b] = mma32(ah, bh[ks], acc[b]);
-                acc[b] = mma32(ah, bl[ks], acc[b]);
-                acc[b] = mma32(al, bh[ks], acc[b]);
+                split8(x, mh[b][ks], ml[b][ks]);
             }
         }
+        if (sg + 1 < a.split) load_step(sg + 1);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                acc[b] = mma32(mh[b][ks], bh[ks], acc[b]);
+                acc[b] = mma32(mh[b][ks], bl[ks], acc[b]);
+                acc[b] = mma32(ml[b][ks], bh[ks], acc[b]);
+            }
         // S_in(s) in B_s's place (the entries this lane read), then the new block into LDS
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -108,12 +138,12 @@ __global__ __launch_bounds__(256) void kda_split_compose_kernel(PrefillArgs a) {
                 const int row = 32 * w + 16 * b + 4 * lg + r;
                 bs[row * D + c0 + ln] = sc[row][ln];
             }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 4; ++r) sc[32 * w + 16 * b + 4 * lg + r][ln] = acc[b][r];
-        __syncthreads();
+        lds_barrier();
     }
     if (a.hT) {
         float* dst = a.hT + p * (int64_t)(D * D);
@@ -157,17 +187,34 @@ __global__ __launch_bounds__(256) void kda_split_fixup_kernel(PrefillArgs a) {
             bm[tb][ks] = __builtin_bit_cast(bf16x8, (u32x4){u0.x, u0.y, u1.x, u1.y});
         }
     }
-#pragma unroll 1
+    // S_in^T rows (S_in columns 16 cb + ln) over the channels of step ks, for the A operands;
+    // the next column block's values are loaded while the current one is multiplied
+    float xs[4][8];
+    auto load_s = [&](int cb) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xs[ks][j] = S[(32 * ks + kslot(j, lg)) * D + 16 * cb + ln];
+    };
+    load_s(0);
+    // this lane's 4 columns 16 cb + 4 lg .. + 3 of token 16 tb + ln (B_t^T q_t, bf16), for every
+    // column block, all in flight from the start
+    uint2 ob[D / 16][4];
+#pragma unroll
+    for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const int tok = 16 * tb + ln;
+            ob[cb][tb] = tok < nt ? *reinterpret_cast<const uint2*>(
+                                        o + ((t0 + tok) * H + h) * D + 16 * cb + 4 * lg)
+                                  : make_uint2(0u, 0u);
+        }
+#pragma unroll
     for (int cb = 0; cb < D / 16; ++cb) {
-        // A operands: S_in^T rows (S_in columns 16 cb + ln) over the channels of step ks
         bf16x8 ah[4], al[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            float x[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] = S[(32 * ks + kslot(j, lg)) * D + 16 * cb + ln];
-            split8(x, ah[ks], al[ks]);
-        }
+        for (int ks = 0; ks < 4; ++ks) split8(xs[ks], ah[ks], al[ks]);
+        if (cb + 1 < D / 16) load_s(cb + 1);
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -179,11 +226,10 @@ __global__ __launch_bounds__(256) void kda_split_fixup_kernel(PrefillArgs a) {
             // acc register r: column 16 cb + 4 lg + r of token 16 tb + ln
             const int tok = 16 * tb + ln;
             if (tok < nt) {
-                uint2* dst = reinterpret_cast<uint2*>(o + ((t0 + tok) * H + h) * D + 16 * cb +
-                                                      4 * lg);
-                const uint2 u = *dst;
-                *dst = make_uint2(pk2(hi_of(u.x, 0) + acc[0], hi_of(u.x, 1) + acc[1]),
-                                  pk2(hi_of(u.y, 0) + acc[2], hi_of(u.y, 1) + acc[3]));
+                const uint2 u = ob[cb][tb];
+                *reinterpret_cast<uint2*>(o + ((t0 + tok) * H + h) * D + 16 * cb + 4 * lg) =
+                    make_uint2(pk2(hi_of(u.x, 0) + acc[0], hi_of(u.x, 1) + acc[1]),
+                               pk2(hi_of(u.y, 0) + acc[2], hi_of(u.y, 1) + acc[3]));
             }
         }
     }
