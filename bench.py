@@ -14,7 +14,9 @@ gate; 3 x 256 B per (token, head) in bf16) on the same [4096, 96, 128] shape, an
 (short convolution, Swish, L2 norm, sigmoid beta, bounded log-decay: reads 3 dk + dv values and
 beta's logit, writes as many per (token, head)) on the same token and head count.  A `varlen`
 object times the prefill on the variable-length batch (16 sequences of 1,024-16,384 tokens with
-initial states, packed with cu_seqlens).
+initial states, packed with cu_seqlens).  A `head_share` object times one GPU's share of the heads under
+8-way head sharding (12 of 96 heads, T = 4096, batch 1) with kda_chunk_fwd and with
+kda_chunk_fwd_split (each sequence also cut into token ranges that run concurrently).
 
 Roofline: algorithmic bytes per launch divided by the kernel's average duration, measured with
 HIP events recorded on the stream the kernels are launched on, against MI355X's 8 TB/s HBM.
@@ -79,6 +81,7 @@ def decode_bytes(d) -> int:
 # the build script (which holds the code-generation options).
 KERNEL_SOURCES = {
     "kda_chunk_fwd": "kda_prefill_mfma.hip",
+    "kda_chunk_fwd_split": ("kda_prefill_mfma.hip", "kda_prefill_split.hip"),
     "kda_chunk_fwd_chunk64": "kda_prefill_c64_mfma.hip",
     "kda_decode": "kda_decode.hip",
     "kda_output_gate": "kda_output_gate.hip",
@@ -91,9 +94,10 @@ def kernel_source_digest(kernel_tag: str) -> str:
     pkg = os.path.join(ROOT, "linear_attention_recurrence_08_amd")
     src = next(f for prefix, f in sorted(KERNEL_SOURCES.items(), key=lambda kv: -len(kv[0]))
                if kernel_tag.startswith(prefix))
+    srcs = (src,) if isinstance(src, str) else src
     h = hashlib.sha256()
-    for path in (os.path.join(pkg, "csrc", src), os.path.join(pkg, "csrc", "kda_internal.h"),
-                 os.path.join(pkg, "build.py")):
+    for path in tuple(os.path.join(pkg, "csrc", f) for f in srcs) + (
+            os.path.join(pkg, "csrc", "kda_internal.h"), os.path.join(pkg, "build.py")):
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -308,6 +312,74 @@ def time_launches(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps, wall  # ms per launch (one kernel per step), seconds
 
 
+def head_share(dev, stream, steps, warmup):
+    """Prefill of one GPU's share of K3's heads under 8-way head sharding (12 of 96, T = 4096,
+    batch 1): kda_chunk_fwd beside kda_chunk_fwd_split with the library's segment count."""
+    import torch
+    from linear_attention_recurrence_08_amd import (inputs, kda_chunk_fwd, kda_chunk_fwd_split,
+                                                    kda_chunk_fwd_split_segments,
+                                                    kda_chunk_fwd_split_workspace_bytes)
+    Hs, Ts = 12, 4096
+    xs = inputs.make_inputs([Ts], H=Hs, dk=128, dv=128, dtype="bf16", seed=1, packed=False)
+    xsd = xs.to(dev)
+    sviews = xsd.call_views()
+    o_s = torch.empty_like(xsd.v)
+    h_s = torch.empty((1, Hs, 128, 128), dtype=torch.float32, device=dev)
+    P = kda_chunk_fwd_split_segments(xsd.q, 1, Ts, Hs, 128, 128, 0)
+    sbytes = kda_chunk_fwd_split_workspace_bytes(xsd.q, 1, Ts, Hs, 128, 128, 0)
+    ws_s = torch.empty(max(sbytes, 1), dtype=torch.uint8, device=dev)
+    print(f"[bench] head share T={Ts} H={Hs}: {P} segments", file=sys.stderr, flush=True)
+
+    def share_plain():
+        kda_chunk_fwd(*sviews, o=o_s, hT=h_s)
+
+    def share_split():
+        kda_chunk_fwd_split(*sviews, segments=0, o=o_s, hT=h_s, workspace=ws_s)
+
+    sp_ms, _ = time_launches(share_plain, steps, warmup, stream)
+    ss_ms, _ = time_launches(share_split, steps, warmup, stream)
+    sb = prefill_bytes(xs)
+    return {
+        "workload": f"prefill_T{Ts}_H{Hs}_d128_bf16 (12 of 96 heads: one GPU under 8-way head "
+                    "sharding)",
+        "kernel": "kda_prefill_mfma (token-range split) + kda_split_compose + kda_split_fixup",
+        "segments": P, "workspace_bytes": sbytes,
+        "unsplit_ms_per_step": round(sp_ms, 5), "ms_per_step": round(ss_ms, 5),
+        "value": round(Ts / (ss_ms * 1e-3), 1), "unit": "tokens/s",
+        "vs_unsplit": round(sp_ms / ss_ms, 3),
+        "roofline": {"bound": "hbm", "achieved": round(sb / (ss_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(sb / (ss_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": sb},
+    }
+
+
+def summarize_split(trace_dir, command):
+    """profiles/kda_chunk_fwd_split_T4096_H12_d128_bf16_kernel_trace.md from a --kernel-trace
+    --stats run of `bench.py --head-share-only` (every kernel of that run: the unsplit prefill, and
+    the split's prefill, composition and correction)."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True):
+        rows += [r for r in csv.DictReader(open(f)) if "kda_" in r["Name"]]
+    path = os.path.join(ROOT, "profiles", "kda_chunk_fwd_split_T4096_H12_d128_bf16_kernel_trace.md")
+    with open(path, "w") as fo:
+        fo.write("# kda_chunk_fwd_split on prefill_T4096_H12_d128_bf16 (12 of 96 heads, batch 1): "
+                 "rocprofv3 kernel trace\n\n")
+        fo.write(f"command: `{command}`\n\n")
+        fo.write("kda_prefill_mfma_kernel<2, 64> is the unsplit prefill (24 workgroups); <1, 64> the "
+                 "split's launch (5 segments: 216 workgroups).\n\n")
+        fo.write("| kernel | calls | average ns | min ns | max ns |\n|---|---|---|---|---|\n")
+        for r in rows:
+            name = re.sub(r"\(kda::PrefillArgs\)|void |kda::\(anonymous namespace\)::", "",
+                          r["Name"])
+            fo.write(f"| {name} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} |\n")
+        fo.write(f"\nsource_digest: {kernel_source_digest('kda_chunk_fwd_split')}\n")
+    print("wrote", path)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -323,6 +395,12 @@ def main():
     ap.add_argument("--no-frontend", action="store_true")
     ap.add_argument("--no-chunk64", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-split", action="store_true")
+    ap.add_argument("--head-share-only", action="store_true",
+                    help="time only the 12-head prefill (kda_chunk_fwd beside kda_chunk_fwd_split)")
+    ap.add_argument("--summarize-split", metavar="DIR",
+                    help="write the split prefill's kernel-trace summary from a rocprofv3 run of "
+                         "--head-share-only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-pass", action="store_true",
                     help="run a 1 GiB calibration copy and 3 launches of each kernel (for "
@@ -332,6 +410,9 @@ def main():
                          "--stats run and/or FETCH_SIZE and WRITE_SIZE counter runs")
     ap.add_argument("--command", default="", help="command line recorded in the summaries")
     args = ap.parse_args()
+    if args.summarize_split:
+        summarize_split(args.summarize_split, args.command)
+        return
     if args.summarize:
         summarize(args.summarize, args.command)
         return
@@ -353,6 +434,9 @@ def main():
     stream = torch.cuda.current_stream(dev)
     if args.traffic_pass:
         traffic_pass(dev)
+        return
+    if args.head_share_only:
+        print(json.dumps(head_share(dev, stream, args.steps, args.warmup)))
         return
 
     # ---------------- prefill ----------------
@@ -465,6 +549,10 @@ def main():
             "chunk16_float32_vector_ms_per_step": round(f16ms, 4),
         }
         del o_c, hT_c, ws
+
+    # ---------------- one GPU's share of the heads: 12 of 96 (8-way head sharding), batch 1 ------
+    if not args.no_split:
+        result["head_share"] = head_share(dev, stream, args.steps, args.warmup)
 
     # ---------------- variable-length batch: 16 sequences of 1,024-16,384 tokens ----------------
     if not args.no_varlen and args.workload != VARLEN_WORKLOAD:
