@@ -268,6 +268,30 @@ def test_resume_from_saved_state_bitwise(oracle_mod):
     assert np.array_equal(h2, hT)
 
 
+def test_affine_in_the_entering_state(oracle_mod):
+    """The recurrence is affine in the state ("Kimi K3's hybrid block, from first principles",
+    section "From linear attention to the delta rule": a chunk maps its entering state S to
+    M S + B): a run from S_in equals its run from zero with the values (B_t, outputs B_t^T q_t)
+    plus M_t S_in, where M_t is the run from the identity with v = 0 (outputs M_t^T q_t), so
+    o_t = B_t^T q_t + S_in^T (M_t^T q_t).  This is what a token-range split composes."""
+    rng = np.random.default_rng(29)
+    T, H, dk, dv = 45, 2, 6, 5
+    q, k, v, g, beta, S_in = _rand_case(rng, T, H, dk, dv)
+    o, hT = oracle_mod.recurrence(q, k, v, g, beta, S_in)
+    oB, B = oracle_mod.recurrence(q, k, v, g, beta, None)
+    eye = np.broadcast_to(np.eye(dk), (1, H, dk, dk)).copy()
+    oM, M = oracle_mod.recurrence(q, k, np.zeros((T, H, dk)), g, beta, eye)
+    assert np.allclose(hT, np.einsum("nhij,nhjk->nhik", M, S_in) + B, rtol=0, atol=1e-12)
+    assert np.allclose(o, oB + np.einsum("thc,hcj->thj", oM, S_in[0]), rtol=0, atol=1e-12)
+    # composing two ranges: the second starts from the first's final state
+    o1, h1 = oracle_mod.recurrence(q[:20], k[:20], v[:20], g[:20], beta[:20], S_in)
+    oB2, B2 = oracle_mod.recurrence(q[20:], k[20:], v[20:], g[20:], beta[20:], None)
+    oM2, M2 = oracle_mod.recurrence(q[20:], k[20:], np.zeros((T - 20, H, dk)), g[20:],
+                                    beta[20:], eye)
+    assert np.allclose(np.einsum("nhij,nhjk->nhik", M2, h1) + B2, hT, rtol=0, atol=1e-12)
+    assert np.allclose(oB2 + np.einsum("thc,hcj->thj", oM2, h1[0]), o[20:], rtol=0, atol=1e-12)
+
+
 def test_decode_equals_prefill_steps(oracle_mod):
     rng = np.random.default_rng(24)
     q, k, v, g, beta, S0 = _rand_case(rng, 6, 2, 5, 4)
