@@ -695,3 +695,18 @@ def test_split_T4096_H12(oracle_mod):
     eo, eh = err(to64(o[:, heads]), o_ref), err(to64(hT[:, heads]), h_ref)
     _say(f"split T4096 H12 heads {heads}: error o={eo:.3e} hT={eh:.3e}")
     assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
+
+
+def test_split_T32768_H12(oracle_mod):
+    # long segments (6,592 tokens each): the composed entering states carry the decay of
+    # thousands of tokens; bimodal gates keep half the channels' memory long
+    from linear_attention_recurrence_08_amd import inputs
+    dev = _dev()
+    x = inputs.make_inputs([32768], H=12, dk=128, dv=128, dtype="bf16", seed=341, gate="bimodal",
+                           h0_sigma=0.02, packed=False)
+    o, hT = gpu_split(x, dev, 0)
+    heads = [0, 7]
+    o_ref, h_ref = oracle_prefill(oracle_mod, x, heads)
+    eo, eh = err(to64(o[:, heads]), o_ref), err(to64(hT[:, heads]), h_ref)
+    _say(f"split T32768 H12 heads {heads}: error o={eo:.3e} hT={eh:.3e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
