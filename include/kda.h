@@ -138,9 +138,9 @@ size_t kda_chunk_fwd_chunk64_workspace_bytes(const int32_t* cu_seqlens, int num_
                                              int T, int H, int dk, int dv, int dtype);
 
 /*
- * kda_chunk_fwd_split -- kda_chunk_fwd for equal-length sequences, with each sequence also cut
- * into token ranges that run at the same time, for batches too small to fill the chip (one GPU's
- * share of the heads at batch 1, for instance).  The recurrence is affine in the state ("Kimi K3's
+ * kda_chunk_fwd_split -- kda_chunk_fwd with each sequence also cut into token ranges that run at
+ * the same time, for batches too small to fill the chip (one GPU's share of the heads at batch 1,
+ * for instance).  The recurrence is affine in the state ("Kimi K3's
  * hybrid block, from first principles", section "From linear attention to the delta rule": a tile
  * maps its entering state S to M S + B, so any run of tokens does too), so a segment that starts
  * from an unknown state S_in has S_t = M_t S_in + B_t.  Segment 0 runs from h0; every later
@@ -150,7 +150,12 @@ size_t kda_chunk_fwd_chunk64_workspace_bytes(const int32_t* cu_seqlens, int num_
  * of segment s.  About twice the state work of the later segments buys a serial chain of T / P
  * tokens instead of T.
  *
- * Arguments as kda_chunk_fwd without cu_seqlens (B sequences of length T), plus
+ * Arguments as kda_chunk_fwd, plus
+ *   max_seqlen       with cu_seqlens: the length the segment plan assumes for the longest
+ *                    sequence (the caller's bound; >= 0, 0 = no split).  Every sequence is cut
+ *                    into segments of the planned length, the last running to its end, so a
+ *                    bound below a real length costs speed, not correctness.  Ignored without
+ *                    cu_seqlens (the plan uses T)
  *   segments         the number of token ranges P requested (at most 16); 0 lets the library
  *                    choose (kda_chunk_fwd_split_segments).  Segments are a multiple of 64
  *                    tokens, so fewer may be used than requested
@@ -158,31 +163,36 @@ size_t kda_chunk_fwd_chunk64_workspace_bytes(const int32_t* cu_seqlens, int num_
  *                    256-byte aligned, owned by the caller; contents on entry do not matter and
  *                    are undefined on return; may be NULL when that size is 0
  *   workspace_bytes  its size
- * The split applies to KDA_BF16 with dk = dv = 128 and B * H <= 65535; otherwise, or when one
+ * The split applies to KDA_BF16 with dk = dv = 128 and N * H <= 65535; otherwise, or when one
  * segment results, the call is kda_chunk_fwd and needs no workspace.  Results equal
  * kda_chunk_fwd's up to rounding (the outputs of later segments are rounded to bf16 twice).
- * Returns KDA_OK, KDA_ERR_SHAPE for segments < 0, KDA_ERR_WORKSPACE, or kda_chunk_fwd's errors.
+ * Returns KDA_OK, KDA_ERR_SHAPE for segments < 0 or max_seqlen < 0 with cu_seqlens,
+ * KDA_ERR_WORKSPACE, or kda_chunk_fwd's errors.
  */
 int kda_chunk_fwd_split(const void* q, const void* k, const void* v, const void* g,
-                        const void* beta, const float* h0, void* o, float* hT,
+                        const void* beta, const float* h0, const int32_t* cu_seqlens,
+                        int num_seqs, int max_seqlen, void* o, float* hT,
                         int B, int T, int H, int dk, int dv, int dtype, int segments,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * kda_chunk_fwd_split_segments -- the number of segments kda_chunk_fwd_split uses for these
- * arguments and request (1: no split).  With segments = 0 it is the largest P whose
- * 2 (2 P - 1) B H matrix-core workgroups hold one of the 256 compute units each, with at least
- * 256 tokens per segment, and 1 once 2 B H >= 128.
+ * kda_chunk_fwd_split_segments -- the number of segments kda_chunk_fwd_split plans for these
+ * arguments and request (1: no split; only whether cu_seqlens is NULL matters, not its contents).
+ * With segments = 0 it is the largest P whose 2 (2 P - 1) N H matrix-core workgroups hold one of
+ * the 256 compute units each, with at least 256 tokens per segment of the planned length (T, or
+ * max_seqlen with cu_seqlens), and 1 once 2 N H >= 128.
  */
-int kda_chunk_fwd_split_segments(int B, int T, int H, int dk, int dv, int dtype, int segments);
+int kda_chunk_fwd_split_segments(const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int B,
+                                 int T, int H, int dk, int dv, int dtype, int segments);
 
 /*
  * kda_chunk_fwd_split_workspace_bytes -- bytes of workspace kda_chunk_fwd_split needs: 0 without
- * a split; else B T H 256 bytes (the M_t^T q_t outputs in bf16) rounded up to 256, plus
- * P * 2 * B * H * 64 KiB (the final states of both runs of every segment).
+ * a split; else Ttot H 256 bytes (the M_t^T q_t outputs in bf16) rounded up to 256, plus
+ * P * 2 * N * H * 64 KiB (the final states of both runs of every segment).
  */
-size_t kda_chunk_fwd_split_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype,
-                                           int segments);
+size_t kda_chunk_fwd_split_workspace_bytes(const int32_t* cu_seqlens, int num_seqs,
+                                           int max_seqlen, int B, int T, int H, int dk, int dv,
+                                           int dtype, int segments);
 
 /*
  * kda_chunk_fwd_snapshots -- kda_chunk_fwd that also saves the state at every multiple of

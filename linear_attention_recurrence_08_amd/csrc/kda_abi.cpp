@@ -81,45 +81,50 @@ int check_gate_range(const void* g, int64_t count, int dtype, hipStream_t s) {
     return KDA_OK;
 }
 
-// Token-range split of equal-length sequences: P segments of seg_len tokens (P = 1: none).  It
-// applies to bf16 with dk = dv = 128.  requested = 0 picks the largest P whose 2 (2 P - 1) B H
-// workgroups hold one CU each (256 CUs), with at least 256 tokens per segment; a requested count
-// is capped at kMaxSplit.  seg_len is a multiple of 64 so that the output fix-up's 64-token blocks
-// never straddle two segments.
+// Token-range split: every sequence is cut into segments of seg_len tokens, at most P of them,
+// the last running to the sequence end (P = 1: none).  It applies to bf16 with dk = dv = 128.
+// The plan is made for sequences of L tokens (T, or the caller's max_seqlen bound with
+// cu_seqlens): requested = 0 picks the largest P whose 2 (2 P - 1) N H workgroups hold one CU each
+// (256 CUs), with at least 256 tokens per segment; a requested count is capped at kMaxSplit.
+// seg_len is a multiple of 64 so that the output correction's 64-token blocks never straddle two
+// segments.
 constexpr int64_t kMaxSplit = 16;
 struct SplitPlan {
     int64_t P = 1;
     int64_t seg_len = 0;
 };
-SplitPlan split_plan(int B, int T, int H, int dk, int dv, int dtype, int requested) {
+SplitPlan split_plan(bool varlen, int num_seqs, int max_seqlen, int B, int T, int H, int dk,
+                     int dv, int dtype, int requested) {
     SplitPlan sp;
-    if (dtype != KDA_BF16 || dk != 128 || dv != 128 || force_general() || B <= 0 || T <= 0 ||
-        H <= 0 || requested < 0)
+    const int64_t N = varlen ? num_seqs : B;
+    const int64_t L = varlen ? max_seqlen : T;
+    if (dtype != KDA_BF16 || dk != 128 || dv != 128 || force_general() || N <= 0 || L <= 0 ||
+        H <= 0 || requested < 0 || (varlen && B != 1))
         return sp;
-    const int64_t pairs = static_cast<int64_t>(B) * H;
+    const int64_t pairs = N * H;
     if (pairs > 65535) return sp;          // the completion kernels put pairs on the grid's y
     int64_t P = requested;
     if (P == 0) {
         if (2 * pairs >= 128) return sp;
-        P = std::min<int64_t>((128 / pairs + 1) / 2, T / 256);
+        P = std::min<int64_t>((128 / pairs + 1) / 2, L / 256);
     }
     P = std::min(P, kMaxSplit);
     if (P <= 1) return sp;
-    const int64_t len = ((T + P - 1) / P + 63) / 64 * 64;
-    const int64_t used = (T + len - 1) / len;
+    const int64_t len = ((L + P - 1) / P + 63) / 64 * 64;
+    const int64_t used = (L + len - 1) / len;
     if (used <= 1) return sp;
     sp.P = used;
     sp.seg_len = len;
     return sp;
 }
-// workspace of a split: M_t^T q_t of every token [B T, H, 128] bf16, then the final states of
-// both parts of every segment [P, 2, B H, 128, 128] float32
-size_t split_om_bytes(int B, int T, int H) {
-    return (static_cast<size_t>(B) * T * H * 128 * 2 + 255) / 256 * 256;
+// workspace of a split: M_t^T q_t of every token [Ttot, H, 128] bf16, then the final states of
+// both parts of every segment [P, 2, N H, 128, 128] float32
+size_t split_om_bytes(int64_t Ttot, int H) {
+    return (static_cast<size_t>(Ttot) * H * 128 * 2 + 255) / 256 * 256;
 }
-size_t split_workspace_bytes(const SplitPlan& sp, int B, int T, int H) {
+size_t split_workspace_bytes(const SplitPlan& sp, int64_t N, int64_t Ttot, int H) {
     if (sp.P <= 1) return 0;
-    return split_om_bytes(B, T, H) + static_cast<size_t>(sp.P) * 2 * B * H * 128 * 128 * 4;
+    return split_om_bytes(Ttot, H) + static_cast<size_t>(sp.P) * 2 * N * H * 128 * 128 * 4;
 }
 
 // Prefill with optional snapshots (snap_stride 0: none); chunk64 selects the 64-token-chunk
@@ -152,8 +157,8 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, c
     if (N == 0 || (Ttot == 0 && !hT)) return KDA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     int64_t c64_chunks = -1;   // >= 0: the 64-token-chunk matrix-core path, with this many chunks
-    const bool splitting = split && split->P > 1 && !cu_seqlens && !want_snaps && !chunk64;
-    if (splitting && (!workspace || workspace_bytes < split_workspace_bytes(*split, B, T, H) ||
+    const bool splitting = split && split->P > 1 && !want_snaps && !chunk64;
+    if (splitting && (!workspace || workspace_bytes < split_workspace_bytes(*split, N, Ttot, H) ||
                       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
         return KDA_ERR_WORKSPACE;
     if (chunk64) {
@@ -204,7 +209,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, c
         a.seg_len = split->seg_len;
         a.oM = workspace;
         a.seg_states = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                split_om_bytes(B, T, H));
+                                                split_om_bytes(Ttot, H));
         e = kda::launch_prefill_mfma(a, s);
         if (e == hipSuccess) e = kda::launch_split_finish(a, s);
     } else if (chunk64)
@@ -272,23 +277,32 @@ size_t kda_chunk_fwd_chunk64_workspace_bytes(const int32_t* cu_seqlens, int num_
 }
 
 int kda_chunk_fwd_split(const void* q, const void* k, const void* v, const void* g,
-                        const void* beta, const float* h0, void* o, float* hT,
+                        const void* beta, const float* h0, const int32_t* cu_seqlens,
+                        int num_seqs, int max_seqlen, void* o, float* hT,
                         int B, int T, int H, int dk, int dv, int dtype, int segments,
                         void* workspace, size_t workspace_bytes, void* stream) {
-    if (segments < 0) return KDA_ERR_SHAPE;
-    const SplitPlan sp = split_plan(B, T, H, dk, dv, dtype, segments);
-    return chunk_fwd_impl(q, k, v, g, beta, h0, nullptr, B, o, hT, nullptr, nullptr, 0, B, T, H,
-                          dk, dv, dtype, stream, false, workspace, workspace_bytes, &sp);
+    if (segments < 0 || (cu_seqlens && max_seqlen < 0)) return KDA_ERR_SHAPE;
+    const SplitPlan sp = split_plan(cu_seqlens != nullptr, num_seqs, max_seqlen, B, T, H, dk, dv,
+                                    dtype, segments);
+    return chunk_fwd_impl(q, k, v, g, beta, h0, cu_seqlens, num_seqs, o, hT, nullptr, nullptr, 0,
+                          B, T, H, dk, dv, dtype, stream, false, workspace, workspace_bytes, &sp);
 }
 
-int kda_chunk_fwd_split_segments(int B, int T, int H, int dk, int dv, int dtype, int segments) {
-    return static_cast<int>(split_plan(B, T, H, dk, dv, dtype, segments).P);
+int kda_chunk_fwd_split_segments(const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int B,
+                                 int T, int H, int dk, int dv, int dtype, int segments) {
+    return static_cast<int>(split_plan(cu_seqlens != nullptr, num_seqs, max_seqlen, B, T, H, dk,
+                                       dv, dtype, segments).P);
 }
 
-size_t kda_chunk_fwd_split_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype,
-                                           int segments) {
-    if (B < 0 || T < 0 || H <= 0 || !rows_ok(H, dk, dv)) return 0;
-    return split_workspace_bytes(split_plan(B, T, H, dk, dv, dtype, segments), B, T, H);
+size_t kda_chunk_fwd_split_workspace_bytes(const int32_t* cu_seqlens, int num_seqs,
+                                           int max_seqlen, int B, int T, int H, int dk, int dv,
+                                           int dtype, int segments) {
+    if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !rows_ok(H, dk, dv)) return 0;
+    const bool varlen = cu_seqlens != nullptr;
+    const int64_t N = varlen ? num_seqs : B;
+    const int64_t Ttot = varlen ? T : static_cast<int64_t>(B) * T;
+    return split_workspace_bytes(split_plan(varlen, num_seqs, max_seqlen, B, T, H, dk, dv, dtype,
+                                            segments), N, Ttot, H);
 }
 
 int kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const void* g,

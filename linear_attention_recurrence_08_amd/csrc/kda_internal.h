@@ -26,8 +26,9 @@ struct PrefillArgs {
     int64_t T;            // per-sequence length when cu == nullptr
     int64_t H, dk, dv;
     int dtype;            // 0 = bf16, 1 = f32
-    // token-range split (split > 1; bf16, dk = dv = 128, cu == nullptr): every sequence is cut
-    // into `split` segments of seg_len tokens (a multiple of 64).  Segment 0 runs from h0 into o;
+    // token-range split (split > 1; bf16, dk = dv = 128): every sequence is cut into segments of
+    // seg_len tokens (a multiple of 64), at most `split` of them, the last one running to the
+    // sequence end.  Segment 0 runs from h0 into o;
     // each later segment runs as a part B (zero entering state, into o) and a part M (v = 0,
     // identity entering state, its outputs M_t^T q_t into oM); every run's final state goes to
     // seg_states.  launch_split_finish composes the entering states, writes hT and adds

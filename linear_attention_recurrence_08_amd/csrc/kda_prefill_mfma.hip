@@ -232,10 +232,12 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     int64_t bos, eos;
     if (a.cu) { bos = a.cu[n]; eos = a.cu[n + 1]; }
     else { bos = n * a.T; eos = bos + a.T; }
-    if (a.split > 1) {                     // the segment's tokens (seg_len is a multiple of 16)
-        bos += seg * a.seg_len;
-        eos = min(eos, bos + a.seg_len);
-        bos = min(bos, eos);
+    if (a.split > 1) {
+        // the segment's tokens: seg_len from its start (a multiple of 64), the last segment up to
+        // the sequence end; segments past the end of a shorter sequence are empty
+        const int64_t send = eos;
+        bos = min(bos + seg * a.seg_len, send);
+        if (seg + 1 < a.split) eos = min(send, bos + a.seg_len);
     }
     const int64_t ntiles = (eos - bos + C - 1) / C;
 

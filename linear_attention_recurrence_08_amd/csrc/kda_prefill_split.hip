@@ -20,6 +20,23 @@ namespace {
 
 constexpr int D = 128;
 
+// first token and length of sequence n in the packed token axis
+__device__ __forceinline__ void seq_bounds(const PrefillArgs& a, int64_t n, int64_t& start,
+                                           int64_t& len) {
+    if (a.cu) {
+        start = a.cu[n];
+        len = a.cu[n + 1] - start;
+    } else {
+        start = n * a.T;
+        len = a.T;
+    }
+}
+// segments sequence n is cut into: seg_len tokens each, at most a.split, the last one running to
+// the sequence end (an empty sequence keeps its segment 0, which passes h0 through)
+__device__ __forceinline__ int64_t seq_segments(const PrefillArgs& a, int64_t len) {
+    return len <= 0 ? 1 : min((len + a.seg_len - 1) / a.seg_len, a.split);
+}
+
 // Workgroup barrier that orders LDS only: the global loads issued ahead stay in flight across it,
 // and the global stores need no ordering within the launch.
 __device__ __forceinline__ void lds_barrier() {
@@ -71,6 +88,9 @@ __global__ __launch_bounds__(256) void kda_split_compose_kernel(PrefillArgs a) {
     const int w = tid >> 6;
     const int64_t c0 = 16 * (int64_t)blockIdx.x;
     const int64_t p = blockIdx.y, pairs = a.N * a.H;
+    int64_t start, len;
+    seq_bounds(a, p / a.H, start, len);
+    const int64_t nseg = seq_segments(a, len);
     auto slot = [&](int64_t seg, int part) {
         return a.seg_states + ((2 * seg + part) * pairs + p) * (int64_t)(D * D);
     };
@@ -97,8 +117,8 @@ __global__ __launch_bounds__(256) void kda_split_compose_kernel(PrefillArgs a) {
             for (int r = 0; r < 4; ++r) br[b][r] = bs[(r0 + 4 * lg + r) * D + c0 + ln];
         }
     };
-    if (a.split > 1) load_step(1);
-    for (int64_t sg = 1; sg < a.split; ++sg) {
+    if (nseg > 1) load_step(1);
+    for (int64_t sg = 1; sg < nseg; ++sg) {
         float* bs = slot(sg, 0);
         // B operands: the entering state's block over channel steps ks (column ln)
         bf16x8 bh[4], bl[4];
@@ -121,7 +141,7 @@ __global__ __launch_bounds__(256) void kda_split_compose_kernel(PrefillArgs a) {
                 split8(x, mh[b][ks], ml[b][ks]);
             }
         }
-        if (sg + 1 < a.split) load_step(sg + 1);
+        if (sg + 1 < nseg) load_step(sg + 1);
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -161,77 +181,83 @@ constexpr int TB = 64;
 __global__ __launch_bounds__(256) void kda_split_fixup_kernel(PrefillArgs a) {
     const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
     const int64_t p = blockIdx.y, H = a.H, n = p / H, h = p % H;
-    const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t trel = a.seg_len + blk * TB;                   // within the sequence
-    if (trel >= a.T) return;                                     // the whole wave leaves
-    const int nt = (int)min<int64_t>(TB, a.T - trel);
-    const int64_t seg = trel / a.seg_len;
-    const float* S = a.seg_states + (2 * seg * a.N * H + p) * (int64_t)(D * D);   // S_in(seg)
-    const int64_t t0 = n * a.T + trel;                           // packed token index
+    int64_t start, len;
+    seq_bounds(a, n, start, len);
     const bf16_t* om = static_cast<const bf16_t*>(a.oM);
     bf16_t* o = static_cast<bf16_t*>(a.o);
-    // B operands: (M_t^T q_t)^T over channel steps ks, token ln of each 16-token sub-block tb
-    bf16x8 bm[4][4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        const int tok = 16 * tb + ln;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            uint2 u0 = make_uint2(0u, 0u), u1 = make_uint2(0u, 0u);
-            if (tok < nt) {
-                const bf16_t* row = om + ((t0 + tok) * H + h) * D + 32 * ks + 4 * lg;
-                u0 = *reinterpret_cast<const uint2*>(row);
-                u1 = *reinterpret_cast<const uint2*>(row + 16);
-            }
-            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-            bm[tb][ks] = __builtin_bit_cast(bf16x8, (u32x4){u0.x, u0.y, u1.x, u1.y});
-        }
-    }
-    // S_in^T rows (S_in columns 16 cb + ln) over the channels of step ks, for the A operands;
-    // the next column block's values are loaded while the current one is multiplied
-    float xs[4][8];
-    auto load_s = [&](int cb) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) xs[ks][j] = S[(32 * ks + kslot(j, lg)) * D + 16 * cb + ln];
-    };
-    load_s(0);
-    // this lane's 4 columns 16 cb + 4 lg .. + 3 of token 16 tb + ln (B_t^T q_t, bf16), for every
-    // column block, all in flight from the start
-    uint2 ob[D / 16][4];
-#pragma unroll
-    for (int cb = 0; cb < D / 16; ++cb)
+    // the sequence's 64-token blocks after segment 0, strided over the grid's waves
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    for (int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);; blk += stride) {
+        const int64_t trel = a.seg_len + blk * TB;                   // within the sequence
+        if (trel >= len) break;                                      // the whole wave leaves
+        const int nt = (int)min<int64_t>(TB, len - trel);
+        const int64_t seg = min(trel / a.seg_len, a.split - 1);
+        const float* S = a.seg_states + (2 * seg * a.N * H + p) * (int64_t)(D * D);   // S_in(seg)
+        const int64_t t0 = start + trel;                             // packed token index
+        // B operands: (M_t^T q_t)^T over channel steps ks, token ln of each 16-token sub-block tb
+        bf16x8 bm[4][4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             const int tok = 16 * tb + ln;
-            ob[cb][tb] = tok < nt ? *reinterpret_cast<const uint2*>(
-                                        o + ((t0 + tok) * H + h) * D + 16 * cb + 4 * lg)
-                                  : make_uint2(0u, 0u);
-        }
-#pragma unroll
-    for (int cb = 0; cb < D / 16; ++cb) {
-        bf16x8 ah[4], al[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) split8(xs[ks], ah[ks], al[ks]);
-        if (cb + 1 < D / 16) load_s(cb + 1);
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                acc = mma32(ah[ks], bm[tb][ks], acc);
-                acc = mma32(al[ks], bm[tb][ks], acc);
-            }
-            // acc register r: column 16 cb + 4 lg + r of token 16 tb + ln
-            const int tok = 16 * tb + ln;
-            if (tok < nt) {
-                const uint2 u = ob[cb][tb];
-                *reinterpret_cast<uint2*>(o + ((t0 + tok) * H + h) * D + 16 * cb + 4 * lg) =
-                    make_uint2(pk2(hi_of(u.x, 0) + acc[0], hi_of(u.x, 1) + acc[1]),
-                               pk2(hi_of(u.y, 0) + acc[2], hi_of(u.y, 1) + acc[3]));
+                uint2 u0 = make_uint2(0u, 0u), u1 = make_uint2(0u, 0u);
+                if (tok < nt) {
+                    const bf16_t* row = om + ((t0 + tok) * H + h) * D + 32 * ks + 4 * lg;
+                    u0 = *reinterpret_cast<const uint2*>(row);
+                    u1 = *reinterpret_cast<const uint2*>(row + 16);
+                }
+                typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                bm[tb][ks] = __builtin_bit_cast(bf16x8, (u32x4){u0.x, u0.y, u1.x, u1.y});
             }
         }
+        // S_in^T rows (S_in columns 16 cb + ln) over the channels of step ks, for the A operands;
+        // the next column block's values are loaded while the current one is multiplied
+        float xs[4][8];
+        auto load_s = [&](int cb) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) xs[ks][j] = S[(32 * ks + kslot(j, lg)) * D + 16 * cb + ln];
+        };
+        load_s(0);
+        // this lane's 4 columns 16 cb + 4 lg .. + 3 of token 16 tb + ln (B_t^T q_t, bf16), for every
+        // column block, all in flight from the start
+        uint2 ob[D / 16][4];
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const int tok = 16 * tb + ln;
+                ob[cb][tb] = tok < nt ? *reinterpret_cast<const uint2*>(
+                                            o + ((t0 + tok) * H + h) * D + 16 * cb + 4 * lg)
+                                      : make_uint2(0u, 0u);
+            }
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb) {
+            bf16x8 ah[4], al[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) split8(xs[ks], ah[ks], al[ks]);
+            if (cb + 1 < D / 16) load_s(cb + 1);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    acc = mma32(ah[ks], bm[tb][ks], acc);
+                    acc = mma32(al[ks], bm[tb][ks], acc);
+                }
+                // acc register r: column 16 cb + 4 lg + r of token 16 tb + ln
+                const int tok = 16 * tb + ln;
+                if (tok < nt) {
+                    const uint2 u = ob[cb][tb];
+                    *reinterpret_cast<uint2*>(o + ((t0 + tok) * H + h) * D + 16 * cb + 4 * lg) =
+                        make_uint2(pk2(hi_of(u.x, 0) + acc[0], hi_of(u.x, 1) + acc[1]),
+                                   pk2(hi_of(u.y, 0) + acc[2], hi_of(u.y, 1) + acc[3]));
+                }
+            }
+        }
+
     }
 }
 
@@ -239,16 +265,15 @@ __global__ __launch_bounds__(256) void kda_split_fixup_kernel(PrefillArgs a) {
 
 hipError_t launch_split_finish(const PrefillArgs& a, hipStream_t s) {
     const int64_t pairs = a.N * a.H;
-    if (a.split <= 1 || pairs <= 0 || a.T <= 0) return hipSuccess;
+    if (a.split <= 1 || pairs <= 0) return hipSuccess;
     hipLaunchKernelGGL(kda_split_compose_kernel, dim3(D / 16, (unsigned)pairs), dim3(256), 0, s,
                        a);
-    const int64_t later = a.T - a.seg_len;
-    if (later > 0) {
-        const int64_t blocks = (later + TB - 1) / TB;            // one wave each, four per group
-        hipLaunchKernelGGL(kda_split_fixup_kernel, dim3((unsigned)((blocks + 3) / 4),
-                                                        (unsigned)pairs),
-                           dim3(256), 0, s, a);
-    }
+    // one wave per 64-token block after segment 0 of the longest sequence the plan assumed
+    // (a.split segments); blocks past it, if a sequence is longer, are taken in a strided loop
+    const int64_t later = (a.split - 1) * a.seg_len;
+    const int64_t blocks = (later + TB - 1) / TB;
+    hipLaunchKernelGGL(kda_split_fixup_kernel, dim3((unsigned)((blocks + 3) / 4), (unsigned)pairs),
+                       dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -4,9 +4,10 @@ in the library's HIP kernels.  PyTorch supplies device memory and the current st
     kda_chunk_fwd(q, k, v, g, beta, h0=None, cu_seqlens=None, output_final_state=True)
         -> (o, hT)
     kda_chunk_fwd_chunk64(...)   the same with 64-token chunks of four 16-token sub-tiles
-    kda_chunk_fwd_split(q, k, v, g, beta, h0=None, segments=0, ...) -> (o, hT)
-                                 the same for equal-length sequences, each also cut into token
-                                 ranges that run concurrently (small batches)
+    kda_chunk_fwd_split(q, k, v, g, beta, h0=None, cu_seqlens=None, max_seqlen=None,
+                        segments=0, ...) -> (o, hT)
+                                 the same with each sequence also cut into token ranges that run
+                                 concurrently (small batches)
     kda_chunk_fwd_snapshots(q, k, v, g, beta, snap_stride, ...) -> (o, hT, snaps, snap_offsets)
     kda_decode_step(q, k, v, g, beta, S) -> o         (S is updated in place)
     kda_decode_step_gated(q, k, v, g, beta, S, gate, weight=None, eps=...) -> (o, y)
@@ -61,12 +62,15 @@ def load_library():
         lib.kda_chunk_fwd_chunk64_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32,
                                                               i32]
         lib.kda_chunk_fwd_chunk64_workspace_bytes.restype = ctypes.c_size_t
-        lib.kda_chunk_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
-                                            i32, i32, i32, vp, ctypes.c_size_t, vp]
+        lib.kda_chunk_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, i32,
+                                            i32, i32, i32, i32, i32, i32, vp, ctypes.c_size_t,
+                                            vp]
         lib.kda_chunk_fwd_split.restype = i32
-        lib.kda_chunk_fwd_split_segments.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        lib.kda_chunk_fwd_split_segments.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                                     i32]
         lib.kda_chunk_fwd_split_segments.restype = i32
-        lib.kda_chunk_fwd_split_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        lib.kda_chunk_fwd_split_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32,
+                                                            i32, i32]
         lib.kda_chunk_fwd_split_workspace_bytes.restype = ctypes.c_size_t
         lib.kda_chunk_fwd_snapshots.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                                 i32, i32, i32, i32, i32, i32, i32, vp]
@@ -216,38 +220,48 @@ def kda_chunk_fwd_chunk64(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: 
 
 
 def kda_chunk_fwd_split_segments(q: torch.Tensor, B: int, T: int, H: int, dk: int, dv: int,
-                                 segments: int = 0) -> int:
-    """Segments kda_chunk_fwd_split uses for these sizes and request (1: no split)."""
-    return int(load_library().kda_chunk_fwd_split_segments(B, T, H, dk, dv, _dtype_code(q),
-                                                           segments))
+                                 segments: int = 0, cu_seqlens: Optional[torch.Tensor] = None,
+                                 num_seqs: int = 0, max_seqlen: int = 0) -> int:
+    """Segments kda_chunk_fwd_split plans for these sizes and request (1: no split)."""
+    return int(load_library().kda_chunk_fwd_split_segments(
+        _ptr(cu_seqlens), num_seqs, max_seqlen, B, T, H, dk, dv, _dtype_code(q), segments))
 
 
 def kda_chunk_fwd_split_workspace_bytes(q: torch.Tensor, B: int, T: int, H: int, dk: int,
-                                        dv: int, segments: int = 0) -> int:
+                                        dv: int, segments: int = 0,
+                                        cu_seqlens: Optional[torch.Tensor] = None,
+                                        num_seqs: int = 0, max_seqlen: int = 0) -> int:
     """Workspace bytes kda_chunk_fwd_split needs for these sizes and request (0: none)."""
-    return int(load_library().kda_chunk_fwd_split_workspace_bytes(B, T, H, dk, dv,
-                                                                  _dtype_code(q), segments))
+    return int(load_library().kda_chunk_fwd_split_workspace_bytes(
+        _ptr(cu_seqlens), num_seqs, max_seqlen, B, T, H, dk, dv, _dtype_code(q), segments))
 
 
 def kda_chunk_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                         beta: torch.Tensor, h0: Optional[torch.Tensor] = None,
+                        cu_seqlens: Optional[torch.Tensor] = None,
+                        max_seqlen: Optional[int] = None,
                         output_final_state: bool = True, segments: int = 0,
                         o: Optional[torch.Tensor] = None, hT: Optional[torch.Tensor] = None,
                         workspace: Optional[torch.Tensor] = None
                         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """kda_chunk_fwd for B equal-length sequences with each sequence also cut into token ranges
-    that run concurrently (segments = 0: the library's choice).  Same results as kda_chunk_fwd;
-    `workspace` (a contiguous device tensor of at least kda_chunk_fwd_split_workspace_bytes bytes)
-    is allocated here when not given."""
-    dev, B, T, H, dk, dv, N, o, hT = _prefill_args(q, k, v, g, beta, h0, None,
+    """kda_chunk_fwd with each sequence also cut into token ranges that run concurrently
+    (segments = 0: the library's choice).  Same results as kda_chunk_fwd.  With cu_seqlens the
+    plan assumes sequences of max_seqlen tokens; when it is None it is read from cu_seqlens (one
+    device-to-host copy).  `workspace` (a contiguous device tensor of at least
+    kda_chunk_fwd_split_workspace_bytes bytes) is allocated here when not given."""
+    dev, B, T, H, dk, dv, N, o, hT = _prefill_args(q, k, v, g, beta, h0, cu_seqlens,
                                                    output_final_state, o, hT)
-    need = kda_chunk_fwd_split_workspace_bytes(q, B, T, H, dk, dv, segments)
+    if cu_seqlens is not None and max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if N > 0 else 0
+    msl = int(max_seqlen or 0)
+    need = kda_chunk_fwd_split_workspace_bytes(q, B, T, H, dk, dv, segments, cu_seqlens, N, msl)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().kda_chunk_fwd_split(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT), B, T, H,
-        dk, dv, _dtype_code(q), int(segments), _ptr(workspace), nbytes, _stream(dev))
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), N, msl,
+        _ptr(o), _ptr(hT), B, T, H, dk, dv, _dtype_code(q), int(segments), _ptr(workspace),
+        nbytes, _stream(dev))
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd_split")
     return o, hT

@@ -143,48 +143,68 @@ def test_chunk64_workspace_errors(lib):
 
 
 def _split(lib, ws=None, ws_bytes=0, **kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, o=FAKE, hT=FAKE, B=1, T=4096,
-             H=12, dk=128, dv=128, dtype=0, segments=0)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, num_seqs=0, max_seqlen=0,
+             o=FAKE, hT=FAKE, B=1, T=4096, H=12, dk=128, dv=128, dtype=0, segments=0)
     a.update(kw)
-    return lib.kda_chunk_fwd_split(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["o"],
-                                   a["hT"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dtype"],
-                                   a["segments"], ws, ws_bytes, None)
+    return lib.kda_chunk_fwd_split(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"],
+                                   a["num_seqs"], a["max_seqlen"], a["o"], a["hT"], a["B"],
+                                   a["T"], a["H"], a["dk"], a["dv"], a["dtype"], a["segments"],
+                                   ws, ws_bytes, None)
+
+
+def _seg(lib, B, T, H, dk=128, dv=128, dtype=0, segments=0, cu=None, num_seqs=0, max_seqlen=0):
+    return lib.kda_chunk_fwd_split_segments(cu, num_seqs, max_seqlen, B, T, H, dk, dv, dtype,
+                                            segments)
+
+
+def _split_ws(lib, B, T, H, dk=128, dv=128, dtype=0, segments=0, cu=None, num_seqs=0,
+              max_seqlen=0):
+    return lib.kda_chunk_fwd_split_workspace_bytes(cu, num_seqs, max_seqlen, B, T, H, dk, dv,
+                                                   dtype, segments)
 
 
 def test_split_plan(lib):
-    seg = lib.kda_chunk_fwd_split_segments
-    # automatic: the largest P with 2 (2 P - 1) B H <= 256 workgroups and >= 256 tokens each
-    assert seg(1, 4096, 12, 128, 128, 0, 0) == 5        # 2 * 12 * 9 = 216 workgroups
-    assert seg(1, 4096, 24, 128, 128, 0, 0) == 3        # 2 * 24 * 5 = 240
-    assert seg(1, 4096, 96, 128, 128, 0, 0) == 1        # 192 workgroups already
-    assert seg(1, 512, 12, 128, 128, 0, 0) == 2         # 256 tokens per segment at least
-    assert seg(1, 300, 12, 128, 128, 0, 0) == 1
+    # automatic: the largest P with 2 (2 P - 1) N H <= 256 workgroups and >= 256 tokens each
+    assert _seg(lib, 1, 4096, 12) == 5        # 2 * 12 * 9 = 216 workgroups
+    assert _seg(lib, 1, 4096, 24) == 3        # 2 * 24 * 5 = 240
+    assert _seg(lib, 1, 4096, 96) == 1        # 192 workgroups already
+    assert _seg(lib, 1, 512, 12) == 2         # 256 tokens per segment at least
+    assert _seg(lib, 1, 300, 12) == 1
     # requested: capped at 16; segments are whole multiples of 64 tokens, so fewer may result
-    assert seg(1, 4096, 96, 128, 128, 0, 3) == 3
-    assert seg(1, 4096, 1, 128, 128, 0, 40) == 16
-    assert seg(1, 100, 1, 128, 128, 0, 4) == 2          # 64-token segments: 64 + 36
-    assert seg(1, 64, 1, 128, 128, 0, 4) == 1
+    assert _seg(lib, 1, 4096, 96, segments=3) == 3
+    assert _seg(lib, 1, 4096, 1, segments=40) == 16
+    assert _seg(lib, 1, 100, 1, segments=4) == 2          # 64-token segments: 64 + 36
+    assert _seg(lib, 1, 64, 1, segments=4) == 1
     # other dtypes and head sizes, and batches beyond the grid's y extent, do not split
-    assert seg(1, 4096, 12, 128, 128, 1, 0) == 1
-    assert seg(1, 4096, 12, 64, 128, 0, 0) == 1
-    assert seg(65536, 4096, 1, 128, 128, 0, 4) == 1
-    assert seg(1, 4096, 12, 128, 128, 0, -1) == 1
+    assert _seg(lib, 1, 4096, 12, dtype=1) == 1
+    assert _seg(lib, 1, 4096, 12, dk=64) == 1
+    assert _seg(lib, 65536, 4096, 1, segments=4) == 1
+    assert _seg(lib, 1, 4096, 12, segments=-1) == 1
+    # variable-length batches plan for max_seqlen tokens and N sequences (contents not read)
+    assert _seg(lib, 1, 9000, 6, cu=FAKE, num_seqs=2, max_seqlen=8000) == 5   # 2*12*9 = 216
+    assert _seg(lib, 1, 9000, 6, cu=FAKE, num_seqs=2, max_seqlen=0) == 1
+    assert _seg(lib, 2, 9000, 6, cu=FAKE, num_seqs=2, max_seqlen=8000) == 1   # B must be 1
 
 
 def test_split_workspace(lib):
-    ws = lib.kda_chunk_fwd_split_workspace_bytes
     # M_t^T q_t in bf16 for every token, then 2 final states per segment and (sequence, head)
-    assert ws(1, 4096, 12, 128, 128, 0, 0) == 4096 * 12 * 256 + 5 * 2 * 12 * 65536
-    assert ws(2, 1000, 3, 128, 128, 0, 2) == (2 * 1000 * 3 * 256 + 255) // 256 * 256 + \
-        2 * 2 * 6 * 65536
-    assert ws(1, 4096, 96, 128, 128, 0, 0) == 0 and ws(1, 4096, 12, 128, 128, 1, 0) == 0
-    need = ws(1, 4096, 12, 128, 128, 0, 0)
+    assert _split_ws(lib, 1, 4096, 12) == 4096 * 12 * 256 + 5 * 2 * 12 * 65536
+    assert _split_ws(lib, 2, 1000, 3, segments=2) == \
+        (2 * 1000 * 3 * 256 + 255) // 256 * 256 + 2 * 2 * 6 * 65536
+    assert _split_ws(lib, 1, 9000, 6, cu=FAKE, num_seqs=2, max_seqlen=8000) == \
+        9000 * 6 * 256 + 5 * 2 * 12 * 65536
+    assert _split_ws(lib, 1, 4096, 96) == 0 and _split_ws(lib, 1, 4096, 12, dtype=1) == 0
+    need = _split_ws(lib, 1, 4096, 12)
     aligned = ctypes.c_void_p(0x10000)   # never dereferenced: the calls fail validation first
     assert _split(lib) == -10                                        # missing
     assert _split(lib, ws=aligned, ws_bytes=need - 1) == -10         # too small
     assert _split(lib, ws=ctypes.c_void_p(0x10010), ws_bytes=need) == -10   # misaligned
     assert _split(lib, segments=-1) == -2
+    assert _split(lib, cu=FAKE, num_seqs=2, max_seqlen=-1) == -2
     assert _split(lib, q=None) == -1 and _split(lib, dtype=3) == -3
+    # varlen: cu_seqlens needs B == 1, as in kda_chunk_fwd
+    assert _split(lib, cu=FAKE, num_seqs=2, max_seqlen=4000, B=2) == -5
+    assert _split(lib, cu=FAKE, num_seqs=2, max_seqlen=4000) == -10  # a split: workspace needed
     # no split (one segment, or the float32 path): kda_chunk_fwd's errors, no workspace needed
     assert _split(lib, H=96, q=None) == -1 and _split(lib, dtype=1, dk=96, q=None) == -1
     assert _split(lib, B=0) == 0

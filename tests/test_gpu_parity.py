@@ -710,3 +710,29 @@ def test_split_T32768_H12(oracle_mod):
     eo, eh = err(to64(o[:, heads]), o_ref), err(to64(hT[:, heads]), h_ref)
     _say(f"split T32768 H12 heads {heads}: error o={eo:.3e} hT={eh:.3e}")
     assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
+
+
+SPLIT_VARLEN = [
+    # (seq_lens, H, max_seqlen passed (None: read from cu_seqlens), segments requested)
+    ([1000, 0, 37, 700], 2, None, 0),      # automatic: 3 segments of 384 tokens
+    ([900, 300], 2, 300, 3),               # bound below the longest: its last segment runs long
+    ([(5 * i + 3) % 300 for i in range(12)], 1, None, 4),   # longest-first dispatch
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_VARLEN, ids=lambda c: f"{len(c[0])}seqs-H{c[1]}-P{c[3]}")
+def test_split_varlen(oracle_mod, case):
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd_split
+    lens, H, msl, segs = case
+    dev = _dev()
+    x = inputs.make_inputs(lens, H=H, dk=128, dv=128, dtype="bf16", seed=350 + len(lens),
+                           h0_sigma=0.1, packed=True)
+    xd = x.to(dev)
+    o, hT = kda_chunk_fwd_split(*xd.call_views(), h0=xd.h0, cu_seqlens=xd.cu_seqlens,
+                                max_seqlen=msl, segments=segs)
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle_prefill(oracle_mod, x)
+    eo, eh = err(to64(o), o_ref), err(to64(hT), h_ref)
+    _say(f"split varlen {len(lens)} seqs H={H}: error o={eo:.3e} hT={eh:.3e}")
+    assert np.isfinite(to64(o)).all() and np.isfinite(to64(hT)).all()
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
