@@ -312,9 +312,10 @@ def time_launches(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps, wall  # ms per launch (one kernel per step), seconds
 
 
-def head_share(dev, stream, steps, warmup):
+def head_share(dev, stream, steps, warmup, unsplit=True):
     """Prefill of one GPU's share of K3's heads under 8-way head sharding (12 of 96, T = 4096,
-    batch 1): kda_chunk_fwd beside kda_chunk_fwd_split with the library's segment count."""
+    batch 1): kda_chunk_fwd beside kda_chunk_fwd_split with the library's segment count
+    (unsplit=False: the split alone)."""
     import torch
     from linear_attention_recurrence_08_amd import (inputs, kda_chunk_fwd, kda_chunk_fwd_split,
                                                     kda_chunk_fwd_split_segments,
@@ -336,7 +337,7 @@ def head_share(dev, stream, steps, warmup):
     def share_split():
         kda_chunk_fwd_split(*sviews, segments=0, o=o_s, hT=h_s, workspace=ws_s)
 
-    sp_ms, _ = time_launches(share_plain, steps, warmup, stream)
+    sp_ms = time_launches(share_plain, steps, warmup, stream)[0] if unsplit else float("nan")
     ss_ms, _ = time_launches(share_split, steps, warmup, stream)
     sb = prefill_bytes(xs)
     return {
@@ -344,9 +345,10 @@ def head_share(dev, stream, steps, warmup):
                     "sharding)",
         "kernel": "kda_prefill_mfma (token-range split) + kda_split_compose + kda_split_fixup",
         "segments": P, "workspace_bytes": sbytes,
-        "unsplit_ms_per_step": round(sp_ms, 5), "ms_per_step": round(ss_ms, 5),
+        "unsplit_ms_per_step": round(sp_ms, 5) if unsplit else None,
+        "ms_per_step": round(ss_ms, 5),
         "value": round(Ts / (ss_ms * 1e-3), 1), "unit": "tokens/s",
-        "vs_unsplit": round(sp_ms / ss_ms, 3),
+        "vs_unsplit": round(sp_ms / ss_ms, 3) if unsplit else None,
         "roofline": {"bound": "hbm", "achieved": round(sb / (ss_ms * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(sb / (ss_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -368,8 +370,8 @@ def summarize_split(trace_dir, command):
         fo.write("# kda_chunk_fwd_split on prefill_T4096_H12_d128_bf16 (12 of 96 heads, batch 1): "
                  "rocprofv3 kernel trace\n\n")
         fo.write(f"command: `{command}`\n\n")
-        fo.write("kda_prefill_mfma_kernel<2, 64> is the unsplit prefill (24 workgroups); <1, 64> the "
-                 "split's launch (5 segments: 216 workgroups).\n\n")
+        fo.write("Every kernel of one split call: the prefill launch (5 segments: 216 workgroups), "
+                 "the composition of the entering states and the output correction.\n\n")
         fo.write("| kernel | calls | average ns | min ns | max ns |\n|---|---|---|---|---|\n")
         for r in rows:
             name = re.sub(r"\(kda::PrefillArgs\)|void |kda::\(anonymous namespace\)::", "",
@@ -398,6 +400,8 @@ def main():
     ap.add_argument("--no-split", action="store_true")
     ap.add_argument("--head-share-only", action="store_true",
                     help="time only the 12-head prefill (kda_chunk_fwd beside kda_chunk_fwd_split)")
+    ap.add_argument("--split-only", action="store_true",
+                    help="with --head-share-only: time the split alone (for a kernel trace)")
     ap.add_argument("--summarize-split", metavar="DIR",
                     help="write the split prefill's kernel-trace summary from a rocprofv3 run of "
                          "--head-share-only")
@@ -436,7 +440,8 @@ def main():
         traffic_pass(dev)
         return
     if args.head_share_only:
-        print(json.dumps(head_share(dev, stream, args.steps, args.warmup)))
+        print(json.dumps(head_share(dev, stream, args.steps, args.warmup,
+                                    unsplit=not args.split_only)))
         return
 
     # ---------------- prefill ----------------
