@@ -70,3 +70,36 @@ def test_summaries_scale_by_the_copy_and_add_kernels_of_a_call(tmp_path, monkeyp
         want, rel=1e-5)
     monkeypatch.setattr(bench, "kernel_source_digest", lambda tag: "fedcba9876543210")
     assert bench.recorded_traffic("kda_frontend_T4096_H96_d128_bf16") is None
+
+
+def test_split_digest_covers_both_sources():
+    # the split's digest changes with the prefill kernel and with its completion kernels
+    d_split = bench.kernel_source_digest("kda_chunk_fwd_split_T4096_H12_d128_bf16")
+    d_prefill = bench.kernel_source_digest("kda_chunk_fwd_prefill_T4096_H96_d128_bf16")
+    assert len(d_split) == 16 and d_split != d_prefill
+
+
+def test_split_summary_lists_every_kernel_of_the_call(tmp_path, monkeypatch):
+    trace = tmp_path / "t" / "split_kernel_stats.csv"
+    trace.parent.mkdir(parents=True)
+    with open(trace, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs"])
+        w.writeheader()
+        for name, ns in (("void kda::(anonymous namespace)::kda_prefill_mfma_kernel<2, 64>"
+                          "(kda::PrefillArgs)", 64000.0),
+                         ("kda::(anonymous namespace)::kda_split_fixup_kernel(kda::PrefillArgs)",
+                          17000.0),
+                         ("kda::(anonymous namespace)::kda_split_compose_kernel"
+                          "(kda::PrefillArgs)", 15000.0),
+                         ("__amd_rocclr_copyBuffer", 3000.0)):
+            w.writerow({"Name": name, "Calls": 23, "AverageNs": ns, "MinNs": ns, "MaxNs": ns})
+    out = tmp_path / "repo"
+    (out / "profiles").mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(out))
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda tag: "0123456789abcdef")
+    bench.summarize_split(str(tmp_path / "t"), "split command")
+    txt = open(out / "profiles" / "kda_chunk_fwd_split_T4096_H12_d128_bf16_kernel_trace.md").read()
+    rows = [l for l in txt.splitlines() if l.startswith("| kda_")]
+    assert [r.split("|")[1].strip() for r in rows] == [
+        "kda_prefill_mfma_kernel<2, 64>", "kda_split_fixup_kernel", "kda_split_compose_kernel"]
+    assert "command: `split command`" in txt and "source_digest: 0123456789abcdef" in txt
