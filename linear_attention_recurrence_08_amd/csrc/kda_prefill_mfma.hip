@@ -21,9 +21,12 @@
 // 128-column slice: each stage-S wave carries two strips, and stages A and B1 run once per head).
 // The two slices of a head are dispatched to the same XCD so their shared q/k/g reads meet in
 // that XCD's L2, and in a variable-length batch of up to 64 sequences the longest sequences are
-// dispatched first (the short ones fill the tail).  Each wave keeps one role for the whole
-// sequence, and the work of a tile runs as a software pipeline with a single workgroup barrier
-// per period; period q holds
+// dispatched first (the short ones fill the tail).  With a token-range split (small batches; the
+// completion kernels are in kda_prefill_split.hip) a workgroup runs one segment of a sequence:
+// segment 0 from h0, or a later segment from a zero state (its part B) or from the identity with
+// v = 0 (its part M), and leaves the segment's final state for the composition.  Each wave keeps
+// one role for the whole sequence, and the work of a tile runs as a software pipeline with a
+// single workgroup barrier per period; period q holds
 //   stage A (waves 4-7) for tile q: wave s loads key channels [32s, 32s+32) of q, k, g and value
 //      columns [16s, 16s+16) of the slice through buffer resources, runs the cumulative
 //      log-decay as a product with a triangular 0/1 matrix, and forms the decayed operands Kp,
