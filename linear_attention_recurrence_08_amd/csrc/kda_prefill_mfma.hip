@@ -498,14 +498,32 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     };
 
     // stage S for tile `tile`: strips s + 4 m; leaves the token-major o fragments in Ot
-    auto stage_s = [&](int64_t tile, bf16x4 (&Ot)[NS]) {
-        const FromB<NS>& B = fb(tile);
+    // With one strip per wave, the decay of the state to the next tile's end and its bf16 copy
+    // run at the end of the previous period (after the update), so that a period opens with
+    // matrix-core products while stage A issues its vector work.
+    constexpr bool kPre = NS == 1;
+    bf16x8 Sb[4];       // one strip (kPre)
+    auto decay = [&](int64_t tile) {
         const float* ec = ecb(tile);
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
             const f32x4 e = *reinterpret_cast<const f32x4*>(&ec[16 * mb + 4 * lg]);
 #pragma unroll
             for (int m = 0; m < NS; ++m) S[m][mb] *= e;                         // St
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) Sb[ks] = cat8(bf4(S[0][2 * ks]), bf4(S[0][2 * ks + 1]));
+    };
+    auto stage_s = [&](int64_t tile, bf16x4 (&Ot)[NS]) {
+        const FromB<NS>& B = fb(tile);
+        if constexpr (!kPre) {
+            const float* ec = ecb(tile);
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) {
+                const f32x4 e = *reinterpret_cast<const f32x4*>(&ec[16 * mb + 4 * lg]);
+#pragma unroll
+                for (int m = 0; m < NS; ++m) S[m][mb] *= e;                     // St
+            }
         }
         // k-steps outside, strips inside: one W / Qpp fragment pair is live at a time
         f32x4 XW[NS], XQ[NS];
@@ -516,7 +534,9 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             const bf16x8 wf = B.w[ks][lane], qf = B.qpp[ks][lane];
 #pragma unroll
             for (int m = 0; m < NS; ++m) {
-                const bf16x8 sb = cat8(bf4(S[m][2 * ks]), bf4(S[m][2 * ks + 1]));
+                bf16x8 sb;
+                if constexpr (kPre) sb = Sb[ks];
+                else sb = cat8(bf4(S[m][2 * ks]), bf4(S[m][2 * ks + 1]));
                 XW[m] = mma32(wf, sb, XW[m]);
                 XQ[m] = mma32(sb, qf, XQ[m]);   // (Qpp St)^T: o already token-major
             }
@@ -617,6 +637,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         const int64_t nfull = (eos - bos) / C;
         int64_t i = 0;
         bf16x4 Ot[NS];
+        if constexpr (kPre) decay(0);
         for (; i < nfull; ++i) {
             stage_s(i, Ot);
             store_o(i, Ot, false);
@@ -625,11 +646,13 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
                 ++snap_idx;
                 snap_at += a.snap_tiles;
             }
+            if constexpr (kPre) if (i + 1 < nsteps) decay(i + 1);
             lds_barrier();
         }
         for (; i < nsteps; ++i) {
             stage_s(i, Ot);
             store_o(i, Ot, true);
+            if constexpr (kPre) if (i + 1 < nsteps) decay(i + 1);
             lds_barrier();
         }
         if (h_out) state_out(h_out);
