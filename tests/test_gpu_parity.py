@@ -736,3 +736,27 @@ def test_split_varlen(oracle_mod, case):
     _say(f"split varlen {len(lens)} seqs H={H}: error o={eo:.3e} hT={eh:.3e}")
     assert np.isfinite(to64(o)).all() and np.isfinite(to64(hT)).all()
     assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (eo, eh)
+
+
+def test_split_without_final_state_and_float32_fallback():
+    # output_final_state=False writes no hT and leaves o unchanged; float32 inputs do not split
+    # and run kda_chunk_fwd's path, bit for bit
+    from linear_attention_recurrence_08_amd import (inputs, kda_chunk_fwd, kda_chunk_fwd_split,
+                                                    kda_chunk_fwd_split_segments)
+    dev = _dev()
+    x = inputs.make_inputs([640], H=2, dk=128, dv=128, dtype="bf16", seed=360, h0_sigma=0.1,
+                           packed=False)
+    xd = x.to(dev)
+    o_a, h_a = kda_chunk_fwd_split(*xd.call_views(), h0=xd.h0, segments=3)
+    o_b, h_b = kda_chunk_fwd_split(*xd.call_views(), h0=xd.h0, segments=3,
+                                   output_final_state=False)
+    torch.cuda.synchronize()
+    assert h_b is None and torch.equal(o_a, o_b)
+    xf = inputs.make_inputs([640], H=2, dk=128, dv=128, dtype="f32", seed=361, h0_sigma=0.1,
+                            packed=False)
+    assert kda_chunk_fwd_split_segments(xf.q, 1, 640, 2, 128, 128, 3) == 1
+    xfd = xf.to(dev)
+    o_s, h_s = kda_chunk_fwd_split(*xfd.call_views(), h0=xfd.h0, segments=3)
+    o_p, h_p = kda_chunk_fwd(*xfd.call_views(), h0=xfd.h0)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_p) and torch.equal(h_s, h_p)
