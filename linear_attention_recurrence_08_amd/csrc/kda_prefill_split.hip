@@ -269,11 +269,13 @@ hipError_t launch_split_finish(const PrefillArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(kda_split_compose_kernel, dim3(D / 16, (unsigned)pairs), dim3(256), 0, s,
                        a);
     // one wave per 64-token block after segment 0 of the longest sequence the plan assumed
-    // (a.split segments); blocks past it, if a sequence is longer, are taken in a strided loop
+    // (a.split segments), at most 256 workgroups per pair; blocks past them, if a sequence is
+    // longer, are taken in the kernel's strided loop
     const int64_t later = (a.split - 1) * a.seg_len;
     const int64_t blocks = (later + TB - 1) / TB;
-    hipLaunchKernelGGL(kda_split_fixup_kernel, dim3((unsigned)((blocks + 3) / 4), (unsigned)pairs),
-                       dim3(256), 0, s, a);
+    const int64_t gx = min((blocks + 3) / 4, (int64_t)256);
+    hipLaunchKernelGGL(kda_split_fixup_kernel, dim3((unsigned)gx, (unsigned)pairs), dim3(256), 0,
+                       s, a);
     return hipGetLastError();
 }
 
