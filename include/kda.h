@@ -140,10 +140,10 @@ size_t kda_chunk_fwd_chunk64_workspace_bytes(const int32_t* cu_seqlens, int num_
 /*
  * kda_chunk_fwd_split -- kda_chunk_fwd with each sequence also cut into token ranges that run at
  * the same time, for batches too small to fill the chip (one GPU's share of the heads at batch 1,
- * for instance).  The recurrence is affine in the state ("Kimi K3's
- * hybrid block, from first principles", section "From linear attention to the delta rule": a tile
- * maps its entering state S to M S + B, so any run of tokens does too), so a segment that starts
- * from an unknown state S_in has S_t = M_t S_in + B_t.  Segment 0 runs from h0; every later
+ * for instance).  The recurrence ("Kimi K3's hybrid block, from first
+ * principles", section "From linear attention to the delta rule") is affine in the state, so any
+ * run of tokens maps its entering state S to M S + B, and a segment that starts from an unknown
+ * state S_in has S_t = M_t S_in + B_t.  Segment 0 runs from h0; every later
  * segment runs twice in the same launch, from a zero state with its values (B_t, outputs
  * B_t^T q_t) and from the identity with v = 0 (M_t, outputs M_t^T q_t).  A composition step then
  * chains S_in(s + 1) = M_s S_in(s) + B_s, writes hT, and adds S_in(s)^T (M_t^T q_t) to the outputs

@@ -1,13 +1,13 @@
 // Completion of a token-range split prefill: the entering state of every segment and the
 // correction of its outputs.
 //
-// The recurrence S_t = (I - b k k^T) Diag(e^g) S_{t-1} + b k v^T is affine in the state ("Kimi
-// K3's hybrid block, from first principles", section "From linear attention to the delta rule":
-// a 16-token tile maps its entering state S to M S + B, and so does any run of tiles).  A segment
+// The recurrence S_t = (I - b k k^T) Diag(e^g) S_{t-1} + b k v^T ("Kimi K3's hybrid block, from
+// first principles", section "From linear attention to the delta rule") is affine in the state,
+// so any run of tokens maps its entering state S to M S + B.  A segment
 // that starts from the unknown state S_in therefore has S_t = M_t S_in + B_t, where B_t is the run
 // from a zero state with the segment's values and M_t the run from the identity with v = 0; its
-// outputs are o_t = S_t^T q_t = B_t^T q_t + S_in^T (M_t^T q_t).  The prefill kernel leaves B_t^T q_t
-// in o, M_t^T q_t in oM and the final B and M of every segment in seg_states; here
+// outputs are o_t = S_t^T q_t = B_t^T q_t + S_in^T (M_t^T q_t).  The prefill kernel leaves
+// B_t^T q_t in o, M_t^T q_t in oM and the final B and M of every segment in seg_states; here
 //   S_in(1) = final state of segment 0,   S_in(s + 1) = M_s S_in(s) + B_s,   hT = S_in(split),
 // then o_t += S_in(s)^T (M_t^T q_t) for every token of segment s >= 1.  Both are matrix-core
 // products whose float32 operands enter as hi + lo bf16 pairs (float32-accurate): one 128 x 128
@@ -94,7 +94,8 @@ __global__ __launch_bounds__(256) void kda_split_compose_kernel(PrefillArgs a) {
     auto slot = [&](int64_t seg, int part) {
         return a.seg_states + ((2 * seg + part) * pairs + p) * (int64_t)(D * D);
     };
-    for (int i = tid; i < D * 16; i += 256) sc[i >> 4][i & 15] = slot(0, 0)[(i >> 4) * D + c0 + (i & 15)];
+    for (int i = tid; i < D * 16; i += 256)
+        sc[i >> 4][i & 15] = slot(0, 0)[(i >> 4) * D + c0 + (i & 15)];
     lds_barrier();
     // this wave's rows of M_s (A operands: row r0 + ln over the channels of step ks) and of B_s
     // (the accumulator's start), loaded one step ahead so that the chain waits only on LDS and
@@ -167,16 +168,17 @@ __global__ __launch_bounds__(256) void kda_split_compose_kernel(PrefillArgs a) {
     }
     if (a.hT) {
         float* dst = a.hT + p * (int64_t)(D * D);
-        for (int i = tid; i < D * 16; i += 256) dst[(i >> 4) * D + c0 + (i & 15)] = sc[i >> 4][i & 15];
+        for (int i = tid; i < D * 16; i += 256)
+            dst[(i >> 4) * D + c0 + (i & 15)] = sc[i >> 4][i & 15];
     }
 }
 
 // One wave per (64-token block of the later segments, pair); a block lies in one segment because
-// seg_len is a multiple of 64.  The correction out^T = S_in^T (M_t^T q_t)^T is a matrix-core product
-// per 16 x 16 block (column block of S_in, 16 tokens): S_in's float32 values enter as a hi + lo
-// pair of bf16 operands (x = hi + lo to 2^-17 relative), M_t^T q_t as the bf16 values the prefill
-// stored; the transposed form leaves each lane 4 consecutive columns of one token, added to the
-// bf16 output B_t^T q_t already in o.
+// seg_len is a multiple of 64.  The correction out^T = S_in^T (M_t^T q_t)^T is a matrix-core
+// product per 16 x 16 block (column block of S_in, 16 tokens): S_in's float32 values enter as a
+// hi + lo pair of bf16 operands (x = hi + lo to 2^-17 relative), M_t^T q_t as the bf16 values the
+// prefill stored; the transposed form leaves each lane 4 consecutive columns of one token, added
+// to the bf16 output B_t^T q_t already in o.
 constexpr int TB = 64;
 __global__ __launch_bounds__(256) void kda_split_fixup_kernel(PrefillArgs a) {
     const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
@@ -218,11 +220,12 @@ __global__ __launch_bounds__(256) void kda_split_fixup_kernel(PrefillArgs a) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) xs[ks][j] = S[(32 * ks + kslot(j, lg)) * D + 16 * cb + ln];
+                for (int j = 0; j < 8; ++j)
+                    xs[ks][j] = S[(32 * ks + kslot(j, lg)) * D + 16 * cb + ln];
         };
         load_s(0);
-        // this lane's 4 columns 16 cb + 4 lg .. + 3 of token 16 tb + ln (B_t^T q_t, bf16), for every
-        // column block, all in flight from the start
+        // this lane's 4 columns 16 cb + 4 lg .. + 3 of token 16 tb + ln (B_t^T q_t, bf16), for
+        // every column block, all in flight from the start
         uint2 ob[D / 16][4];
 #pragma unroll
         for (int cb = 0; cb < D / 16; ++cb)

@@ -269,9 +269,9 @@ def test_resume_from_saved_state_bitwise(oracle_mod):
 
 
 def test_affine_in_the_entering_state(oracle_mod):
-    """The recurrence is affine in the state ("Kimi K3's hybrid block, from first principles",
-    section "From linear attention to the delta rule": a chunk maps its entering state S to
-    M S + B): a run from S_in equals its run from zero with the values (B_t, outputs B_t^T q_t)
+    """The recurrence ("Kimi K3's hybrid block, from first principles", section "From linear
+    attention to the delta rule") is affine in the state, so a run maps its entering state S to
+    M S + B: a run from S_in equals its run from zero with the values (B_t, outputs B_t^T q_t)
     plus M_t S_in, where M_t is the run from the identity with v = 0 (outputs M_t^T q_t), so
     o_t = B_t^T q_t + S_in^T (M_t^T q_t).  This is what a token-range split composes."""
     rng = np.random.default_rng(29)
