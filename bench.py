@@ -295,6 +295,18 @@ def summarize(dirs, command):
                 print("wrote", path)
 
 
+def _cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def time_launches(fn, steps, warmup, stream):
     import torch
     for _ in range(warmup):
@@ -743,6 +755,7 @@ def main():
             "value": round(cpu_value, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{args.workload}: sequence 0 tokens [{a},{e}), heads 0..{nh - 1} of "
                       f"{x.H}; float64 token loop; {cpu_s:.2f} s wall",
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(),
         }
         if x.h0 is None and a == 0 and e == x.seq_bounds()[0][1]:
             o_gpu = to64(o.reshape(x.total_tokens, x.H, x.dv)[sl, :nh])

@@ -103,3 +103,8 @@ def test_split_summary_lists_every_kernel_of_the_call(tmp_path, monkeypatch):
     assert [r.split("|")[1].strip() for r in rows] == [
         "kda_prefill_mfma_kernel<2, 64>", "kda_split_fixup_kernel", "kda_split_compose_kernel"]
     assert "command: `split command`" in txt and "source_digest: 0123456789abcdef" in txt
+
+
+def test_cpu_model_is_read():
+    m = bench._cpu_model()
+    assert isinstance(m, str) and m
