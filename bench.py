@@ -484,6 +484,11 @@ def main():
         else "kda_prefill_general",
         "algorithmic_bytes_per_launch": nbytes,
         "algorithmic_flops_per_launch": flops,
+        # per (token, head): this count, 6 dk dv + d (5 C - 1), and for context the fit
+        # 6 d^2 + 3 C d + C^2 to the pages' "about 127,000 at chunk 64" (126,976 at C = 64)
+        "flops_per_token_head": 6 * x.dk * x.dv + x.dk * (5 * CHUNK - 1),
+        "pages_fit_flops_per_token_head": {"C16": 6 * x.dk * x.dk + 3 * 16 * x.dk + 16 * 16,
+                                           "C64": 6 * x.dk * x.dk + 3 * 64 * x.dk + 64 * 64},
         "kernel_ms": round(ms, 5),
         "mfma_bf16_tflops": round(tflops, 2),
         "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFS, 4),
