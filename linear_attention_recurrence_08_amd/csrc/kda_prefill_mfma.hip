@@ -283,11 +283,24 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t row = 16 * mb + 4 * lg + r;
-                    S[m][mb][r] = src ? src[row * D + col + 64 * m]
-                                      : (ident && row == col + 64 * m ? 1.f : 0.f);
-                }
+                for (int r = 0; r < 4; ++r)
+                    S[m][mb][r] = src ? src[(int64_t)(16 * mb + 4 * lg + r) * D + col + 64 * m]
+                                      : 0.f;
+        if (ident) {
+            // the diagonal entry of column col + 64 m lies in row block (col - ln + 64 m) / 16
+            // (the same for the whole wave), in register ln % 4 of lane group ln / 4
+#pragma unroll
+            for (int m = 0; m < NS; ++m) {
+                const int mbd = (int)((col - ln + 64 * m) >> 4);
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb)
+                    if (mb == mbd) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (4 * lg + r == ln) S[m][mb][r] = 1.f;
+                    }
+            }
+        }
     };
     auto state_out = [&](float* dst) {
 #pragma unroll
