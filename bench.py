@@ -14,7 +14,9 @@ gate; 3 x 256 B per (token, head) in bf16) on the same [4096, 96, 128] shape, an
 (short convolution, Swish, L2 norm, sigmoid beta, bounded log-decay: reads 3 dk + dv values and
 beta's logit, writes as many per (token, head)) on the same token and head count.  A `varlen`
 object times the prefill on the variable-length batch (16 sequences of 1,024-16,384 tokens with
-initial states, packed with cu_seqlens).  A `head_share` object times one GPU's share of the heads under
+initial states, packed with cu_seqlens).  A `long` object times the long-context prefill (one
+sequence of 131,072 tokens, H=96: the same work per token over a 32 times longer chain of tiles).
+A `head_share` object times one GPU's share of the heads under
 8-way head sharding (12 of 96 heads, T = 4096, batch 1) with kda_chunk_fwd and with
 kda_chunk_fwd_split (each sequence also cut into token ranges that run concurrently).
 
@@ -52,6 +54,7 @@ PREFILL_WORKLOADS = ("prefill_T4096_H96_d128_bf16", "varlen_16seq_H96_d128_bf16"
                      "long_T131072_H96_d128_bf16", "tiny_T64_H2_d32_f32")
 DECODE_WORKLOAD = "decode_N256_H96_d128_bf16"
 VARLEN_WORKLOAD = "varlen_16seq_H96_d128_bf16"
+LONG_WORKLOAD = "long_T131072_H96_d128_bf16"
 
 
 def _esize(dtype):
@@ -324,6 +327,40 @@ def time_launches(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps, wall  # ms per launch (one kernel per step), seconds
 
 
+def long_context(dev, stream, steps):
+    """The long-context prefill (B = 1, T = 131,072, H = 96, bimodal per-channel decay): the same
+    work per token as the 4,096-token layer, over a 32 times longer serial chain of tiles."""
+    import torch
+    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd
+    t0 = time.perf_counter()
+    xl = inputs.make_workload(LONG_WORKLOAD)
+    xld = xl.to(dev)
+    gen_s = time.perf_counter() - t0
+    lviews = xld.call_views()
+    ol = torch.empty_like(lviews[2])
+    hTl = torch.empty((xl.num_seqs, xl.H, xl.dk, xl.dv), dtype=torch.float32, device=dev)
+    print(f"[bench] long context {LONG_WORKLOAD}: T={xl.total_tokens} H={xl.H} steps={steps} "
+          f"(inputs drawn in {gen_s:.1f} s)", file=sys.stderr, flush=True)
+
+    def prefill_long():
+        kda_chunk_fwd(*lviews, h0=xld.h0, cu_seqlens=xld.cu_seqlens, o=ol, hT=hTl)
+
+    lms, _ = time_launches(prefill_long, steps, 1, stream)
+    lbytes = prefill_bytes(xl)
+    lgbs = lbytes / (lms * 1e-3) / 1e9
+    out = {
+        "workload": LONG_WORKLOAD, "total_tokens": xl.total_tokens, "steps": steps,
+        "ms_per_step": round(lms, 4), "value": round(xl.total_tokens / (lms * 1e-3), 1),
+        "unit": "tokens/s",
+        "roofline": {"bound": "hbm", "achieved": round(lgbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(lgbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic("kda_chunk_fwd_" + LONG_WORKLOAD),
+                     "kernel": "kda_prefill_mfma", "algorithmic_bytes_per_launch": lbytes},
+    }
+    del xl, xld, lviews, ol, hTl
+    return out
+
+
 def head_share(dev, stream, steps, warmup, unsplit=True):
     """Prefill of one GPU's share of K3's heads under 8-way head sharding (12 of 96, T = 4096,
     batch 1): kda_chunk_fwd beside kda_chunk_fwd_split with the library's segment count
@@ -409,6 +446,7 @@ def main():
     ap.add_argument("--no-frontend", action="store_true")
     ap.add_argument("--no-chunk64", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-split", action="store_true")
     ap.add_argument("--head-share-only", action="store_true",
                     help="time only the 12-head prefill (kda_chunk_fwd beside kda_chunk_fwd_split)")
@@ -575,6 +613,11 @@ def main():
     # ---------------- one GPU's share of the heads: 12 of 96 (8-way head sharding), batch 1 ------
     if not args.no_split:
         result["head_share"] = head_share(dev, stream, args.steps, args.warmup)
+
+    # ---------------- long context: one sequence of 131,072 tokens ----------------
+    if not args.no_long and args.workload != LONG_WORKLOAD:
+        result["long"] = long_context(dev, stream, max(3, args.steps // 4))
+        torch.cuda.empty_cache()
 
     # ---------------- variable-length batch: 16 sequences of 1,024-16,384 tokens ----------------
     if not args.no_varlen and args.workload != VARLEN_WORKLOAD:

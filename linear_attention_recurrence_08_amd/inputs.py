@@ -37,7 +37,9 @@ BLOCK_TOKENS = 2048  # token block of the draw order (one random stream per bloc
 H0_STREAM = 10 ** 6
 LEN_STREAM = 2 * 10 ** 6
 
-GATE_RECIPES = ("sigmoid", "sigmoid_shift1", "sigmoid_shiftm1", "bimodal", "zero")
+GATE_RECIPES = ("sigmoid", "sigmoid_shift1", "sigmoid_shiftm1", "bimodal", "zero", "floor",
+                "floor_half")
+BETA_RECIPES = ("sigmoid", "zero", "one")
 
 
 @dataclasses.dataclass
@@ -134,18 +136,39 @@ def _gate(z: np.ndarray, recipe: str) -> np.ndarray:
         return np.clip(centre + np.float32(0.01) * z, -5.0, 0.0).astype(np.float32)
     if recipe == "zero":             # alpha = 1 everywhere
         return np.zeros_like(z, dtype=np.float32)
+    if recipe == "floor":            # every channel at the log-decay floor -5 (exact in bf16)
+        return np.full_like(z, -5.0, dtype=np.float32)
+    if recipe == "floor_half":       # key channels [0, dk/2) at the floor, the rest at 0
+        dk = z.shape[-1]
+        row = np.where(np.arange(dk) < dk // 2, np.float32(-5.0), np.float32(0.0))
+        return np.broadcast_to(row, z.shape).astype(np.float32)
     raise ValueError(f"unknown gate recipe {recipe!r}")
+
+
+def _beta(b: np.ndarray, recipe: str) -> np.ndarray:
+    """beta from standard-normal noise b: sigmoid(N(0,1)), or the constants 0 and 1."""
+    if recipe == "sigmoid":
+        return _sigmoid(b)
+    if recipe == "zero":
+        return np.zeros_like(b, dtype=np.float32)
+    if recipe == "one":
+        return np.ones_like(b, dtype=np.float32)
+    raise ValueError(f"unknown beta recipe {recipe!r}")
 
 
 def make_inputs(seq_lens: Sequence[int], H: int, dk: int, dv: int, dtype: str, seed: int,
                 gate: str = "sigmoid", h0_sigma: Optional[float] = None,
-                packed: Optional[bool] = None, name: str = "") -> KDAInputs:
+                packed: Optional[bool] = None, name: str = "",
+                beta: str = "sigmoid") -> KDAInputs:
     """Draw one batch.
 
     seq_lens: the sequence lengths.  With packed=False (default when all lengths are equal) the
     batch is B equal-length sequences without cu_seqlens; otherwise it is one packed batch with
-    cu_seqlens.  h0_sigma None means h0 = zeros (passed as None).
+    cu_seqlens.  h0_sigma None means h0 = zeros (passed as None).  gate and beta name the
+    recipes for g (GATE_RECIPES) and beta (BETA_RECIPES); the draw order does not depend on
+    them, so two recipes give the same q, k and v.
     """
+    beta_recipe = beta
     seq_lens = [int(s) for s in seq_lens]
     if packed is None:
         packed = len(set(seq_lens)) > 1
@@ -157,7 +180,7 @@ def make_inputs(seq_lens: Sequence[int], H: int, dk: int, dv: int, dtype: str, s
     k = torch.empty((ttot, H, dk), dtype=tdt)
     v = torch.empty((ttot, H, dv), dtype=tdt)
     g = torch.empty((ttot, H, dk), dtype=tdt)
-    beta = torch.empty((ttot, H), dtype=tdt)
+    beta_t = torch.empty((ttot, H), dtype=tdt)
 
     def draw_block(b):
         t0 = b * BLOCK_TOKENS
@@ -171,7 +194,7 @@ def make_inputs(seq_lens: Sequence[int], H: int, dk: int, dv: int, dtype: str, s
         q[t0:t0 + n] = torch.from_numpy(_l2_normalise(qb)).to(tdt)
         k[t0:t0 + n] = torch.from_numpy(_l2_normalise(kb)).to(tdt)
         v[t0:t0 + n] = torch.from_numpy(vb).to(tdt)
-        beta[t0:t0 + n] = torch.from_numpy(_sigmoid(bb)).to(tdt)
+        beta_t[t0:t0 + n] = torch.from_numpy(_beta(bb, beta_recipe)).to(tdt)
         g[t0:t0 + n] = torch.from_numpy(_gate(zb, gate)).to(tdt)
 
     N = len(seq_lens)
@@ -191,10 +214,10 @@ def make_inputs(seq_lens: Sequence[int], H: int, dk: int, dv: int, dtype: str, s
             list(ex.map(draw_h0, range(N)))
     if packed:
         cu = torch.tensor(np.concatenate([[0], np.cumsum(seq_lens)]), dtype=torch.int32)
-        return KDAInputs(q, k, v, g, beta, h0, cu, 1, ttot, H, dk, dv, dtype, name)
+        return KDAInputs(q, k, v, g, beta_t, h0, cu, 1, ttot, H, dk, dv, dtype, name)
     B = N
     T = seq_lens[0] if N else 0
-    return KDAInputs(q, k, v, g, beta, h0, None, B, T, H, dk, dv, dtype, name)
+    return KDAInputs(q, k, v, g, beta_t, h0, None, B, T, H, dk, dv, dtype, name)
 
 
 def varlen_lengths(seed: int, n: int = 16, lo: int = 1024, hi: int = 16384):

@@ -159,12 +159,17 @@ def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, output_final_state, o, hT):
     if o is None:
         o = torch.empty((*lead, H, dv), dtype=dt, device=dev)
     else:
+        # the kernels write every (token, head) row of o: a smaller buffer would be overrun
         _check(o, "o", dev, dt)
+        if tuple(o.shape) != (*lead, H, dv):
+            raise ValueError(f"o must be {[*lead, H, dv]}, got {list(o.shape)}")
     if output_final_state:
         if hT is None:
             hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
         else:
             _check(hT, "hT", dev, torch.float32)
+            if tuple(hT.shape) != (N, H, dk, dv):
+                raise ValueError(f"hT must be [{N}, {H}, {dk}, {dv}], got {list(hT.shape)}")
     else:
         hT = None
     return dev, B, T, H, dk, dv, N, o, hT
@@ -296,16 +301,20 @@ def kda_chunk_fwd_snapshots(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g
         _check(snap_offsets, "snap_offsets", dev, torch.int32)
         if snap_offsets.numel() != N + 1:
             raise ValueError(f"snap_offsets must have {N + 1} entries")
+        # the kernels write snapshot rows up to snap_offsets[-1]: the buffer must hold them all
+        # (reading that count back is one device-to-host synchronisation)
+        n_snaps = int(snap_offsets[-1].item()) if N > 0 else 0
         if snaps is None:
-            snaps = torch.empty((int(snap_offsets[-1].item()), H, dk, dv), dtype=torch.float32,
-                                device=dev)
+            snaps = torch.empty((n_snaps, H, dk, dv), dtype=torch.float32, device=dev)
+        elif snaps.dim() != 4 or snaps.shape[0] < n_snaps:
+            raise ValueError(f"snaps needs {n_snaps} entries, got {list(snaps.shape)}")
     else:
         if snap_offsets is not None:
             raise ValueError("snap_offsets is only used with cu_seqlens")
         if snaps is None:
             snaps = torch.empty((N * (T // stride), H, dk, dv), dtype=torch.float32, device=dev)
-        elif snaps.shape[0] < N * (T // stride):
-            raise ValueError(f"snaps needs {N * (T // stride)} entries")
+        elif snaps.dim() != 4 or snaps.shape[0] < N * (T // stride):
+            raise ValueError(f"snaps needs {N * (T // stride)} entries, got {list(snaps.shape)}")
     _check(snaps, "snaps", dev, torch.float32)
     if snaps.shape[1:] != (H, dk, dv):
         raise ValueError(f"snaps must be [*, {H}, {dk}, {dv}]")
@@ -335,6 +344,8 @@ def _decode_args(q, k, v, g, beta, S, o):
         o = torch.empty((N, H, dv), dtype=dt, device=dev)
     else:
         _check(o, "o", dev, dt)
+        if tuple(o.shape) != (N, H, dv):
+            raise ValueError(f"o must be [{N}, {H}, {dv}], got {list(o.shape)}")
     return dev, N, H, dk, dv, o
 
 
@@ -378,6 +389,8 @@ def kda_decode_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: 
         y = torch.empty_like(o)
     else:
         _check(y, "y", dev, q.dtype)
+        if tuple(y.shape) != (N, H, dv):
+            raise ValueError(f"y must be [{N}, {H}, {dv}], got {list(y.shape)}")
     st = load_library().kda_decode_step_gated(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(gate), _ptr(weight),
         float(eps), _ptr(o), _ptr(y), N, H, dk, dv, _dtype_code(q), _stream(dev))

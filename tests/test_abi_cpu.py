@@ -326,3 +326,71 @@ def test_frontend_argument_errors(lib, kw, code):
 def test_frontend_empty_is_noop(lib):
     assert _front(lib, B=0) == 0
     assert _front(lib, T=0) == 0
+
+
+class _NoCalls:
+    """Stands in for the library: any call into it fails the test (the binding must reject the
+    arguments before reaching the C ABI)."""
+    def __getattr__(self, name):
+        raise AssertionError(f"the binding called {name} with arguments it should have rejected")
+
+
+@pytest.fixture
+def host_binding(monkeypatch):
+    """The binding with its device checks relaxed so that host tensors reach the shape checks."""
+    import torch
+    from linear_attention_recurrence_08_amd import kda
+
+    def check(t, name, device, dtype=None):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}")
+    monkeypatch.setattr(kda, "_check", check)
+    monkeypatch.setattr(kda, "_stream", lambda dev: None)
+    monkeypatch.setattr(kda, "load_library", lambda: _NoCalls())
+    return kda, torch
+
+
+def _bf(torch, *shape):
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("which,shape", [
+    ("o", (16, 2, 64)), ("o", (15, 2, 128)), ("o", (16, 3, 128)),
+    ("hT", (1, 2, 128, 64)), ("hT", (2, 2, 128, 128)),
+])
+def test_binding_rejects_small_prefill_outputs(host_binding, which, shape):
+    """A caller's o or hT whose shape differs from (lead, H, dv) / (N, H, dk, dv) is rejected:
+    the kernels write every row, so a smaller buffer would be written past its end."""
+    kda, torch = host_binding
+    x = _bf(torch, 16, 2, 128)
+    kw = {which: _bf(torch, *shape) if which == "o" else torch.zeros(*shape)}
+    with pytest.raises(ValueError):
+        kda.kda_chunk_fwd(x, x, x, x, _bf(torch, 16, 2), **kw)
+
+
+def test_binding_rejects_small_decode_outputs(host_binding):
+    kda, torch = host_binding
+    q = _bf(torch, 4, 2, 128)
+    S = torch.zeros(4, 2, 128, 128)
+    with pytest.raises(ValueError):
+        kda.kda_decode_step(q, q, q, q, _bf(torch, 4, 2), S, o=_bf(torch, 3, 2, 128))
+    with pytest.raises(ValueError):
+        kda.kda_decode_step_gated(q, q, q, q, _bf(torch, 4, 2), S, q, y=_bf(torch, 4, 2, 64))
+
+
+def test_binding_rejects_small_snapshot_buffers(host_binding):
+    kda, torch = host_binding
+    x = _bf(torch, 64, 2, 128)
+    # equal-length batch: 64 / 16 = 4 snapshots needed
+    with pytest.raises(ValueError):
+        kda.kda_chunk_fwd_snapshots(x, x, x, x, _bf(torch, 64, 2), 16,
+                                    snaps=torch.zeros(3, 2, 128, 128))
+    # packed batch: the offsets say 5 snapshots (lengths 48 and 32 at stride 16)
+    cu = torch.tensor([0, 48, 80], dtype=torch.int32)
+    offs = torch.tensor([0, 3, 5], dtype=torch.int32)
+    xp = _bf(torch, 80, 2, 128)
+    with pytest.raises(ValueError):
+        kda.kda_chunk_fwd_snapshots(xp, xp, xp, xp, _bf(torch, 80, 2), 16, cu_seqlens=cu,
+                                    snap_offsets=offs, snaps=torch.zeros(4, 2, 128, 128))

@@ -51,6 +51,32 @@ def oracle_prefill(oracle, x, heads=None):
                              to64(x.g[:, hs]), to64(x.beta[:, hs]), h0, cu)
 
 
+def check_prefill_all_heads(oracle_mod, x, dev, tol=None, label="", head_batch=32):
+    """Every head of a large workload against the oracle, in batches of heads so that the float64
+    copies stay within host memory; the error is max-normalised over the whole tensor."""
+    tol = tol or TOL[x.dtype]
+    _say(f"{label}: GPU prefill Ttot={x.total_tokens} N={x.num_seqs} H={x.H} {x.dtype}")
+    o, hT = gpu_prefill(x, dev)
+    num = {"o": 0.0, "hT": 0.0}
+    den = {"o": 0.0, "hT": 0.0}
+    for h0 in range(0, x.H, head_batch):
+        hs = list(range(h0, min(x.H, h0 + head_batch)))
+        t0 = time.time()
+        o_ref, h_ref = oracle_prefill(oracle_mod, x, hs)
+        og, hg = to64(o[:, hs]), to64(hT[:, hs])
+        assert np.isfinite(og).all() and np.isfinite(hg).all()
+        num["o"] = max(num["o"], float(np.abs(og - o_ref).max()))
+        den["o"] = max(den["o"], float(np.abs(o_ref).max()))
+        num["hT"] = max(num["hT"], float(np.abs(hg - h_ref).max()))
+        den["hT"] = max(den["hT"], float(np.abs(h_ref).max()))
+        del o_ref, h_ref, og, hg
+        _say(f"{label}: heads {hs[0]}..{hs[-1]} checked ({time.time() - t0:.1f} s)")
+    eo, eh = num["o"] / max(den["o"], 1e-30), num["hT"] / max(den["hT"], 1e-30)
+    _say(f"{label}: all {x.H} heads, error o={eo:.3e} hT={eh:.3e} (bar {tol})")
+    assert eo <= tol and eh <= tol, (eo, eh)
+    return o, hT
+
+
 def check_prefill(oracle_mod, x, dev, heads=None, tol=None, label=""):
     tol = tol or TOL[x.dtype]
     _say(f"{label}: GPU prefill Ttot={x.total_tokens} N={x.num_seqs} H={x.H} "
@@ -133,22 +159,31 @@ def test_prefill_T4096_H96(oracle_mod):
     check_prefill(oracle_mod, x, dev, heads=None, label="prefill_T4096_H96")
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("gate", ["sigmoid_shift1", "sigmoid_shiftm1"])
 def test_varlen_16seq_H96(oracle_mod, gate):
+    """The 16-sequence packed batch (113,799 tokens, initial states), every head: the 128-column
+    kernel with longest-first dispatch remaps (sequence, head) pairs, so all of them are
+    checked."""
     dev = _dev()
     from linear_attention_recurrence_08_amd import inputs
     x = inputs.make_workload("varlen_16seq_H96_d128_bf16", gate=gate)
-    check_prefill(oracle_mod, x, dev, heads=[0, 41, 95], label=f"varlen[{gate}]")
+    check_prefill_all_heads(oracle_mod, x, dev, label=f"varlen[{gate}]")
 
 
+@pytest.mark.timeout(900)
 def test_long_T131072_H96(oracle_mod):
+    """131,072 tokens, every head, outputs and final state."""
     dev = _dev()
     from linear_attention_recurrence_08_amd import inputs
     x = inputs.make_workload("long_T131072_H96_d128_bf16")
-    check_prefill(oracle_mod, x, dev, heads=[0, 95], label="long_T131072")
+    check_prefill_all_heads(oracle_mod, x, dev, label="long_T131072")
 
 
+@pytest.mark.timeout(600)
 def test_decode_N256_H96(oracle_mod):
+    """The batched decode step, every one of the 24,576 (sequence, head) units, in batches of
+    sequences (the float64 states of all of them would be 3.2 GB at once)."""
     dev = _dev()
     from linear_attention_recurrence_08_amd import inputs, kda_decode_step
     d = inputs.make_workload("decode_N256_H96_d128_bf16")
@@ -156,16 +191,18 @@ def test_decode_N256_H96(oracle_mod):
     S = d.h0.to(dev)
     o = kda_decode_step(d.q.to(dev), d.k.to(dev), d.v.to(dev), d.g.to(dev), d.beta.to(dev), S)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(99)
-    units = sorted(set(map(tuple, rng.integers(0, [256, 96], size=(96, 2)).tolist())))
-    ns = [u[0] for u in units]
-    hs = [u[1] for u in units]
-    sel = lambda t: to64(t[ns, hs])[:, None]  # [units, 1, ...]
-    o_ref, S_ref = oracle_mod.decode_step(sel(d.q), sel(d.k), sel(d.v), sel(d.g),
-                                          to64(d.beta[ns, hs])[:, None], sel(d.h0))
-    eo = err(to64(o[ns, hs]), o_ref[:, 0])
-    es = err(to64(S[ns, hs]), S_ref[:, 0])
-    _say(f"decode_N256_H96: {len(units)} sampled units, error o={eo:.3e} S={es:.3e}")
+    num_o = den_o = num_s = den_s = 0.0
+    for n0 in range(0, 256, 32):
+        ns = slice(n0, n0 + 32)
+        o_ref, S_ref = oracle_mod.decode_step(to64(d.q[ns]), to64(d.k[ns]), to64(d.v[ns]),
+                                              to64(d.g[ns]), to64(d.beta[ns]), to64(d.h0[ns]))
+        og, sg = to64(o[ns]), to64(S[ns])
+        num_o, den_o = max(num_o, float(np.abs(og - o_ref).max())), \
+            max(den_o, float(np.abs(o_ref).max()))
+        num_s, den_s = max(num_s, float(np.abs(sg - S_ref).max())), \
+            max(den_s, float(np.abs(S_ref).max()))
+    eo, es = num_o / den_o, num_s / den_s
+    _say(f"decode_N256_H96: all 24,576 units, error o={eo:.3e} S={es:.3e}")
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 

@@ -52,3 +52,22 @@ def test_decode_inputs_layout():
     assert d.q.shape == (5, 3, 32) and d.v.shape == (5, 3, 16) and d.beta.shape == (5, 3)
     assert d.h0.shape == (5, 3, 32, 16) and d.h0.dtype == torch.float32
     assert 0.03 < float(d.h0.std()) < 0.07
+
+
+def test_floor_and_constant_beta_recipes():
+    """The edge-case recipes hold exactly the values they name, in bf16 as well, and keep the
+    draw order (q, k, v are the same as with the default recipes)."""
+    base = inputs.make_inputs([40], H=2, dk=128, dv=128, dtype="bf16", seed=9)
+    fl = inputs.make_inputs([40], H=2, dk=128, dv=128, dtype="bf16", seed=9, gate="floor",
+                            beta="one")
+    assert float(fl.g.float().min()) == -5.0 and float(fl.g.float().max()) == -5.0
+    assert float(fl.beta.float().min()) == 1.0 and float(fl.beta.float().max()) == 1.0
+    assert torch.equal(base.q, fl.q) and torch.equal(base.k, fl.k) and torch.equal(base.v, fl.v)
+    half = inputs.make_inputs([40], H=2, dk=128, dv=128, dtype="bf16", seed=9, gate="floor_half",
+                              beta="zero")
+    g = half.g.float()
+    assert float(g[..., :64].min()) == -5.0 and float(g[..., :64].max()) == -5.0
+    assert float(g[..., 64:].abs().max()) == 0.0
+    assert float(half.beta.float().abs().max()) == 0.0
+    # a whole 16-token tile at the floor reaches the bound's edge: cumulative log-decay -80
+    assert float(fl.g.float()[:16, 0, 0].sum()) == -80.0

@@ -199,8 +199,62 @@ def pin_snapshots(rec):
             assert np.array_equal(snaps[scu[n + 1] - 1], hT[n])
 
 
+def _delta_rule_matrix_form(q, k, v, alpha, beta, S0):
+    """DeltaNet / Gated DeltaNet written as explicit transition matrices, one head:
+    S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T and o_t = S_t^T q_t, with a_t one
+    scalar per token (a_t = 1 for DeltaNet).  A different formulation from the oracle's
+    fade / error / write loop: the erase is an explicit dk x dk matrix and the decay multiplies
+    the whole product."""
+    T, dk = k.shape
+    S = S0.copy()
+    o = np.zeros((T, v.shape[1]))
+    for t in range(T):
+        E = np.eye(dk) - beta[t] * np.outer(k[t], k[t])
+        S = alpha[t] * (E @ S) + beta[t] * np.outer(k[t], v[t])
+        o[t] = S.T @ q[t]
+    return o, S
+
+
+def pin_deltanet_reduction(rec):
+    """alpha = 1 (g = 0) reduces KDA to plain DeltaNet, the delta rule with no forgetting ("Kimi
+    K3's hybrid block, from first principles", section "From linear attention to the delta
+    rule": the delta rule alone, before any decay is added).  Compared with the matrix form
+    above on general keys (not unit length) and a nonzero h0."""
+    rng = np.random.default_rng(17)
+    T, H, dk, dv = 12, 2, 5, 4
+    q, k, v, _, beta, S0 = _rand_case(rng, T, H, dk, dv, unit_keys=False)
+    g = np.zeros((T, H, dk))
+    o, hT = rec(q, k, v, g, beta, S0)
+    for h in range(H):
+        o_ref, S_ref = _delta_rule_matrix_form(q[:, h], k[:, h], v[:, h], np.ones(T),
+                                               beta[:, h], S0[0, h])
+        np.testing.assert_allclose(o[:, h], o_ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(hT[0, h], S_ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_gated_deltanet_reduction(rec):
+    """The same log-decay on every key channel reduces KDA to Gated DeltaNet, one decay per head
+    ("Kimi K3's hybrid block, from first principles", section "From linear attention to the delta
+    rule": Gated DeltaNet pairs the delta rule with a single decay per head; "Kimi K3", section
+    "Forgetting different features at different rates": KDA generalises it to one factor per
+    channel).  Compared with the matrix form above, where the scalar decay multiplies the
+    erase-and-write product."""
+    rng = np.random.default_rng(18)
+    T, H, dk, dv = 12, 2, 5, 4
+    q, k, v, _, beta, S0 = _rand_case(rng, T, H, dk, dv, unit_keys=False)
+    gs = -rng.uniform(0.0, 3.0, size=(T, H))          # one log-decay per (token, head)
+    g = np.repeat(gs[:, :, None], dk, axis=2)
+    o, hT = rec(q, k, v, g, beta, S0)
+    for h in range(H):
+        o_ref, S_ref = _delta_rule_matrix_form(q[:, h], k[:, h], v[:, h], np.exp(gs[:, h]),
+                                               beta[:, h], S0[0, h])
+        np.testing.assert_allclose(o[:, h], o_ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(hT[0, h], S_ref, rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [pin_unit_key_beta_one, pin_unit_key_partial_beta, pin_gradient_step, pin_pure_decay,
-            pin_half_life, pin_whiteboard, pin_snapshots]
+            pin_half_life, pin_whiteboard, pin_snapshots, pin_deltanet_reduction,
+            pin_gated_deltanet_reduction]
 
 
 # --------------------------------------------------------------------------------------------
@@ -397,6 +451,18 @@ def _read_before_write(src):
     return src.replace(WRITE_ANCHOR, READ_BLOCK + WRITE_ANCHOR)
 
 
+def _decay_after_write(src):
+    """Fade the state after the erase-and-write instead of before it: S <- Diag(a) (S + k u^T)
+    with u computed from the unfaded state."""
+    fade = ("        for (int64_t r = 0; r < dk; ++r) {\n"
+            "            a[r] = J->gate_is_alpha ? gt[r] : exp(gt[r]);\n"
+            "            for (int64_t c = 0; c < dv; ++c) S[r * dv + c] *= a[r];\n"
+            "        }\n")
+    assert fade in src and READ_BLOCK in src
+    src = src.replace(fade, "")
+    return src.replace(READ_BLOCK, fade + READ_BLOCK)
+
+
 MUTANTS = {
     "error_sign": _swap("u[c] = bt * (vt[c] - pred[c]);", "u[c] = bt * (vt[c] + pred[c]);"),
     "beta_dropped": _swap("u[c] = bt * (vt[c] - pred[c]);", "u[c] = (vt[c] - pred[c]);"),
@@ -409,6 +475,7 @@ MUTANTS = {
     "write_along_query": _swap("S[r * dv + c] += kt[r] * u[c];", "S[r * dv + c] += qt[r] * u[c];"),
     "h0_ignored": _swap("S[i] = h0 ? h0[i] : 0.0;", "S[i] = 0.0;"),
     "read_before_write": _read_before_write,
+    "decay_after_write": _decay_after_write,
     # snapshot bookkeeping (in-bounds for the pin's lengths)
     "snapshot_one_token_early": _swap("const int64_t done = t - J->cu[n] + 1;",
                                       "const int64_t done = t - J->cu[n] + 2;"),
@@ -441,3 +508,33 @@ def test_planted_mistake_is_caught(oracle_mod, tmp_path, name):
     except AssertionError:
         caught.append("pin_brute_force")
     assert caught, f"mutant {name} passed every pin"
+
+
+# Mutants each reduction pin must catch on its own (a pin that passes a wrong recurrence pins
+# nothing): with alpha = 1 every mistake in the delta term shows; with one decay per head the
+# decay's presence and its place before the write show as well.
+REDUCTION_CATCHES = {
+    "pin_deltanet_reduction": ["error_sign", "beta_dropped", "read_with_key", "write_along_query",
+                               "h0_ignored", "read_before_write"],
+    "pin_gated_deltanet_reduction": ["error_sign", "beta_dropped", "read_with_key",
+                                     "write_along_query", "h0_ignored", "read_before_write",
+                                     "no_decay", "decay_after_write"],
+}
+
+
+@pytest.mark.parametrize("pin_name", sorted(REDUCTION_CATCHES))
+def test_reduction_pin_catches_mutants(oracle_mod, tmp_path, pin_name):
+    if shutil.which("gcc") is None:
+        pytest.skip("no host compiler")
+    pin = globals()[pin_name]
+    base = open(os.path.join(os.path.dirname(oracle_mod.__file__), "kda_oracle.c")).read()
+    for name in REDUCTION_CATCHES[pin_name]:
+        cfile = tmp_path / f"{name}.c"
+        cfile.write_text(MUTANTS[name](base))
+        so = tmp_path / f"lib{name}.so"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", str(cfile),
+                        "-o", str(so), "-lm"], check=True)
+        lib = oracle_mod.kda_oracle.load_library(str(so))
+        rec = lambda *a, **kw: oracle_mod.recurrence(*a, lib=lib, **kw)
+        with pytest.raises(AssertionError):
+            pin(rec)
