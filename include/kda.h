@@ -34,7 +34,9 @@
  *
  * Ownership and streams.  The caller owns every buffer (device memory, e.g. allocated by PyTorch)
  * and passes a HIP stream (hipStream_t as void*, NULL = the null stream).  The library allocates
- * nothing, keeps no state between calls and is thread-safe.  Calls are asynchronous: the return
+ * nothing, keeps no state between calls and is thread-safe, with one exception:
+ * kda_chunk_fwd_split_noalloc keeps its workspace in a static device array per GPU, which calls
+ * that overlap on one GPU share.  Calls are asynchronous: the return
  * status reports argument errors and launch failures; execution faults surface at the caller's
  * next synchronisation of the stream.
  *
@@ -70,8 +72,10 @@ enum {
     KDA_ERR_STRIDE = -8,      /* snapshot stride not a positive multiple of 16, or (KDA_VALIDATE)
                                  snap_offsets inconsistent with the sequence lengths */
     KDA_ERR_ALIGN = -9,       /* a buffer of the output stage is not 16-byte aligned */
-    KDA_ERR_WORKSPACE = -10   /* workspace NULL, smaller than the size query returns, or not
+    KDA_ERR_WORKSPACE = -10,  /* workspace NULL, smaller than the size query returns, or not
                                  256-byte aligned */
+    KDA_ERR_SCRATCH = -11     /* the call needs more workspace than the library's static device
+                                 array holds (kda_chunk_fwd_split_noalloc: 32 MiB per device) */
 };
 
 /*
@@ -193,6 +197,26 @@ int kda_chunk_fwd_split_segments(const int32_t* cu_seqlens, int num_seqs, int ma
 size_t kda_chunk_fwd_split_workspace_bytes(const int32_t* cu_seqlens, int num_seqs,
                                            int max_seqlen, int B, int T, int H, int dk, int dv,
                                            int dtype, int segments);
+
+/*
+ * kda_chunk_fwd_split_noalloc -- kda_chunk_fwd_split for callers that cannot allocate device
+ * memory: code under HIP stream capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The workspace is a static device array of the library, 32 MiB per device (KDA_ERR_SCRATCH for
+ * a call whose kda_chunk_fwd_split_workspace_bytes exceeds it, returned before anything runs);
+ * the call itself allocates nothing.  The array's device address is looked up once per device,
+ * on the first call made with that device current (the stream must belong to the current
+ * device).  Every call on one GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.  Its contents between calls
+ * do not matter.
+ *
+ * Arguments, results and the other errors as kda_chunk_fwd_split, without workspace and
+ * workspace_bytes.
+ */
+int kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void* v, const void* g,
+                                const void* beta, const float* h0, const int32_t* cu_seqlens,
+                                int num_seqs, int max_seqlen, void* o, float* hT,
+                                int B, int T, int H, int dk, int dv, int dtype, int segments,
+                                void* stream);
 
 /*
  * kda_chunk_fwd_snapshots -- kda_chunk_fwd that also saves the state at every multiple of

@@ -245,6 +245,9 @@ const char* kda_status_string(int status) {
             return "workspace missing, smaller than the size its query returns "
                    "(kda_chunk_fwd_chunk64_workspace_bytes, kda_chunk_fwd_split_workspace_bytes), "
                    "or not 256-byte aligned";
+        case KDA_ERR_SCRATCH:
+            return "the call needs more workspace than the library's static device array holds "
+                   "(kda_chunk_fwd_split_noalloc: 32 MiB per device)";
         default: return "unknown status";
     }
 }

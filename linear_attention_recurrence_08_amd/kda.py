@@ -34,6 +34,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_BF16, KDA_F32 = 0, 1
 KDA_OK = 0
 KDA_ERR_STRIDE = -8
+KDA_ERR_SCRATCH = -11
 _lib = None
 
 
@@ -66,6 +67,9 @@ def load_library():
                                             i32, i32, i32, i32, i32, i32, vp, ctypes.c_size_t,
                                             vp]
         lib.kda_chunk_fwd_split.restype = i32
+        lib.kda_chunk_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp,
+                                                    i32, i32, i32, i32, i32, i32, i32, vp]
+        lib.kda_chunk_fwd_split_noalloc.restype = i32
         lib.kda_chunk_fwd_split_segments.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                                      i32]
         lib.kda_chunk_fwd_split_segments.restype = i32
@@ -269,6 +273,32 @@ def kda_chunk_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
         nbytes, _stream(dev))
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd_split")
+    return o, hT
+
+
+def kda_chunk_fwd_split_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                g: torch.Tensor, beta: torch.Tensor,
+                                h0: Optional[torch.Tensor] = None,
+                                cu_seqlens: Optional[torch.Tensor] = None,
+                                max_seqlen: Optional[int] = None,
+                                output_final_state: bool = True, segments: int = 0,
+                                o: Optional[torch.Tensor] = None,
+                                hT: Optional[torch.Tensor] = None
+                                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_chunk_fwd_split with its workspace in the library's static device array (32 MiB per
+    device) instead of a caller buffer: the C call allocates nothing.  Pass o (and hT) to keep
+    this function from allocating them.  Calls that overlap on one GPU share the array and race.
+    With cu_seqlens and no max_seqlen, max_seqlen is read from cu_seqlens (one synchronisation)."""
+    dev, B, T, H, dk, dv, N, o, hT = _prefill_args(q, k, v, g, beta, h0, cu_seqlens,
+                                                   output_final_state, o, hT)
+    if cu_seqlens is not None and max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if N > 0 else 0
+    st = load_library().kda_chunk_fwd_split_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), N,
+        int(max_seqlen or 0), _ptr(o), _ptr(hT), B, T, H, dk, dv, _dtype_code(q), int(segments),
+        _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd_split_noalloc")
     return o, hT
 
 

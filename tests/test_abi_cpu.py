@@ -31,6 +31,7 @@ def test_header_declares_the_boundary():
     assert _declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_chunk64",
                                      "kda_chunk_fwd_chunk64_workspace_bytes",
                                      "kda_chunk_fwd_snapshots", "kda_chunk_fwd_split",
+                                     "kda_chunk_fwd_split_noalloc",
                                      "kda_chunk_fwd_split_segments",
                                      "kda_chunk_fwd_split_workspace_bytes",
                                      "kda_decode_step", "kda_decode_step_gated", "kda_frontend",
@@ -45,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     from linear_attention_recurrence_08_amd.kda import kda_status_string
     assert kda_status_string(0) == "ok"
-    for code in range(-10, 0):
+    for code in range(-11, 0):
         s = kda_status_string(code)
         assert s and s != "unknown status"
     assert kda_status_string(-99) == "unknown status"
