@@ -373,7 +373,7 @@ def head_share(dev, stream, steps, warmup, unsplit=True):
     xs = inputs.make_inputs([Ts], H=Hs, dk=128, dv=128, dtype="bf16", seed=1, packed=False)
     xsd = xs.to(dev)
     sviews = xsd.call_views()
-    o_s = torch.empty_like(xsd.v)
+    o_s = torch.empty_like(sviews[2])
     h_s = torch.empty((1, Hs, 128, 128), dtype=torch.float32, device=dev)
     P = kda_chunk_fwd_split_segments(xsd.q, 1, Ts, Hs, 128, 128, 0)
     sbytes = kda_chunk_fwd_split_workspace_bytes(xsd.q, 1, Ts, Hs, 128, 128, 0)
