@@ -51,78 +51,17 @@
 // For the K = 32 products over key channels, slot j of lane group lg stands for channel
 // 16 (j / 4) + 4 lg + (j % 4) of the 32-channel group; A and B operands always use this order.
 #include "kda_internal.h"
+#include "kda_mfma.h"
 
 namespace kda {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using namespace mfma;
 
 constexpr int C = 16;      // tile tokens
 constexpr int D = 128;     // dk = dv
 constexpr int NT = 768;    // threads per workgroup (12 waves: 4 per stage)
 constexpr int kLptMaxSeqs = 64;   // varlen batches up to this many sequences run longest first
-constexpr float LOG2E = 1.4426950408889634f;
-constexpr float L2E_HI = 1.4453125f;          // bf16(log2 e)
-constexpr float L2E_LO = -0.00262451171875f;  // bf16(log2 e - L2E_HI)
-
-__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-// float32 -> bf16, round to nearest even, two values per v_cvt_pk_bf16_f32.  Going through 32-bit
-// integers keeps the conversions paired when the result feeds a matrix-core operand.
-__device__ __forceinline__ uint32_t pk2(float a, float b) {
-    const f32x2 v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-__device__ __forceinline__ bf16x4 bf4(f32x4 x) {
-    const u32x2 u = {pk2(x[0], x[1]), pk2(x[2], x[3])};
-    return __builtin_bit_cast(bf16x4, u);
-}
-__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ __forceinline__ f32x4 zero4() { return (f32x4){0.f, 0.f, 0.f, 0.f}; }
-__device__ __forceinline__ bf16x4 as_bf4(uint2 u) { return __builtin_bit_cast(bf16x4, u); }
-__device__ __forceinline__ uint2 as_u2(bf16x4 b) { return __builtin_bit_cast(uint2, b); }
-__device__ __forceinline__ f32x4 unpack4(uint2 u) {  // bf16 x4 -> float32 x4 (exact)
-    return (f32x4){__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                   __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
-}
-// LDS transpose read (ds_read_b64_tr_b16): in each group of 16 lanes, lane i receives, as
-// element e, element i % 4 of the four 16-bit values that lane 4e + i / 4 of the group addresses.
-// With lane 16q + 4r + a addressing the four values (row 4q + r, columns 4a .. 4a+3) of a
-// row-major 16 x 16 block, lane 16q + i receives column i of rows 4q .. 4q+3: the accumulator
-// layout of the block (the transpose of its row-major operand fragment).
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ bf16x4 lds_tr16(const void* p) {
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
-}
-// Raw buffer resource word 3 for gfx9 (32-bit data format, no swizzle, no thread-id offset);
-// loads past the record count return zero.
-constexpr int kBufferFlags = 0x00020000;
-__device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
-// Workgroup barrier that orders LDS only: global loads issued before it stay in flight (a full
-// __syncthreads() would also wait for the prefetched tiles).
-// The scheduling fences keep the compiler from hoisting the next tile's arithmetic above the
-// barrier, where it would consume registers whose loads were issued only one tile ago.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    __builtin_amdgcn_sched_barrier(0);
-}
 
 // (workgroup index) -> (pair index p = n * H + head, slice) with both slices of a pair on one XCD
 // (workgroups are dealt to the 8 XCDs round-robin by index); one slice per pair: p = b.

@@ -14,9 +14,12 @@
 // product per segment and head on the serial chain of the composition, and one 128 x 128 product
 // per token of the later segments for the correction.
 #include "kda_internal.h"
+#include "kda_mfma.h"
 
 namespace kda {
 namespace {
+
+using namespace mfma;
 
 constexpr int D = 128;
 
@@ -37,27 +40,6 @@ __device__ __forceinline__ int64_t seq_segments(const PrefillArgs& a, int64_t le
     return len <= 0 ? 1 : min((len + a.seg_len - 1) / a.seg_len, a.split);
 }
 
-// Workgroup barrier that orders LDS only: the global loads issued ahead stay in flight across it,
-// and the global stores need no ordering within the launch.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ uint32_t pk2(float x, float y) {
-    const f32x2 v = {x, y};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 __device__ __forceinline__ float hi_of(uint32_t u, int half) {   // one bf16 of a pair, as float
     return __uint_as_float(half ? (u & 0xffff0000u) : (u << 16));
 }
