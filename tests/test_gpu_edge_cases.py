@@ -13,9 +13,11 @@ per-channel decay (same section).  Besides the oracle comparison, two closed for
 the GPU outputs directly: with beta = 1 and q = k every output reads back its own value, and with
 beta = 0 every output is q_t^T Diag(exp(sum of g up to t)) h0.
 
-Variants: the 64-column matrix-core kernel with stage A's and with stage B's issue priority, the
-128-column one (256 or more (sequence, head) pairs), the float32 general kernel (bf16 forced onto
-it, and float32 inputs), chunk 64 on the matrix cores and in float32, and the token-range split.
+Variants: the producer/consumer kernel (opt-in, up to 128 (sequence, head) pairs; its ring in L2,
+and with every ring access at system scope), the 64-column matrix-core kernel with stage A's and with stage
+B's issue priority, the 128-column one (256 or more pairs), the float32 general kernel (bf16
+forced onto it, and float32 inputs), chunk 64 on the matrix cores and in float32, and the
+token-range split.
 """
 import numpy as np
 import pytest
@@ -38,17 +40,27 @@ def err(x, ref):
     return float(np.abs(x - ref).max() / max(np.abs(ref).max(), 1e-30))
 
 
-# (name, seq_lens, H, dtype, packed, entry, env)
+# (name, seq_lens, H, dtype, packed, entry, env: {name: value})
 VARIANTS = [
+    ("producer_consumer", [96, 37], 2, "bf16", True, "chunk16", {"KDA_PC": "1"}),
+    ("producer_consumer_coherent", [150, 37, 16], 3, "bf16", True, "chunk16",
+     {"KDA_PC": "1", "KDA_PC_COHERENT": "1"}),
     ("mfma64_stageB_prio", [96, 37], 2, "bf16", True, "chunk16", None),
     ("mfma64_stageA_prio", [80], 64, "bf16", False, "chunk16", None),
     ("mfma128", [40, 37, 16, 50], 64, "bf16", True, "chunk16", None),
-    ("general_bf16", [70, 33], 2, "bf16", True, "chunk16", "KDA_FORCE_GENERAL"),
+    ("general_bf16", [70, 33], 2, "bf16", True, "chunk16", {"KDA_FORCE_GENERAL": "1"}),
     ("general_f32", [70, 33], 2, "f32", True, "chunk16", None),
     ("chunk64_mfma", [150, 64, 21], 2, "bf16", True, "chunk64", None),
     ("chunk64_f32", [150, 64, 21], 2, "f32", True, "chunk64", None),
     ("split", [640], 2, "bf16", False, "split", None),
 ]
+
+
+def _setenv(monkeypatch, env):
+    for k, v in (env or {}).items():
+        monkeypatch.setenv(k, v)
+
+
 RECIPES = [("floor", "sigmoid"), ("floor_half", "sigmoid"), ("sigmoid", "one"),
            ("sigmoid", "zero"), ("floor", "one"), ("floor_half", "zero")]
 
@@ -80,8 +92,7 @@ def _cu(x):
 def test_edge_against_oracle(oracle_mod, monkeypatch, variant, recipe):
     dev = _dev()
     name, lens, H, dt, packed, entry, env = variant
-    if env:
-        monkeypatch.setenv(env, "1")
+    _setenv(monkeypatch, env)
     x = _inputs(lens, H, dt, packed, recipe[0], recipe[1], seed=len(lens) * 7 + H)
     print(f"edge {name} g={recipe[0]} beta={recipe[1]} lens={lens} H={H} {dt}", flush=True)
     xd = x.to(dev)
@@ -104,8 +115,7 @@ def test_unit_key_beta_one_reads_back_v(monkeypatch, variant, gate):
     are unit length to bf16 rounding, so the bar is the dtype's."""
     dev = _dev()
     name, lens, H, dt, packed, entry, env = variant
-    if env:
-        monkeypatch.setenv(env, "1")
+    _setenv(monkeypatch, env)
     x = _inputs(lens, H, dt, packed, gate, "one", seed=11 + H)
     x.q = x.k.clone()
     xd = x.to(dev)
@@ -125,8 +135,7 @@ def test_beta_zero_is_pure_decay(monkeypatch, variant, gate):
     in numpy, no oracle)."""
     dev = _dev()
     name, lens, H, dt, packed, entry, env = variant
-    if env:
-        monkeypatch.setenv(env, "1")
+    _setenv(monkeypatch, env)
     x = _inputs(lens, H, dt, packed, gate, "zero", seed=13 + H)
     xd = x.to(dev)
     o, hT = _run(entry, xd)
