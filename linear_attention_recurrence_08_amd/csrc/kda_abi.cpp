@@ -216,8 +216,7 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, c
         e = c64_chunks >= 0 ? kda::launch_prefill_c64_mfma(a, workspace, c64_chunks, s)
                             : kda::launch_prefill_c64(a, s);
     else if (dtype == KDA_BF16 && dk == 128 && dv == 128 && !force_general())
-        e = kda::prefill_pc_applicable(a, s) ? kda::launch_prefill_pc(a, s)
-                                             : kda::launch_prefill_mfma(a, s);
+        e = kda::launch_prefill_mfma(a, s);
     else
         e = kda::launch_prefill_general(a, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

@@ -96,10 +96,6 @@ struct FrontArgs {
 // Each launcher returns hipSuccess or the launch error.
 hipError_t launch_prefill_general(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);   // bf16, dk = dv = 128
-// bf16, dk = dv = 128, at most 128 (sequence, head) pairs: a producer and a consumer workgroup
-// per pair joined through a ring in L2 (opt-in with KDA_PC=1; never under stream capture)
-bool prefill_pc_applicable(const PrefillArgs& a, hipStream_t s);
-hipError_t launch_prefill_pc(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_c64(const PrefillArgs& a, hipStream_t s);    // 64-token chunks
 hipError_t launch_split_finish(const PrefillArgs& a, hipStream_t s);   // after a split prefill
 hipError_t launch_decode_d128(const DecodeArgs& a, hipStream_t s);     // dk = dv = 128

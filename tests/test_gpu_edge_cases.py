@@ -13,8 +13,7 @@ per-channel decay (same section).  Besides the oracle comparison, two closed for
 the GPU outputs directly: with beta = 1 and q = k every output reads back its own value, and with
 beta = 0 every output is q_t^T Diag(exp(sum of g up to t)) h0.
 
-Variants: the producer/consumer kernel (opt-in, up to 128 (sequence, head) pairs; its ring in L2,
-and with every ring access at system scope), the 64-column matrix-core kernel with stage A's and with stage
+Variants: the 64-column matrix-core kernel with stage A's and with stage
 B's issue priority, the 128-column one (256 or more pairs), the float32 general kernel (bf16
 forced onto it, and float32 inputs), chunk 64 on the matrix cores and in float32, and the
 token-range split.
@@ -42,9 +41,6 @@ def err(x, ref):
 
 # (name, seq_lens, H, dtype, packed, entry, env: {name: value})
 VARIANTS = [
-    ("producer_consumer", [96, 37], 2, "bf16", True, "chunk16", {"KDA_PC": "1"}),
-    ("producer_consumer_coherent", [150, 37, 16], 3, "bf16", True, "chunk16",
-     {"KDA_PC": "1", "KDA_PC_COHERENT": "1"}),
     ("mfma64_stageB_prio", [96, 37], 2, "bf16", True, "chunk16", None),
     ("mfma64_stageA_prio", [80], 64, "bf16", False, "chunk16", None),
     ("mfma128", [40, 37, 16, 50], 64, "bf16", True, "chunk16", None),

@@ -152,16 +152,12 @@ def test_general_path_matches_fast_path_bf16(oracle_mod, monkeypatch):
 # ------------------------------------------------------------------------------------------------
 # full-size workloads
 # ------------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("kernel", ["producer_consumer", "one_workgroup_64col"])
-def test_prefill_T4096_H96(oracle_mod, monkeypatch, kernel):
-    """The benchmark workload, every head, on the 64-column one-workgroup kernel (the default) and
-    on the opt-in producer/consumer kernel."""
+def test_prefill_T4096_H96(oracle_mod):
+    """The benchmark workload, every head."""
     dev = _dev()
     from linear_attention_recurrence_08_amd import inputs
-    if kernel == "producer_consumer":
-        monkeypatch.setenv("KDA_PC", "1")
     x = inputs.make_workload("prefill_T4096_H96_d128_bf16")
-    check_prefill(oracle_mod, x, dev, heads=None, label=f"prefill_T4096_H96[{kernel}]")
+    check_prefill(oracle_mod, x, dev, heads=None, label="prefill_T4096_H96")
 
 
 @pytest.mark.timeout(900)
