@@ -100,7 +100,8 @@ def kernel_source_digest(kernel_tag: str) -> str:
     srcs = (src,) if isinstance(src, str) else src
     h = hashlib.sha256()
     for path in tuple(os.path.join(pkg, "csrc", f) for f in srcs) + (
-            os.path.join(pkg, "csrc", "kda_internal.h"), os.path.join(pkg, "build.py")):
+            os.path.join(pkg, "csrc", "kda_internal.h"), os.path.join(pkg, "csrc", "kda_mfma.h"),
+            os.path.join(pkg, "build.py")):
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -205,24 +206,28 @@ def _algorithmic_bytes(workload):
         w["dk"] * w["dv"] * 4
 
 
-def summarize(dirs, command):
+def summarize(dirs, command, workload=None):
     """profiles/<kernel>_<workload>_kernel_trace.md from a --kernel-trace --stats run and
     profiles/<kernel>_<workload>_hbm_traffic.md from FETCH_SIZE + WRITE_SIZE counter runs (each
     scaled by what the same counter reads for the 1 GiB calibration copy).  Where one entry point
-    launches several kernels, the summary lists each and adds them up per call."""
+    launches several kernels, the summary lists each and adds them up per call.  With `workload`,
+    the runs timed kda_chunk_fwd alone on that prefill workload (bench.py --workload NAME)."""
     import csv
     import glob
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
+    kernels = SUMMARY_KERNELS
+    if workload is not None:
+        kernels = {"kda_prefill_mfma_kernel": ("kda_chunk_fwd_" + workload, workload)}
     tags = {}
-    for frag, (tag, wl) in SUMMARY_KERNELS.items():
+    for frag, (tag, wl) in kernels.items():
         tags.setdefault(tag, (wl, []))[1].append(frag)
     trace = {}        # tag -> list of (fragment, stats row)
     counters = {}     # (fragment or "copy", counter) -> list of per-dispatch values (KiB)
     for d in dirs:
         for f in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
-                for frag, (tag, _) in SUMMARY_KERNELS.items():
+                for frag, (tag, _) in kernels.items():
                     if frag in r["Name"]:
                         trace.setdefault(tag, []).append((frag, r))
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
@@ -231,7 +236,7 @@ def summarize(dirs, command):
                 key = None
                 if "elementwise" in name or "vectorized" in name:
                     key = "copy"
-                for frag in SUMMARY_KERNELS:
+                for frag in kernels:
                     if frag in name:
                         key = frag
                 if key is None:
@@ -463,12 +468,15 @@ def main():
                     help="write profiles/*.md from rocprofv3 output directories: a kernel-trace "
                          "--stats run and/or FETCH_SIZE and WRITE_SIZE counter runs")
     ap.add_argument("--command", default="", help="command line recorded in the summaries")
+    ap.add_argument("--summary-workload", default=None, metavar="NAME",
+                    help="with --summarize: the runs timed kda_chunk_fwd alone on this prefill "
+                         "workload (bench.py --workload NAME)")
     args = ap.parse_args()
     if args.summarize_split:
         summarize_split(args.summarize_split, args.command)
         return
     if args.summarize:
-        summarize(args.summarize, args.command)
+        summarize(args.summarize, args.command, args.summary_workload)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
