@@ -82,8 +82,8 @@ enum {
  * kda_chunk_fwd -- prefill: run the recurrence over whole sequences and return every output and
  * the final state.  Computed chunkwise, in parallel inside 16-token tiles and recurrently across
  * tiles ("Kimi K3's hybrid block, from first principles", section "From linear attention to the
- * delta rule": KDA runs in parallel inside a chunk and recurrently across chunks; the cumulative
- * log-decay over a 16-token tile stays within (-80, 0)).  The chunked result equals the token
+ * delta rule": the tokens of a chunk are processed together and a state is passed from chunk to
+ * chunk; with the -5 floor the summed log-decay of a 16-token tile lies in (-80, 0)).  The chunked result equals the token
  * loop up to floating-point rounding ("Kimi K3", section "Forgetting different features at
  * different rates").  Tiles restart at every sequence start; a sequence's last tile may be
  * partial.
@@ -269,8 +269,9 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g, 
 /*
  * kda_output_gate -- the output stage after the mixer: every (token, head) row of dv outputs is
  * RMS-normalised and multiplied by a sigmoid gate of the token ("Kimi K3's hybrid block, from first
- * principles", section "From linear attention to the delta rule": the layer's output is
- * RMSNorm'd per head and multiplied by a full-rank sigmoid gate before the output projection):
+ * principles", section "From linear attention to the delta rule": each head's output row is
+ * normalised by its root mean square and scaled, ahead of the output projection, by a sigmoid gate
+ * computed from the token at full rank):
  *
  *     y[t,h,:] = o[t,h,:] / sqrt(mean_c o[t,h,c]^2 + eps) * weight * sigmoid(gate[t,h,:])
  *
@@ -303,10 +304,10 @@ int kda_decode_step_gated(const void* q, const void* k, const void* v, const voi
 /*
  * kda_frontend -- the input stage before the mixer: turns the projected pre-activations of every
  * token into q, k, v, g and beta for kda_chunk_fwd / kda_decode_step ("Kimi K3's hybrid block,
- * from first principles", section "From linear attention to the delta rule": queries and keys
- * pass through a short convolution of width 4, Swish and L2 normalisation; values through the
- * convolution and Swish; beta is a sigmoid of a projection of the token; the log-decay is bounded
- * below by g_min with one learned scale A_h per head).  Per token t, head h, channel c:
+ * from first principles", section "From linear attention to the delta rule": q and k get a
+ * four-tap causal convolution, the Swish activation and unit-length normalisation, v the
+ * convolution and Swish only; beta comes from a sigmoid over a projection of the token; the
+ * log-decay has the floor g_min and one learned scale A_h per head).  Per token t, head h, channel c:
  *
  *     conv(x)[t,c] = sum_{i<4} w[c,i] x[t-3+i,c]     causal and depthwise; at a sequence start the
  *                                                   three earlier inputs come from conv_in (zeros

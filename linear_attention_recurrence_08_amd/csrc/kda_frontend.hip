@@ -1,10 +1,10 @@
 // KDA input stage: turns the projected pre-activations of a token into the recurrence's inputs.
 //
 // "Kimi K3's hybrid block, from first principles", section "From linear attention to the delta
-// rule": queries and keys pass through a short convolution of width 4, Swish and L2 normalisation;
-// values through the convolution and Swish; beta is a sigmoid of a projection of the token; the
-// decay logit is a low-rank projection plus a per-channel bias, and the log-decay is bounded below
-// by g_min with one learned scale A_h per head.  Per (token t, head h, channel c):
+// rule": q and k get a four-tap causal convolution, the Swish activation and unit-length
+// normalisation, v the convolution and Swish only; beta comes from a sigmoid over a projection of
+// the token; the decay logit is a low-rank projection with a bias per channel, and the log-decay
+// has the floor g_min and one learned scale A_h per head.  Per (token t, head h, channel c):
 //     conv(x)[t,c] = sum_{i<4} w[c,i] x[t-3+i, c]      (causal, depthwise, restarts per sequence
 //                                                      from the saved last three inputs or zeros)
 //     q = l2(swish(conv(x_q))),  k = l2(swish(conv(x_k))),  v = swish(conv(x_v)),

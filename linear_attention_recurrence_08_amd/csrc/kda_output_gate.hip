@@ -1,4 +1,5 @@
-// KDA output stage: per-head RMSNorm of the mixer output times a full-rank sigmoid gate.
+// KDA output stage: the mixer output, normalised per head by its root mean square, times a sigmoid
+// gate of full width.
 //
 // "Kimi K3's hybrid block, from first principles", section "From linear attention to the delta
 // rule": the layer's output is RMS-normalised per head and multiplied by a sigmoid gate of the

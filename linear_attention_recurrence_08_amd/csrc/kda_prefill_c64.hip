@@ -2,9 +2,9 @@
 // chunk, the intra-chunk coupling runs as separate diagonal and off-diagonal sub-tile products.
 //
 // "Kimi K3's hybrid block, from first principles", section "From linear attention to the delta
-// rule": KDA trains chunkwise, parallel inside a chunk and recurrent across chunks, and the
-// cumulative log-decay over a 16-token tile stays within (-80, 0) so every tile, the diagonal
-// ones included, runs as dense products; "What's new in Kimi K3", section "KDA in one page": the
+// rule": KDA is trained chunk by chunk, the tokens of a chunk together and the state passed
+// between chunks, and the summed log-decay of a 16-token tile lies in (-80, 0), so every tile,
+// the diagonal ones included, runs as dense products; "What's new in Kimi K3", section "KDA in one page": the
 // per-token cost is quoted for chunks of 64.  Over 64 tokens the cumulative decay reaches -320,
 // beyond float32's range, so every exponent below is kept within one sub-tile or is <= 0:
 //

@@ -3,8 +3,8 @@
 //
 // Method ("What's new in Kimi K3", section "KDA in one page": the per-token cost is quoted for
 // chunks of 64, length-independent; "Kimi K3's hybrid block, from first principles", section "From
-// linear attention to the delta rule": parallel inside a chunk, recurrent across chunks, and the
-// cumulative log-decay over 16 tokens stays within (-80, 0)).  For a chunk of L = 64 tokens with
+// linear attention to the delta rule": the tokens of a chunk are handled together and the state
+// passes from chunk to chunk; the summed log-decay of 16 tokens lies in (-80, 0)).  For a chunk of L = 64 tokens with
 // entering state S and Gam_t the inclusive per-channel cumsum of g from the chunk start:
 //     Kg = K.e^{Gam},  Qg = Q.e^{Gam},  Kl = K.e^{Gam_L - Gam}            (every factor <= 1)
 //     A = strict_lower(A_ij = sum_c k_ic k_jc e^{Gam_ic - Gam_jc}),  P = lower(same with q_i)

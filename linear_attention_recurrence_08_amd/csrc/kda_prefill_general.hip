@@ -3,8 +3,8 @@
 // other than 128, and the in-place decode of those sizes (one-token sequences).
 //
 // The chunked algorithm ("Kimi K3's hybrid block, from first principles", section "From linear
-// attention to the delta rule": parallel inside a chunk, recurrent across chunks, cumulative
-// log-decay over 16-token tiles).  For a tile of C = 16 tokens entering with state S (dk x dv)
+// attention to the delta rule": the tokens of a chunk together, the state passed between chunks,
+// the cumulative log-decay taken over 16-token tiles).  For a tile of C = 16 tokens entering with state S (dk x dv)
 // and Gam_i = sum_{j<=i} g_j (inclusive, per key channel, restarted at every tile):
 //     A_ij = sum_c k_ic k_jc e^{Gam_ic - Gam_jc}  (j < i)     P_ij = sum_c q_ic k_jc e^{...} (j <= i)
 //     (I + Diag(beta) A) U = Diag(beta) (V - (K.e^Gam) S)        solved by forward substitution

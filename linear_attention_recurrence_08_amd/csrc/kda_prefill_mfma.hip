@@ -1,9 +1,9 @@
 // KDA chunkwise prefill on the CDNA4 matrix cores: bf16 inputs, dk = dv = 128, float32 state.
 //
 // Method ("Kimi K3's hybrid block, from first principles", section "From linear attention to the
-// delta rule": parallel inside a chunk, recurrent across chunks; the cumulative log-decay over a
-// 16-token tile stays within (-80, 0) so the rescaling factors stay finite and every tile runs as
-// dense matrix products).  Per 16-token tile with entering state S (dk x dv), write
+// delta rule": the tokens of a chunk together, the state passed between chunks; the summed
+// log-decay of a 16-token tile lies in (-80, 0), so the rescaling factors stay finite and every
+// tile runs as dense matrix products).  Per 16-token tile with entering state S (dk x dv), write
 //     Gp_i = Gam_i - Gam_C = -sum_{j>i} g_j >= 0        (log-decay to the tile end, per channel)
 //     E = e^{Gp} >= 1,  D = e^{-Gp} <= 1,  eC = e^{Gam_C}  (per channel)
 //     Kp = K.E,  Qp = Q.E,  Kd = K.D,  St = Diag(eC) S       (St: the state decayed to the tile end)

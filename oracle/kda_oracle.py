@@ -153,8 +153,8 @@ def decode_step(q, k, v, g, beta, S, nthreads: Optional[int] = None):
 
 # ---------------------------------------------------------------------------------------------
 # Independent chunkwise form.  Follows "Kimi K3's hybrid block, from first principles", section
-# "From linear attention to the delta rule" (KDA runs in parallel inside a chunk and recurrently
-# across chunks; the cumulative log-decay is taken over a 16-token tile) and "Kimi K3", section
+# "From linear attention to the delta rule" (the tokens of a chunk are handled together and a state
+# is passed from chunk to chunk; the cumulative log-decay is taken over a 16-token tile) and "Kimi K3", section
 # "Forgetting different features at different rates" (the chunked algorithm gives the same
 # result as the token loop).
 #
@@ -348,11 +348,11 @@ def output_gate(o, gate, weight=None, eps: float = 1e-6):
 
 # ---------------------------------------------------------------------------------------------
 # Input stage.  "Kimi K3's hybrid block, from first principles", section "From linear attention to
-# the delta rule": queries and keys pass through a short convolution of width 4, Swish and L2
-# normalisation; values through the convolution and Swish; beta_t is a sigmoid of a projection of
-# the token; the decay logit z_t is a low-rank projection plus a per-channel bias, and the
-# log-decay is bounded below by g_min = -5 with one learned scale A_h per head (every factor then
-# lies between e^-5 and 1).  Readings where the pages are silent or garbled:
+# the delta rule": q and k get a four-tap causal convolution, the Swish activation and unit-length
+# normalisation, v the convolution and Swish only; beta_t comes from a sigmoid over a projection
+# of the token; the decay logit z_t is a low-rank projection with a bias per channel, and the
+# log-decay has the floor g_min = -5 and one learned scale A_h per head (so every retention
+# factor lies between e^-5 and 1).  Readings where the pages are silent or garbled:
 #   * the convolution is causal and depthwise along tokens, y[t,c] = sum_{i<4} w[c,i] x[t-3+i,c]
 #     (w[c,3] weighs the current token), without bias, restarting at every sequence start from a
 #     saved state of the last three inputs (zeros when none is given);
