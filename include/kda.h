@@ -50,6 +50,7 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus

@@ -1,0 +1,74 @@
+"""CPU sanitizer builds of the host code (no GPU).
+
+* The float64 oracle (oracle/kda_oracle.c) under AddressSanitizer + UndefinedBehaviorSanitizer,
+  and under ThreadSanitizer for its worker threads, driven by tests/sanitize/oracle_driver.c.
+* The C ABI's argument validation (csrc/kda_abi.cpp, compiled for the host only) under
+  AddressSanitizer + UndefinedBehaviorSanitizer, with stand-in launchers, driven by
+  tests/sanitize/abi_driver.cpp: every rejected call returns its status before anything runs, and
+  the validation mode (KDA_VALIDATE=1) reads exactly the host bytes it is given.
+
+Each build fails the test on any sanitizer report (-fno-sanitize-recover) or unmet expectation.
+The ABI's source goes through clang in HIP host-only mode, with the sanitizer flags applied to the
+host pass only.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HERE = os.path.join(ROOT, "tests", "sanitize")
+CLANG = "/opt/rocm/llvm/bin/clang++"
+
+
+def _run(cmd, env=None, timeout=240):
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout, env=env)
+    assert r.returncode == 0, f"{' '.join(cmd)}\nstdout:\n{r.stdout}\nstderr:\n{r.stderr[-4000:]}"
+    return r
+
+
+def _env(**extra):
+    env = dict(os.environ)
+    env.pop("KDA_VALIDATE", None)
+    env.pop("KDA_FORCE_GENERAL", None)
+    env.update(extra)
+    return env
+
+
+@pytest.fixture(scope="module")
+def outdir(tmp_path_factory):
+    return str(tmp_path_factory.mktemp("sanitize"))
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not found")
+@pytest.mark.parametrize("kind", ["address,undefined", "thread"])
+def test_oracle_under_sanitizer(outdir, kind):
+    exe = os.path.join(outdir, f"oracle_{kind.replace(',', '_')}")
+    _run(["gcc", "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer", f"-fsanitize={kind}",
+          "-fno-sanitize-recover=all", os.path.join(ROOT, "oracle", "kda_oracle.c"),
+          os.path.join(HERE, "oracle_driver.c"), "-lm", "-lpthread", "-o", exe])
+    opts = {"ASAN_OPTIONS": "detect_leaks=1:abort_on_error=0",
+            "UBSAN_OPTIONS": "print_stacktrace=1:halt_on_error=1",
+            "TSAN_OPTIONS": "halt_on_error=1"}
+    r = _run([exe], env=_env(**opts))
+    assert "all expectations hold" in r.stdout
+
+
+@pytest.mark.skipif(not os.path.exists(CLANG), reason="ROCm clang++ not found")
+def test_abi_validation_under_sanitizer(outdir):
+    exe = os.path.join(outdir, "abi_driver")
+    csrc = os.path.join(ROOT, "linear_attention_recurrence_08_amd", "csrc")
+    flags = ["-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all",
+             "-I", os.path.join(ROOT, "include"), "-I", csrc]
+    objs = []
+    for src in (os.path.join(csrc, "kda_abi.cpp"), os.path.join(HERE, "abi_driver.cpp")):
+        obj = os.path.join(outdir, os.path.basename(src) + ".o")
+        _run([CLANG, "-x", "hip", "--cuda-host-only", *flags, "-c", src, "-o", obj])
+        objs.append(obj)
+    _run([CLANG, "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+          *objs, "-o", exe])
+    r = _run([exe], env=_env(ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="halt_on_error=1"))
+    assert "all expectations hold" in r.stdout
