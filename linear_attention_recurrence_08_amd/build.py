@@ -54,23 +54,26 @@ def _run(cmd, verbose):
         raise RuntimeError("hipcc failed: " + " ".join(cmd))
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, host_flags=()) -> str:
+    """Compile and link the library to `out`.  host_flags are extra options for the host pass of
+    every compile and for the link (a variant build, e.g. the CPU sanitizer checks; each option
+    is given as "-Xarch_host", option)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     with tempfile.TemporaryDirectory(prefix="kda_build_") as objdir:
         jobs = []
         for src in sources():
             name = os.path.basename(src)
             obj = os.path.join(objdir, name + ".o")
-            jobs.append(([hipcc] + hipcc_flags() + PER_SOURCE.get(name, []) +
+            jobs.append(([hipcc] + hipcc_flags() + PER_SOURCE.get(name, []) + list(host_flags) +
                          ["-c", src, "-o", obj], obj))
         workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
         with concurrent.futures.ThreadPoolExecutor(workers) as pool:
             list(pool.map(lambda j: _run(j[0], verbose), jobs))
-        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + [o for _, o in jobs] +
-             ["-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + list(host_flags) +
+             [o for _, o in jobs] + ["-o", tmp], verbose)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

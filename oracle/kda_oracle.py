@@ -72,9 +72,13 @@ def load_library(path: str):
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=True)
-        _lib = load_library(_LIB)
+        variant = os.environ.get("KDA_ORACLE_LIB")   # a test-built variant (sanitizer runs)
+        if variant:
+            _lib = load_library(variant)
+        else:
+            if not os.path.exists(_LIB):
+                build(force=True)
+            _lib = load_library(_LIB)
     return _lib
 
 

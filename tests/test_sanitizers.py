@@ -1,19 +1,23 @@
 """CPU sanitizer builds of the host code (no GPU).
 
 * The float64 oracle (oracle/kda_oracle.c) under AddressSanitizer + UndefinedBehaviorSanitizer,
-  and under ThreadSanitizer for its worker threads, driven by tests/sanitize/oracle_driver.c.
+  and under ThreadSanitizer for its worker threads, driven by tests/sanitize/oracle_driver.c; and
+  every pin of tests/test_oracle_pins.py run on an ASan + UBSan build of the oracle library.
 * The C ABI's argument validation (csrc/kda_abi.cpp, compiled for the host only) under
   AddressSanitizer + UndefinedBehaviorSanitizer, with stand-in launchers, driven by
   tests/sanitize/abi_driver.cpp: every rejected call returns its status before anything runs, and
-  the validation mode (KDA_VALIDATE=1) reads exactly the host bytes it is given.
+  the validation mode (KDA_VALIDATE=1) reads exactly the host bytes it is given; and every case of
+  tests/test_abi_cpu.py run on the whole library built with the sanitizers on its host pass.
 
 Each build fails the test on any sanitizer report (-fno-sanitize-recover) or unmet expectation.
-The ABI's source goes through clang in HIP host-only mode, with the sanitizer flags applied to the
-host pass only.
+HIP sources go through clang / hipcc with the sanitizer options applied to the host pass only
+(-Xarch_host); the libraries are loaded into Python with the sanitizer runtime preloaded.
 """
+import glob
 import os
 import shutil
 import subprocess
+import sys
 
 import pytest
 
@@ -23,7 +27,7 @@ CLANG = "/opt/rocm/llvm/bin/clang++"
 
 
 def _run(cmd, env=None, timeout=240):
-    r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout, env=env)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout, env=env, cwd=ROOT)
     assert r.returncode == 0, f"{' '.join(cmd)}\nstdout:\n{r.stdout}\nstderr:\n{r.stderr[-4000:]}"
     return r
 
@@ -72,3 +76,43 @@ def test_abi_validation_under_sanitizer(outdir):
           *objs, "-o", exe])
     r = _run([exe], env=_env(ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="halt_on_error=1"))
     assert "all expectations hold" in r.stdout
+
+
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-g"]
+
+
+def _pytest_in_subprocess(env, *args):
+    return _run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                 "-m", "not gpu", *args], env=env, timeout=600)
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not found")
+def test_oracle_pins_on_sanitized_oracle(outdir):
+    lib = os.path.join(outdir, "liboracle_kda_san.so")
+    _run(["gcc", "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer",
+          "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fPIC", "-shared",
+          "-pthread", os.path.join(ROOT, "oracle", "kda_oracle.c"), "-o", lib, "-lm"])
+    runtime = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True,
+                             text=True).stdout.strip()
+    env = _env(LD_PRELOAD=runtime, ASAN_OPTIONS="detect_leaks=0", KDA_ORACLE_LIB=lib)
+    r = _pytest_in_subprocess(env, "tests/test_oracle_pins.py")
+    assert " passed" in r.stdout and " failed" not in r.stdout
+
+
+@pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc"), reason="hipcc not found")
+def test_abi_cases_on_sanitized_library(outdir):
+    from linear_attention_recurrence_08_amd import build
+    lib = build.build(out=os.path.join(outdir, "libkda_san.so"), host_flags=HOST_SANITIZE)
+    runtimes = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+    assert runtimes, "clang's AddressSanitizer runtime not found"
+    env = _env(LD_PRELOAD=runtimes[0], ASAN_OPTIONS="detect_leaks=0",
+               KDA_SANITIZED_LIB=lib)
+    # the binding opens the sanitized build instead of libkda.so
+    script = ("import os, sys; sys.path[:0] = [os.getcwd(), os.path.join(os.getcwd(), 'tests')]; "
+              "from linear_attention_recurrence_08_amd import kda; "
+              "kda.LIB_PATH = os.environ['KDA_SANITIZED_LIB']; import pytest; "
+              "sys.exit(pytest.main(['-q', '-x', '-p', 'no:cacheprovider', '-m', 'not gpu', "
+              "'tests/test_abi_cpu.py']))")
+    r = _run([sys.executable, "-c", script], env=env, timeout=600)
+    assert " passed" in r.stdout and " failed" not in r.stdout
