@@ -410,6 +410,75 @@ def head_share(dev, stream, steps, warmup, unsplit=True):
     }
 
 
+SQ_PASS1 = ("SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
+            "SQ_INSTS_SALU SQ_INSTS_VMEM")
+SQ_PASS2 = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT "
+            "SQ_INSTS_VALU_TRANS_F32 SQ_WAIT_INST_LDS SQ_BUSY_CU_CYCLES SQ_ACTIVE_INST_ANY")
+
+
+def summarize_sq(dirs, command):
+    """profiles/kda_chunk_fwd_prefill_T4096_H96_d128_bf16_sq_counters.md from two rocprofv3 --pmc
+    runs of --traffic-pass (the SQ_PASS1 and SQ_PASS2 counter sets).  The prefill kernel runs one
+    workgroup of 12 waves per (sequence, head, 64-column half) on a CU of its own (one per
+    (sequence, head) from 256 pairs up), each SIMD holding one wave of each of the three roles,
+    and walks nsteps + 4 pipeline periods (nsteps = the tile count rounded up to even); counts are
+    given per SIMD and period."""
+    import csv
+    import glob
+    from linear_attention_recurrence_08_amd import inputs
+    wl = "prefill_T4096_H96_d128_bf16"
+    w = inputs.WORKLOADS[wl]
+    pairs = len(w["seq_lens"]) * w["H"]
+    wgs = pairs if pairs >= 256 else 2 * pairs
+    ntiles = (max(w["seq_lens"]) + 15) // 16
+    periods = ntiles + (ntiles & 1) + 4
+    simds, waves = 4 * wgs, 12 * wgs
+    vals = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if "kda_prefill_mfma_kernel" in r["Kernel_Name"]:
+                    vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    m = {k: sum(v) / len(v) for k, v in vals.items()}
+    ndisp = len(vals.get("SQ_WAVES", []))
+    assert round(m["SQ_WAVES"]) == waves, (m["SQ_WAVES"], waves)
+
+    def per(k, x4=False):
+        return m[k] * (4 if x4 else 1) / simds / periods
+    rows = [(k, m[k], f"{per(k):.1f}") for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+                                                  "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS",
+                                                  "SQ_INSTS_SALU", "SQ_INSTS_VMEM")]
+    for k in ("SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+              "SQ_WAIT_INST_LDS"):
+        rows.append((k + " (x4)", m[k], f"{per(k, True):.0f} cycles"))
+    rows.append(("SQ_VALU_MFMA_BUSY_CYCLES", m["SQ_VALU_MFMA_BUSY_CYCLES"],
+                 f"{per('SQ_VALU_MFMA_BUSY_CYCLES'):.0f} cycles"))
+    rows.append(("SQ_LDS_BANK_CONFLICT", m["SQ_LDS_BANK_CONFLICT"],
+                 f"{m['SQ_LDS_BANK_CONFLICT'] / wgs / periods:.0f} cycles per CU"))
+    wave_cyc = m["SQ_WAVE_CYCLES"] * 4 / waves
+    rows.append(("SQ_WAVE_CYCLES (x4)", m["SQ_WAVE_CYCLES"],
+                 f"{wave_cyc:.0f} cycles per wave in all"))
+    period = wave_cyc / periods
+    other = (m["SQ_INSTS_VALU"] - m["SQ_INSTS_MFMA"]) / simds / periods
+    active = per("SQ_ACTIVE_INST_ANY", True) / period
+    busy = per("SQ_VALU_MFMA_BUSY_CYCLES") / period
+    path = os.path.join(ROOT, "profiles", f"kda_chunk_fwd_{wl}_sq_counters.md")
+    with open(path, "w") as fo:
+        fo.write(f"# kda_prefill_mfma_kernel on {wl}: SQ instruction counters\n\n")
+        fo.write(f"command: `{command}`\n\n")
+        fo.write(f"Means over the {ndisp} dispatches of the traffic pass; {waves} waves = {wgs} "
+                 f"workgroups of 12 waves, {simds} SIMDs, {periods} pipeline periods per "
+                 "workgroup. Cycle counters marked (x4) count in units of four cycles.\n\n")
+        fo.write("| counter | per launch | per SIMD and period |\n|---|---|---|\n")
+        for k, v, dsc in rows:
+            fo.write(f"| {k} | {v:.4g} | {dsc} |\n")
+        fo.write(f"\nDerived: VALU instructions other than MFMA {other:.0f} per SIMD and period; a "
+                 f"period of {period:.0f} cycles; instruction issue active {100 * active:.0f}% of "
+                 f"a SIMD's cycles; MFMA unit busy {100 * busy:.0f}%.\n\n")
+        fo.write(f"source_digest: {kernel_source_digest('kda_chunk_fwd')}\n")
+    print("wrote", path)
+
+
 def summarize_split(trace_dir, command):
     """profiles/kda_chunk_fwd_split_T4096_H12_d128_bf16_kernel_trace.md from a --kernel-trace
     --stats run of `bench.py --head-share-only` (every kernel of that run: the unsplit prefill, and
@@ -468,12 +537,18 @@ def main():
                     help="write profiles/*.md from rocprofv3 output directories: a kernel-trace "
                          "--stats run and/or FETCH_SIZE and WRITE_SIZE counter runs")
     ap.add_argument("--command", default="", help="command line recorded in the summaries")
+    ap.add_argument("--summarize-sq", nargs=2, metavar="DIR",
+                    help="write the prefill kernel's SQ counter summary from two rocprofv3 --pmc "
+                         "runs of --traffic-pass (counter sets SQ_PASS1 and SQ_PASS2)")
     ap.add_argument("--summary-workload", default=None, metavar="NAME",
                     help="with --summarize: the runs timed kda_chunk_fwd alone on this prefill "
                          "workload (bench.py --workload NAME)")
     args = ap.parse_args()
     if args.summarize_split:
         summarize_split(args.summarize_split, args.command)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq, args.command)
         return
     if args.summarize:
         summarize(args.summarize, args.command, args.summary_workload)
