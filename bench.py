@@ -315,10 +315,22 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def time_launches(fn, steps, warmup, stream):
+SETTLE_S = 0.3   # untimed launches continue after the warm-up steps until this much wall time
+
+
+def time_launches(fn, steps, warmup, stream, settle_s=None):
+    """Mean time per launch of `steps` launches of fn on `stream` (HIP events), after `warmup`
+    untimed launches; the untimed launches continue until settle_s seconds have passed, so that
+    the timed ones run at the clocks the GPU holds under sustained load."""
     import torch
-    for _ in range(warmup):
+    settle_s = SETTLE_S if settle_s is None else settle_s
+    t0 = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t0 < settle_s:
         fn()
+        done += 1
+        if done % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -669,8 +681,8 @@ def main():
 
         c64ms, _ = time_launches(prefill_c64, max(5, args.steps // 2), 2, stream)
         fsteps = max(3, args.steps // 10)
-        f64ms, _ = time_launches(forced_float32(prefill_c64), fsteps, 1, stream)
-        f16ms, _ = time_launches(forced_float32(prefill_c16), fsteps, 1, stream)
+        f64ms, _ = time_launches(forced_float32(prefill_c64), fsteps, 1, stream, settle_s=0)
+        f16ms, _ = time_launches(forced_float32(prefill_c16), fsteps, 1, stream, settle_s=0)
         # the workspace round trip: every (chunk, head) record written once and read back
         ws_traffic = 2 * ws_bytes
         result["chunk64"] = {
