@@ -84,9 +84,9 @@ enum {
  * the final state.  Computed chunkwise, in parallel inside 16-token tiles and recurrently across
  * tiles ("Kimi K3's hybrid block, from first principles", section "From linear attention to the
  * delta rule": the tokens of a chunk are processed together and a state is passed from chunk to
- * chunk; with the -5 floor the summed log-decay of a 16-token tile lies in (-80, 0)).  The chunked result equals the token
- * loop up to floating-point rounding ("Kimi K3", section "Forgetting different features at
- * different rates").  Tiles restart at every sequence start; a sequence's last tile may be
+ * chunk; with the -5 floor the summed log-decay of a 16-token tile lies in (-80, 0)).  The
+ * chunked result equals the token loop up to floating-point rounding ("Kimi K3", section
+ * "Forgetting different features at different rates").  Tiles restart at every sequence start; a sequence's last tile may be
  * partial.
  *
  *   q, k, g   [Ttot, H, dk]  dtype    device      inputs (g = log alpha, natural log)
@@ -108,6 +108,39 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
                   const float* h0, const int32_t* cu_seqlens, int num_seqs,
                   void* o, float* hT,
                   int B, int T, int H, int dk, int dv, int dtype, void* stream);
+
+/*
+ * kda_chunk_fwd_gated -- kda_chunk_fwd followed by the output stage of kda_output_gate on its
+ * outputs: y[t,h,:] = o[t,h,:] / sqrt(mean_c o[t,h,c]^2 + eps) * weight * sigmoid(gate[t,h,:])
+ * ("Kimi K3's hybrid block, from first principles", section "From linear attention to the delta
+ * rule": each head's output row is normalised by its root mean square and scaled by a sigmoid
+ * gate of the token before the output projection).  For bf16 with dk = dv = 128 and at least
+ * 256 (sequence, head) pairs (kda_chunk_fwd_gated_fuses) the stage runs inside the prefill
+ * kernel, on each tile's outputs while they are still on chip: o is then written only if asked
+ * for, and never read back.  Otherwise the prefill writes o (into y when o is NULL) and the
+ * output stage runs after it.  The norm is taken over o as rounded to dtype, as kda_output_gate
+ * would read it.
+ *
+ *   arguments as kda_chunk_fwd, plus
+ *   gate      [Ttot, H, dv]  dtype    device      the gate's pre-activation per output element
+ *   weight    [dv]           float32  device      the norm's gain per value channel; NULL = ones
+ *   eps       >= 0 (KDA_ERR_RANGE otherwise)
+ *   o         [Ttot, H, dv]  dtype    device      the mixer output (written); NULL = not wanted
+ *   y         [Ttot, H, dv]  dtype    device      the gated output (written)
+ * gate, y and o (when given) must be 16-byte aligned (KDA_ERR_ALIGN); y may alias o or gate.
+ * Returns KDA_OK or a negative status; nothing is written on an argument error.
+ */
+int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void* g,
+                        const void* beta, const float* h0, const int32_t* cu_seqlens,
+                        int num_seqs, const void* gate, const float* weight, float eps, void* o,
+                        void* y, float* hT, int B, int T, int H, int dk, int dv, int dtype,
+                        void* stream);
+
+/*
+ * kda_chunk_fwd_gated_fuses -- 1 when kda_chunk_fwd_gated runs the output stage inside the
+ * prefill kernel for these arguments (varlen != 0: N = num_seqs, else N = B), else 0.
+ */
+int kda_chunk_fwd_gated_fuses(int num_seqs, int B, int H, int dk, int dv, int dtype, int varlen);
 
 /*
  * kda_chunk_fwd_chunk64 -- kda_chunk_fwd computed with 64-token chunks made of four 16-token

@@ -127,18 +127,33 @@ size_t split_workspace_bytes(const SplitPlan& sp, int64_t N, int64_t Ttot, int H
     return split_om_bytes(Ttot, H) + static_cast<size_t>(sp.P) * 2 * N * H * 128 * 128 * 4;
 }
 
+// The output stage after a prefill, y = RMSNorm(o) * weight * sigmoid(gate) per (token, head).
+struct GateSpec {
+    const void* gate;
+    const float* weight;
+    float eps;
+    void* y;
+};
+
+// The fused output stage runs inside the one-workgroup-per-head prefill kernel.
+bool gate_fuses(int64_t N, int H, int dk, int dv, int dtype) {
+    return dtype == KDA_BF16 && dk == 128 && dv == 128 && !force_general() && N * H >= 256;
+}
+
 // Prefill with optional snapshots (snap_stride 0: none); chunk64 selects the 64-token-chunk
-// kernel (no snapshots); split (P > 1) the token-range split of the matrix-core kernel.
+// kernel (no snapshots); split (P > 1) the token-range split of the matrix-core kernel; gs the
+// output stage (no snapshots, chunk64 or split; o may then be NULL).
 int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* beta,
                    const float* h0, const int32_t* cu_seqlens, int num_seqs, void* o, float* hT,
                    float* snaps, const int32_t* snap_offsets, int snap_stride, int B, int T,
                    int H, int dk, int dv, int dtype, void* stream, bool chunk64 = false,
                    void* workspace = nullptr, size_t workspace_bytes = 0,
-                   const SplitPlan* split = nullptr) {
+                   const SplitPlan* split = nullptr, const GateSpec* gs = nullptr) {
     if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
     if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERR_SHAPE;
     if (!supported_dim(dk) || !supported_dim(dv)) return KDA_ERR_UNSUPPORTED;
     if (!rows_ok(H, dk, dv)) return KDA_ERR_SHAPE;
+    if (gs && (!(gs->eps >= 0.f) || !std::isfinite(gs->eps))) return KDA_ERR_RANGE;
     if (snap_stride < 0 || snap_stride % 16 != 0) return KDA_ERR_STRIDE;
     const bool want_snaps = snap_stride > 0;
     int64_t N, Ttot;
@@ -151,7 +166,11 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, c
         N = B;
         Ttot = static_cast<int64_t>(B) * T;
     }
-    if (Ttot > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
+    if (Ttot > 0 && (!q || !k || !v || !g || !beta || (!o && !gs))) return KDA_ERR_NULL;
+    if (gs && Ttot > 0 && (!gs->gate || !gs->y)) return KDA_ERR_NULL;
+    if (gs && Ttot > 0 &&
+        (!aligned(gs->gate, 16) || !aligned(gs->y, 16) || (o && !aligned(o, 16))))
+        return KDA_ERR_ALIGN;
     // with equal lengths, snapshots exist iff T >= stride; with cu_seqlens the offsets say so
     if (want_snaps && !snaps && !cu_seqlens && N > 0 && T >= snap_stride) return KDA_ERR_NULL;
     if (N == 0 || (Ttot == 0 && !hT)) return KDA_OK;
@@ -192,9 +211,17 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, c
         if (st) return st;
     }
 
+    // the output stage: inside the prefill kernel, or after it on the outputs (written into y
+    // when the caller wants no o, so that the stage then runs in place)
+    const bool fused = gs && gate_fuses(N, H, dk, dv, dtype);
+    if (gs && !fused && !o) o = gs->y;
+
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.h0 = h0; a.cu = cu_seqlens; a.o = o; a.hT = hT;
+    if (fused) {
+        a.gate = gs->gate; a.weight = gs->weight; a.eps = gs->eps; a.y = gs->y;
+    }
     a.N = N; a.T = cu_seqlens ? 0 : T; a.H = H; a.dk = dk; a.dv = dv; a.dtype = dtype;
     if (want_snaps && snaps) {
         a.snaps = snaps;
@@ -219,6 +246,12 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, c
         e = kda::launch_prefill_mfma(a, s);
     else
         e = kda::launch_prefill_general(a, s);
+    if (e == hipSuccess && gs && !fused && Ttot > 0) {
+        kda::GateArgs ga;
+        ga.o = o; ga.gate = gs->gate; ga.weight = gs->weight; ga.eps = gs->eps; ga.y = gs->y;
+        ga.rows = Ttot * H; ga.dv = dv; ga.dtype = dtype;
+        e = kda::launch_output_gate(ga, s);
+    }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -257,6 +290,22 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
                   int B, int T, int H, int dk, int dv, int dtype, void* stream) {
     return chunk_fwd_impl(q, k, v, g, beta, h0, cu_seqlens, num_seqs, o, hT, nullptr, nullptr, 0,
                           B, T, H, dk, dv, dtype, stream);
+}
+
+int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void* g,
+                        const void* beta, const float* h0, const int32_t* cu_seqlens,
+                        int num_seqs, const void* gate, const float* weight, float eps, void* o,
+                        void* y, float* hT, int B, int T, int H, int dk, int dv, int dtype,
+                        void* stream) {
+    const GateSpec gs{gate, weight, eps, y};
+    return chunk_fwd_impl(q, k, v, g, beta, h0, cu_seqlens, num_seqs, o, hT, nullptr, nullptr, 0,
+                          B, T, H, dk, dv, dtype, stream, false, nullptr, 0, nullptr, &gs);
+}
+
+int kda_chunk_fwd_gated_fuses(int num_seqs, int B, int H, int dk, int dv, int dtype,
+                              int varlen) {
+    if (B < 0 || num_seqs < 0 || H <= 0) return 0;
+    return gate_fuses(varlen ? num_seqs : B, H, dk, dv, dtype) ? 1 : 0;
 }
 
 int kda_chunk_fwd_chunk64(const void* q, const void* k, const void* v, const void* g,

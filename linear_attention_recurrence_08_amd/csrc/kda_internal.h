@@ -37,6 +37,13 @@ struct PrefillArgs {
     int64_t seg_len = 0;
     void* oM = nullptr;             // [Ttot, H, dk] bf16
     float* seg_states = nullptr;    // [split, 2, N * H, dk, dv]
+    // fused output stage (gate != nullptr; bf16, dk = dv = 128, the one-workgroup-per-head
+    // kernel): y = RMSNorm(o) * weight * sigmoid(gate) per (token, head) row; o may then be
+    // nullptr (not written)
+    const void* gate = nullptr;          // [Ttot, H, dv]
+    const float* weight = nullptr;       // [dv] or nullptr (ones)
+    float eps = 0.f;
+    void* y = nullptr;                   // [Ttot, H, dv]
 };
 
 struct DecodeArgs {

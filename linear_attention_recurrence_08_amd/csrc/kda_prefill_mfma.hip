@@ -53,6 +53,8 @@
 #include "kda_internal.h"
 #include "kda_mfma.h"
 
+#include <type_traits>
+
 namespace kda {
 namespace {
 
@@ -92,6 +94,7 @@ __device__ __forceinline__ void map_workgroup(int64_t b, int64_t pairs, int nsli
 struct Raw {
     uint2 q0, q1, k0, k1, g0, g1, v[2];
     uint32_t b;   // raw bf16 bits of beta in the low half
+    uint2 gz[2];  // fused output stage: the gate of tile - 3 at the columns of v
 };
 
 // Stage-to-stage buffers, grouped by hand-off so that one dynamic base address reaches every
@@ -128,11 +131,31 @@ struct Shared {
     float ec[8][D];            // e^{Gam_C} (stage A -> stage S, tile % 8)
 };
 
+// The fused output stage (GATED, one workgroup per head).  y = o / sqrt(mean(o^2) + eps) * w *
+// sigmoid(gate) per (token, head) row ("Kimi K3's hybrid block, from first principles", section
+// "From linear attention to the delta rule": each head's output row is normalised by its root
+// mean square and scaled by a sigmoid gate of the token before the output projection).  Stage A
+// loads the gate of tile j - 3 with the inputs of tile j and, in period j, leaves w * sigmoid(gate)
+// (bf16) for the stage-S wave and lane that hold those columns of o; stage S finishes tile j - 3
+// in period j + 1.  The row's sum of squares spans the four stage-S waves: each adds its 32
+// columns, leaves the sum in ssq, and waits until all four have arrived for this tile (an LDS
+// counter; the waves run the same tiles in the same period, so the wait only covers their skew).
+struct GateLds {
+    uint4 gw[2][4][64];     // by tile % 2, stage-S wave, lane: bf16 w * sigmoid(gate) of token ln,
+                            // columns 16 s + 4 lg + r (.xy) and 64 + 16 s + 4 lg + r (.zw)
+    float ssq[C][4];        // per token of the tile: the stage-S waves' sums of o^2
+    float w[D];             // the gain per column (ones without one)
+    uint32_t arrive;        // stage-S arrivals: 4 per tile
+};
+constexpr int kArriveSpin = 1 << 22;   // bound on the polls of one arrival wait
+
 // PRIO_ROLE: the role whose waves win issue ties on their SIMD (1: stage A, 2: stage B).
-template <int PRIO_ROLE, int BVT>
+template <int PRIO_ROLE, int BVT, bool GATED>
 __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     constexpr int NS = BVT / 64;       // 16-column strips per stage-S wave
+    static_assert(!GATED || NS == 2, "the fused output stage needs a whole head per workgroup");
     __shared__ Shared<NS> sh;
+    __shared__ typename std::conditional<GATED, GateLds, char>::type gsh;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -189,6 +212,13 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     const bf16_t* __restrict__ g = static_cast<const bf16_t*>(a.g);
     const bf16_t* __restrict__ beta = static_cast<const bf16_t*>(a.beta);
     bf16_t* __restrict__ o = static_cast<bf16_t*>(part_m ? a.oM : a.o);
+    const bf16_t* __restrict__ gate = static_cast<const bf16_t*>(a.gate);
+    bf16_t* __restrict__ y = static_cast<bf16_t*>(a.y);
+    if constexpr (GATED) {
+        // read before the first barrier of every role; the first use comes three periods later
+        if (tid < D) gsh.w[tid] = a.weight ? a.weight[tid] : 1.f;
+        if (tid == 0) gsh.arrive = 0u;
+    }
 
     // ---- constant fragments ----
     bf16x8 sel[2];   // selector: channel-major transpose of 32-channel-group half hh (B, K = 32)
@@ -307,6 +337,18 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
         for (int m = 0; m < NS; ++m) R.v[m] = ld8(rv, vo_v + 128 * m);
         R.b = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, vo_b, 0, 0);
+        if constexpr (GATED) {
+            // the gate of tile ld_tile - 3, at the columns of v (zeros before the first tile
+            // and past the sequence end)
+            const int gt = ld_tile - 3;
+            const int nvg = gt < 0 ? 0 : min(max(len32 - gt * C, 0), C);
+            const int nrecg = max((nvg - 1) * rb32 + D * 2, 0);
+            const int64_t tg0 = bos + min((int64_t)max(gt, 0) * C, len);
+            const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(gate + (tg0 * H + h) * D), (short)0, nrecg, kBufferFlags);
+#pragma unroll
+            for (int m = 0; m < NS; ++m) R.gz[m] = ld8(rz, vo_v + 128 * m);
+        }
         ++ld_tile;
     };
 
@@ -357,6 +399,27 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         A.kd[s][lane] = cat8(Kdb[0], Kdb[1]);
 #pragma unroll
         for (int m = 0; m < NS; ++m) A.vraw[s + 4 * m][lane] = R.v[m];
+    };
+
+    // fused output stage, stage A's part: w * sigmoid(gate) of tile tg (whose gate R holds) for
+    // the stage-S wave and lane that hold those columns, into the buffer of tile tg % 2
+    auto gate_step = [&](int64_t tg, const Raw& R) {
+        if constexpr (GATED) {
+            if (tg < 0) return;
+            uint32_t pk[4];
+#pragma unroll
+            for (int m = 0; m < NS; ++m) {
+                const f32x4 z = unpack4(R.gz[m]);
+                const f32x4 w = *reinterpret_cast<const f32x4*>(&gsh.w[64 * m + 16 * s + 4 * lg]);
+                f32x4 gw;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    gw[r] = w[r] * __builtin_amdgcn_rcpf(1.f + __expf(-z[r]));
+                pk[2 * m] = pk2(gw[0], gw[1]);
+                pk[2 * m + 1] = pk2(gw[2], gw[3]);
+            }
+            gsh.gw[(uint32_t)tg & 1u][s][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        }
     };
 
     // stage B1 for tile `tile`: A, A^T, P^T over all 128 channels and the inverse T, in two
@@ -510,12 +573,64 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             for (int m = 0; m < NS; ++m) S[m][mb] = mma16(kdf, Ub[m], S[m][mb]);
         }
     };
+    // with the fused output stage o is optional; y's lane offset within a tile's token rows
+    const bool want_o = !GATED || o != nullptr;
+    const uint32_t vo_y = (uint32_t)((ln * H + h) * D + vcol0) * 2u;
     auto store_o = [&](int64_t tile, const bf16x4 (&Ot)[NS], bool masked) {
         const int64_t t0 = bos + tile * C;
         bf16_t* dst = o + ((t0 + ln) * H + h) * D + vcol0;
-        if (!masked || t0 + ln < eos) {
+        if (want_o && (!masked || t0 + ln < eos)) {
 #pragma unroll
             for (int m = 0; m < NS; ++m) *reinterpret_cast<uint2*>(dst + 64 * m) = as_u2(Ot[m]);
+        }
+    };
+    // fused output stage, stage S's part for tile `tile`: the row norm over the four stage-S
+    // waves, then y from o (as rounded to bf16, as stored) and stage A's w * sigmoid(gate)
+    auto y_step = [&](int64_t tile, const bf16x4 (&Ot)[NS], bool masked) {
+        if constexpr (GATED) {
+            float ss = 0.f;
+#pragma unroll
+            for (int m = 0; m < NS; ++m) {
+                const f32x4 of = unpack4(as_u2(Ot[m]));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ss += of[r] * of[r];
+            }
+            // the four lane groups hold the same token (columns 4 lg .. 4 lg + 3 of each strip)
+            ss += __shfl_xor(ss, 16);
+            ss += __shfl_xor(ss, 32);
+            if (lg == 0) gsh.ssq[ln][s] = ss;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the sum is in LDS
+            if (lane == 0)
+                __hip_atomic_fetch_add(&gsh.arrive, 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            const uint32_t want = 4u * (uint32_t)(tile + 1);
+            for (int it = 0; it < kArriveSpin; ++it) {
+                if (__hip_atomic_load(&gsh.arrive, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_WORKGROUP) >= want)
+                    break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            asm volatile("" ::: "memory");   // the sums are read after the arrivals are seen
+            const f32x4 sq = *reinterpret_cast<const f32x4*>(&gsh.ssq[ln][0]);
+            const float rn = __builtin_amdgcn_rsqf((sq[0] + sq[1] + sq[2] + sq[3]) / (float)D +
+                                                   a.eps);
+            const uint4 gwv = gsh.gw[(uint32_t)tile & 1u][s][lane];
+            const uint2 gwm[2] = {make_uint2(gwv.x, gwv.y), make_uint2(gwv.z, gwv.w)};
+            // stored through a buffer resource at the tile's first token row: a scalar base, the
+            // lane offset computed once, and a record count that drops tokens past the end
+            const int64_t t0 = bos + tile * C;
+            const int nv = masked ? (int)min(max(eos - t0, (int64_t)0), (int64_t)C) : C;
+            const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(y + t0 * H * D), (short)0, nv * rb32, kBufferFlags);
+#pragma unroll
+            for (int m = 0; m < NS; ++m) {
+                const f32x4 gw = unpack4(gwm[m]), of = unpack4(as_u2(Ot[m]));
+                f32x4 yv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) yv[r] = of[r] * rn * gw[r];
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, as_u2(bf4(yv))),
+                                                      ry, vo_y + 128u * m, 0, 0);
+            }
         }
     };
 
@@ -539,14 +654,19 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         stage_a(1, R1);
         load_tile(R1);     // tile 3
         lds_barrier();
+        // (with the fused output stage, the gate of tile j - 3 rides with tile j's inputs and is
+        // turned into w * sigmoid(gate) in period j, one period before stage S finishes tile j - 3)
         for (int64_t i = 0; i < nsteps; i += 2) {
             stage_a(i + 2, R0);
+            gate_step(i - 1, R0);
             load_tile(R0);     // tile i + 4
             lds_barrier();
             stage_a(i + 3, R1);
+            gate_step(i, R1);
             load_tile(R1);     // tile i + 5
             lds_barrier();
         }
+        gate_step(nsteps - 1, R0);
         lds_barrier();
         lds_barrier();
     } else if (role == 2) {
@@ -593,7 +713,8 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         for (; i < nfull; ++i) {
             stage_s(i, Ot);
             store_o(i, Ot, false);
-            if (i + 1 == snap_at) {
+            y_step(i, Ot, false);
+            if (!GATED && i + 1 == snap_at) {
                 state_out(a.snaps + (snap_idx * H + h) * (int64_t)(D * D));
                 ++snap_idx;
                 snap_at += a.snap_tiles;
@@ -604,6 +725,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         for (; i < nsteps; ++i) {
             stage_s(i, Ot);
             store_o(i, Ot, true);
+            y_step(i, Ot, true);
             if constexpr (kPre) if (i + 1 < nsteps) decay(i + 1);
             lds_barrier();
         }
@@ -617,18 +739,24 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s) {
     // with a token-range split every (sequence, head) pair runs 2 split - 1 units
     const int64_t pairs = a.N * a.H * (a.split > 1 ? 2 * a.split - 1 : 1);
     if (pairs <= 0) return hipSuccess;
-    if (pairs >= 256) {
+    if (a.gate) {
+        // the fused output stage needs a whole head per workgroup (the caller checks pairs >= 256
+        // and no split or snapshots)
+        if (pairs < 256 || a.split > 1 || a.snaps) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((kda_prefill_mfma_kernel<1, 128, true>), dim3((unsigned)pairs),
+                           dim3(NT), 0, s, a);
+    } else if (pairs >= 256) {
         // every CU is busy with one workgroup per (sequence, head): a workgroup takes all 128
         // columns, so stages A and B1 run once per head instead of once per 64-column half
-        hipLaunchKernelGGL((kda_prefill_mfma_kernel<1, 128>), dim3((unsigned)pairs), dim3(NT), 0,
-                           s, a);
+        hipLaunchKernelGGL((kda_prefill_mfma_kernel<1, 128, false>), dim3((unsigned)pairs),
+                           dim3(NT), 0, s, a);
     } else if (2 * pairs >= 128 && a.split <= 1) {
         // at least half of the 256 CUs hold a workgroup; a split's launch keeps stage B's priority
         // instead (measured 3-5% faster at 12 and 24 heads, 4,096 and 32,768 tokens)
-        hipLaunchKernelGGL((kda_prefill_mfma_kernel<1, 64>), dim3((unsigned)(2 * pairs)),
+        hipLaunchKernelGGL((kda_prefill_mfma_kernel<1, 64, false>), dim3((unsigned)(2 * pairs)),
                            dim3(NT), 0, s, a);
     } else {
-        hipLaunchKernelGGL((kda_prefill_mfma_kernel<2, 64>), dim3((unsigned)(2 * pairs)),
+        hipLaunchKernelGGL((kda_prefill_mfma_kernel<2, 64, false>), dim3((unsigned)(2 * pairs)),
                            dim3(NT), 0, s, a);
     }
     return hipGetLastError();

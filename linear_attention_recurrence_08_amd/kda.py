@@ -83,6 +83,11 @@ def load_library():
         lib.kda_decode_step.restype = i32
         f32 = ctypes.c_float
         lib.kda_output_gate.argtypes = [vp, vp, vp, f32, vp, i32, i32, i32, i32, vp]
+        lib.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, f32, vp, vp,
+                                            vp, i32, i32, i32, i32, i32, i32, vp]
+        lib.kda_chunk_fwd_gated.restype = i32
+        lib.kda_chunk_fwd_gated_fuses.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        lib.kda_chunk_fwd_gated_fuses.restype = i32
         lib.kda_output_gate.restype = i32
         lib.kda_decode_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, i32,
                                               i32, i32, i32, i32, vp]
@@ -129,8 +134,9 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, output_final_state, o, hT):
-    """Shape/device checks shared by the prefill entry points; allocates o and hT if needed."""
+def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, output_final_state, o, hT, want_o=True):
+    """Shape/device checks shared by the prefill entry points; allocates o (when wanted) and hT
+    if needed."""
     dev = q.device
     dt = q.dtype
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
@@ -161,7 +167,8 @@ def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, output_final_state, o, hT):
         if h0.shape != (N, H, dk, dv):
             raise ValueError(f"h0 must be [{N}, {H}, {dk}, {dv}]")
     if o is None:
-        o = torch.empty((*lead, H, dv), dtype=dt, device=dev)
+        if want_o:
+            o = torch.empty((*lead, H, dv), dtype=dt, device=dev)
     else:
         # the kernels write every (token, head) row of o: a smaller buffer would be overrun
         _check(o, "o", dev, dt)
@@ -194,6 +201,49 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd")
     return o, hT
+
+
+def kda_chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                        beta: torch.Tensor, gate: torch.Tensor,
+                        weight: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                        h0: Optional[torch.Tensor] = None,
+                        cu_seqlens: Optional[torch.Tensor] = None,
+                        output_final_state: bool = True, want_o: bool = False,
+                        o: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                        hT: Optional[torch.Tensor] = None
+                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Chunkwise KDA prefill followed by the output stage y = RMSNorm(o) * weight * sigmoid(gate)
+    (inside the prefill kernel for bf16 128 x 128 heads with at least 256 (sequence, head) pairs).
+    gate has o's shape; weight [dv] float32 or None.  Returns (y, o, hT): o is None unless want_o
+    is set or o is passed; hT is None when output_final_state is False."""
+    dev, B, T, H, dk, dv, N, o, hT = _prefill_args(q, k, v, g, beta, h0, cu_seqlens,
+                                                   output_final_state, o, hT,
+                                                   want_o=want_o)
+    lead = tuple(v.shape[:-2])
+    _check(gate, "gate", dev, q.dtype)
+    if tuple(gate.shape) != (*lead, H, dv):
+        raise ValueError(f"gate must be {[*lead, H, dv]}, got {list(gate.shape)}")
+    weight = _gate_weight(weight, dv, dev)
+    if y is None:
+        y = torch.empty((*lead, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _check(y, "y", dev, q.dtype)
+        if tuple(y.shape) != (*lead, H, dv):
+            raise ValueError(f"y must be {[*lead, H, dv]}, got {list(y.shape)}")
+    st = load_library().kda_chunk_fwd_gated(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens), N,
+        _ptr(gate), _ptr(weight), float(eps), _ptr(o), _ptr(y), _ptr(hT), B, T, H, dk, dv,
+        _dtype_code(q), _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd_gated")
+    return y, o, hT
+
+
+def kda_chunk_fwd_gated_fuses(q: torch.Tensor, num_seqs: int, B: int, H: int, dk: int, dv: int,
+                              varlen: bool) -> bool:
+    """Whether kda_chunk_fwd_gated runs the output stage inside the prefill kernel."""
+    return bool(load_library().kda_chunk_fwd_gated_fuses(num_seqs, B, H, dk, dv, _dtype_code(q),
+                                                         1 if varlen else 0))
 
 
 def kda_chunk_fwd_chunk64_workspace_bytes(q: torch.Tensor, cu_seqlens: Optional[torch.Tensor],

@@ -346,6 +346,39 @@ void test_decode_and_stages() {
     EXPECT(og(1e-6f, o.data(), -1) == KDA_ERR_SHAPE);
 }
 
+void test_gated_prefill() {
+    // fused: bf16, 128 x 128 heads, N * H >= 256 pairs -> one launch carrying the gate
+    auto run = [&](Prefill& p, void* gate, void* y, bool with_o, float eps) {
+        reset();
+        return kda_chunk_fwd_gated(p.q.data(), p.k.data(), p.v.data(), p.g.data(), p.beta.data(),
+                                   p.h0.data(), p.cup(), p.nseq(), gate, nullptr, eps,
+                                   with_o ? p.o.data() : nullptr, y, p.hT.data(), p.B, p.T, p.H,
+                                   p.dk, p.dv, p.dtype, nullptr);
+    };
+    {
+        Prefill p(2, 32, 128, 128, 128, KDA_BF16);
+        std::vector<unsigned char> gate(p.o.size()), y(p.o.size());
+        EXPECT(kda_chunk_fwd_gated_fuses(0, 2, 128, 128, 128, KDA_BF16, 0) == 1);
+        EXPECT(run(p, gate.data(), y.data(), false, 1e-6f) == KDA_OK);
+        EXPECT(g_launches == 1 && std::strcmp(g_last, "mfma") == 0);
+        EXPECT(g_prefill.gate == gate.data() && g_prefill.y == y.data() && g_prefill.o == nullptr);
+        EXPECT(run(p, gate.data(), y.data(), false, -1.f) == KDA_ERR_RANGE && g_launches == 0);
+        EXPECT(run(p, nullptr, y.data(), false, 1e-6f) == KDA_ERR_NULL && g_launches == 0);
+        EXPECT(run(p, gate.data() + 2, y.data(), false, 1e-6f) == KDA_ERR_ALIGN &&
+               g_launches == 0);
+    }
+    {
+        // unfused (too few pairs): the prefill writes o into y, then the output stage in place
+        Prefill p(1, 40, 2, 128, 128, KDA_BF16);
+        std::vector<unsigned char> gate(p.o.size()), y(p.o.size());
+        EXPECT(kda_chunk_fwd_gated_fuses(0, 1, 2, 128, 128, KDA_BF16, 0) == 0);
+        EXPECT(run(p, gate.data(), y.data(), false, 1e-6f) == KDA_OK);
+        EXPECT(g_launches == 2 && std::strcmp(g_last, "output_gate") == 0);
+        EXPECT(g_prefill.o == y.data() && g_prefill.gate == nullptr);
+        EXPECT(run(p, gate.data(), y.data(), true, 1e-6f) == KDA_OK && g_prefill.o == p.o.data());
+    }
+}
+
 void test_frontend() {
     const int T = 20, H = 2, d = 64;
     std::vector<float> xq(T * H * d + 4), xk(T * H * d + 4), xv(T * H * d + 4), xz(T * H * d + 4),
@@ -383,6 +416,7 @@ int main() {
     test_snapshots_args();
     test_workspaces();
     test_decode_and_stages();
+    test_gated_prefill();
     test_frontend();
     if (g_failures) {
         std::fprintf(stderr, "%d expectation(s) failed\n", g_failures);

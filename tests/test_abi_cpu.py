@@ -30,6 +30,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert _declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_chunk64",
                                      "kda_chunk_fwd_chunk64_workspace_bytes",
+                                     "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_fuses",
                                      "kda_chunk_fwd_snapshots", "kda_chunk_fwd_split",
                                      "kda_chunk_fwd_split_noalloc",
                                      "kda_chunk_fwd_split_segments",
@@ -395,3 +396,36 @@ def test_binding_rejects_small_snapshot_buffers(host_binding):
     with pytest.raises(ValueError):
         kda.kda_chunk_fwd_snapshots(xp, xp, xp, xp, _bf(torch, 80, 2), 16, cu_seqlens=cu,
                                     snap_offsets=offs, snaps=torch.zeros(4, 2, 128, 128))
+
+
+def _gated(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=None, cu=None, num_seqs=0, gate=FAKE,
+             weight=None, eps=1e-6, o=None, y=FAKE, hT=FAKE, B=1, T=16, H=2, dk=128, dv=128,
+             dtype=0)
+    a.update(kw)
+    return lib.kda_chunk_fwd_gated(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"],
+                                   a["num_seqs"], a["gate"], a["weight"], ctypes.c_float(a["eps"]),
+                                   a["o"], a["y"], a["hT"], a["B"], a["T"], a["H"], a["dk"],
+                                   a["dv"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -3), (dict(H=0), -2), (dict(dk=120), -4),
+    (dict(eps=-1.0), -6), (dict(eps=float("nan")), -6), (dict(eps=float("inf")), -6),
+    (dict(q=None), -1), (dict(gate=None), -1), (dict(y=None), -1),
+    (dict(gate=ctypes.c_void_p(0x1008)), -9), (dict(y=ctypes.c_void_p(0x1004)), -9),
+    (dict(o=ctypes.c_void_p(0x1002)), -9),
+    (dict(cu=FAKE, B=2, num_seqs=3), -5),
+])
+def test_gated_prefill_argument_errors(lib, kw, code):
+    assert _gated(lib, **kw) == code
+
+
+def test_gated_prefill_fuses_query(lib):
+    # the output stage runs inside the prefill kernel for bf16 128 x 128 heads and >= 256 pairs
+    assert lib.kda_chunk_fwd_gated_fuses(0, 2, 128, 128, 128, 0, 0) == 1
+    assert lib.kda_chunk_fwd_gated_fuses(0, 1, 255, 128, 128, 0, 0) == 0
+    assert lib.kda_chunk_fwd_gated_fuses(16, 1, 96, 128, 128, 0, 1) == 1
+    assert lib.kda_chunk_fwd_gated_fuses(0, 2, 128, 128, 128, 1, 0) == 0    # float32
+    assert lib.kda_chunk_fwd_gated_fuses(0, 2, 128, 64, 128, 0, 0) == 0     # dk = 64
+    assert lib.kda_chunk_fwd_gated_fuses(0, -1, 128, 128, 128, 0, 0) == 0
