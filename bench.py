@@ -739,6 +739,43 @@ def main():
                          "frac": round(vbytes / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "algorithmic_bytes_per_launch": vbytes},
         }
+        # the prefill with the output stage (kda_chunk_fwd_gated, fused for these 1,536 pairs)
+        # against the prefill followed by the output-stage kernel
+        if not args.no_output_gate:
+            from linear_attention_recurrence_08_amd import (kda_chunk_fwd_gated,
+                                                            kda_chunk_fwd_gated_fuses)
+            _, zv, wv = inputs.make_output_gate_inputs(xv.total_tokens, xv.H, xv.dv, "bf16", 61)
+            zv, wv = zv.to(dev).reshape(vviews[2].shape), wv.to(dev)
+            yv = torch.empty_like(ov)
+
+            def gated_varlen():
+                kda_chunk_fwd_gated(*vviews, zv, weight=wv, h0=xvd.h0, cu_seqlens=xvd.cu_seqlens,
+                                    y=yv, hT=hTv)
+
+            def unfused_varlen():
+                prefill_varlen()
+                kda_output_gate(ov, zv, wv, y=yv)
+
+            gvms, _ = time_launches(gated_varlen, vsteps, 1, stream)
+            uvms, _ = time_launches(unfused_varlen, vsteps, 1, stream)
+            row = xv.total_tokens * xv.H * xv.dv * 2          # one [Ttot, H, dv] bf16 tensor
+            gbytes = vbytes + row                              # + gate read; y written in o's place
+            result["varlen"]["gated"] = {
+                "entry": "kda_chunk_fwd_gated",
+                "fused": kda_chunk_fwd_gated_fuses(xvd.q, xv.num_seqs, 1, xv.H, xv.dk, xv.dv,
+                                                   True),
+                "ms_per_step": round(gvms, 4),
+                "value": round(xv.total_tokens / (gvms * 1e-3), 1), "unit": "tokens/s",
+                "unfused_ms_per_step": round(uvms, 4), "vs_unfused": round(uvms / gvms, 3),
+                "algorithmic_bytes_per_launch": gbytes,
+                "unfused_algorithmic_bytes": vbytes + 3 * row,
+                "hbm_bytes_removed": 2 * row,
+                "roofline": {"bound": "hbm",
+                             "achieved": round(gbytes / (gvms * 1e-3) / 1e9, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(gbytes / (gvms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            }
+            del zv, wv, yv
         del xv, xvd, vviews, ov, hTv
         torch.cuda.empty_cache()
 
