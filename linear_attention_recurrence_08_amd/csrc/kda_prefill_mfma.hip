@@ -20,9 +20,9 @@
 // when the (sequence, head) pairs alone fill the chip, one workgroup owns a whole head (a
 // 128-column slice: each stage-S wave carries two strips, and stages A and B1 run once per head).
 // The two slices of a head are dispatched to the same XCD so their shared q/k/g reads meet in
-// that XCD's L2, and in a variable-length batch of up to 64 sequences the longest sequences are
-// dispatched first (the short ones fill the tail).  With a token-range split (small batches; the
-// completion kernels are in kda_prefill_split.hip) a workgroup runs one segment of a sequence:
+// that XCD's L2, and in a variable-length batch (up to 65,536 sequences) the longest sequences
+// are dispatched first (the short ones fill the tail).  With a token-range split (small batches;
+// the completion kernels are in kda_prefill_split.hip) a workgroup runs one segment of a sequence:
 // segment 0 from h0, or a later segment from a zero state (its part B) or from the identity with
 // v = 0 (its part M), and leaves the segment's final state for the composition.  Each wave keeps
 // one role for the whole sequence, and the work of a tile runs as a software pipeline with a
@@ -63,7 +63,7 @@ using namespace mfma;
 constexpr int C = 16;      // tile tokens
 constexpr int D = 128;     // dk = dv
 constexpr int NT = 768;    // threads per workgroup (12 waves: 4 per stage)
-constexpr int kLptMaxSeqs = 64;   // varlen batches up to this many sequences run longest first
+constexpr int kLptMaxSeqs = 65536;   // varlen batches up to this many sequences run longest first
 
 // (workgroup index) -> (pair index p = n * H + head, slice) with both slices of a pair on one XCD
 // (workgroups are dealt to the 8 XCDs round-robin by index); one slice per pair: p = b.
@@ -84,6 +84,123 @@ __device__ __forceinline__ void map_workgroup(int64_t b, int64_t pairs, int nsli
         slice = (int)(t % 2);
         p = (pairs / 8) * 8 + t / 2;
     }
+}
+
+// The sequence of rank r (0 <= r < N <= 65536) in the order of decreasing length, ties by
+// increasing index, for the whole workgroup: a radix select over the unique 48-bit keys
+// (length << 16) | (0xFFFF - index), eight bits per pass from the highest digit in which the keys
+// differ; batches whose lengths lie within a sixteenth of the shortest keep index order.  Each pass counts the keys that still match the digits chosen so far into 256 bins
+// (LDS), and one wave picks the bin that holds the rank.  scratch: 264 + NT / 16 words of LDS,
+// free until the barrier at the end.
+constexpr int kSelectHeld = 4;     // keys a thread keeps in registers (N <= 4 NT: one load)
+__device__ __forceinline__ uint64_t length_key(const int32_t* cu, int i) {
+    return ((uint64_t)(uint32_t)(cu[i + 1] - cu[i]) << 16) | (uint64_t)(0xFFFF - i);
+}
+__device__ int select_by_length(const int32_t* cu, int N, int r, int tid, uint32_t* scratch) {
+    uint32_t* hist = scratch;
+    uint32_t* sel = scratch + 256;    // the chosen bin, and the keys counted above it
+    uint64_t prefix = 0, mask = 0;
+    uint32_t rem = (uint32_t)r;       // the rank among the keys that match the prefix
+    const bool held = N <= kSelectHeld * NT;
+    uint64_t kh[kSelectHeld];
+    uint64_t kmin = ~uint64_t{0}, kmax = 0;
+#pragma unroll
+    for (int c = 0; c < kSelectHeld; ++c) {
+        const int i = tid + c * NT;
+        kh[c] = (held && i < N) ? length_key(cu, i) : 0;
+        if (held && i < N) {
+            kmin = min(kmin, kh[c]);
+            kmax = max(kmax, kh[c]);
+        }
+    }
+    if (!held) {
+        for (int i = tid; i < N; i += NT) {
+            const uint64_t key = length_key(cu, i);
+            kmin = min(kmin, key);
+            kmax = max(kmax, key);
+        }
+    }
+    // the digits above the highest one in which the smallest and largest keys differ are common
+    // to all keys: the passes start there (equal lengths leave only the index digits, which
+    // spread over the bins instead of piling onto one)
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        kmin = min(kmin, (uint64_t)__shfl_xor((unsigned long long)kmin, d));
+        kmax = max(kmax, (uint64_t)__shfl_xor((unsigned long long)kmax, d));
+    }
+    uint64_t* wmm = reinterpret_cast<uint64_t*>(scratch + 264);   // [NT / 64][2]
+    if ((tid & 63) == 0) {
+        wmm[2 * (tid >> 6)] = kmin;
+        wmm[2 * (tid >> 6) + 1] = kmax;
+    }
+    __syncthreads();
+    for (int w = 0; w < NT / 64; ++w) {
+        kmin = min(kmin, wmm[2 * w]);
+        kmax = max(kmax, wmm[2 * w + 1]);
+    }
+    // lengths within a sixteenth of the shortest: little to gain from reordering, so the batch
+    // keeps index order (the order the ranks already are in when all lengths are equal)
+    const uint64_t lmin = kmin >> 16, lmax = kmax >> 16;
+    if (lmax - lmin <= lmin / 16) {
+        __syncthreads();   // every thread has read wmm before the scratch is reused
+        return r;
+    }
+    const uint64_t diff = kmin ^ kmax;    // nonzero: N >= 2 distinct keys
+    const int top = (63 - __builtin_clzll(diff)) & ~7;
+    mask = ~((uint64_t{1} << (top + 8)) - 1);
+    prefix = kmax & mask;
+    for (int shift = top; shift >= 0; shift -= 8) {
+        for (int b = tid; b < 256; b += NT) hist[b] = 0u;
+        __syncthreads();
+        if (held) {
+#pragma unroll
+            for (int c = 0; c < kSelectHeld; ++c)
+                if (tid + c * NT < N && (kh[c] & mask) == prefix)
+                    atomicAdd(&hist[(kh[c] >> shift) & 255u], 1u);
+        } else {
+            for (int i = tid; i < N; i += NT) {
+                const uint64_t key = length_key(cu, i);
+                if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            }
+        }
+        __syncthreads();
+        if (tid < 64) {
+            // lane j holds bins 255 - 4 j .. 252 - 4 j (the largest digits first)
+            uint32_t c[4], tot = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                c[e] = hist[255 - 4 * tid - e];
+                tot += c[e];
+            }
+            uint32_t incl = tot;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t u = __shfl_up(incl, d);
+                if (tid >= d) incl += u;
+            }
+            const uint32_t excl = incl - tot;
+            if (excl <= rem && rem < incl) {   // exactly one lane
+                uint32_t before = excl;
+                int bin = 255 - 4 * tid;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (rem < before + c[e]) {
+                        bin = 255 - 4 * tid - e;
+                        break;
+                    }
+                    before += c[e];
+                }
+                sel[0] = (uint32_t)bin;
+                sel[1] = before;
+            }
+        }
+        __syncthreads();
+        prefix |= (uint64_t)sel[0] << shift;
+        mask |= (uint64_t)0xFF << shift;
+        rem -= sel[1];
+    }
+    __syncthreads();   // every thread has read sel before the scratch is reused
+    return 0xFFFF - (int)(prefix & 0xFFFFu);
 }
 
 // Raw inputs of one tile for one stage-A lane: token ln, key channels 32s + 16hh + 4lg + r,
@@ -179,19 +296,10 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     if (a.cu && a.N > 1 && a.N <= kLptMaxSeqs) {
         // longest first: pair index p / H is a rank in the order of decreasing length (ties by
         // index), so the longest sequences are dispatched first and the short ones fill the tail
-        __shared__ int lpt_seq;
-        const int N = (int)a.N, r = (int)n;
-        for (int i = tid; i < N; i += NT) {
-            const int li = a.cu[i + 1] - a.cu[i];
-            int rank = 0;
-            for (int jx = 0; jx < N; ++jx) {
-                const int lj = a.cu[jx + 1] - a.cu[jx];
-                rank += (lj > li || (lj == li && jx < i)) ? 1 : 0;
-            }
-            if (rank == r) lpt_seq = i;
-        }
-        __syncthreads();
-        n = lpt_seq;
+        // (the pipeline's LDS serves as scratch; its first use comes after the barrier inside)
+        // (the same in every lane: readfirstlane keeps what derives from it in scalar registers)
+        n = __builtin_amdgcn_readfirstlane(
+            select_by_length(a.cu, (int)a.N, (int)n, tid, reinterpret_cast<uint32_t*>(&sh)));
         p = n * H + h;                                   // the state's (sequence, head) index
     }
     int64_t bos, eos;

@@ -110,11 +110,14 @@ SMALL = [
     # 256 or more (sequence, head) pairs: one workgroup per head takes all 128 columns
     ([37, 0, 16, 5, 81, 1, 130, 64], 32, 128, 128, "bf16", 0.1, "sigmoid", True),
     ([64, 64, 64, 64], 64, 128, 128, "bf16", None, "sigmoid", False),
-    # varlen batches around the 64-sequence limit of the longest-first dispatch (lengths 0..40
-    # with ties): 70 sequences dispatch in index order, 64 by length rank
+    # varlen batches dispatched longest first by the radix select over (length, index) keys
+    # (lengths 0..40 with many ties; several hundred sequences, more than the 768 threads of a
+    # workgroup take one at a time in one pass)
     ([(7 * i) % 41 for i in range(70)], 4, 128, 128, "bf16", 0.1, "sigmoid", True),
     ([(5 * i + 3) % 37 for i in range(64)], 4, 128, 128, "bf16", 0.1, "sigmoid", True),
     ([(7 * i) % 41 for i in range(70)], 1, 128, 128, "bf16", 0.1, "sigmoid", True),
+    ([(11 * i + 5) % 29 for i in range(900)], 1, 128, 128, "bf16", 0.1, "sigmoid", True),
+    ([(3 * i) % 23 for i in range(300)], 2, 128, 128, "bf16", None, "sigmoid", True),
 ]
 
 
