@@ -264,7 +264,6 @@ struct GateLds {
     float w[D];             // the gain per column (ones without one)
     uint32_t arrive;        // stage-S arrivals: 4 per tile
 };
-constexpr int kArriveSpin = 1 << 22;   // bound on the polls of one arrival wait
 
 // PRIO_ROLE: the role whose waves win issue ties on their SIMD (1: stage A, 2: stage B).
 template <int PRIO_ROLE, int BVT, bool GATED>
@@ -712,16 +711,18 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
                 __hip_atomic_fetch_add(&gsh.arrive, 1u, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_WORKGROUP);
             const uint32_t want = 4u * (uint32_t)(tile + 1);
-            for (int it = 0; it < kArriveSpin; ++it) {
-                if (__hip_atomic_load(&gsh.arrive, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_WORKGROUP) >= want)
-                    break;
-                __builtin_amdgcn_s_sleep(1);
+            bool arrived = false;
+            for (int64_t it = 0; it < a.arrive_spin && !arrived; ++it) {
+                arrived = __hip_atomic_load(&gsh.arrive, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_WORKGROUP) >= want;
+                if (!arrived) __builtin_amdgcn_s_sleep(1);
             }
             asm volatile("" ::: "memory");   // the sums are read after the arrivals are seen
             const f32x4 sq = *reinterpret_cast<const f32x4*>(&gsh.ssq[ln][0]);
-            const float rn = __builtin_amdgcn_rsqf((sq[0] + sq[1] + sq[2] + sq[3]) / (float)D +
-                                                   a.eps);
+            // a wait that ran out leaves the tile's y NaN rather than normalised by a partial sum
+            const float rn = arrived ? __builtin_amdgcn_rsqf((sq[0] + sq[1] + sq[2] + sq[3]) /
+                                                             (float)D + a.eps)
+                                     : __builtin_nanf("");
             const uint4 gwv = gsh.gw[(uint32_t)tile & 1u][s][lane];
             const uint2 gwm[2] = {make_uint2(gwv.x, gwv.y), make_uint2(gwv.z, gwv.w)};
             // stored through a buffer resource at the tile's first token row: a scalar base, the
