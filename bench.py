@@ -14,10 +14,12 @@ gate; 3 x 256 B per (token, head) in bf16) on the same [4096, 96, 128] shape, an
 (short convolution, Swish, L2 norm, sigmoid beta, bounded log-decay: reads 3 dk + dv values and
 beta's logit, writes as many per (token, head)) on the same token and head count.  A `varlen`
 object times the prefill on the variable-length batch (16 sequences of 1,024-16,384 tokens with
-initial states, packed with cu_seqlens).  A `long` object times the long-context prefill (one
-sequence of 131,072 tokens, H=96: the same work per token over a 32 times longer chain of tiles).
-A `head_share` object times one GPU's share of the heads under
-8-way head sharding (12 of 96 heads, T = 4096, batch 1) with kda_chunk_fwd and with
+initial states, packed with cu_seqlens); `varlen.gated` the prefill with the output stage fused
+(kda_chunk_fwd_gated) against the prefill and the output-stage kernel, and `varlen.layer` the
+whole token mixer (the input stage, then the gated prefill) against three separate passes.  A
+`long` object times the long-context prefill (one sequence of 131,072 tokens, H=96: the same work
+per token over a 32 times longer chain of tiles).  A `head_share` object times one GPU's share of
+the heads under 8-way head sharding (12 of 96 heads, T = 4096, batch 1) with kda_chunk_fwd and with
 kda_chunk_fwd_split (each sequence also cut into token ranges that run concurrently).
 
 Roofline: algorithmic bytes per launch divided by the kernel's average duration, measured with
@@ -775,6 +777,42 @@ def main():
                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(gbytes / (gvms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
             }
+            # the whole token mixer on the same batch: the input stage, then the gated prefill
+            # on its outputs, against the input stage, the prefill and the output-stage kernel
+            if not args.no_frontend:
+                fr = inputs.make_frontend_inputs(lens, xv.H, xv.dk, xv.dv, "bf16",
+                                                 seed=93).to(dev)
+                fst = torch.empty((xv.num_seqs, 3, xv.H * (2 * xv.dk + xv.dv)),
+                                  dtype=fr.x_q.dtype, device=dev)
+
+                def front_varlen():
+                    return kda_frontend(fr.x_q, fr.x_k, fr.x_v, fr.x_z, fr.x_b, fr.w_q, fr.w_k,
+                                        fr.w_v, fr.z_bias, fr.A, cu_seqlens=fr.cu_seqlens,
+                                        conv_out=fst)[:5]
+
+                def layer_fused():
+                    kda_chunk_fwd_gated(*front_varlen(), zv, weight=wv, h0=xvd.h0,
+                                        cu_seqlens=xvd.cu_seqlens, y=yv, hT=hTv)
+
+                def layer_three_passes():
+                    kda_chunk_fwd(*front_varlen(), h0=xvd.h0, cu_seqlens=xvd.cu_seqlens, o=ov,
+                                  hT=hTv)
+                    kda_output_gate(ov, zv, wv, y=yv)
+
+                lms, _ = time_launches(layer_fused, vsteps, 1, stream)
+                l3ms, _ = time_launches(layer_three_passes, vsteps, 1, stream)
+                fbytes = 2 * xv.total_tokens * xv.H * ((3 * xv.dk + xv.dv) * 2 + 2)
+                result["varlen"]["layer"] = {
+                    "entries": "kda_frontend + kda_chunk_fwd_gated",
+                    "ms_per_step": round(lms, 4),
+                    "value": round(xv.total_tokens / (lms * 1e-3), 1), "unit": "tokens/s",
+                    "three_pass_ms_per_step": round(l3ms, 4),
+                    "vs_three_passes": round(l3ms / lms, 3),
+                    "algorithmic_bytes_per_launch": fbytes + gbytes,
+                    "three_pass_algorithmic_bytes": fbytes + vbytes + 3 * row,
+                    "hbm_bytes_removed": 2 * row,
+                }
+                del fr, fst
             del zv, wv, yv
         del xv, xvd, vviews, ov, hTv
         torch.cuda.empty_cache()
