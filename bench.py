@@ -10,7 +10,10 @@ object the prefill that also saves the state every 64 tokens (kda_chunk_fwd_snap
 head and snapshot, the stride at which saved states cost as much as the per-token cache they
 replace).  An `output_gate` object times the output stage (per-head RMSNorm times a sigmoid
 gate; 3 x 256 B per (token, head) in bf16) on the same [4096, 96, 128] shape, and
-`decode.gated` the decode step with that stage fused.  A `frontend` object times the input stage
+`decode.gated` the decode step with that stage fused; `decode.layer` the whole mixer's decode
+step in one launch (input stage, decode, output stage: kda_decode_step_layer) on the same batch;
+`decode.serving_graph` that step for 4 sequences, as three launches and as one, each eager and as
+a captured HIP graph replayed per token.  A `frontend` object times the input stage
 (short convolution, Swish, L2 norm, sigmoid beta, bounded log-decay: reads 3 dk + dv values and
 beta's logit, writes as many per (token, head)) on the same token and head count.  A `varlen`
 object times the prefill on the variable-length batch (16 sequences of 1,024-16,384 tokens with
@@ -344,6 +347,54 @@ def time_launches(fn, steps, warmup, stream, settle_s=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     return start.elapsed_time(end) / steps, wall  # ms per launch (one kernel per step), seconds
+
+
+def serving_step_graph(dev, stream, steps, N=4):
+    """The per-token serving step of the token mixer for a small batch, N sequences x 96 heads:
+    the input stage (its convolution state updated in place), the decode (the recurrent state
+    updated in place) and the output stage, as three launches (kda_frontend, then
+    kda_decode_step_gated) and as one (kda_decode_step_layer).  Each is timed as eager calls and as
+    one captured HIP graph replayed per token; at this size the launches cost more than the
+    kernels."""
+    import torch
+    from linear_attention_recurrence_08_amd import (inputs, kda_decode_step_gated,
+                                                    kda_decode_step_layer, kda_frontend)
+    H = 96
+    f = inputs.make_frontend_inputs([1] * N, H, 128, 128, "bf16", seed=650,
+                                    with_state=True).to(dev)
+    _, z, w = (t.to(dev) for t in inputs.make_output_gate_inputs(N, H, 128, "bf16", 651))
+    S = inputs.make_decode_inputs(N, H, 128, 128, "bf16", seed=652).h0.to(dev)
+    ones = torch.arange(N + 1, dtype=torch.int32, device=dev)
+    conv = f.conv_in
+
+    def step():
+        q, k, v, g, b, _ = kda_frontend(f.x_q, f.x_k, f.x_v, f.x_z, f.x_b, f.w_q, f.w_k, f.w_v,
+                                        f.z_bias, f.A, cu_seqlens=ones, conv_in=conv,
+                                        conv_out=conv)
+        kda_decode_step_gated(q, k, v, g, b, S, z, w)
+
+    def step_fused():
+        kda_decode_step_layer(f.x_q, f.x_k, f.x_v, f.x_z, f.x_b, f.w_q, f.w_k, f.w_v, f.z_bias,
+                              f.A, conv, S, z, w)
+
+    out = {"N": N, "H": H}
+    for tag, fn, launches, entries in (
+            ("three_kernels", step, 3, "kda_frontend + kda_decode_step_gated"),
+            ("one_kernel", step_fused, 1, "kda_decode_step_layer")):
+        fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        eager_ms, _ = time_launches(fn, steps, 3, stream)
+        graph_ms, _ = time_launches(graph.replay, steps, 3, stream)
+        out[tag] = {"entries": entries, "launches_per_token": launches,
+                    "eager_us_per_token": round(eager_ms * 1e3, 2),
+                    "graph_us_per_token": round(graph_ms * 1e3, 2),
+                    "graph_tokens_per_s": round(N / (graph_ms * 1e-3), 1),
+                    "graph_vs_eager": round(eager_ms / graph_ms, 3)}
+        del graph
+    return out
 
 
 def long_context(dev, stream, steps):
@@ -943,7 +994,48 @@ def main():
                              "kernel": "kda_decode_d128 (gated)",
                              "algorithmic_bytes_per_launch": gdbytes},
             }
+            # the whole mixer's decode step in one launch (input stage, decode, output stage)
+            # against the input-stage kernel followed by the gated decode
+            if not args.no_frontend:
+                from linear_attention_recurrence_08_amd import kda_decode_step_layer
+                fr = inputs.make_frontend_inputs([1] * 256, 96, 128, 128, "bf16", seed=653,
+                                                 with_state=True).to(dev)
+                ones = torch.arange(257, dtype=torch.int32, device=dev)
+                taps = (fr.w_q, fr.w_k, fr.w_v, fr.z_bias, fr.A)
+                xs = (fr.x_q, fr.x_k, fr.x_v, fr.x_z, fr.x_b)
+
+                def decode_layer():
+                    kda_decode_step_layer(*xs, *taps, fr.conv_in, S, dz, dw, y=dy)
+
+                def decode_three():
+                    q5 = kda_frontend(*xs, *taps, cu_seqlens=ones, conv_in=fr.conv_in,
+                                      conv_out=fr.conv_in)[:5]
+                    kda_decode_step_gated(*q5, S, dz, dw, 1e-6, o=od, y=dy)
+
+                lms, _ = time_launches(decode_layer, ksteps, args.warmup, stream)
+                l3ms, _ = time_launches(decode_three, ksteps, args.warmup, stream)
+                # per (sequence, head): the state in and out, the pre-activations, the saved
+                # inputs in and out, gate and y; the taps, bias, A and gain once
+                per_unit = (2 * 128 * 128 * 4 + (3 * 128 + 128) * 2 + 2 + 2 * 3 * 384 * 2 +
+                            2 * 128 * 2)
+                lbytes = 256 * 96 * per_unit + 96 * (384 * 16 + 128 * 4 + 4) + 128 * 4
+                result["decode"]["layer"] = {
+                    "entry": "kda_decode_step_layer", "ms_per_step": round(lms, 5),
+                    "value": round(256 / (lms * 1e-3), 1), "unit": "tokens/s",
+                    "three_kernel_ms_per_step": round(l3ms, 5),
+                    "vs_three_kernels": round(l3ms / lms, 3),
+                    "roofline": {"bound": "hbm",
+                                 "achieved": round(lbytes / (lms * 1e-3) / 1e9, 1),
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(lbytes / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "kernel": "kda_decode_d128 (input and output stages)",
+                                 "algorithmic_bytes_per_launch": lbytes},
+                }
+                del fr, ones, taps, xs
             del dz, dw, dy
+        # the whole mixer's serving step for a small batch, eager and as a replayed HIP graph
+        if not args.no_output_gate and not args.no_frontend:
+            result["decode"]["serving_graph"] = serving_step_graph(dev, stream, ksteps)
         del qd, kd, vd, gd, bd, S, od
         torch.cuda.empty_cache()
 

@@ -40,6 +40,12 @@
  * status reports argument errors and launch failures; execution faults surface at the caller's
  * next synchronisation of the stream.
  *
+ * Graph capture.  Outside the validation mode (KDA_VALIDATE, which copies to the host and
+ * synchronises), a compute entry point only enqueues kernels on the given stream: no allocation,
+ * no synchronisation, no memset.  Calls may therefore be captured into a HIP graph and replayed
+ * (the kernels read their inputs at replay time).  kda_chunk_fwd_split_noalloc looks up its
+ * static array on its first call on a device: make that first call outside a capture.
+ *
  * Supported sizes.  dk and dv: multiples of 16 from 16 to 128 (any combination).  The fast
  * matrix-core path is used for dtype KDA_BF16 with dk = dv = 128; every other supported
  * combination runs the general float32 tile path.  H >= 1 with H * max(dk, dv) <= 2^20 (one
@@ -377,6 +383,38 @@ int kda_frontend(const void* x_q, const void* x_k, const void* x_v, const void* 
                  const int32_t* cu_seqlens, int num_seqs, const void* conv_in, void* conv_out,
                  void* q, void* k, void* v, void* g, void* beta,
                  int B, int T, int H, int dk, int dv, int dtype, void* stream);
+
+/*
+ * kda_decode_step_layer -- the whole token mixer for one token per sequence in one launch: the
+ * input stage of kda_frontend (decode mode, the convolution state updated in place), the decode
+ * step of kda_decode_step (the recurrent state updated in place) and the output stage of
+ * kda_output_gate ("Kimi K3's hybrid block, from first principles", section "From linear
+ * attention to the delta rule": the short convolution, Swish and unit-length normalisation of q
+ * and k, the bounded log-decay and the sigmoid beta before the recurrence, and the gated RMS
+ * normalisation of each head's output row after it).  q, k, v, g and beta stay in float32 inside
+ * the kernel, where kda_frontend followed by kda_decode_step_gated would store them in dtype.
+ *
+ *   x_q, x_k, x_z [N, H, dk], x_v [N, H, dv], x_b [N, H]   dtype    device  the token's
+ *                                                         pre-activations
+ *   w_q, w_k, w_v, z_bias, A, g_min, norm_eps            as kda_frontend (norm_eps: the L2 norms)
+ *   conv_state [N, 3, H*(2dk+dv)]  dtype    device  the last three inputs of q | k | v before the
+ *                                                  token, oldest first; read, then overwritten
+ *                                                  with the three inputs that end at the token
+ *   S          [N, H, dk, dv]      float32  device  read, then overwritten with the new state
+ *   gate, weight, eps              as kda_decode_step_gated
+ *   o          [N, H, dv]          dtype    device  written, or NULL (not written)
+ *   y          [N, H, dv]          dtype    device  written; may alias o or gate
+ * dk = dv = 128 only (KDA_ERR_UNSUPPORTED otherwise: other head sizes call kda_frontend, then
+ * kda_decode_step_gated).  S 16-byte aligned; gate, o and y 8-byte aligned for bf16 and 16-byte
+ * for float32 (KDA_ERR_ALIGN).  g_min < 0, norm_eps >= 0, eps >= 0 (KDA_ERR_RANGE).
+ * Returns KDA_OK or a negative status.
+ */
+int kda_decode_step_layer(const void* x_q, const void* x_k, const void* x_v, const void* x_z,
+                          const void* x_b, const float* w_q, const float* w_k, const float* w_v,
+                          const float* z_bias, const float* A, float g_min, float norm_eps,
+                          void* conv_state, float* S, const void* gate, const float* weight,
+                          float eps, void* o, void* y, int N, int H, int dk, int dv, int dtype,
+                          void* stream);
 
 /* Text for a status code (static storage; never NULL). */
 const char* kda_status_string(int status);

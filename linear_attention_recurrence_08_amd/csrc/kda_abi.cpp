@@ -502,4 +502,36 @@ int kda_frontend(const void* x_q, const void* x_k, const void* x_v, const void* 
     return kda::launch_frontend(a, s) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_decode_step_layer(const void* x_q, const void* x_k, const void* x_v, const void* x_z,
+                          const void* x_b, const float* w_q, const float* w_k, const float* w_v,
+                          const float* z_bias, const float* A, float g_min, float norm_eps,
+                          void* conv_state, float* S, const void* gate, const float* weight,
+                          float eps, void* o, void* y, int N, int H, int dk, int dv, int dtype,
+                          void* stream) {
+    if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
+    if (N < 0 || H <= 0) return KDA_ERR_SHAPE;
+    if (dk != 128 || dv != 128) return KDA_ERR_UNSUPPORTED;   // the fused kernel's head size
+    if (!rows_ok(H, dk, dv)) return KDA_ERR_SHAPE;
+    if (!(g_min < 0.f) || !std::isfinite(g_min) || !(norm_eps >= 0.f) ||
+        !std::isfinite(norm_eps) || !(eps >= 0.f) || !std::isfinite(eps))
+        return KDA_ERR_RANGE;
+    if (N == 0) return KDA_OK;
+    if (!x_q || !x_k || !x_v || !x_z || !x_b || !w_q || !w_k || !w_v || !z_bias || !A ||
+        !conv_state || !S || !gate || !y)
+        return KDA_ERR_NULL;
+    // 16-byte state accesses, 4-element gate/o/y accesses (the inputs are read per element)
+    const uintptr_t va = dtype == KDA_BF16 ? 8 : 16;
+    if (!aligned(S, 16) || !aligned(gate, va) || !aligned(y, va) || (o && !aligned(o, va)))
+        return KDA_ERR_ALIGN;
+    kda::DecodeArgs a;
+    a.q = a.k = a.v = a.g = a.beta = nullptr;
+    a.S = S; a.o = o; a.N = N; a.H = H; a.dk = dk; a.dv = dv; a.dtype = dtype;
+    a.gate = gate; a.weight = weight; a.eps = eps; a.y = y;
+    a.xq = x_q; a.xk = x_k; a.xv = x_v; a.xz = x_z; a.xb = x_b;
+    a.wq = w_q; a.wk = w_k; a.wv = w_v; a.zbias = z_bias; a.A = A;
+    a.g_min = g_min; a.norm_eps = norm_eps; a.conv = conv_state;
+    return kda::launch_decode_d128(a, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

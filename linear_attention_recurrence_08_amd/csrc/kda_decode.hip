@@ -12,7 +12,8 @@
 // thread (rg, cg) holds rows rg, rg+8, ..., rg+120 (16 rows) x columns 4cg..4cg+3 of S in
 // registers as 16 float4, so the state is loaded once with full 16-byte accesses, reduced over
 // the key axis (two column partial sums S'^T k and S'^T q, plus k.q) with one cross-lane step
-// and one LDS step, then written back once with non-temporal stores.
+// and one LDS step, then written back once with non-temporal stores.  Variants fuse the output
+// stage after the step and the input stage before it (the whole token mixer in one launch).
 #include "kda_internal.h"
 
 namespace kda {
@@ -54,6 +55,8 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float x[4]) {
 constexpr int D = 128;
 constexpr int NRED = 9;  // per column group: S'^T k (4), S'^T q (4), k.q
 
+__device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+
 // HPW heads per workgroup: every head's 64 KiB state is requested before the first one is
 // reduced, so the second head's loads are in flight while the first head is reduced and stored.
 // GATED adds the output stage y = o / sqrt(mean(o^2) + eps) * w * sigmoid(gate) over the head's
@@ -61,10 +64,19 @@ constexpr int NRED = 9;  // per column group: S'^T k (4), S'^T q (4), k.q
 // the delta rule": the output is RMS-normalised per head and multiplied by a sigmoid gate of the
 // token): every 32-lane half-wave holds the whole row (4 columns per lane), so the sum of squares
 // is five xor shuffles.
-template <typename Tin, int HPW, bool GATED>
+// FRONT adds the input stage in front (same section: q and k get a four-tap causal convolution,
+// Swish and unit-length normalisation, v the convolution and Swish, beta a sigmoid of the token's
+// logit, and the log-decay g = g_min sigmoid(A_h (z + bias_c)), the reading kda_frontend takes).
+// Thread (head hp, channel c) convolves its channel of q, k and v over the three saved inputs and
+// the current one, shifts the saved inputs by one token in place, and forms g and beta; the two
+// L2 norms of a head span its two waves and meet in LDS.  q, k, v, g and beta stay in float32 and
+// never reach HBM, while the state loads issued before them are in flight.
+template <typename Tin, int HPW, bool GATED, bool FRONT>
 __global__ __launch_bounds__(256) void kda_decode_d128_kernel(DecodeArgs a) {
+    static_assert(!FRONT || GATED, "the fused input stage comes with the output stage");
     __shared__ float sk[HPW][D], sq[HPW][D], sa[HPW][D];
     __shared__ float red[HPW][4][32][NRED + 1];
+    __shared__ float sv[FRONT ? HPW : 1][D], sb[HPW], snorm[HPW][2][2];
 
     const int tid = threadIdx.x;
     const int cg = tid & 31;          // columns 4cg .. 4cg+3
@@ -83,21 +95,84 @@ __global__ __launch_bounds__(256) void kda_decode_d128_kernel(DecodeArgs a) {
             s[hp][i] = __builtin_nontemporal_load(
                 reinterpret_cast<const f4*>(S + (rg + 8 * i) * D + 4 * cg));
     }
+    if constexpr (FRONT) {
+        const int hp = tid >> 7, c = tid & (D - 1);   // this thread's head and channel
+        float yq = 0.f, yk = 0.f, yv = 0.f, al = 0.f, bt = 0.f;
+        if (hp < HPW) {
+            const int64_t unit = unit0 + hp, n = unit / a.H, h = unit % a.H;
+            const int64_t C = a.H * 3 * D;            // columns of the convolution state
+            Tin* cs = static_cast<Tin*>(a.conv) + n * 3 * C;
+            const int64_t col[3] = {h * D + c, (a.H + h) * D + c, (2 * a.H + h) * D + c};
+            const Tin* xs[3] = {static_cast<const Tin*>(a.xq), static_cast<const Tin*>(a.xk),
+                                static_cast<const Tin*>(a.xv)};
+            const float* ws[3] = {a.wq, a.wk, a.wv};
+            float y3[3];
 #pragma unroll
-    for (int hp = 0; hp < HPW; ++hp) {
-        const int64_t unit = unit0 + hp;
-        const Tin* q = static_cast<const Tin*>(a.q) + unit * D;
-        const Tin* k = static_cast<const Tin*>(a.k) + unit * D;
-        const Tin* g = static_cast<const Tin*>(a.g) + unit * D;
-        if (tid < D) {
-            sk[hp][tid] = io<Tin>::load(k + tid);
-            sq[hp][tid] = io<Tin>::load(q + tid);
-            sa[hp][tid] = __expf(io<Tin>::load(g + tid));
+            for (int t = 0; t < 3; ++t) {
+                const float x = io<Tin>::load(xs[t] + unit * D + c);
+                const float s0 = io<Tin>::load(cs + col[t]);
+                const float s1 = io<Tin>::load(cs + C + col[t]);
+                const float s2 = io<Tin>::load(cs + 2 * C + col[t]);
+                const float* w = ws[t] + (h * D + c) * 4;
+                const float u = w[0] * s0 + w[1] * s1 + w[2] * s2 + w[3] * x;
+                y3[t] = u * sigm(u);
+                // the saved inputs move on by one token (this thread alone reads this column)
+                io<Tin>::store(cs + col[t], s1);
+                io<Tin>::store(cs + C + col[t], s2);
+                io<Tin>::store(cs + 2 * C + col[t], x);
+            }
+            yq = y3[0];
+            yk = y3[1];
+            yv = y3[2];
+            const float z = io<Tin>::load(static_cast<const Tin*>(a.xz) + unit * D + c);
+            al = __expf(a.g_min * sigm(a.A[h] * (z + a.zbias[h * D + c])));
+            if (c == 0) bt = sigm(io<Tin>::load(static_cast<const Tin*>(a.xb) + unit));
         }
-        load4<Tin>(static_cast<const Tin*>(a.v) + unit * D + 4 * cg, vv[hp]);
-        b[hp] = io<Tin>::load(static_cast<const Tin*>(a.beta) + unit);
+        // the sums of squares of q and k over the head's 128 channels (two waves)
+        float ssq = yq * yq, ssk = yk * yk;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            ssq += __shfl_xor(ssq, m, 64);
+            ssk += __shfl_xor(ssk, m, 64);
+        }
+        if (hp < HPW && lane == 0) {
+            snorm[hp][w & 1][0] = ssq;
+            snorm[hp][w & 1][1] = ssk;
+        }
+        __syncthreads();
+        if (hp < HPW) {
+            const float rq = __builtin_amdgcn_rsqf(snorm[hp][0][0] + snorm[hp][1][0] + a.norm_eps);
+            const float rk = __builtin_amdgcn_rsqf(snorm[hp][0][1] + snorm[hp][1][1] + a.norm_eps);
+            sq[hp][c] = yq * rq;
+            sk[hp][c] = yk * rk;
+            sa[hp][c] = al;
+            sv[hp][c] = yv;
+            if (c == 0) sb[hp] = bt;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int hp2 = 0; hp2 < HPW; ++hp2) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vv[hp2][j] = sv[hp2][4 * cg + j];
+            b[hp2] = sb[hp2];
+        }
+    } else {
+#pragma unroll
+        for (int hp = 0; hp < HPW; ++hp) {
+            const int64_t unit = unit0 + hp;
+            const Tin* q = static_cast<const Tin*>(a.q) + unit * D;
+            const Tin* k = static_cast<const Tin*>(a.k) + unit * D;
+            const Tin* g = static_cast<const Tin*>(a.g) + unit * D;
+            if (tid < D) {
+                sk[hp][tid] = io<Tin>::load(k + tid);
+                sq[hp][tid] = io<Tin>::load(q + tid);
+                sa[hp][tid] = __expf(io<Tin>::load(g + tid));
+            }
+            load4<Tin>(static_cast<const Tin*>(a.v) + unit * D + 4 * cg, vv[hp]);
+            b[hp] = io<Tin>::load(static_cast<const Tin*>(a.beta) + unit);
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
 #pragma unroll
     for (int hp = 0; hp < HPW; ++hp) {
@@ -134,7 +209,7 @@ __global__ __launch_bounds__(256) void kda_decode_d128_kernel(DecodeArgs a) {
             u[j] = b[hp] * (vv[hp][j] - tot[j]);
             out[j] = tot[4 + j] + tot[8] * u[j];
         }
-        if (rg == 0) store4<Tin>(static_cast<Tin*>(a.o) + unit * D + 4 * cg, out);
+        if (rg == 0 && (!FRONT || a.o)) store4<Tin>(static_cast<Tin*>(a.o) + unit * D + 4 * cg, out);
         if (GATED) {
             float gz[4];
             load4<Tin>(static_cast<const Tin*>(a.gate) + unit * D + 4 * cg, gz);
@@ -165,17 +240,25 @@ __global__ __launch_bounds__(256) void kda_decode_d128_kernel(DecodeArgs a) {
 }  // namespace
 
 namespace {
-template <bool GATED>
+template <bool GATED, bool FRONT>
 void launch_d128(const DecodeArgs& a, hipStream_t s, int64_t units) {
     const bool pair = (units % 2) == 0;
     const dim3 grid((unsigned)(pair ? units / 2 : units));
     const dim3 block(256);
     if (a.dtype == 0) {
-        if (pair) hipLaunchKernelGGL((kda_decode_d128_kernel<bf16_t, 2, GATED>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((kda_decode_d128_kernel<bf16_t, 1, GATED>), grid, block, 0, s, a);
+        if (pair)
+            hipLaunchKernelGGL((kda_decode_d128_kernel<bf16_t, 2, GATED, FRONT>), grid, block, 0,
+                               s, a);
+        else
+            hipLaunchKernelGGL((kda_decode_d128_kernel<bf16_t, 1, GATED, FRONT>), grid, block, 0,
+                               s, a);
     } else {
-        if (pair) hipLaunchKernelGGL((kda_decode_d128_kernel<float, 2, GATED>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((kda_decode_d128_kernel<float, 1, GATED>), grid, block, 0, s, a);
+        if (pair)
+            hipLaunchKernelGGL((kda_decode_d128_kernel<float, 2, GATED, FRONT>), grid, block, 0,
+                               s, a);
+        else
+            hipLaunchKernelGGL((kda_decode_d128_kernel<float, 1, GATED, FRONT>), grid, block, 0,
+                               s, a);
     }
 }
 }  // namespace
@@ -183,8 +266,14 @@ void launch_d128(const DecodeArgs& a, hipStream_t s, int64_t units) {
 hipError_t launch_decode_d128(const DecodeArgs& a, hipStream_t s) {
     const int64_t units = a.N * a.H;
     if (units <= 0) return hipSuccess;
-    if (a.gate) launch_d128<true>(a, s, units);
-    else launch_d128<false>(a, s, units);
+    if (a.xq) {
+        if (!a.gate) return hipErrorInvalidValue;   // the input stage comes with the output stage
+        launch_d128<true, true>(a, s, units);
+    } else if (a.gate) {
+        launch_d128<true, false>(a, s, units);
+    } else {
+        launch_d128<false, false>(a, s, units);
+    }
     return hipGetLastError();
 }
 

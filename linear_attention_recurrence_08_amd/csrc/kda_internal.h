@@ -62,6 +62,21 @@ struct DecodeArgs {
     const float* weight = nullptr;       // [dv] or nullptr (ones)
     float eps = 0.f;
     void* y = nullptr;                   // [N, H, dv]
+    // fused input stage (xq != nullptr; with the output stage, dk = dv = 128): q, k, v, g and
+    // beta come from the token's pre-activations and the convolution state, which is updated in
+    // place; q, k, v, g and beta above are then unused, and o may be nullptr (not written)
+    const void* xq = nullptr;            // [N, H, dk] pre-activations (dtype)
+    const void* xk = nullptr;
+    const void* xv = nullptr;            // [N, H, dv]
+    const void* xz = nullptr;            // [N, H, dk] decay logits before the bias
+    const void* xb = nullptr;            // [N, H] write-strength logits
+    const float* wq = nullptr;           // [H * dk, 4] convolution taps (tap 3 = current token)
+    const float* wk = nullptr;
+    const float* wv = nullptr;           // [H * dv, 4]
+    const float* zbias = nullptr;        // [H * dk]
+    const float* A = nullptr;            // [H]
+    float g_min = 0.f, norm_eps = 0.f;
+    void* conv = nullptr;                // [N, 3, H * (2 dk + dv)] (dtype), read and overwritten
 };
 
 // Output stage over rows of dv values: y = o / sqrt(mean(o^2) + eps) * weight * sigmoid(gate).

@@ -14,6 +14,10 @@ in the library's HIP kernels.  PyTorch supplies device memory and the current st
     kda_output_gate(o, gate, weight=None, eps=...) -> y
     kda_frontend(x_q, x_k, x_v, x_z, x_b, w_q, w_k, w_v, z_bias, A, ...)
         -> (q, k, v, g, beta, conv_state)
+    kda_decode_step_layer(x_q, x_k, x_v, x_z, x_b, w_q, w_k, w_v, z_bias, A, conv_state, S,
+                          gate, ...) -> (y, o)
+                                 the input stage, the decode step and the output stage in one
+                                 launch (conv_state and S updated in place)
     kda_status_string(code) -> str
 
 Layouts (see include/kda.h): q, k, g [B, T, H, dk] or packed [Ttot, H, dk]; v [.., H, dv];
@@ -95,6 +99,10 @@ def load_library():
         lib.kda_frontend.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, f32, vp, i32,
                                      vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
         lib.kda_frontend.restype = i32
+        lib.kda_decode_step_layer.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, f32,
+                                              vp, vp, vp, vp, f32, vp, vp, i32, i32, i32, i32,
+                                              i32, vp]
+        lib.kda_decode_step_layer.restype = i32
         lib.kda_status_string.argtypes = [i32]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_version.argtypes = []
@@ -569,3 +577,62 @@ def kda_frontend(x_q: torch.Tensor, x_k: torch.Tensor, x_v: torch.Tensor, x_z: t
     if st != KDA_OK:
         raise KDAError(st, "kda_frontend")
     return q, k, v, g, beta, conv_out
+
+
+def kda_decode_step_layer(x_q: torch.Tensor, x_k: torch.Tensor, x_v: torch.Tensor,
+                          x_z: torch.Tensor, x_b: torch.Tensor, w_q: torch.Tensor,
+                          w_k: torch.Tensor, w_v: torch.Tensor, z_bias: torch.Tensor,
+                          A: torch.Tensor, conv_state: torch.Tensor, S: torch.Tensor,
+                          gate: torch.Tensor, weight: Optional[torch.Tensor] = None,
+                          g_min: float = -5.0, norm_eps: float = 1e-6, eps: float = 1e-6,
+                          want_o: bool = False, o: Optional[torch.Tensor] = None,
+                          y: Optional[torch.Tensor] = None
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """The whole token mixer for one token per sequence in one launch: the input stage (the
+    convolution state [N, 3, H*(2dk+dv)] updated in place), the decode step (S [N, H, dk, dv]
+    float32 updated in place) and the output stage.  x_q, x_k, x_z [N, H, dk], x_v [N, H, dv],
+    x_b [N, H] and gate [N, H, dv] in one dtype; taps, z_bias, A and weight float32 as in
+    kda_frontend and kda_decode_step_gated.  dk = dv = 128.  Returns (y, o); o is None unless
+    want_o is set or o is passed."""
+    dev = x_q.device
+    dt = x_q.dtype
+    for name, t in (("x_q", x_q), ("x_k", x_k), ("x_v", x_v), ("x_z", x_z), ("x_b", x_b),
+                    ("gate", gate), ("conv_state", conv_state)):
+        _check(t, name, dev, dt)
+    if x_q.dim() != 3:
+        raise ValueError("x_q must be [N, H, dk]")
+    N, H, dk = x_q.shape
+    dv = x_v.shape[-1]
+    if x_k.shape != x_q.shape or x_z.shape != x_q.shape or x_v.shape != (N, H, dv) \
+            or x_b.shape != (N, H) or gate.shape != (N, H, dv):
+        raise ValueError("inconsistent pre-activation or gate shapes")
+    if tuple(conv_state.shape) != (N, 3, H * (2 * dk + dv)):
+        raise ValueError(f"conv_state must be [{N}, 3, {H * (2 * dk + dv)}]")
+    _check(S, "S", dev, torch.float32)
+    if tuple(S.shape) != (N, H, dk, dv):
+        raise ValueError(f"S must be [{N}, {H}, {dk}, {dv}]")
+    for name, t, shape in (("w_q", w_q, (H * dk, 4)), ("w_k", w_k, (H * dk, 4)),
+                           ("w_v", w_v, (H * dv, 4)), ("z_bias", z_bias, (H * dk,)),
+                           ("A", A, (H,))):
+        _check(t, name, dev, torch.float32)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {list(shape)}")
+    weight = _gate_weight(weight, dv, dev)
+    for name in ("o", "y"):
+        t = o if name == "o" else y
+        if t is not None:
+            _check(t, name, dev, dt)
+            if tuple(t.shape) != (N, H, dv):
+                raise ValueError(f"{name} must be [{N}, {H}, {dv}], got {list(t.shape)}")
+    if o is None and want_o:
+        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    if y is None:
+        y = torch.empty((N, H, dv), dtype=dt, device=dev)
+    st = load_library().kda_decode_step_layer(
+        _ptr(x_q), _ptr(x_k), _ptr(x_v), _ptr(x_z), _ptr(x_b), _ptr(w_q), _ptr(w_k), _ptr(w_v),
+        _ptr(z_bias), _ptr(A), float(g_min), float(norm_eps), _ptr(conv_state), _ptr(S),
+        _ptr(gate), _ptr(weight), float(eps), _ptr(o), _ptr(y), N, H, dk, dv, _dtype_code(x_q),
+        _stream(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_decode_step_layer")
+    return y, o

@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
                                      "kda_chunk_fwd_split_noalloc",
                                      "kda_chunk_fwd_split_segments",
                                      "kda_chunk_fwd_split_workspace_bytes",
-                                     "kda_decode_step", "kda_decode_step_gated", "kda_frontend",
+                                     "kda_decode_step", "kda_decode_step_gated",
+                                     "kda_decode_step_layer", "kda_frontend",
                                      "kda_output_gate", "kda_status_string", "kda_version"]
 
 
@@ -330,6 +331,37 @@ def test_frontend_empty_is_noop(lib):
     assert _front(lib, T=0) == 0
 
 
+def _layer(lib, **kw):
+    a = dict(xq=FAKE, xk=FAKE, xv=FAKE, xz=FAKE, xb=FAKE, wq=FAKE, wk=FAKE, wv=FAKE, zb=FAKE,
+             A=FAKE, gmin=-5.0, neps=1e-6, conv=FAKE, S=FAKE, gate=FAKE, w=None, eps=1e-6,
+             o=None, y=FAKE, N=4, H=2, dk=128, dv=128, dtype=0)
+    a.update(kw)
+    return lib.kda_decode_step_layer(*(a[n] for n in (
+        "xq", "xk", "xv", "xz", "xb", "wq", "wk", "wv", "zb", "A", "gmin", "neps", "conv", "S",
+        "gate", "w", "eps", "o", "y", "N", "H", "dk", "dv", "dtype")), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), -3), (dict(N=-1), -2), (dict(H=0), -2),
+    # the fused kernel's head size only
+    (dict(dk=64), -4), (dict(dv=64), -4), (dict(dk=96, dv=96), -4),
+    (dict(gmin=0.0), -6), (dict(neps=-1.0), -6), (dict(eps=-1.0), -6),
+    (dict(eps=float("nan")), -6), (dict(gmin=float("-inf")), -6),
+    (dict(xq=None), -1), (dict(xb=None), -1), (dict(wv=None), -1), (dict(zb=None), -1),
+    (dict(A=None), -1), (dict(conv=None), -1), (dict(S=None), -1), (dict(gate=None), -1),
+    (dict(y=None), -1),
+    (dict(S=UNALIGNED), -9), (dict(o=ctypes.c_void_p(0x1004)), -9),
+    (dict(y=ctypes.c_void_p(0x1004)), -9), (dict(gate=UNALIGNED, dtype=1), -9),
+    (dict(H=8193), -2),
+])
+def test_layer_decode_argument_errors(lib, kw, code):
+    assert _layer(lib, **kw) == code
+
+
+def test_layer_decode_empty_is_noop(lib):
+    assert _layer(lib, N=0, xq=None, conv=None, S=None, y=None) == 0
+
+
 class _NoCalls:
     """Stands in for the library: any call into it fails the test (the binding must reject the
     arguments before reaching the C ABI)."""
@@ -380,6 +412,25 @@ def test_binding_rejects_small_decode_outputs(host_binding):
         kda.kda_decode_step(q, q, q, q, _bf(torch, 4, 2), S, o=_bf(torch, 3, 2, 128))
     with pytest.raises(ValueError):
         kda.kda_decode_step_gated(q, q, q, q, _bf(torch, 4, 2), S, q, y=_bf(torch, 4, 2, 64))
+
+
+@pytest.mark.parametrize("bad", ["conv_state", "S", "y", "gate", "w_v"])
+def test_binding_rejects_wrong_layer_decode_buffers(host_binding, bad):
+    """kda_decode_step_layer writes the whole convolution state, S and y in place: a buffer of
+    another shape is rejected before the C ABI is reached."""
+    kda, torch = host_binding
+    N, H = 4, 2
+    x = _bf(torch, N, H, 128)
+    a = dict(conv_state=_bf(torch, N, 3, H * 384), S=torch.zeros(N, H, 128, 128),
+             gate=_bf(torch, N, H, 128), y=None, w_v=torch.zeros(H * 128, 4))
+    a[bad] = {"conv_state": _bf(torch, N, 3, H * 384 - 8), "S": torch.zeros(N - 1, H, 128, 128),
+              "y": _bf(torch, N, H, 64), "gate": _bf(torch, N, H + 1, 128),
+              "w_v": torch.zeros(H * 128, 3)}[bad]
+    taps = torch.zeros(H * 128, 4)
+    with pytest.raises(ValueError):
+        kda.kda_decode_step_layer(x, x, x, x, _bf(torch, N, H), taps, taps, a["w_v"],
+                                  torch.zeros(H * 128), torch.ones(H), a["conv_state"], a["S"],
+                                  a["gate"], y=a["y"])
 
 
 def test_binding_rejects_small_snapshot_buffers(host_binding):

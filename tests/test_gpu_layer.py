@@ -116,12 +116,16 @@ def test_layer_prefill_against_oracle(oracle_mod, case):
     assert np.array_equal(to64(conv), conv_ref)
 
 
-def test_layer_prefill_then_decode_against_oracle(oracle_mod):
+@pytest.mark.parametrize("decode", ["three_kernels", "one_kernel"])
+def test_layer_prefill_then_decode_against_oracle(oracle_mod, decode):
     """A server's flow: the prompts through the input stage and the gated prefill, then five decode
-    steps that take over the convolution state and the recurrent state and update both in place.
-    Every y of prompt and continuation against one oracle run over the whole sequences."""
+    steps that take over the convolution state and the recurrent state and update both in place,
+    either as kda_frontend then kda_decode_step_gated or as kda_decode_step_layer (one launch;
+    its q, k, v, g and beta stay in float32, where the reference rounds them to bf16 as the other
+    paths store them).  Every y of prompt and continuation against one oracle run over the whole
+    sequences."""
     from linear_attention_recurrence_08_amd import (kda_chunk_fwd_gated, kda_decode_step_gated,
-                                                    kda_frontend)
+                                                    kda_decode_step_layer, kda_frontend)
     dev = _dev()
     prompts, steps, H, dt = [70, 33, 0, 18], 5, 64, "bf16"
     full = [p + steps for p in prompts]
@@ -137,7 +141,7 @@ def test_layer_prefill_then_decode_against_oracle(oracle_mod):
     zd, wd = z.to(dev), w.to(dev)
     xs = (fd.x_q, fd.x_k, fd.x_v, fd.x_z, fd.x_b)
     taps = (fd.w_q, fd.w_k, fd.w_v, fd.z_bias, fd.A)
-    _say(f"layer serve: prompts={prompts} then {steps} decode steps, H={H} {dt}")
+    _say(f"layer serve: prompts={prompts} then {steps} decode steps ({decode}), H={H} {dt}")
     pr = torch.from_numpy(prompt_rows).to(dev)
     q, k, v, g, beta, conv = kda_frontend(*(x[pr] for x in xs), *taps, G_MIN, EPS_NORM,
                                           cu_seqlens=cu_p, conv_in=fd.conv_in,
@@ -147,9 +151,13 @@ def test_layer_prefill_then_decode_against_oracle(oracle_mod):
     y_steps = []
     for r in step_rows:
         rd = torch.from_numpy(r).to(dev)
-        q, k, v, g, beta, _ = kda_frontend(*(x[rd] for x in xs), *taps, G_MIN, EPS_NORM,
-                                           cu_seqlens=ones, conv_in=conv, conv_out=conv)
-        _, y = kda_decode_step_gated(q, k, v, g, beta, S, zd[rd], wd, eps=EPS_RMS)
+        if decode == "one_kernel":
+            y, _ = kda_decode_step_layer(*(x[rd] for x in xs), *taps, conv, S, zd[rd], wd,
+                                         g_min=G_MIN, norm_eps=EPS_NORM, eps=EPS_RMS)
+        else:
+            q, k, v, g, beta, _ = kda_frontend(*(x[rd] for x in xs), *taps, G_MIN, EPS_NORM,
+                                               cu_seqlens=ones, conv_in=conv, conv_out=conv)
+            _, y = kda_decode_step_gated(q, k, v, g, beta, S, zd[rd], wd, eps=EPS_RMS)
         y_steps.append(y)
     torch.cuda.synchronize()
     heads = [0, 21, 63]
@@ -184,3 +192,64 @@ def test_layer_T4096_H96(oracle_mod):
     ey, eh = err(to64(y[:, heads]) * rms, y_ref * rms), err(to64(hT[:, heads]), h_ref)
     _say(f"  heads {heads}: error y {ey:.3e}, hT {eh:.3e}")
     assert ey <= TOL["bf16"] and eh <= TOL["bf16"], (ey, eh)
+
+
+# (N, H, dtype): 256 x 96 (two heads per workgroup); 3 x 3 (an odd unit count: one head per
+# workgroup); float32
+DECODES = [(256, 96, "bf16"), (3, 3, "bf16"), (5, 2, "f32")]
+
+
+@pytest.mark.parametrize("N,H,dt", DECODES, ids=lambda c: str(c))
+def test_layer_decode_step_against_oracle(oracle_mod, N, H, dt):
+    """kda_decode_step_layer (the input stage, the decode step and the output stage in one launch)
+    and kda_frontend followed by kda_decode_step_gated, both against the oracle's chain on the
+    same token.  The two GPU paths differ by the rounding of q, k, v, g and beta to dtype between
+    the two launches of the second (about 1e-2 of max |y| in bf16; the one-launch path keeps them
+    in float32 and lands closer to the oracle); in float32 they agree to 1e-4."""
+    from linear_attention_recurrence_08_amd import (inputs, kda_decode_step_gated,
+                                                    kda_decode_step_layer, kda_frontend)
+    dev = _dev()
+    f = inputs.make_frontend_inputs([1] * N, H, 128, 128, dt, seed=700 + N, with_state=True)
+    _, z, w = inputs.make_output_gate_inputs(N, H, 128, dt, 701 + N)
+    S0 = inputs.make_decode_inputs(N, H, 128, 128, dt, seed=702 + N).h0
+    fd = f.to(dev)
+    zd, wd = z.to(dev), w.to(dev)
+    xs = (fd.x_q, fd.x_k, fd.x_v, fd.x_z, fd.x_b)
+    taps = (fd.w_q, fd.w_k, fd.w_v, fd.z_bias, fd.A)
+    _say(f"layer decode N={N} H={H} {dt}")
+    S1, conv1 = S0.to(dev), fd.conv_in.clone()
+    y1, o1 = kda_decode_step_layer(*xs, *taps, conv1, S1, zd, wd, g_min=G_MIN,
+                                   norm_eps=EPS_NORM, eps=EPS_RMS, want_o=True)
+    S2, conv2 = S0.to(dev), fd.conv_in.clone()
+    ones = torch.arange(N + 1, dtype=torch.int32, device=dev)
+    q, k, v, g, beta, _ = kda_frontend(*xs, *taps, G_MIN, EPS_NORM, cu_seqlens=ones,
+                                       conv_in=conv2, conv_out=conv2)
+    o2, y2 = kda_decode_step_gated(q, k, v, g, beta, S2, zd, wd, eps=EPS_RMS)
+    torch.cuda.synchronize()
+    assert torch.equal(conv1, conv2), "the convolution state moves on the same way"
+    # the oracle's chain in float64 on a sample of (sequence, head) units
+    rng = np.random.default_rng(N)
+    units = sorted(set(map(tuple, rng.integers(0, [N, H], size=(min(96, N * H), 2)).tolist())) |
+                   {(N - 1, H - 1)})
+    ns, hs = [u[0] for u in units], [u[1] for u in units]
+    fq, fk, fv, fg, fb, conv_ref = oracle_mod.frontend(
+        to64(f.x_q), to64(f.x_k), to64(f.x_v), to64(f.x_z), to64(f.x_b), to64(f.w_q),
+        to64(f.w_k), to64(f.w_v), to64(f.z_bias), to64(f.A), G_MIN, f.cu_seqlens.tolist(),
+        to64(f.conv_in), EPS_NORM)
+    assert np.array_equal(to64(conv1), conv_ref)
+    sel = lambda a: a[ns, hs][:, None]
+    o_ref, S_ref = oracle_mod.decode_step(sel(fq), sel(fk), sel(fv), sel(fg), fb[ns, hs][:, None],
+                                          to64(S0[ns, hs])[:, None])
+    y_ref = oracle_mod.output_gate(o_ref[:, 0], to64(z[ns, hs]), to64(w), EPS_RMS)
+    eo = err(to64(o1[ns, hs]), o_ref[:, 0])
+    ey = err(to64(y1[ns, hs]), y_ref)
+    es = err(to64(S1[ns, hs]), S_ref[:, 0])
+    eo2, ey2 = err(to64(o2[ns, hs]), o_ref[:, 0]), err(to64(y2[ns, hs]), y_ref)
+    es2 = err(to64(S2[ns, hs]), S_ref[:, 0])
+    d = err(to64(y1), to64(y2))
+    _say(f"  one launch: error o={eo:.3e} y={ey:.3e} S={es:.3e}; three launches: o={eo2:.3e} "
+         f"y={ey2:.3e} S={es2:.3e}; between them {d:.3e}")
+    assert eo <= TOL[dt] and ey <= TOL[dt] and es <= TOL[dt], (eo, ey, es)
+    assert eo2 <= TOL[dt] and ey2 <= TOL[dt] and es2 <= TOL[dt], (eo2, ey2, es2)
+    if dt == "f32":
+        assert d <= 1e-4, d
