@@ -79,6 +79,13 @@ def prefill_flops(x) -> int:
     return x.total_tokens * x.H * (6 * x.dk * x.dv + d * (5 * CHUNK - 1))
 
 
+def decode_layer_bytes(N, H) -> int:
+    """kda_decode_step_layer (dk = dv = 128, bf16): per (sequence, head) the state in and out, the
+    pre-activations, the saved inputs in and out, gate and y; the taps, bias, A and gain once."""
+    per_unit = 2 * 128 * 128 * 4 + (3 * 128 + 128) * 2 + 2 + 2 * 3 * 384 * 2 + 2 * 128 * 2
+    return N * H * per_unit + H * (384 * 16 + 128 * 4 + 4) + 128 * 4
+
+
 def decode_bytes(d) -> int:
     es = _esize(d.dtype)
     per = 2 * d.dk * d.dv * 4 + (3 * d.dk + 2 * d.dv) * es + es
@@ -156,8 +163,14 @@ def traffic_pass(dev):
     _, dz, dw = (t.to(dev) for t in inputs.make_output_gate_inputs(256, 96, 128, "bf16", 62))
     for _ in range(3):
         kda_decode_step_gated(qd, kd, vd, gd, bd, S, dz, dw, 1e-6)
+    from linear_attention_recurrence_08_amd import kda_decode_step_layer
+    fr = inputs.make_frontend_inputs([1] * 256, 96, 128, 128, "bf16", seed=653,
+                                     with_state=True).to(dev)
+    for _ in range(3):
+        kda_decode_step_layer(fr.x_q, fr.x_k, fr.x_v, fr.x_z, fr.x_b, fr.w_q, fr.w_k, fr.w_v,
+                              fr.z_bias, fr.A, fr.conv_in, S, dz, dw)
     torch.cuda.synchronize()
-    del qd, kd, vd, gd, bd, S, dz, dw
+    del qd, kd, vd, gd, bd, S, dz, dw, fr
     og, gz, gw = (t.to(dev) for t in inputs.make_output_gate_inputs(4096, 96, 128, "bf16", 61))
     for _ in range(3):
         kda_output_gate(og, gz, gw, 1e-6)
@@ -180,10 +193,13 @@ SUMMARY_KERNELS = {
                             "prefill_T4096_H96_d128_bf16"),
     "kda_c64_carry_kernel<1>": ("kda_chunk_fwd_chunk64_prefill_T4096_H96_d128_bf16",
                                 "prefill_T4096_H96_d128_bf16"),
-    "kda_decode_d128_kernel<unsigned short, 2, false>": ("kda_decode_decode_N256_H96_d128_bf16",
-                                                         "decode_N256_H96_d128_bf16"),
-    "kda_decode_d128_kernel<unsigned short, 2, true>": (
+    "kda_decode_d128_kernel<unsigned short, 2, false, false>": (
+        "kda_decode_decode_N256_H96_d128_bf16", "decode_N256_H96_d128_bf16"),
+    "kda_decode_d128_kernel<unsigned short, 2, true, false>": (
         "kda_decode_step_gated_decode_N256_H96_d128_bf16", "decode_gated_N256_H96_d128_bf16"),
+    # the whole mixer's decode step in one launch (input stage, decode, output stage)
+    "kda_decode_d128_kernel<unsigned short, 2, true, true>": (
+        "kda_decode_step_layer_decode_N256_H96_d128_bf16", "decode_layer_N256_H96_d128_bf16"),
     "kda_output_gate_kernel<unsigned short>": ("kda_output_gate_T4096_H96_d128_bf16",
                                                "output_gate_T4096_H96_d128_bf16"),
     # the input stage: one kernel streams q, k, v and the gates, a second saves the conv state
@@ -194,11 +210,40 @@ SUMMARY_KERNELS = {
 }
 
 
+# Kernels that other timed entries of the same bench run launch at other sizes (the serving
+# step's 4 sequences, the one-launch decode's three-launch comparison): their summaries keep the
+# dispatches of their own workload, told apart by the grid (threads in x and y).
+SUMMARY_GRIDS = {
+    "kda_decode_d128_kernel<unsigned short, 2, false, false>": (256 * 96 // 2 * 256, 1),
+    "kda_decode_d128_kernel<unsigned short, 2, true, false>": (256 * 96 // 2 * 256, 1),
+    "kda_decode_d128_kernel<unsigned short, 2, true, true>": (256 * 96 // 2 * 256, 1),
+    "kda_frontend_conv_kernel<unsigned short, true>": (4096 // 128 * 96 * 64, 4),
+    "kda_frontend_state_kernel<unsigned short>": (96 * 384, 1),
+}
+
+
+def _dispatch_stats(trace_csvs, frag, grid):
+    """Calls, mean, min, max and total duration (ns) of the dispatches of one kernel with the
+    given grid, from rocprofv3 kernel-trace rows; None without any."""
+    import csv
+    durs = []
+    for f in trace_csvs:
+        for r in csv.DictReader(open(f)):
+            if frag in r["Kernel_Name"] and (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"])) == grid:
+                durs.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    if not durs:
+        return None
+    return {"Calls": str(len(durs)), "AverageNs": sum(durs) / len(durs), "MinNs": min(durs),
+            "MaxNs": max(durs), "TotalDurationNs": sum(durs)}
+
+
 def _algorithmic_bytes(workload):
     from linear_attention_recurrence_08_amd import inputs
     tok_head = 4096 * 96
     if workload == "decode_gated_N256_H96_d128_bf16":
         return 256 * 96 * (2 * 128 * 128 * 4 + (3 * 128 + 2 * 128) * 2 + 2 + 2 * 128 * 2) + 512
+    if workload == "decode_layer_N256_H96_d128_bf16":
+        return decode_layer_bytes(256, 96)
     if workload == "output_gate_T4096_H96_d128_bf16":
         return 3 * tok_head * 128 * 2 + 128 * 4
     if workload == "frontend_T4096_H96_d128_bf16":
@@ -230,11 +275,17 @@ def summarize(dirs, command, workload=None):
     trace = {}        # tag -> list of (fragment, stats row)
     counters = {}     # (fragment or "copy", counter) -> list of per-dispatch values (KiB)
     for d in dirs:
+        per_dispatch = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
         for f in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 for frag, (tag, _) in kernels.items():
                     if frag in r["Name"]:
-                        trace.setdefault(tag, []).append((frag, r))
+                        row = r
+                        if frag in SUMMARY_GRIDS and workload is None:
+                            row = _dispatch_stats(per_dispatch, frag, SUMMARY_GRIDS[frag])
+                            if row is None:
+                                continue
+                        trace.setdefault(tag, []).append((frag, row))
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
                 name = r["Kernel_Name"]
@@ -1014,11 +1065,7 @@ def main():
 
                 lms, _ = time_launches(decode_layer, ksteps, args.warmup, stream)
                 l3ms, _ = time_launches(decode_three, ksteps, args.warmup, stream)
-                # per (sequence, head): the state in and out, the pre-activations, the saved
-                # inputs in and out, gate and y; the taps, bias, A and gain once
-                per_unit = (2 * 128 * 128 * 4 + (3 * 128 + 128) * 2 + 2 + 2 * 3 * 384 * 2 +
-                            2 * 128 * 2)
-                lbytes = 256 * 96 * per_unit + 96 * (384 * 16 + 128 * 4 + 4) + 128 * 4
+                lbytes = decode_layer_bytes(256, 96)
                 result["decode"]["layer"] = {
                     "entry": "kda_decode_step_layer", "ms_per_step": round(lms, 5),
                     "value": round(256 / (lms * 1e-3), 1), "unit": "tokens/s",
@@ -1028,6 +1075,8 @@ def main():
                                  "achieved": round(lbytes / (lms * 1e-3) / 1e9, 1),
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": round(lbytes / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "traffic": recorded_traffic(
+                                     "kda_decode_step_layer_decode_N256_H96_d128_bf16"),
                                  "kernel": "kda_decode_d128 (input and output stages)",
                                  "algorithmic_bytes_per_launch": lbytes},
                 }

@@ -108,3 +108,37 @@ def test_split_summary_lists_every_kernel_of_the_call(tmp_path, monkeypatch):
 def test_cpu_model_is_read():
     m = bench._cpu_model()
     assert isinstance(m, str) and m
+
+
+def test_trace_summary_keeps_its_workloads_dispatches(tmp_path, monkeypatch):
+    """A kernel that other timed entries launch at other sizes in the same run (the decode at 4
+    sequences in the serving step) is summarised from its own workload's dispatches only, told
+    apart by the grid."""
+    name = "void kda::(anonymous namespace)::kda_decode_d128_kernel<unsigned short, 2, true, true>(x)"
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "t_kernel_stats.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs",
+                                          "TotalDurationNs"])
+        w.writeheader()
+        w.writerow({"Name": name, "Calls": 4, "AverageNs": 300, "MinNs": 10, "MaxNs": 600,
+                    "TotalDurationNs": 1200})
+    big = bench.SUMMARY_GRIDS[name.split("::")[-1].split("(")[0]]
+    with open(d / "t_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp",
+                                          "Grid_Size_X", "Grid_Size_Y"])
+        w.writeheader()
+        for start, dur, grid in ((0, 500, big), (1000, 600, big), (2000, 10, (49152, 1)),
+                                 (3000, 90, (49152, 1))):
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": start,
+                        "End_Timestamp": start + dur, "Grid_Size_X": grid[0],
+                        "Grid_Size_Y": grid[1]})
+    out = tmp_path / "repo"
+    (out / "profiles").mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(out))
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda tag: "0123456789abcdef")
+    bench.summarize([str(d)], "test command")
+    txt = open(out / "profiles" /
+               "kda_decode_step_layer_decode_N256_H96_d128_bf16_kernel_trace.md").read()
+    row = [l for l in txt.splitlines() if l.startswith("| kda_decode_d128_kernel")][0]
+    assert [c.strip() for c in row.split("|")[2:7]] == ["2", "550", "500", "600", "1100"]
