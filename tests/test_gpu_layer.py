@@ -253,3 +253,27 @@ def test_layer_decode_step_against_oracle(oracle_mod, N, H, dt):
     assert eo2 <= TOL[dt] and ey2 <= TOL[dt] and es2 <= TOL[dt], (eo2, ey2, es2)
     if dt == "f32":
         assert d <= 1e-4, d
+
+
+def test_layer_decode_step_y_aliases_gate():
+    """kda_decode_step_layer may write y over the gate (each element is read before it is
+    overwritten) and over o; the results are those of separate buffers."""
+    from linear_attention_recurrence_08_amd import inputs, kda_decode_step_layer
+    dev = _dev()
+    N, H = 6, 32
+    f = inputs.make_frontend_inputs([1] * N, H, 128, 128, "bf16", seed=710,
+                                    with_state=True).to(dev)
+    _, z, w = (t.to(dev) for t in inputs.make_output_gate_inputs(N, H, 128, "bf16", 711))
+    S0 = inputs.make_decode_inputs(N, H, 128, 128, "bf16", seed=712).h0.to(dev)
+    args = (f.x_q, f.x_k, f.x_v, f.x_z, f.x_b, f.w_q, f.w_k, f.w_v, f.z_bias, f.A)
+    S1, c1 = S0.clone(), f.conv_in.clone()
+    y_sep, o_sep = kda_decode_step_layer(*args, c1, S1, z, w, want_o=True)
+    S2, c2, z2 = S0.clone(), f.conv_in.clone(), z.clone()
+    y_al, _ = kda_decode_step_layer(*args, c2, S2, z2, w, y=z2)
+    S3, c3, z3 = S0.clone(), f.conv_in.clone(), z.clone()
+    o3 = torch.empty_like(z)
+    y_o, o_o = kda_decode_step_layer(*args, c3, S3, z3, w, o=o3, y=o3)
+    torch.cuda.synchronize()
+    assert y_al.data_ptr() == z2.data_ptr() and torch.equal(y_al, y_sep)
+    assert y_o.data_ptr() == o3.data_ptr() and torch.equal(y_o, y_sep)
+    assert torch.equal(S1, S2) and torch.equal(S1, S3) and torch.equal(c1, c2)

@@ -300,3 +300,37 @@ def test_past_4gib_decode_states(oracle_mod):
     eo, es = err(sel(o), o_ref), err(sel(S), S_ref)
     _say(f"  error o={eo:.3e} S={es:.3e}")
     assert eo <= TOL and es <= TOL, (eo, es)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("N,H", [(2, WIDE_H), (700, BIG_H)], ids=["widest_rows", "past_4gib"])
+def test_layer_decode_at_the_limits(oracle_mod, N, H):
+    """kda_decode_step_layer (input stage, decode step and output stage in one launch) on rows of
+    2^20 values, and over 4.4 GB of states; sampled heads against the oracle's chain."""
+    from linear_attention_recurrence_08_amd import kda_decode_step_layer
+    dev = _dev()
+    gen = torch.Generator(device=dev).manual_seed(520 + N)
+    xs = [_draw((N, H, 128), gen, "normal", dev) for _ in range(4)]
+    xs.append(_draw((N, H), gen, "normal", dev))
+    taps = _front_weights(H, gen, dev)
+    conv = _draw((N, 3, H * 384), gen, "normal", dev)
+    S = _draw((N, H, 128, 128), gen, "state", dev, torch.float32)
+    z = _draw((N, H, 128), gen, "normal", dev)
+    w = (1.0 + 0.1 * torch.randn(128, generator=gen, device=dev)).float()
+    heads = [0, H // 2, H - 1]
+    ch = torch.tensor([h * 128 + c for h in heads for c in range(128)], device=dev)
+    cols = torch.cat([ch, H * 128 + ch, 2 * H * 128 + ch])
+    conv_in, S_in = to64(conv[:, :, cols]), to64(S[:, heads])
+    _say(f"layer decode at the limits: N={N} H={H} (states {S.numel() * 4 / 1e9:.2f} GB)")
+    y, o = kda_decode_step_layer(*xs, *taps, conv, S, z, w, want_o=True)
+    torch.cuda.synchronize()
+    fq, fk, fv, fg, fb, conv_ref = oracle_mod.frontend(
+        *(to64(x[:, heads]) for x in xs), *(to64(t[ch]) for t in taps[:4]),
+        to64(taps[4][heads]), -5.0, list(range(N + 1)), conv_in, 1e-6)
+    o_ref, S_ref = oracle_mod.decode_step(fq, fk, fv, fg, fb, S_in)
+    y_ref = oracle_mod.output_gate(o_ref, to64(z[:, heads]), to64(w), 1e-6)
+    eo, ey = err(to64(o[:, heads]), o_ref), err(to64(y[:, heads]), y_ref)
+    es = err(to64(S[:, heads]), S_ref)
+    _say(f"  error o={eo:.3e} y={ey:.3e} S={es:.3e}")
+    assert eo <= TOL and ey <= TOL and es <= TOL, (eo, ey, es)
+    assert np.array_equal(to64(conv[:, :, cols]), conv_ref)
