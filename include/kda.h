@@ -134,9 +134,6 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g, co
  *   o         [Ttot, H, dv]  dtype    device      the mixer output (written); NULL = not wanted
  *   y         [Ttot, H, dv]  dtype    device      the gated output (written)
  * gate, y and o (when given) must be 16-byte aligned (KDA_ERR_ALIGN); y may alias o or gate.
- * Inside the kernel the four waves that share a row wait for each other's sums; each wait is
- * bounded (KDA_GATE_SPIN_LIMIT polls, default 2^22, an environment setting for tests), and a wait
- * that runs out leaves that tile's y NaN.
  * Returns KDA_OK or a negative status; nothing is written on an argument error.
  */
 int kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void* g,

@@ -221,10 +221,6 @@ int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g, c
     a.h0 = h0; a.cu = cu_seqlens; a.o = o; a.hT = hT;
     if (fused) {
         a.gate = gs->gate; a.weight = gs->weight; a.eps = gs->eps; a.y = gs->y;
-        // KDA_GATE_SPIN_LIMIT bounds the waits of the in-kernel row reduction (tests force a
-        // wait to run out with 0; such a tile's y is NaN)
-        if (const char* e = std::getenv("KDA_GATE_SPIN_LIMIT"))
-            a.arrive_spin = std::max<int64_t>(0, std::atoll(e));
     }
     a.N = N; a.T = cu_seqlens ? 0 : T; a.H = H; a.dk = dk; a.dv = dv; a.dtype = dtype;
     if (want_snaps && snaps) {

@@ -44,7 +44,6 @@ struct PrefillArgs {
     const float* weight = nullptr;       // [dv] or nullptr (ones)
     float eps = 0.f;
     void* y = nullptr;                   // [Ttot, H, dv]
-    int64_t arrive_spin = 1 << 22;       // bound on the polls of one wait of the row reduction
 };
 
 struct DecodeArgs {

@@ -252,17 +252,17 @@ struct Shared {
 // sigmoid(gate) per (token, head) row ("Kimi K3's hybrid block, from first principles", section
 // "From linear attention to the delta rule": each head's output row is normalised by its root
 // mean square and scaled by a sigmoid gate of the token before the output projection).  Stage A
-// loads the gate of tile j - 3 with the inputs of tile j and, in period j, leaves w * sigmoid(gate)
-// (bf16) for the stage-S wave and lane that hold those columns of o; stage S finishes tile j - 3
-// in period j + 1.  The row's sum of squares spans the four stage-S waves: each adds its 32
-// columns, leaves the sum in ssq, and waits until all four have arrived for this tile (an LDS
-// counter; the waves run the same tiles in the same period, so the wait only covers their skew).
+// loads the gate of tile j - 4 with the inputs of tile j and, in period j, leaves w * sigmoid(gate)
+// (bf16) for the stage-S wave and lane that hold those columns of o.  The row's sum of squares
+// spans the four stage-S waves: in the period that forms tile j's o (period j + 4) each adds its
+// 32 columns and leaves the sum in ssq; in the next period, after the barrier that orders those
+// writes, each reads the four sums and finishes tile j's y from the o it kept in registers.  No
+// wave waits for another outside the pipeline's own barrier.
 struct GateLds {
     uint4 gw[2][4][64];     // by tile % 2, stage-S wave, lane: bf16 w * sigmoid(gate) of token ln,
                             // columns 16 s + 4 lg + r (.xy) and 64 + 16 s + 4 lg + r (.zw)
-    float ssq[C][4];        // per token of the tile: the stage-S waves' sums of o^2
+    float ssq[2][C][4];     // by tile % 2, token of the tile: the stage-S waves' sums of o^2
     float w[D];             // the gain per column (ones without one)
-    uint32_t arrive;        // stage-S arrivals: 4 per tile
 };
 
 // PRIO_ROLE: the role whose waves win issue ties on their SIMD (1: stage A, 2: stage B).
@@ -324,7 +324,6 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     if constexpr (GATED) {
         // read before the first barrier of every role; the first use comes three periods later
         if (tid < D) gsh.w[tid] = a.weight ? a.weight[tid] : 1.f;
-        if (tid == 0) gsh.arrive = 0u;
     }
 
     // ---- constant fragments ----
@@ -445,9 +444,9 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         for (int m = 0; m < NS; ++m) R.v[m] = ld8(rv, vo_v + 128 * m);
         R.b = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, vo_b, 0, 0);
         if constexpr (GATED) {
-            // the gate of tile ld_tile - 3, at the columns of v (zeros before the first tile
+            // the gate of tile ld_tile - 4, at the columns of v (zeros before the first tile
             // and past the sequence end)
-            const int gt = ld_tile - 3;
+            const int gt = ld_tile - 4;
             const int nvg = gt < 0 ? 0 : min(max(len32 - gt * C, 0), C);
             const int nrecg = max((nvg - 1) * rb32 + D * 2, 0);
             const int64_t tg0 = bos + min((int64_t)max(gt, 0) * C, len);
@@ -691,9 +690,10 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             for (int m = 0; m < NS; ++m) *reinterpret_cast<uint2*>(dst + 64 * m) = as_u2(Ot[m]);
         }
     };
-    // fused output stage, stage S's part for tile `tile`: the row norm over the four stage-S
-    // waves, then y from o (as rounded to bf16, as stored) and stage A's w * sigmoid(gate)
-    auto y_step = [&](int64_t tile, const bf16x4 (&Ot)[NS], bool masked) {
+    // fused output stage, stage S's part.  In the period that forms tile t's o: this wave's sum of
+    // o^2 per token (as rounded to bf16, as stored) into ssq.  In the next period: the four sums,
+    // then y from the o kept in registers and stage A's w * sigmoid(gate).
+    auto ssq_step = [&](int64_t tile, const bf16x4 (&Ot)[NS]) {
         if constexpr (GATED) {
             float ss = 0.f;
 #pragma unroll
@@ -705,30 +705,20 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             // the four lane groups hold the same token (columns 4 lg .. 4 lg + 3 of each strip)
             ss += __shfl_xor(ss, 16);
             ss += __shfl_xor(ss, 32);
-            if (lg == 0) gsh.ssq[ln][s] = ss;
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the sum is in LDS
-            if (lane == 0)
-                __hip_atomic_fetch_add(&gsh.arrive, 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-            const uint32_t want = 4u * (uint32_t)(tile + 1);
-            bool arrived = false;
-            for (int64_t it = 0; it < a.arrive_spin && !arrived; ++it) {
-                arrived = __hip_atomic_load(&gsh.arrive, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_WORKGROUP) >= want;
-                if (!arrived) __builtin_amdgcn_s_sleep(1);
-            }
-            asm volatile("" ::: "memory");   // the sums are read after the arrivals are seen
-            const f32x4 sq = *reinterpret_cast<const f32x4*>(&gsh.ssq[ln][0]);
-            // a wait that ran out leaves the tile's y NaN rather than normalised by a partial sum
-            const float rn = arrived ? __builtin_amdgcn_rsqf((sq[0] + sq[1] + sq[2] + sq[3]) /
-                                                             (float)D + a.eps)
-                                     : __builtin_nanf("");
+            if (lg == 0) gsh.ssq[(uint32_t)tile & 1u][ln][s] = ss;
+        }
+    };
+    auto y_finish = [&](int64_t tile, const bf16x4 (&Ot)[NS]) {
+        if constexpr (GATED) {
+            const f32x4 sq = *reinterpret_cast<const f32x4*>(&gsh.ssq[(uint32_t)tile & 1u][ln][0]);
+            const float rn = __builtin_amdgcn_rsqf((sq[0] + sq[1] + sq[2] + sq[3]) / (float)D +
+                                                   a.eps);
             const uint4 gwv = gsh.gw[(uint32_t)tile & 1u][s][lane];
             const uint2 gwm[2] = {make_uint2(gwv.x, gwv.y), make_uint2(gwv.z, gwv.w)};
             // stored through a buffer resource at the tile's first token row: a scalar base, the
             // lane offset computed once, and a record count that drops tokens past the end
             const int64_t t0 = bos + tile * C;
-            const int nv = masked ? (int)min(max(eos - t0, (int64_t)0), (int64_t)C) : C;
+            const int nv = (int)min(max(eos - t0, (int64_t)0), (int64_t)C);
             const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(y + t0 * H * D), (short)0, nv * rb32, kBufferFlags);
 #pragma unroll
@@ -763,21 +753,29 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         stage_a(1, R1);
         load_tile(R1);     // tile 3
         lds_barrier();
-        // (with the fused output stage, the gate of tile j - 3 rides with tile j's inputs and is
-        // turned into w * sigmoid(gate) in period j, one period before stage S finishes tile j - 3)
+        // (with the fused output stage, the gate of tile j - 4 rides with tile j's inputs and is
+        // turned into w * sigmoid(gate) in period j, one period before stage S finishes tile j - 4)
         for (int64_t i = 0; i < nsteps; i += 2) {
             stage_a(i + 2, R0);
-            gate_step(i - 1, R0);
+            gate_step(i - 2, R0);
             load_tile(R0);     // tile i + 4
             lds_barrier();
             stage_a(i + 3, R1);
-            gate_step(i, R1);
+            gate_step(i - 1, R1);
             load_tile(R1);     // tile i + 5
             lds_barrier();
         }
-        gate_step(nsteps - 1, R0);
-        lds_barrier();
-        lds_barrier();
+        if constexpr (GATED) {
+            // the gates of the last two tiles; one more period for stage S to finish the last y
+            gate_step(nsteps - 2, R0);
+            lds_barrier();
+            gate_step(nsteps - 1, R1);
+            lds_barrier();
+            lds_barrier();
+        } else {
+            lds_barrier();
+            lds_barrier();
+        }
     } else if (role == 2) {
         // with few workgroups the chain through stage B paces the period instead
         if (PRIO_ROLE == 2) __builtin_amdgcn_s_setprio(1);
@@ -804,6 +802,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             b2_at(q);
             lds_barrier();
         }
+        if constexpr (GATED) lds_barrier();   // stage S finishes the last y one period later
     } else {
         state_in(h_in, part_m);
         lds_barrier();
@@ -817,12 +816,17 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         // tiles whose 16 tokens all lie inside the sequence store without a mask
         const int64_t nfull = (eos - bos) / C;
         int64_t i = 0;
-        bf16x4 Ot[NS];
+        bf16x4 Ot[NS], Oprev[NS];   // Oprev: the previous tile's o, whose y is finished next
         if constexpr (kPre) decay(0);
         for (; i < nfull; ++i) {
             stage_s(i, Ot);
             store_o(i, Ot, false);
-            y_step(i, Ot, false);
+            if constexpr (GATED) {
+                ssq_step(i, Ot);
+                if (i > 0) y_finish(i - 1, Oprev);
+#pragma unroll
+                for (int m = 0; m < NS; ++m) Oprev[m] = Ot[m];
+            }
             if (!GATED && i + 1 == snap_at) {
                 state_out(a.snaps + (snap_idx * H + h) * (int64_t)(D * D));
                 ++snap_idx;
@@ -834,8 +838,17 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         for (; i < nsteps; ++i) {
             stage_s(i, Ot);
             store_o(i, Ot, true);
-            y_step(i, Ot, true);
+            if constexpr (GATED) {
+                ssq_step(i, Ot);
+                if (i > 0) y_finish(i - 1, Oprev);
+#pragma unroll
+                for (int m = 0; m < NS; ++m) Oprev[m] = Ot[m];
+            }
             if constexpr (kPre) if (i + 1 < nsteps) decay(i + 1);
+            lds_barrier();
+        }
+        if constexpr (GATED) {
+            if (nsteps > 0) y_finish(nsteps - 1, Oprev);
             lds_barrier();
         }
         if (h_out) state_out(h_out);

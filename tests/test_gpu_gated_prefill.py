@@ -187,23 +187,3 @@ def test_gated_prefill_varlen_16seq_H96(oracle_mod):
     eh = err(to64(hT[:, heads]), h_ref)
     _say(f"  heads {heads}: error stage {es:.3e}, end to end {ey:.3e}, hT {eh:.3e}")
     assert es <= TOL["bf16"] and ey <= TOL["bf16"] and eh <= TOL["bf16"], (es, ey, eh)
-
-
-def test_gated_prefill_reduction_wait_that_runs_out(monkeypatch):
-    """The in-kernel row reduction's waits are bounded: forced to run out at once
-    (KDA_GATE_SPIN_LIMIT=0, set from the host; every wave still exits normally), every y is NaN,
-    while o and hT, which do not depend on the reduction, are still exact."""
-    from linear_attention_recurrence_08_amd import inputs, kda_chunk_fwd, kda_chunk_fwd_gated
-    dev = _dev()
-    x = inputs.make_inputs([64, 40, 23, 80], 64, 128, 128, "bf16", seed=6, h0_sigma=0.1)
-    z, w = _gate_inputs(x, seed=10)
-    xd = x.to(dev)
-    zd, wd = _on_device(xd, z, dev), w.to(dev)
-    monkeypatch.setenv("KDA_GATE_SPIN_LIMIT", "0")
-    y, o, hT = kda_chunk_fwd_gated(*xd.call_views(), zd, weight=wd, h0=xd.h0,
-                                   cu_seqlens=xd.cu_seqlens, want_o=True)
-    monkeypatch.delenv("KDA_GATE_SPIN_LIMIT")
-    o_plain, h_plain = kda_chunk_fwd(*xd.call_views(), h0=xd.h0, cu_seqlens=xd.cu_seqlens)
-    torch.cuda.synchronize()
-    assert torch.isnan(y.float()).all()
-    assert torch.equal(o, o_plain) and torch.equal(hT, h_plain)
