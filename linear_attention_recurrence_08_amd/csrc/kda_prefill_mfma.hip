@@ -39,6 +39,8 @@
 //   stage S (waves 0-3) for tile q-4: wave s carries its 128 x 16 strip of S (two strips in the
 //      128-column slice), which lives in registers as eight 16x16 float32 accumulator blocks per
 //      strip for the whole sequence, and writes o.
+// (The wave numbers are those of the 64-column kernel; the plain 128-column kernel rotates the
+// roles by one group of four: stage A on waves 0-3, B on 4-7, S on 8-11.)
 // Three waves share each SIMD.  Loads run two tiles ahead of their use.  All products use
 // v_mfma_f32_16x16x{16,32}_bf16.  Token-major -> channel-major changes of layout are LDS transpose
 // reads where the data already sits in LDS, and a product with a 0/1 selector matrix on the
@@ -276,7 +278,13 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
     const int lane = tid & 63, ln = lane & 15, lg = lane >> 4;
-    const int role = wave >> 2;        // 0: stage S, 1: stage A, 2: stage B
+    // 0: stage S, 1: stage A, 2: stage B.  Wave slots 0-3 hold stage S, except in the plain
+    // 128-column kernel, where they hold stage A and stage S takes slots 8-11.  The same code
+    // in a different wave order measured: 64 columns at H = 96, 1% faster with S first; plain
+    // 128 columns on the 16-sequence batch, 2.5% faster with A first (neutral at 4 x 4096
+    // tokens); 128 columns with the output stage, 0.4% faster with S first.
+    constexpr int kRoleShift = (BVT == 128 && !GATED) ? 1 : 0;
+    const int role = ((wave >> 2) + kRoleShift) % 3;
     const int s = wave & 3;            // channel group / strip index of this wave
     const int64_t H = a.H;
 
