@@ -19,6 +19,7 @@ namespace {
 int g_launches = 0;               // launcher calls since the last reset
 const char* g_last = "";          // name of the last launcher called
 kda::PrefillArgs g_prefill;       // arguments of the last prefill launch
+kda::DecodeArgs g_decode;         // arguments of the last decode launch
 int64_t g_c64_chunks = -1;
 
 void reset() {
@@ -41,8 +42,8 @@ hipError_t launch_prefill_c64(const PrefillArgs& a, hipStream_t) {
 hipError_t launch_split_finish(const PrefillArgs& a, hipStream_t) {
     ++g_launches; g_last = "split_finish"; g_prefill = a; return hipSuccess;
 }
-hipError_t launch_decode_d128(const DecodeArgs&, hipStream_t) {
-    ++g_launches; g_last = "decode_d128"; return hipSuccess;
+hipError_t launch_decode_d128(const DecodeArgs& a, hipStream_t) {
+    ++g_launches; g_last = "decode_d128"; g_decode = a; return hipSuccess;
 }
 hipError_t launch_output_gate(const GateArgs&, hipStream_t) {
     ++g_launches; g_last = "output_gate"; return hipSuccess;
@@ -404,6 +405,45 @@ void test_frontend() {
     EXPECT(fe(-5.f, bad.data(), 2, 1, xq.data()) == KDA_ERR_SEQLENS && g_launches == 0);
     set_validate(false);
 }
+void test_layer_decode() {
+    const int N = 3, H = 2, d = 128;
+    std::vector<uint16_t> xq(N * H * d), xk(N * H * d), xv(N * H * d), xz(N * H * d), xb(N * H),
+        gate(N * H * d + 8), o(N * H * d + 8), y(N * H * d + 8), conv(N * 3 * H * 3 * d);
+    std::vector<float> wq(H * d * 4), wk(H * d * 4), wv(H * d * 4), zb(H * d), A(H),
+        S(N * H * d * d + 4);
+    auto lay = [&](float gmin, float eps, void* cs, float* s, void* gt, void* oo, void* yy, int dk,
+                   int n) {
+        reset();
+        return kda_decode_step_layer(xq.data(), xk.data(), xv.data(), xz.data(), xb.data(),
+                                     wq.data(), wk.data(), wv.data(), zb.data(), A.data(), gmin,
+                                     1e-6f, cs, s, gt, nullptr, eps, oo, yy, n, H, dk, dk,
+                                     KDA_BF16, nullptr);
+    };
+    EXPECT(lay(-5.f, 1e-6f, conv.data(), S.data(), gate.data(), nullptr, y.data(), d, N) ==
+               KDA_OK &&
+           g_launches == 1 && std::strcmp(g_last, "decode_d128") == 0);
+    // one launch carrying the input stage and the output stage; no q, k, v, g or beta buffers
+    EXPECT(g_decode.xq == xq.data() && g_decode.xb == xb.data() && g_decode.conv == conv.data() &&
+           g_decode.gate == gate.data() && g_decode.y == y.data() && g_decode.o == nullptr &&
+           g_decode.q == nullptr && g_decode.beta == nullptr && g_decode.g_min == -5.f);
+    EXPECT(lay(-5.f, 1e-6f, conv.data(), S.data(), gate.data(), o.data(), y.data(), d, N) ==
+               KDA_OK && g_decode.o == o.data());
+    EXPECT(lay(-5.f, 1e-6f, conv.data(), S.data(), gate.data(), nullptr, y.data(), 64, N) ==
+               KDA_ERR_UNSUPPORTED && g_launches == 0);
+    EXPECT(lay(0.f, 1e-6f, conv.data(), S.data(), gate.data(), nullptr, y.data(), d, N) ==
+               KDA_ERR_RANGE && g_launches == 0);
+    EXPECT(lay(-5.f, -1.f, conv.data(), S.data(), gate.data(), nullptr, y.data(), d, N) ==
+               KDA_ERR_RANGE && g_launches == 0);
+    EXPECT(lay(-5.f, 1e-6f, nullptr, S.data(), gate.data(), nullptr, y.data(), d, N) ==
+               KDA_ERR_NULL && g_launches == 0);
+    EXPECT(lay(-5.f, 1e-6f, conv.data(), S.data() + 1, gate.data(), nullptr, y.data(), d, N) ==
+               KDA_ERR_ALIGN && g_launches == 0);
+    unsigned char* y2 = reinterpret_cast<unsigned char*>(y.data()) + 2;
+    EXPECT(lay(-5.f, 1e-6f, conv.data(), S.data(), gate.data(), nullptr, y2, d, N) ==
+               KDA_ERR_ALIGN && g_launches == 0);
+    EXPECT(lay(-5.f, 1e-6f, nullptr, nullptr, nullptr, nullptr, nullptr, d, 0) == KDA_OK &&
+           g_launches == 0);
+}
 }  // namespace
 
 int main() {
@@ -418,6 +458,7 @@ int main() {
     test_decode_and_stages();
     test_gated_prefill();
     test_frontend();
+    test_layer_decode();
     if (g_failures) {
         std::fprintf(stderr, "%d expectation(s) failed\n", g_failures);
         return 1;
