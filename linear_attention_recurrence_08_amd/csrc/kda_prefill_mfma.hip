@@ -253,7 +253,8 @@ struct Shared {
 // The fused output stage (GATED, one workgroup per head).  y = o / sqrt(mean(o^2) + eps) * w *
 // sigmoid(gate) per (token, head) row ("Kimi K3's hybrid block, from first principles", section
 // "From linear attention to the delta rule": each head's output row is normalised by its root
-// mean square and scaled by a sigmoid gate of the token before the output projection).  Stage A
+// mean square and, ahead of the output projection, scaled by a sigmoid gate computed from the
+// token).  Stage A
 // loads the gate of tile j - 4 with the inputs of tile j and, in period j, leaves w * sigmoid(gate)
 // (bf16) for the stage-S wave and lane that hold those columns of o.  The row's sum of squares
 // spans the four stage-S waves: in the period that forms tile j's o (period j + 4) each adds its

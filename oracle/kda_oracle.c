@@ -24,8 +24,8 @@
  *    and writes only the error, which is one gradient step on 1/2 |S^T k_t - v_t|^2 with step
  *    beta_t; KDA makes the decay one factor per key channel, alpha_t in (0,1)^dk.
  *  - "Kimi K3, explained", section "Kimi Delta Attention: making the radical option work": per
- *    token the update fades the memory, removes the old association for the key and writes the
- *    new value; k and v update S(t-1) and q reads the updated S(t).
+ *    token first weakens what is stored, then clears the entry held for its key, then stores its
+ *    value; k and v update S(t-1) and q reads the updated S(t).
  *  - "What's new in Kimi K3", section "KDA in one page": (I - beta k k^T) erases what the memory
  *    holds for the key before writing, and the forget gate alpha_t sits in front of it.
  * Expanding the fade/erase/write steps gives S_t = (I - b k k^T) Diag(a) S_{t-1} + b k v^T,

@@ -332,8 +332,9 @@ def exact(q, k, v, alpha, beta, h0=None, cu_seqlens=None):
 
 # ---------------------------------------------------------------------------------------------
 # Output stage.  "Kimi K3's hybrid block, from first principles", section "From linear attention
-# to the delta rule": the layer's output is RMS-normalised per head and multiplied by a full-rank
-# sigmoid gate of the token before the output projection.  Per (token, head) row of dv outputs:
+# to the delta rule": each head's output row is divided by its root mean square, then scaled
+# element by element by a sigmoid gate computed at full rank from the token; the output
+# projection comes after.  Per (token, head) row of dv outputs:
 #     y = o / sqrt(mean_c o_c^2 + eps) * w * sigmoid(gate)
 # with w the norm's gain per value channel (ones when not given).
 # ---------------------------------------------------------------------------------------------

@@ -1,7 +1,7 @@
 """GPU parity at the method's edge cases, on every prefill kernel variant.
 
-The log-decay floor: K3 bounds log alpha below by -5, so over a 16-token tile the cumulative
-log-decay stays within (-80, 0), and that bound is what keeps the chunked kernel's rescaling
+The log-decay floor: K3 bounds log alpha below by -5, so the log-decay summed over one 16-token
+tile cannot fall below -80, and that bound is what keeps the chunked kernel's rescaling
 factors finite ("Kimi K3's hybrid block, from first principles", section "From linear attention
 to the delta rule"; "Kimi K3", section "Forgetting different features at different rates").  The
 recipes "floor" (every channel at -5 for every token: whole tiles at -80) and "floor_half" (half

@@ -1,7 +1,8 @@
 """GPU parity of kda_chunk_fwd_gated: the prefill followed by the output stage y = RMSNorm(o) *
 weight * sigmoid(gate) per (token, head) row ("Kimi K3's hybrid block, from first principles",
 section "From linear attention to the delta rule": each head's output row is normalised by its root
-mean square and scaled by a sigmoid gate of the token before the output projection).
+mean square and, ahead of the output projection, scaled by a sigmoid gate computed from the
+token).
 
 Two references, both float64 from the oracle (bar 2e-2 max-normalised for bf16, 1e-4 for
 float32):

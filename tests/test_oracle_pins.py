@@ -272,8 +272,8 @@ def test_brute_force(oracle_mod):
 @pytest.mark.parametrize("T,dk,dv,chunk", [(64, 32, 32, 16), (53, 32, 16, 16), (37, 8, 12, 4),
                                            (16, 16, 16, 16), (1, 8, 8, 16)])
 def test_chunked_form_matches(oracle_mod, T, dk, dv, chunk):
-    """The chunkwise form gives the token loop's result (the pages: the chunked algorithm
-    processes blocks of tokens at once without changing the result)."""
+    """The chunkwise form gives the token loop's result (the pages: handling a whole block of
+    tokens together gives the same outputs as the token loop)."""
     rng = np.random.default_rng(T * 1000 + dk)
     q, k, v, g, beta, S0 = _rand_case(rng, T, 2, dk, dv)
     o, hT = oracle_mod.recurrence(q, k, v, g, beta, S0)
