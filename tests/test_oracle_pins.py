@@ -178,9 +178,9 @@ def pin_brute_force(rec, brute):
 def pin_snapshots(rec):
     """Every saved state is the state that resumes its prefix: snapshot j of sequence n equals, bit
     for bit, the final state of a run over the first 16 j tokens of that sequence alone ("Kimi
-    K3's hybrid block, from first principles", paragraph "The cache, in bytes": a cached prefix is
-    reusable only if the state was saved at exactly that boundary).  Saving snapshots leaves o and
-    hT unchanged."""
+    K3's hybrid block, from first principles", paragraph "The cache, in bytes": a prefix can be
+    resumed only from a state stored at that very token).  Saving snapshots leaves o and hT
+    unchanged."""
     rng = np.random.default_rng(16)
     lens = [37, 0, 32, 15, 48]
     cu = np.concatenate([[0], np.cumsum(lens)])
