@@ -3,6 +3,8 @@ rejects bad arguments with the documented status codes before touching the GPU."
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -480,3 +482,29 @@ def test_gated_prefill_fuses_query(lib):
     assert lib.kda_chunk_fwd_gated_fuses(0, 2, 128, 128, 128, 1, 0) == 0    # float32
     assert lib.kda_chunk_fwd_gated_fuses(0, 2, 128, 64, 128, 0, 0) == 0     # dk = 64
     assert lib.kda_chunk_fwd_gated_fuses(0, -1, 128, 128, 128, 0, 0) == 0
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not found")
+def test_header_is_plain_c(tmp_path, lib):
+    """include/kda.h is a C ABI: a C99 program that includes it compiles with -pedantic -Werror,
+    links against libkda.so and calls it (argument validation only, no GPU)."""
+    src = tmp_path / "use_kda.c"
+    src.write_text(
+        '#include "kda.h"\n#include <stdio.h>\n#include <string.h>\n'
+        "int main(void) {\n"
+        "    if (kda_version() < 100) return 1;\n"
+        "    if (strcmp(kda_status_string(KDA_OK), \"ok\") != 0) return 2;\n"
+        "    /* a NULL q with tokens present is rejected before anything runs */\n"
+        "    if (kda_chunk_fwd(NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL, NULL, 1, 16, 2,\n"
+        "                      128, 128, KDA_BF16, NULL) != KDA_ERR_NULL) return 3;\n"
+        "    puts(\"c ok\");\n"
+        "    return 0;\n"
+        "}\n")
+    libdir = os.path.join(ROOT, "linear_attention_recurrence_08_amd")
+    exe = str(tmp_path / "use_kda")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        "-I", os.path.join(ROOT, "include"), str(src), "-L", libdir, "-lkda",
+                        f"-Wl,-rpath,{libdir}", "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "c ok" in r.stdout, (r.returncode, r.stdout, r.stderr)
