@@ -886,8 +886,12 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s) {
                            dim3(NT), 0, s, a);
     } else if (pairs >= 256) {
         // every CU is busy with one workgroup per (sequence, head): a workgroup takes all 128
-        // columns, so stages A and B1 run once per head instead of once per 64-column half
-        hipLaunchKernelGGL((kda_prefill_mfma_kernel<1, 128, false>), dim3((unsigned)pairs),
+        // columns, so stages A and B1 run once per head instead of once per 64-column half.
+        // Stage B's waves take the raised priority here (1.1% faster on the 16-sequence batch and
+        // 1.4% at 4 x 4096 tokens than stage A's; stage S's was slower than both).  With the
+        // output stage, stage A (which then also forms the gate's sigmoid) keeps it: stage B's
+        // priority made that kernel 17% slower.
+        hipLaunchKernelGGL((kda_prefill_mfma_kernel<2, 128, false>), dim3((unsigned)pairs),
                            dim3(NT), 0, s, a);
     } else if (2 * pairs >= 128 && a.split <= 1) {
         // at least half of the 256 CUs hold a workgroup; a split's launch keeps stage B's priority
