@@ -39,8 +39,9 @@
 //   stage S (waves 0-3) for tile q-4: wave s carries its 128 x 16 strip of S (two strips in the
 //      128-column slice), which lives in registers as eight 16x16 float32 accumulator blocks per
 //      strip for the whole sequence, and writes o.
-// (The wave numbers are those of the 64-column kernel; the plain 128-column kernel rotates the
-// roles by one group of four: stage A on waves 0-3, B on 4-7, S on 8-11.)
+// (The wave numbers are those of the 64-column kernel.  The plain 128-column kernel rotates the
+// roles by one group of four: stage A on waves 0-3, B on 4-7, S on 8-11.  Both 128-column
+// kernels run B1 on one wave of each pair only.)
 // Three waves share each SIMD.  Loads run two tiles ahead of their use.  All products use
 // v_mfma_f32_16x16x{16,32}_bf16.  Token-major -> channel-major changes of layout are LDS transpose
 // reads where the data already sits in LDS, and a product with a 0/1 selector matrix on the
@@ -254,13 +255,12 @@ struct Shared {
 // sigmoid(gate) per (token, head) row ("Kimi K3's hybrid block, from first principles", section
 // "From linear attention to the delta rule": each head's output row is normalised by its root
 // mean square and, ahead of the output projection, scaled by a sigmoid gate computed from the
-// token).  Stage A
-// loads the gate of tile j - 4 with the inputs of tile j and, in period j, leaves w * sigmoid(gate)
-// (bf16) for the stage-S wave and lane that hold those columns of o.  The row's sum of squares
-// spans the four stage-S waves: in the period that forms tile j's o (period j + 4) each adds its
-// 32 columns and leaves the sum in ssq; in the next period, after the barrier that orders those
-// writes, each reads the four sums and finishes tile j's y from the o it kept in registers.  No
-// wave waits for another outside the pipeline's own barrier.
+// token).  Stage A loads the gate of tile j - 4 with the inputs of tile j and, in period j, leaves
+// w * sigmoid(gate) (bf16) for the stage-S wave and lane that hold those columns of o.  The row's
+// sum of squares spans the four stage-S waves: in the period that forms tile j's o (period j + 4)
+// each adds its 32 columns and leaves the sum in ssq; in the next period, after the barrier that
+// orders those writes, each reads the four sums and finishes tile j's y from the o it kept in
+// registers.  No wave waits for another outside the pipeline's own barrier.
 struct GateLds {
     uint4 gw[2][4][64];     // by tile % 2, stage-S wave, lane: bf16 w * sigmoid(gate) of token ln,
                             // columns 16 s + 4 lg + r (.xy) and 64 + 16 s + 4 lg + r (.zw)
@@ -801,7 +801,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         }
         // The two waves of a pair would compute the same B1 and leave identical values in LDS,
         // where stage B2 reads them (the carried registers stay with the wave that formed them).
-        // In the 128-column kernel the second wave skips it: 1.3% faster on the 16-sequence
+        // In the 128-column kernel the second wave skips it: 1.3-1.8% faster on the 16-sequence
         // batch with bit-identical outputs.  In the 64-column kernel both keep it, one half per
         // SIMD and period (skipping measured no faster at H = 96, and 0.2-0.4% slower at 12 and
         // 64 heads).
