@@ -41,7 +41,8 @@
 //      strip for the whole sequence, and writes o.
 // (The wave numbers are those of the 64-column kernel.  The plain 128-column kernel rotates the
 // roles by one group of four: stage A on waves 0-3, B on 4-7, S on 8-11.  Both 128-column
-// kernels run B1 on one wave of each pair only.)
+// kernels run B1 on one wave of each pair only, and in the one with the output stage the
+// stage-B waves also carry the gate.)
 // Three waves share each SIMD.  Loads run two tiles ahead of their use.  All products use
 // v_mfma_f32_16x16x{16,32}_bf16.  Token-major -> channel-major changes of layout are LDS transpose
 // reads where the data already sits in LDS, and a product with a 0/1 selector matrix on the
@@ -214,7 +215,6 @@ __device__ int select_by_length(const int32_t* cu, int N, int r, int tid, uint32
 struct Raw {
     uint2 q0, q1, k0, k1, g0, g1, v[2];
     uint32_t b;   // raw bf16 bits of beta in the low half
-    uint2 gz[2];  // fused output stage: the gate of tile - 3 at the columns of v
 };
 
 // Stage-to-stage buffers, grouped by hand-off so that one dynamic base address reaches every
@@ -255,12 +255,14 @@ struct Shared {
 // sigmoid(gate) per (token, head) row ("Kimi K3's hybrid block, from first principles", section
 // "From linear attention to the delta rule": each head's output row is normalised by its root
 // mean square and, ahead of the output projection, scaled by a sigmoid gate computed from the
-// token).  Stage A loads the gate of tile j - 4 with the inputs of tile j and, in period j, leaves
-// w * sigmoid(gate) (bf16) for the stage-S wave and lane that hold those columns of o.  The row's
-// sum of squares spans the four stage-S waves: in the period that forms tile j's o (period j + 4)
-// each adds its 32 columns and leaves the sum in ssq; in the next period, after the barrier that
-// orders those writes, each reads the four sums and finishes tile j's y from the o it kept in
-// registers.  No wave waits for another outside the pipeline's own barrier.
+// token).  Stage-B wave s loads the gate of tile j in period j + 2 and, in period j + 4, leaves
+// w * sigmoid(gate) (bf16) for stage-S wave s, lane by lane, at the columns of o that lane holds.
+// The row's sum of squares spans the four stage-S waves: in the period that forms tile j's o
+// (period j + 4) each adds its 32 columns and leaves the sum in ssq; in the next period, after the
+// barrier that orders those writes, each reads the four sums and finishes tile j's y from the o
+// it kept in registers.  No wave waits for another outside the pipeline's own barrier.  (Stage A
+// carrying the gate instead measured 1.7-3.3% slower: it paces the period when most CUs are
+// busy.)
 struct GateLds {
     uint4 gw[2][4][64];     // by tile % 2, stage-S wave, lane: bf16 w * sigmoid(gate) of token ln,
                             // columns 16 s + 4 lg + r (.xy) and 64 + 16 s + 4 lg + r (.zw)
@@ -452,18 +454,6 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
         for (int m = 0; m < NS; ++m) R.v[m] = ld8(rv, vo_v + 128 * m);
         R.b = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, vo_b, 0, 0);
-        if constexpr (GATED) {
-            // the gate of tile ld_tile - 4, at the columns of v (zeros before the first tile
-            // and past the sequence end)
-            const int gt = ld_tile - 4;
-            const int nvg = gt < 0 ? 0 : min(max(len32 - gt * C, 0), C);
-            const int nrecg = max((nvg - 1) * rb32 + D * 2, 0);
-            const int64_t tg0 = bos + min((int64_t)max(gt, 0) * C, len);
-            const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(gate + (tg0 * H + h) * D), (short)0, nrecg, kBufferFlags);
-#pragma unroll
-            for (int m = 0; m < NS; ++m) R.gz[m] = ld8(rz, vo_v + 128 * m);
-        }
         ++ld_tile;
     };
 
@@ -516,15 +506,25 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         for (int m = 0; m < NS; ++m) A.vraw[s + 4 * m][lane] = R.v[m];
     };
 
-    // fused output stage, stage A's part: w * sigmoid(gate) of tile tg (whose gate R holds) for
-    // the stage-S wave and lane that hold those columns, into the buffer of tile tg % 2
-    auto gate_step = [&](int64_t tg, const Raw& R) {
+    // fused output stage, stage B's part: stage-B wave s serves stage-S wave s.  In period t + 2
+    // it loads the gate of tile t at that wave's columns (zeros past the sequence end), and in
+    // period t + 4 it leaves w * sigmoid(gate) per lane in the buffer of tile t % 2.
+    struct GateRaw { uint2 z[NS]; };
+    auto gate_load = [&](int64_t tile, GateRaw& G) {
+        const int nvg = min(max(len32 - (int)tile * C, 0), C);
+        const int nrecg = max((nvg - 1) * rb32 + D * 2, 0);
+        const int64_t tg0 = bos + min(tile * C, len);
+        const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(gate + (tg0 * H + h) * D), (short)0, nrecg, kBufferFlags);
+#pragma unroll
+        for (int m = 0; m < NS; ++m) G.z[m] = ld8(rz, vo_v + 128 * m);
+    };
+    auto gate_step = [&](int64_t tile, const GateRaw& G) {
         if constexpr (GATED) {
-            if (tg < 0) return;
             uint32_t pk[4];
 #pragma unroll
             for (int m = 0; m < NS; ++m) {
-                const f32x4 z = unpack4(R.gz[m]);
+                const f32x4 z = unpack4(G.z[m]);
                 const f32x4 w = *reinterpret_cast<const f32x4*>(&gsh.w[64 * m + 16 * s + 4 * lg]);
                 f32x4 gw;
 #pragma unroll
@@ -533,7 +533,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
                 pk[2 * m] = pk2(gw[0], gw[1]);
                 pk[2 * m + 1] = pk2(gw[2], gw[3]);
             }
-            gsh.gw[(uint32_t)tg & 1u][s][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            gsh.gw[(uint32_t)tile & 1u][s][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
         }
     };
 
@@ -701,7 +701,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     };
     // fused output stage, stage S's part.  In the period that forms tile t's o: this wave's sum of
     // o^2 per token (as rounded to bf16, as stored) into ssq.  In the next period: the four sums,
-    // then y from the o kept in registers and stage A's w * sigmoid(gate).
+    // then y from the o kept in registers and stage B's w * sigmoid(gate).
     auto ssq_step = [&](int64_t tile, const bf16x4 (&Ot)[NS]) {
         if constexpr (GATED) {
             float ss = 0.f;
@@ -762,29 +762,17 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         stage_a(1, R1);
         load_tile(R1);     // tile 3
         lds_barrier();
-        // (with the fused output stage, the gate of tile j - 4 rides with tile j's inputs and is
-        // turned into w * sigmoid(gate) in period j, one period before stage S finishes tile j - 4)
         for (int64_t i = 0; i < nsteps; i += 2) {
             stage_a(i + 2, R0);
-            gate_step(i - 2, R0);
             load_tile(R0);     // tile i + 4
             lds_barrier();
             stage_a(i + 3, R1);
-            gate_step(i - 1, R1);
             load_tile(R1);     // tile i + 5
             lds_barrier();
         }
-        if constexpr (GATED) {
-            // the gates of the last two tiles; one more period for stage S to finish the last y
-            gate_step(nsteps - 2, R0);
-            lds_barrier();
-            gate_step(nsteps - 1, R1);
-            lds_barrier();
-            lds_barrier();
-        } else {
-            lds_barrier();
-            lds_barrier();
-        }
+        lds_barrier();
+        lds_barrier();
+        if constexpr (GATED) lds_barrier();   // stage S finishes the last y one period later
     } else if (role == 2) {
         // with few workgroups the chain through stage B paces the period instead
         if (PRIO_ROLE == 2) __builtin_amdgcn_s_setprio(1);
@@ -806,20 +794,44 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         // SIMD and period (skipping measured no faster at H = 96, and 0.2-0.4% slower at 12 and
         // 64 heads).
         const bool do_b1 = BVT == 64 || (s & 1) == 0;
+        // the gate registers: GX holds the tiles loaded in the first period of each pair below,
+        // GY those of the second (the pairs keep their order into the last loop)
+        GateRaw GX, GY;
+        auto gate_at = [&](int64_t qq, GateRaw& G) {
+            if constexpr (GATED) {
+                if (qq >= 4 && qq - 4 < nsteps) gate_step(qq - 4, G);
+                if (qq >= 2 && qq - 2 < nsteps) gate_load(qq - 2, G);
+            }
+        };
         for (int64_t j = par; j < nsteps; j += 2) {
             b2_at(q++);
             B1Carry c;
             if (do_b1) c = stage_b1a(j);
+            gate_at(q - 1, GX);
             lds_barrier();
             b2_at(q++);
             if (do_b1) stage_b1b(j, c);
+            gate_at(q - 1, GY);
             lds_barrier();
         }
-        for (; q < nsteps + 4; ++q) {
-            b2_at(q);
-            lds_barrier();
+        if constexpr (GATED) {
+            // (stage S finishes the last y one period after its last tile)
+            for (; q < nsteps + 5; q += 2) {
+                b2_at(q);
+                gate_at(q, GX);
+                lds_barrier();
+                if (q + 1 < nsteps + 5) {
+                    b2_at(q + 1);
+                    gate_at(q + 1, GY);
+                    lds_barrier();
+                }
+            }
+        } else {
+            for (; q < nsteps + 4; ++q) {
+                b2_at(q);
+                lds_barrier();
+            }
         }
-        if constexpr (GATED) lds_barrier();   // stage S finishes the last y one period later
     } else {
         state_in(h_in, part_m);
         lds_barrier();
@@ -880,17 +892,17 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s) {
     if (pairs <= 0) return hipSuccess;
     if (a.gate) {
         // the fused output stage needs a whole head per workgroup (the caller checks pairs >= 256
-        // and no split or snapshots)
+        // and no split or snapshots).  Its gate work rides on the stage-B waves, which take the
+        // raised priority here too: 1.7% faster on the 16-sequence batch and 3.3% at 4 x 4096
+        // tokens than the same work in stage A with stage A's priority.
         if (pairs < 256 || a.split > 1 || a.snaps) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((kda_prefill_mfma_kernel<1, 128, true>), dim3((unsigned)pairs),
+        hipLaunchKernelGGL((kda_prefill_mfma_kernel<2, 128, true>), dim3((unsigned)pairs),
                            dim3(NT), 0, s, a);
     } else if (pairs >= 256) {
         // every CU is busy with one workgroup per (sequence, head): a workgroup takes all 128
         // columns, so stages A and B1 run once per head instead of once per 64-column half.
         // Stage B's waves take the raised priority here (1.1% faster on the 16-sequence batch and
-        // 1.4% at 4 x 4096 tokens than stage A's; stage S's was slower than both).  With the
-        // output stage, stage A (which then also forms the gate's sigmoid) keeps it: stage B's
-        // priority made that kernel 17% slower.
+        // 1.4% at 4 x 4096 tokens than stage A's; stage S's was slower than both).
         hipLaunchKernelGGL((kda_prefill_mfma_kernel<2, 128, false>), dim3((unsigned)pairs),
                            dim3(NT), 0, s, a);
     } else if (2 * pairs >= 128 && a.split <= 1) {
