@@ -59,7 +59,13 @@ template <typename Tin> constexpr int sub_of() { return sizeof(Tin) == 2 ? 8 : 4
 constexpr int CONV_CHUNK = 32;
 constexpr int kBufNT = 2;                    // buffer cache policy: non-temporal (streaming)
 
-// eight consecutive elements through a buffer resource: one 16-byte access for bf16, two for f32
+// eight consecutive elements through a buffer resource: one 16-byte access for bf16, two for f32.
+// Loads take the row offset as the scalar offset; stores fold it into the lane offset and pass a
+// zero scalar offset.  With the row offset in a scalar register, the compiler let the next vector
+// instruction overwrite a 16-byte store's data registers right after the store, and the outputs
+// of the last four lanes of every 16-lane row came out corrupted, differently from run to run.
+// With a zero scalar offset it leaves the store its wait states, and the outputs are those of the
+// earlier form (whose per-access loops kept the two apart).
 template <typename Tin> struct BufRow;
 template <> struct BufRow<bf16_t> {
     static __device__ __forceinline__ void load(Raw8<bf16_t>& r, __amdgpu_buffer_rsrc_t rs,
@@ -71,7 +77,7 @@ template <> struct BufRow<bf16_t> {
                                                  uint32_t voff, uint32_t soff) {
         const u32v4 u = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
                          pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32v4, u), rs, voff, soff,
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32v4, u), rs, voff + soff, 0,
                                                kBufNT);
     }
 };
@@ -86,10 +92,10 @@ template <> struct BufRow<float> {
     static __device__ __forceinline__ void store(const float y[8], __amdgpu_buffer_rsrc_t rs,
                                                  uint32_t voff, uint32_t soff) {
         const f32v4 lo = {y[0], y[1], y[2], y[3]}, hi = {y[4], y[5], y[6], y[7]};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32v4, lo), rs, voff, soff,
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32v4, lo), rs, voff + soff, 0,
                                                kBufNT);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32v4, hi), rs, voff + 16,
-                                               soff, kBufNT);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32v4, hi), rs,
+                                               voff + soff + 16, 0, kBufNT);
     }
 };
 
@@ -101,7 +107,10 @@ __global__ __launch_bounds__(256) void kda_frontend_conv_kernel(FrontArgs a) {
     const int j = tid & 15, grp = (tid >> 4) & 3;
     const int64_t H = a.H;
     const int64_t nchunks = (a.Ttot + CONV_CHUNK - 1) / CONV_CHUNK;
-    const int64_t wv = (int64_t)blockIdx.x * 4 + (tid >> 6);   // wave: one head, four chunks
+    // wave: one head, four chunks.  The wave index goes through readfirstlane so that the
+    // compiler sees it (and the buffer resources built from it) as uniform; otherwise it keeps
+    // the resources in vector registers and wraps every buffer access in a readfirstlane loop.
+    const int64_t wv = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t h = wv % H, chunk0 = (wv / H) * 4;
     if (chunk0 >= nchunks) return;                              // the whole wave leaves
     const int64_t chunk = chunk0 + grp;
