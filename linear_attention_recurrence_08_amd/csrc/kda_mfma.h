@@ -75,6 +75,9 @@ __device__ __forceinline__ bf16x4 lds_tr16(const void* p) {
 __device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 // Workgroup barrier that orders LDS only: global loads issued before it stay in flight (a full
 // __syncthreads() would also wait for the prefetched tiles).  The scheduling fences keep the
 // compiler from hoisting the next step's arithmetic above the barrier, where it would consume
