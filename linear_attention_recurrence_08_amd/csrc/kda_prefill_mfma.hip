@@ -209,11 +209,12 @@ __device__ int select_by_length(const int32_t* cu, int N, int r, int tid, uint32
 }
 
 // Raw inputs of one tile for one stage-A lane: token ln, key channels 32s + 8lg .. 32s + 8lg + 7
-// (one 16-byte load per tensor), value columns 64m + 16s + 4lg + r of the slice (m < slice
-// width / 64), beta of token ln.  They are read through buffer resources whose record count ends
-// at the sequence's last token, so a token past the end (and every token of a tile past the end)
-// reads as zero: with beta = 0 and k = v = 0 it neither writes the state nor reaches a stored
-// output, and with g = 0 it does not decay the state.
+// (one 16-byte load per tensor), value columns 32s + 8lg .. + 7 with the output stage (16 bytes,
+// as v[0], v[1]) or 64m + 16s + 4lg .. + 3 (8 bytes each, v[m]), beta of token ln.  They
+// are read through buffer resources whose record count ends at the sequence's last token, so a
+// token past the end (and every token of a tile past the end) reads as zero: with beta = 0 and
+// k = v = 0 it neither writes the state nor reaches a stored output, and with g = 0 it does not
+// decay the state.
 struct Raw {
     uint4 q, k, g;
     uint2 v[2];
@@ -435,7 +436,15 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     const int64_t len = eos - bos;
     const int64_t row_bytes = H * D * 2;                       // one token, all heads
     const uint32_t vo_qkg = (uint32_t)(ln * row_bytes + chan0 * 2);
-    const uint32_t vo_v = (uint32_t)(ln * row_bytes + vcol0 * 2);
+    // v: with the output stage (128 columns), 16 bytes per lane (columns 32 s + 8 lg .. + 7),
+    // which stage A scatters to the stage-S strips in LDS; otherwise 8 bytes per lane (columns
+    // 16 s + 4 lg .. + 3 of each strip, the lane's own strip entries).  Against 8-byte loads
+    // (outputs bit-identical), the 16-byte form was 3.4-5.6% faster with the output stage on the
+    // 16-sequence batch, within +-0.6% without it, and 6-10% slower with 64 columns, where only
+    // two stage-A waves would carry v.
+    constexpr bool kV16 = GATED;
+    const uint32_t vo_v = kV16 ? (uint32_t)(ln * row_bytes + (32 * s + 8 * lg) * 2)
+                               : (uint32_t)(ln * row_bytes + vcol0 * 2);
     const uint32_t vo_b = (uint32_t)(ln * H * 2);
     int ld_tile = 0;                                           // next tile to load (uniform)
     const int len32 = (int)len;                                // token counts fit int32 (ABI)
@@ -461,8 +470,14 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         R.q = ld16(rq, vo_qkg);
         R.k = ld16(rk, vo_qkg);
         R.g = ld16(rg, vo_qkg);
+        if constexpr (kV16) {
+            const uint4 t = ld16(rv, vo_v);
+            R.v[0] = make_uint2(t.x, t.y);
+            R.v[1] = make_uint2(t.z, t.w);
+        } else {
 #pragma unroll
-        for (int m = 0; m < NS; ++m) R.v[m] = ld8(rv, vo_v + 128 * m);
+            for (int m = 0; m < NS; ++m) R.v[m] = ld8(rv, vo_v + 128 * m);
+        }
         R.b = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, vo_b, 0, 0);
         ++ld_tile;
     };
@@ -514,8 +529,18 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         A.kp[s][lane] = cat8(Kpb[0], Kpb[1]);
         A.qp[s][lane] = cat8(Qpb[0], Qpb[1]);
         A.kd[s][lane] = cat8(Kdb[0], Kdb[1]);
+        if constexpr (kV16) {
+            // columns c .. c + 3 of token ln go to strip (c % 64) / 16 + 4 (c / 64), at the lane
+            // of the stage-S layout that holds them, ln + 16 ((c % 16) / 4)
+            const int c0 = 32 * s + 8 * lg;
+            uint2* dst = A.vraw[((c0 & 63) >> 4) + 4 * (c0 >> 6)];
+            const int l0 = ln + 16 * ((c0 & 15) >> 2);
+            dst[l0] = R.v[0];
+            dst[l0 + 16] = R.v[1];
+        } else {
 #pragma unroll
-        for (int m = 0; m < NS; ++m) A.vraw[s + 4 * m][lane] = R.v[m];
+            for (int m = 0; m < NS; ++m) A.vraw[s + 4 * m][lane] = R.v[m];
+        }
     };
 
     // fused output stage, stage B's part.  In period t + 2 stage-B wave s loads the gate of tile
