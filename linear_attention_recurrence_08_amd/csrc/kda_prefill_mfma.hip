@@ -241,7 +241,7 @@ struct FromB1 {                // stage B1 -> stage B2 (indexed by tile % 2)
 };
 template <int NS>
 struct FromB {                 // stage B2 -> stage S (indexed by tile % 2)
-    uint2 kdc[8][64];          // channel-major Kd per block (A operand of Kd^T U)
+    uint4 kdc[4][64];          // channel-major Kd, blocks 2j (.xy) and 2j + 1 (.zw)
     bf16x8 w[4][64];           // A operands of W per 32-channel k-step
     bf16x8 qpp[4][64];         // A operands of Qpp per 32-channel k-step
     f32x4 ut[4 * NS][64];      // Ut per strip (accumulator fragments)
@@ -478,7 +478,8 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
             for (int m = 0; m < NS; ++m) R.v[m] = ld8(rv, vo_v + 128 * m);
         }
-        R.b = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, vo_b, 0, 0);
+        // beta: stage-A wave 0 alone (the tile's 16 values reach every stage through LDS)
+        if (s == 0) R.b = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, vo_b, 0, 0);
         ++ld_tile;
     };
 
@@ -525,7 +526,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             Kdb[hh] = bf4(kd);
             A.qpf[2 * s + hh][lane] = qp;
         }
-        A.beta[ln] = bt;   // every writer of an entry holds the same value
+        if (s == 0) A.beta[ln] = bt;   // the four lane groups write the same value
         A.kp[s][lane] = cat8(Kpb[0], Kpb[1]);
         A.qp[s][lane] = cat8(Qpb[0], Qpb[1]);
         A.kd[s][lane] = cat8(Kdb[0], Kdb[1]);
@@ -651,14 +652,15 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         // which stage-A lane (token) + 16 (ln % 4) stored
         const int src = 4 * lg + (ln >> 2) + 16 * (ln & 3);
         bf16x4 Wf[2], Qf[2];
+        uint2 kdh[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const bf16x4 kpc = lds_tr16(reinterpret_cast<const char*>(&A.kp[s][src]) + 8 * hh);
-            B.kdc[2 * s + hh][lane] =
-                as_u2(lds_tr16(reinterpret_cast<const char*>(&A.kd[s][src]) + 8 * hh));
+            kdh[hh] = as_u2(lds_tr16(reinterpret_cast<const char*>(&A.kd[s][src]) + 8 * hh));
             Wf[hh] = bf4(mma16(kpc, TbTb, zero4()));                   // W^T
             Qf[hh] = bf4(mma16(kpc, nY3b, A.qpf[2 * s + hh][lane]));   // Qpp^T
         }
+        B.kdc[s][lane] = make_uint4(kdh[0].x, kdh[0].y, kdh[1].x, kdh[1].y);
         B.w[s][lane] = cat8(Wf[0], Wf[1]);
         B.qpp[s][lane] = cat8(Qf[0], Qf[1]);
 #pragma unroll
@@ -726,10 +728,14 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         }
         // S <- St + Kd^T U, blocks outside and strips inside: each Kd fragment serves both strips
 #pragma unroll
-        for (int mb = 0; mb < 8; ++mb) {
-            const bf16x4 kdf = as_bf4(B.kdc[mb][lane]);
+        for (int j = 0; j < 4; ++j) {
+            const uint4 kd2 = B.kdc[j][lane];
+            const bf16x4 kdf0 = as_bf4(make_uint2(kd2.x, kd2.y));
+            const bf16x4 kdf1 = as_bf4(make_uint2(kd2.z, kd2.w));
 #pragma unroll
-            for (int m = 0; m < NS; ++m) S[m][mb] = mma16(kdf, Ub[m], S[m][mb]);
+            for (int m = 0; m < NS; ++m) S[m][2 * j] = mma16(kdf0, Ub[m], S[m][2 * j]);
+#pragma unroll
+            for (int m = 0; m < NS; ++m) S[m][2 * j + 1] = mma16(kdf1, Ub[m], S[m][2 * j + 1]);
         }
     };
     // with the fused output stage o is optional; y's lane offset within a tile's token rows
