@@ -641,8 +641,24 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
 
     // stage B2 for tile `tile`, wave 8 + s: W and Qpp for channels [32s, 32s+32), Ut and PUt for
     // columns [16s, 16s+16), and the channel-major Kd blocks of those channels
-    auto stage_b2 = [&](int64_t tile) {
+    // stage B2's inputs from stage A, read at the end of the period before (stage A wrote them two
+    // periods before that), so that only stage B1's hand-off is read after the barrier
+    struct B2In { bf16x4 kpc[2]; uint2 kdh[2]; f32x4 qpf[2]; bf16x4 vcs[NS]; };
+    auto b2_in = [&](int64_t tile) -> B2In {
         const FromA<NS>& A = fa(tile);
+        const int src = 4 * lg + (ln >> 2) + 16 * (ln & 3);
+        B2In x;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            x.kpc[hh] = lds_tr16(reinterpret_cast<const char*>(&A.kp[s][src]) + 8 * hh);
+            x.kdh[hh] = as_u2(lds_tr16(reinterpret_cast<const char*>(&A.kd[s][src]) + 8 * hh));
+            x.qpf[hh] = A.qpf[2 * s + hh][lane];
+        }
+#pragma unroll
+        for (int m = 0; m < NS; ++m) x.vcs[m] = lds_tr16(&A.vraw[s + 4 * m][src]);
+        return x;
+    };
+    auto stage_b2 = [&](int64_t tile, const B2In& x) {
         FromB<NS>& B = fb(tile);
         const uint2 tbu = fb1(tile).tbt[lane], y3u = fb1(tile).y3[lane];
         const bf16x4 TbTb = as_bf4(tbu), Y3b = as_bf4(y3u);
@@ -650,22 +666,18 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         // channel-major blocks by transpose reads of the token-major fragments: this lane
         // addresses token 4lg + ln / 4, channels 4 (ln % 4) .. +3 of each 16-channel half,
         // which stage-A lane (token) + 16 (ln % 4) stored
-        const int src = 4 * lg + (ln >> 2) + 16 * (ln & 3);
         bf16x4 Wf[2], Qf[2];
-        uint2 kdh[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const bf16x4 kpc = lds_tr16(reinterpret_cast<const char*>(&A.kp[s][src]) + 8 * hh);
-            kdh[hh] = as_u2(lds_tr16(reinterpret_cast<const char*>(&A.kd[s][src]) + 8 * hh));
-            Wf[hh] = bf4(mma16(kpc, TbTb, zero4()));                   // W^T
-            Qf[hh] = bf4(mma16(kpc, nY3b, A.qpf[2 * s + hh][lane]));   // Qpp^T
+            Wf[hh] = bf4(mma16(x.kpc[hh], TbTb, zero4()));                   // W^T
+            Qf[hh] = bf4(mma16(x.kpc[hh], nY3b, x.qpf[hh]));                 // Qpp^T
         }
-        B.kdc[s][lane] = make_uint4(kdh[0].x, kdh[0].y, kdh[1].x, kdh[1].y);
+        B.kdc[s][lane] = make_uint4(x.kdh[0].x, x.kdh[0].y, x.kdh[1].x, x.kdh[1].y);
         B.w[s][lane] = cat8(Wf[0], Wf[1]);
         B.qpp[s][lane] = cat8(Qf[0], Qf[1]);
 #pragma unroll
         for (int m = 0; m < NS; ++m) {
-            const bf16x4 vcs = lds_tr16(&A.vraw[s + 4 * m][src]);  // column-major V
+            const bf16x4 vcs = x.vcs[m];                           // column-major V
             B.ut[s + 4 * m][lane] = mma16(TbTb, vcs, zero4());     // Tb V
             const f32x4 pu = mma16(vcs, Y3b, zero4());             // (P Tb V)^T
             if constexpr (NS == 1) B.put[s][lane] = pu;
@@ -829,12 +841,17 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         // every stage-B wave runs B2 of period q (tile q - 3) for its channel group, and its pair
         // alternates the two halves of B1 for the tiles of its parity
         const int par = s >> 1;            // tiles of this parity
+        B2In nx;                           // the inputs of the next period's B2
         auto b2_at = [&](int64_t q) {
-            if (q >= 3 && q - 3 < nsteps) stage_b2(q - 3);
+            if (q >= 3 && q - 3 < nsteps) stage_b2(q - 3, nx);
+        };
+        auto b2_pre = [&](int64_t q) {     // at the end of period q - 1, for period q
+            if (q >= 3 && q - 3 < nsteps) nx = b2_in(q - 3);
         };
         int64_t q = 0;                     // period
         for (; q < 1 + par; ++q) {
             b2_at(q);
+            b2_pre(q + 1);
             lds_barrier();
         }
         // The two waves of a pair would compute the same B1 and leave identical values in LDS,
@@ -858,10 +875,12 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             B1Carry c;
             if (do_b1) c = stage_b1a(j);
             gate_at(q - 1, GX);
+            b2_pre(q);
             lds_barrier();
             b2_at(q++);
             if (do_b1) stage_b1b(j, c);
             gate_at(q - 1, GY);
+            b2_pre(q);
             lds_barrier();
         }
         if constexpr (GATED) {
@@ -869,16 +888,19 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             for (; q < nsteps + 5; q += 2) {
                 b2_at(q);
                 gate_at(q, GX);
+                b2_pre(q + 1);
                 lds_barrier();
                 if (q + 1 < nsteps + 5) {
                     b2_at(q + 1);
                     gate_at(q + 1, GY);
+                    b2_pre(q + 2);
                     lds_barrier();
                 }
             }
         } else {
             for (; q < nsteps + 4; ++q) {
                 b2_at(q);
+                b2_pre(q + 1);
                 lds_barrier();
             }
         }
