@@ -27,15 +27,17 @@
 // v = 0 (its part M), and leaves the segment's final state for the composition.  Each wave keeps
 // one role for the whole sequence, and the work of a tile runs as a software pipeline with a
 // single workgroup barrier per period; period q holds
-//   stage A (waves 4-7) for tile q: wave s loads key channels [32s, 32s+32) of q, k, g and value
-//      columns [16s, 16s+16) of the slice through buffer resources, runs the cumulative
-//      log-decay as a product with a triangular 0/1 matrix, and forms the decayed operands Kp,
-//      Qp, Kd (the exponentials are the only transcendental work);
+//   stage A (waves 4-7) for tile q: wave s loads key channels [32s, 32s+32) of q, k, g (eight
+//      consecutive channels per lane, one 16-byte load per tensor) and value columns of the slice
+//      through buffer resources (wave 0 also beta), runs the cumulative log-decay as a product
+//      with a triangular 0/1 matrix, and forms the decayed operands Kp, Qp, Kd (the exponentials
+//      are the only transcendental work);
 //   stage B1 (waves 8-11) for tiles q-1 and q-2: A, A^T, P^T over all 128 channels and T, split
 //      into two halves that run in consecutive periods; waves 8-9 take even tiles and waves
 //      10-11 odd ones, so each SIMD carries half an inverse per period;
 //   stage B2 (waves 8-11, beside B1) for tile q-3: W and Qpp for key channels [32s, 32s+32), Ut
-//      and PUt for columns [16s, 16s+16), and the channel-major Kd blocks the carry consumes;
+//      and PUt for columns [16s, 16s+16), and the channel-major Kd blocks the carry consumes
+//      (its inputs from stage A are read at the end of the period before);
 //   stage S (waves 0-3) for tile q-4: wave s carries its 128 x 16 strip of S (two strips in the
 //      128-column slice), which lives in registers as eight 16x16 float32 accumulator blocks per
 //      strip for the whole sequence, and writes o.
@@ -52,8 +54,10 @@
 // Fragment conventions for a 16x16 block, lane l = ln + 16 lg (ln = l % 16, lg = l / 16):
 //   accumulator  acc(X): register r holds X[4 lg + r][ln]
 //   A operand of Z = X Y is acc(X^T) (as bf16); B operand is acc(Y).
-// For the K = 32 products over key channels, slot j of lane group lg stands for channel
-// 16 (j / 4) + 4 lg + (j % 4) of the 32-channel group; A and B operands always use this order.
+// For the K = 32 products over key channels, slot j of lane group lg stands for channel 8 lg + j of
+// the 32-channel group, as stage A loads it; A and B operands always use this order.  Split into
+// 16-channel halves hh = j / 4 (the 16x16 blocks of the transposes, the scan and the state's rows),
+// internal channel (hh, 4 lg + r) is key channel 8 lg + 4 hh + r of the group.
 #include "kda_internal.h"
 #include "kda_mfma.h"
 
@@ -504,8 +508,8 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         for (int hh = 0; hh < 2; ++hh) {
             const bf16x4 gc = bf4(mma32(ga, sel[hh], zero4()));   // channel-major g (exact)
             X[hh] = mma32(cat8(gc, gc), scanHL, zero4());
-            // Gam_C of channel 32s + 16hh + ln, in every register and lane group; all four lane
-            // groups store the same value
+            // Gam_C of internal channel (hh, ln), in every register and lane group, stored at its
+            // internal row 32s + 16hh + ln; all four lane groups store the same value
             const f32x4 gsum = mma16(onesA, gc, zero4());
             ec[32 * s + 16 * hh + ln] = __builtin_amdgcn_exp2f(gsum[0] * LOG2E);
         }
