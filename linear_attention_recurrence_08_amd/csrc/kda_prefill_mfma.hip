@@ -756,7 +756,19 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     };
     // with the fused output stage o is optional; y's lane offset within a tile's token rows
     const bool want_o = !GATED || o != nullptr;
-    const uint32_t vo_y = (uint32_t)((ln * H + h) * D + vcol0) * 2u;
+    // y (fused output stage, two strips): lane rows lg and lg ^ 1 trade pieces so that each lane
+    // stores 8 consecutive columns of its token as one 16-byte store: rows with lg even take strip
+    // 0's columns 16 s + 4 lg .. + 7, rows with lg odd strip 1's 64 + 16 s + 4 (lg - 1) .. + 7.
+    // Against two 8-byte stores per lane (outputs bit-identical): 1.3-4.0% faster on the
+    // 16-sequence batch and 3.1-3.9% at 4 x 4096 tokens (two builds).  The same pairing for o in
+    // the plain kernel measured 0.3-1.2% slower, so o keeps one 8-byte store per strip.
+    const int64_t ycol = (int64_t)slice * BVT + 16 * s + 4 * (lg & ~1) + 64 * (lg & 1);
+    auto pair_strips = [&](uint2 a0, uint2 a1) -> uint4 {
+        const auto x = __builtin_amdgcn_permlane16_swap(a0.x, a1.x, false, false);
+        const auto z = __builtin_amdgcn_permlane16_swap(a0.y, a1.y, false, false);
+        return make_uint4(x[0], z[0], x[1], z[1]);
+    };
+    const uint32_t vo_y = (uint32_t)((ln * H + h) * D + ycol) * 2u;
     auto store_o = [&](int64_t tile, const bf16x4 (&Ot)[NS], bool masked) {
         const int64_t t0 = bos + tile * C;
         bf16_t* dst = o + ((t0 + ln) * H + h) * D + vcol0;
@@ -796,15 +808,18 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             const int nv = (int)min(max(eos - t0, (int64_t)0), (int64_t)C);
             const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(y + t0 * H * D), (short)0, nv * rb32, kBufferFlags);
+            uint2 yb[NS];
 #pragma unroll
             for (int m = 0; m < NS; ++m) {
                 const f32x4 gw = unpack4(gwm[m]), of = unpack4(as_u2(Ot[m]));
                 f32x4 yv;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) yv[r] = of[r] * rn * gw[r];
-                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, as_u2(bf4(yv))),
-                                                      ry, vo_y + 128u * m, 0, 0);
+                yb[m] = as_u2(bf4(yv));
             }
+            // one 16-byte store per lane (zero scalar offset), the two strips paired as for o
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4, pair_strips(yb[0], yb[1])), ry, vo_y, 0, 0);
         }
     };
 
