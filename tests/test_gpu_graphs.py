@@ -87,9 +87,10 @@ def test_decode_token_loop_in_a_graph(decode):
 
 
 def test_prefill_entry_points_in_a_graph():
-    """One graph holding four prefills (two 64-column workgroups per head; one per head with the
-    output stage fused; the token-range split in the library's static workspace) and the
-    output-stage kernel, replayed three times on new inputs."""
+    """One graph holding five prefills (two 64-column workgroups per head; one per head with the
+    output stage fused; one per head without it, whose kernel spills registers to scratch
+    memory; the token-range split in the library's static workspace) and the output-stage
+    kernel, replayed three times on new inputs."""
     from linear_attention_recurrence_08_amd import (inputs, kda_chunk_fwd, kda_chunk_fwd_gated,
                                                     kda_chunk_fwd_gated_fuses,
                                                     kda_chunk_fwd_split_noalloc,
@@ -103,17 +104,20 @@ def test_prefill_entry_points_in_a_graph():
                                h0_sigma=0.1).to(dev)
         c = inputs.make_inputs([1024], 12, 128, 128, "bf16", seed=630 + r, h0_sigma=0.1,
                                packed=False).to(dev)
+        d = inputs.make_inputs([200, 64, 131, 16], 64, 128, 128, "bf16", seed=650 + r,
+                               h0_sigma=0.1).to(dev)
         _, zb, wb = inputs.make_output_gate_inputs(b.total_tokens, 64, 128, "bf16", 640 + r)
-        sets.append((a, b, c, zb.to(dev).reshape(b.call_views()[2].shape), wb.to(dev)))
+        sets.append((a, b, c, d, zb.to(dev).reshape(b.call_views()[2].shape), wb.to(dev)))
     assert kda_chunk_fwd_gated_fuses(sets[0][1].q, 4, 1, 64, 128, 128, True)
 
-    def run(a, b, c, zb, wb):
+    def run(a, b, c, d, zb, wb):
         oa, ha = kda_chunk_fwd(*a.call_views(), h0=a.h0)
         yb, _, hb = kda_chunk_fwd_gated(*b.call_views(), zb, weight=wb, h0=b.h0,
                                         cu_seqlens=b.cu_seqlens)
         oc, hc = kda_chunk_fwd_split_noalloc(*c.call_views(), h0=c.h0)
+        od, hd = kda_chunk_fwd(*d.call_views(), h0=d.h0, cu_seqlens=d.cu_seqlens)
         ya = kda_output_gate(oa, a.call_views()[2], None)   # v serves as a gate of o's shape
-        return oa, ha, yb, hb, oc, hc, ya
+        return oa, ha, yb, hb, oc, hc, od, hd, ya
 
     run(*sets[0])       # warm-up (the split's first call sets up its static workspace)
     torch.cuda.synchronize()
@@ -122,18 +126,18 @@ def test_prefill_entry_points_in_a_graph():
     fields = ("q", "k", "v", "g", "beta", "h0", "cu_seqlens")
     clone = lambda x: dataclasses.replace(x, **{n: getattr(x, n).clone() for n in fields
                                                 if getattr(x, n) is not None})
-    A, B, Cc = (clone(x) for x in sets[0][:3])
-    zs, ws = sets[0][3].clone(), sets[0][4].clone()
+    A, B, Cc, Dd = (clone(x) for x in sets[0][:4])
+    zs, ws = sets[0][4].clone(), sets[0][5].clone()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        outs = run(A, B, Cc, zs, ws)
+        outs = run(A, B, Cc, Dd, zs, ws)
     names = ("o (64-column)", "hT (64-column)", "y (fused gated)", "hT (fused gated)",
-             "o (split)", "hT (split)", "y (output stage)")
+             "o (split)", "hT (split)", "o (128-column)", "hT (128-column)", "y (output stage)")
     for r in (2, 0, 1):
-        a, b, c, zb, wb = sets[r]
-        ref = [t.clone() for t in run(a, b, c, zb, wb)]
+        a, b, c, d, zb, wb = sets[r]
+        ref = [t.clone() for t in run(a, b, c, d, zb, wb)]
         torch.cuda.synchronize()
-        for src, dst in ((a, A), (b, B), (c, Cc)):
+        for src, dst in ((a, A), (b, B), (c, Cc), (d, Dd)):
             for n in fields:
                 if getattr(src, n) is not None:
                     getattr(dst, n).copy_(getattr(src, n))
