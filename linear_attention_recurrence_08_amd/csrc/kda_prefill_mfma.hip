@@ -497,7 +497,6 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
     auto stage_a = [&](int64_t tile, const Raw& R) {
         FromA<NS>& A = fa(tile);
         float* ec = ecb(tile);
-        const float bt = __uint_as_float(R.b << 16);
         // internal channel (hh, 4 lg + r) of this lane is key channel 32 s + 8 lg + 4 hh + r, which
         // half hh of its 16-byte loads holds; the selector below picks g's channels in that order
         const bf16x8 ga = __builtin_bit_cast(bf16x8, R.g);
@@ -530,7 +529,7 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
             Kdb[hh] = bf4(kd);
             A.qpf[2 * s + hh][lane] = qp;
         }
-        if (s == 0) A.beta[ln] = bt;   // the four lane groups write the same value
+        if (s == 0) A.beta[ln] = __uint_as_float(R.b << 16);   // every lane group writes the same
         A.kp[s][lane] = cat8(Kpb[0], Kpb[1]);
         A.qp[s][lane] = cat8(Qpb[0], Qpb[1]);
         A.kd[s][lane] = cat8(Kdb[0], Kdb[1]);
