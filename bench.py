@@ -136,13 +136,21 @@ def recorded_traffic(kernel_tag: str):
 CALIB_BYTES = 1 << 30   # calibration copy: reads and writes exactly this many bytes
 
 
-def traffic_pass(dev):
+def traffic_pass(dev, workload=None):
     """A plain copy of known size (y = x * 1 over 1 GiB of float32), then 3 launches of each
-    entry point the bench line times, on its benchmark workload."""
+    entry point the bench line times, on its benchmark workload.  With `workload` (a prefill
+    workload other than the bench line's), 3 launches of kda_chunk_fwd on it alone."""
     import torch
     from linear_attention_recurrence_08_amd import (inputs, kda_chunk_fwd, kda_chunk_fwd_snapshots,
                                                     kda_decode_step, kda_decode_step_gated,
                                                     kda_frontend, kda_output_gate)
+    if workload is not None:
+        w = inputs.make_workload(workload).to(dev)
+        for _ in range(3):
+            kda_chunk_fwd(*w.call_views(), h0=w.h0, cu_seqlens=w.cu_seqlens)
+        torch.cuda.synchronize()
+        print("traffic pass done", file=sys.stderr)
+        return
     x = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
     y = torch.empty_like(x)
     torch.mul(x, 1.0, out=y)
@@ -526,28 +534,38 @@ def head_share(dev, stream, steps, warmup, unsplit=True):
     }
 
 
+DEFAULT_WORKLOAD = "prefill_T4096_H96_d128_bf16"   # the bench line's prefill
 SQ_PASS1 = ("SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
             "SQ_INSTS_SALU SQ_INSTS_VMEM")
 SQ_PASS2 = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT "
             "SQ_INSTS_VALU_TRANS_F32 SQ_WAIT_INST_LDS SQ_BUSY_CU_CYCLES SQ_ACTIVE_INST_ANY")
 
 
-def summarize_sq(dirs, command):
-    """profiles/kda_chunk_fwd_prefill_T4096_H96_d128_bf16_sq_counters.md from two rocprofv3 --pmc
-    runs of --traffic-pass (the SQ_PASS1 and SQ_PASS2 counter sets).  The prefill kernel runs one
-    workgroup of 12 waves per (sequence, head, 64-column half) on a CU of its own (one per
-    (sequence, head) from 256 pairs up), each SIMD holding one wave of each of the three roles,
-    and walks nsteps + 4 pipeline periods (nsteps = the tile count rounded up to even); counts are
-    given per SIMD and period."""
+def summarize_sq(dirs, command, wl=None):
+    """profiles/kda_chunk_fwd_<workload>_sq_counters.md from two rocprofv3 --pmc runs of
+    --traffic-pass (the SQ_PASS1 and SQ_PASS2 counter sets; for a workload other than the bench
+    line's, runs of --traffic-pass --workload NAME).  The prefill kernel runs one workgroup of 12
+    waves per (sequence, head, 64-column half) on a CU of its own (one per (sequence, head) from
+    256 pairs up), each SIMD holding one wave of each of the three roles, and walks nsteps + 4
+    pipeline periods (nsteps = the sequence's tile count rounded up to even); counts are given
+    per SIMD and period, over all workgroups' periods."""
     import csv
     import glob
     from linear_attention_recurrence_08_amd import inputs
-    wl = "prefill_T4096_H96_d128_bf16"
-    w = inputs.WORKLOADS[wl]
-    pairs = len(w["seq_lens"]) * w["H"]
-    wgs = pairs if pairs >= 256 else 2 * pairs
-    ntiles = (max(w["seq_lens"]) + 15) // 16
-    periods = ntiles + (ntiles & 1) + 4
+    wl = wl or "prefill_T4096_H96_d128_bf16"
+    x = inputs.make_workload(wl)
+    cu = x.cu_seqlens.tolist() if x.cu_seqlens is not None else None
+    lens = [b - a for a, b in zip(cu, cu[1:])] if cu else [x.T] * x.B
+    H = x.H
+    pairs = len(lens) * H
+    halves = 1 if pairs >= 256 else 2
+    wgs = halves * pairs
+
+    def walk(n):
+        nt = (n + 15) // 16
+        return nt + (nt & 1) + 4
+    total_periods = halves * H * sum(walk(n) for n in lens)   # summed over workgroups
+    periods = total_periods / wgs                              # per workgroup, mean
     simds, waves = 4 * wgs, 12 * wgs
     vals = {}
     for d in dirs:
@@ -583,8 +601,8 @@ def summarize_sq(dirs, command):
         fo.write(f"# kda_prefill_mfma_kernel on {wl}: SQ instruction counters\n\n")
         fo.write(f"command: `{command}`\n\n")
         fo.write(f"Means over the {ndisp} dispatches of the traffic pass; {waves} waves = {wgs} "
-                 f"workgroups of 12 waves, {simds} SIMDs, {periods} pipeline periods per "
-                 "workgroup. Cycle counters marked (x4) count in units of four cycles.\n\n")
+                 f"workgroups of 12 waves, {simds} SIMDs, {periods:.1f} pipeline periods per "
+                 "workgroup (mean). Cycle counters marked (x4) count in units of four cycles.\n\n")
         fo.write("| counter | per launch | per SIMD and period |\n|---|---|---|\n")
         for k, v, dsc in rows:
             fo.write(f"| {k} | {v:.4g} | {dsc} |\n")
@@ -626,7 +644,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill_T4096_H96_d128_bf16",
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=PREFILL_WORKLOADS)
     ap.add_argument("--decode-steps", type=int, default=None)
     ap.add_argument("--no-decode", action="store_true")
@@ -664,7 +682,7 @@ def main():
         summarize_split(args.summarize_split, args.command)
         return
     if args.summarize_sq:
-        summarize_sq(args.summarize_sq, args.command)
+        summarize_sq(args.summarize_sq, args.command, args.summary_workload)
         return
     if args.summarize:
         summarize(args.summarize, args.command, args.summary_workload)
@@ -686,7 +704,7 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     if args.traffic_pass:
-        traffic_pass(dev)
+        traffic_pass(dev, None if args.workload == DEFAULT_WORKLOAD else args.workload)
         return
     if args.head_share_only:
         print(json.dumps(head_share(dev, stream, args.steps, args.warmup,
