@@ -214,11 +214,11 @@ __device__ int select_by_length(const int32_t* cu, int N, int r, int tid, uint32
 
 // Raw inputs of one tile for one stage-A lane: token ln, key channels 32s + 8lg .. 32s + 8lg + 7
 // (one 16-byte load per tensor), value columns 32s + 8lg .. + 7 with the output stage (16 bytes,
-// as v[0], v[1]) or 64m + 16s + 4lg .. + 3 (8 bytes each, v[m]), beta of token ln.  They
-// are read through buffer resources whose record count ends at the sequence's last token, so a
-// token past the end (and every token of a tile past the end) reads as zero: with beta = 0 and
-// k = v = 0 it neither writes the state nor reaches a stored output, and with g = 0 it does not
-// decay the state.
+// as v[0], v[1]) or 64m + 16s + 4lg .. + 3 (8 bytes each, v[m]), and on stage-A wave 0 beta of
+// token ln.  They are read through buffer resources whose record count ends at the sequence's
+// last token, so a token past the end (and every token of a tile past the end) reads as zero:
+// with beta = 0 and k = v = 0 it neither writes the state nor reaches a stored output, and with
+// g = 0 it does not decay the state.
 struct Raw {
     uint4 q, k, g;
     uint2 v[2];
@@ -587,8 +587,9 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
 
     // stage B1 for tile `tile`: A, A^T, P^T over all 128 channels and the inverse T, in two
     // halves that run in consecutive periods (the registers in B1Carry cross the barrier).  Waves
-    // 8 and 9 take the even tiles and waves 10 and 11 the odd ones, so every SIMD runs one half
-    // per period; the two waves of a pair compute identical results.
+    // 8 and 9 take the even tiles and waves 10 and 11 the odd ones.  In the 64-column kernel both
+    // waves of a pair compute it (identical results), so every SIMD runs one half per period; the
+    // 128-column kernels run it on the first wave of each pair only.
     struct B1Carry { f32x4 N4, N4t, Gt, Pt, brow; float bcol; };
     auto stage_b1a = [&](int64_t tile) -> B1Carry {
         const FromA<NS>& A = fa(tile);
