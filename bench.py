@@ -552,11 +552,11 @@ def summarize_sq(dirs, command, wl=None):
     import csv
     import glob
     from linear_attention_recurrence_08_amd import inputs
-    wl = wl or "prefill_T4096_H96_d128_bf16"
-    x = inputs.make_workload(wl)
-    cu = x.cu_seqlens.tolist() if x.cu_seqlens is not None else None
-    lens = [b - a for a, b in zip(cu, cu[1:])] if cu else [x.T] * x.B
-    H = x.H
+    wl = wl or DEFAULT_WORKLOAD
+    w = inputs.WORKLOADS[wl]
+    lens = (inputs.varlen_lengths(w["seed"], w["n_seqs"]) if w["kind"] == "varlen"
+            else list(w["seq_lens"]))
+    H = w["H"]
     pairs = len(lens) * H
     halves = 1 if pairs >= 256 else 2
     wgs = halves * pairs

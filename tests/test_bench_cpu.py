@@ -142,3 +142,44 @@ def test_trace_summary_keeps_its_workloads_dispatches(tmp_path, monkeypatch):
                "kda_decode_step_layer_decode_N256_H96_d128_bf16_kernel_trace.md").read()
     row = [l for l in txt.splitlines() if l.startswith("| kda_decode_d128_kernel")][0]
     assert [c.strip() for c in row.split("|")[2:7]] == ["2", "550", "500", "600", "1100"]
+
+
+@pytest.mark.parametrize("wl,wgs,periods", [
+    # one sequence of 256 tiles, 96 heads in two 64-column halves
+    ("prefill_T4096_H96_d128_bf16", 192, 260.0),
+    # 16 sequences x 96 heads, one 128-column workgroup each; each walks its own tile count
+    # (rounded up to even) plus 4 periods
+    ("varlen_16seq_H96_d128_bf16", 1536, None)])
+def test_sq_summary_counts_each_workgroups_periods(tmp_path, monkeypatch, wl, wgs, periods):
+    from linear_attention_recurrence_08_amd import inputs
+    w = inputs.WORKLOADS[wl]
+    lens = (inputs.varlen_lengths(w["seed"], w["n_seqs"]) if w["kind"] == "varlen"
+            else w["seq_lens"])
+    halves = wgs // (len(lens) * w["H"])
+    total = halves * w["H"] * sum((n + 15) // 16 + ((n + 15) // 16) % 2 + 4 for n in lens)
+    if periods is not None:
+        assert total / wgs == periods
+    # every wave lives 2,000 cycles per period of its workgroup (the counter counts by 4)
+    counters = {"SQ_WAVES": 12 * wgs, "SQ_WAVE_CYCLES": 12 * total * 2000 / 4}
+    for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS",
+              "SQ_INSTS_SALU", "SQ_INSTS_VMEM", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+              "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_VALU_MFMA_BUSY_CYCLES",
+              "SQ_LDS_BANK_CONFLICT"):
+        counters[k] = 4 * total   # one per SIMD and period
+    d = tmp_path / "c"
+    d.mkdir()
+    with open(d / "x_counter_collection.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for k, v in counters.items():
+            wr.writerow({"Kernel_Name": "void kda::kda_prefill_mfma_kernel<1, 64, false>()",
+                         "Counter_Name": k, "Counter_Value": v})
+    out = tmp_path / "repo"
+    (out / "profiles").mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(out))
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda tag: "0123456789abcdef")
+    bench.summarize_sq([str(d)], "sq command", wl)
+    txt = open(out / "profiles" / f"kda_chunk_fwd_{wl}_sq_counters.md").read()
+    assert f"{wgs} workgroups" in txt and f"{total / wgs:.1f} pipeline periods" in txt
+    assert "a period of 2000 cycles" in txt
+    assert "| SQ_INSTS_VALU | " in txt and "| 1.0 |" in txt
