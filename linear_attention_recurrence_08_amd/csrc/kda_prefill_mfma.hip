@@ -905,8 +905,8 @@ __global__ __launch_bounds__(NT) void kda_prefill_mfma_kernel(PrefillArgs a) {
         // where stage B2 reads them (the carried registers stay with the wave that formed them).
         // In the 128-column kernel the second wave skips it: 1.3-1.8% faster on the 16-sequence
         // batch with bit-identical outputs.  In the 64-column kernel both keep it, one half per
-        // SIMD and period (skipping measured no faster at H = 96, and 0.2-0.4% slower at 12 and
-        // 64 heads).
+        // SIMD and period: skipping there measured 6.6% slower at H = 96 and 4.5% at 12 heads,
+        // probably because B1 then becomes a branch instead of straight-line code beside B2.
         const bool do_b1 = BVT == 64 || (s & 1) == 0;
         // the gate registers: GX holds the tiles loaded in the first period of each pair below,
         // GY those of the second (the pairs keep their order into the last loop)
